@@ -1,0 +1,267 @@
+"""CPU oracle for the RG-LRU temporal branch: causal depthwise Conv1D (width 4) -> RG-LRU.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import or run this module.  The HIP library never calls it, and it
+shares no code with the HIP path (no kernels, headers, helpers or constants).
+
+Plain, slow and sequential on purpose: NumPy, every operation in fp64, the recurrence a
+Python loop over time vectorised over (batch, channel), the gate projections one
+library matmul each.  No blocking, fusion or reordering beyond the definitions.
+
+Sources (cited by page title and section; no other source is used):
+  [ARCH]  "Griffin: Mixing Gated Linear Recurrences with Local Attention for Efficient
+          Language Models" - model-architecture page (Chinese translation of the
+          paper's Model Architecture section, downcodes.com):
+            section "Recurrent block"   : Conv1D of temporal width 4 before the RG-LRU,
+                                          only 4*D parameters (depthwise);
+            section "Real-Gated Linear Recurrent Unit (RG-LRU)": Eq. (1)-(4), output
+                                          y_t = h_t, a = sigma(Lambda), c = 8, a^{c r_t}
+                                          computed in log space, diagonal recurrence;
+            section "Gate behaviour"   : r_t -> 0 keeps the previous state.
+  [BLOG]  "Griffin's Compromise: Combining Gated Linear Recurrence with Local Attention"
+          (ql.gl): section "Hawk: Redesigning RNN State with Gates" (h_t = a_t h_{t-1} +
+          b_t x_t; generation reads and writes only the current token and a fixed-size
+          state) and "Term explanation: Parallel scan".
+
+Readings where the pages leave a step open (each also listed in the design notes):
+  * x_t in Eq. (1), (2) and (4) is the conv output u; the gates and the input term both
+    use u.  W is stored [out, in]: z = W u + b.
+  * "log space": log a_t = c * r_t * log sigma(Lambda), log sigma computed as
+    -log1p(exp(-Lambda)) (stable form); sqrt(1 - a_t^2) = sqrt(-expm1(2 log a_t)).
+  * Tap k of the conv multiplies x_{t-k}; history before the first token is the given
+    conv state (x_{-3}, x_{-2}, x_{-1}) or zeros.
+  * Rounding points of the I/O dtype: R1 - u is rounded to the I/O dtype (nearest-even)
+    and that rounded u feeds both the gates and the scan; R2 - y_t is h_t rounded to the
+    I/O dtype.  The state h and h_T stay unrounded.
+  * Backward (not on the pages): chain rule through the same definitions, R1 and R2
+    treated as identity; where m_t = sqrt(1 - a_t^2) = 0 the m-path term of d(log a_t)
+    is defined as 0.
+
+Parity pins: every function here is pinned by a test against closed forms, invariants,
+brute force or library routines (tests/test_oracle_pins.py, tests/test_oracle_grad.py).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+_BF16_MAX = 3.3895313892515355e38   # largest finite bf16
+_BF16_MIN_ULP_EXP = -133            # exponent of the smallest bf16 subnormal
+
+
+# ----------------------------------------------------------------------------------
+# I/O rounding (R1, R2)
+# ----------------------------------------------------------------------------------
+def round_io(v, io: str) -> np.ndarray:
+    """Round fp64 values to the I/O dtype, nearest-even, and return them as fp64.
+
+    bf16 keeps 8 significant bits and fp32's exponent range; fp32 is IEEE single.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    if io == "f64":                    # no rounding: used only by the gradient checks
+        return v.copy()
+    if io == "f32":
+        return v.astype(np.float32).astype(np.float64)
+    if io != "bf16":
+        raise ValueError(f"unknown io dtype {io!r}")
+    _, e = np.frexp(v)                              # |v| = m 2^e, 0.5 <= m < 1
+    ulp_exp = np.maximum(e - 8, _BF16_MIN_ULP_EXP)  # 8 significant bits
+    q = np.rint(np.ldexp(v, -ulp_exp))              # rint: ties to even
+    r = np.ldexp(q, ulp_exp)
+    return np.where(np.abs(r) > _BF16_MAX, np.copysign(np.inf, v), r)
+
+
+# ----------------------------------------------------------------------------------
+# Scalar functions of Eq. (1)-(3)
+# ----------------------------------------------------------------------------------
+def sigmoid(z) -> np.ndarray:
+    """sigma(z) = 1 / (1 + e^{-z})  ([ARCH] RG-LRU: the nonlinearity is the sigmoid).
+
+    Evaluated without overflow: 1/(1+e^{-z}) for z >= 0, e^{z}/(1+e^{z}) for z < 0.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    out = np.empty_like(z)
+    pos = z >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-z[pos]))
+    ez = np.exp(z[~pos])
+    out[~pos] = ez / (1.0 + ez)
+    return out
+
+
+def log_sigmoid(lam) -> np.ndarray:
+    """log sigma(Lambda), the log of the diagonal recurrent weight a = sigma(Lambda)
+    ([ARCH] RG-LRU, the parametrisation of a in Eq. (3); computed in log space)."""
+    lam = np.asarray(lam, dtype=np.float64)
+    return np.where(lam >= 0,
+                    -np.log1p(np.exp(-np.abs(lam))),
+                    lam - np.log1p(np.exp(-np.abs(lam))))
+
+
+def gates(zr, zi, lam, c):
+    """Eq. (1)-(3) and the input scaling of Eq. (4) from the pre-activations.
+
+    zr = W_a u + b_a, zi = W_x u + b_x  ->  r, i, log a, a, m = sqrt(1 - a^2).
+    log a_t = c * r_t * log sigma(Lambda)  (log space);  a_t = exp(log a_t);
+    m_t = sqrt(1 - a_t^2) = sqrt(-expm1(2 log a_t)).
+    """
+    r = sigmoid(zr)
+    i = sigmoid(zi)
+    L = log_sigmoid(lam)
+    ell = c * r * L
+    a = np.exp(ell)
+    m = np.sqrt(-np.expm1(2.0 * ell))
+    return r, i, ell, a, m
+
+
+# ----------------------------------------------------------------------------------
+# Conv1D of the recurrent block
+# ----------------------------------------------------------------------------------
+def _history(x, conv_state_in):
+    """X = [x_{-3}, x_{-2}, x_{-1}, x_0 .. x_{T-1}] along time, fp64, shape [B, T+3, D]."""
+    B, T, D = x.shape
+    hist = (np.zeros((B, 3, D)) if conv_state_in is None
+            else np.asarray(conv_state_in, dtype=np.float64))
+    return np.concatenate([hist, np.asarray(x, dtype=np.float64)], axis=1)
+
+
+def conv1d_causal4(x, conv_w, conv_b, conv_state_in, io):
+    """Causal depthwise Conv1D with temporal width 4 ([ARCH] "Recurrent block").
+
+    u[b,t,d] = conv_b[d] + sum_{k=0..3} conv_w[k,d] * X[b,t-k,d], then u is rounded to
+    the I/O dtype (R1).  Returns (u [B,T,D] fp64, conv_state_out [B,3,D] = the last three
+    time rows of [conv_state_in || x]).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    B, T, D = x.shape
+    X = _history(x, conv_state_in)
+    w = np.asarray(conv_w, dtype=np.float64)
+    u = np.zeros((B, T, D)) if conv_b is None else np.broadcast_to(
+        np.asarray(conv_b, dtype=np.float64), (B, T, D)).copy()
+    for k in range(4):
+        u += w[k] * X[:, 3 - k:3 - k + T, :]
+    return round_io(u, io), X[:, T:T + 3, :].copy()
+
+
+# ----------------------------------------------------------------------------------
+# Forward
+# ----------------------------------------------------------------------------------
+def forward(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, c, io,
+            channels=None, keep=False):
+    """The temporal branch forward: conv (R1) -> Eq. (1)-(4) -> y_t = h_t (R2).
+
+    x [B,T,D]; conv_w [4,D] or None (then x is already the RG-LRU input u); conv_b [D]
+    or None; conv_state_in [B,3,D] or None; W_a, W_x [D,D] ([out,in]); b_a, b_x, lam [D];
+    h0 [B,D] or None (zeros).  ``channels``: optional index array S of output channels;
+    every output is then restricted to S (channels are independent through the
+    diagonal recurrence, so the values on S do not depend on the other outputs).
+
+    Returns dict with y [B,T,|S|] (I/O-rounded, fp64), h_T [B,|S|] (fp64),
+    conv_state_out [B,3,D]; with keep=True also u, r, i, ell, a, m, h_prev.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    B, T, D = x.shape
+    S = np.arange(D) if channels is None else np.asarray(channels)
+    if conv_w is None:
+        u = x.copy()
+        cs_out = _history(x, conv_state_in)[:, T:T + 3, :].copy()
+    else:
+        u, cs_out = conv1d_causal4(x, conv_w, conv_b, conv_state_in, io)
+    Wa = np.asarray(W_a, dtype=np.float64)[S]
+    Wx = np.asarray(W_x, dtype=np.float64)[S]
+    zr = np.empty((B, T, len(S)))
+    zi = np.empty((B, T, len(S)))
+    for b in range(B):                                  # z = W u + b   (Eq. (1), (2))
+        zr[b] = u[b] @ Wa.T
+        zi[b] = u[b] @ Wx.T
+    zr += np.asarray(b_a, dtype=np.float64)[S]
+    zi += np.asarray(b_x, dtype=np.float64)[S]
+    r, i, ell, a, m = gates(zr, zi, np.asarray(lam, dtype=np.float64)[S], c)
+    uS = u[:, :, S]
+    h = np.zeros((B, len(S))) if h0 is None else np.asarray(h0, dtype=np.float64)[:, S].copy()
+    y = np.empty((B, T, len(S)))
+    h_prev = np.empty((B, T, len(S))) if keep else None
+    for t in range(T):                                   # Eq. (4), sequential in t
+        if keep:
+            h_prev[:, t] = h
+        h = a[:, t] * h + m[:, t] * (i[:, t] * uS[:, t])
+        y[:, t] = h
+    out = {"y": round_io(y, io), "h_T": h, "conv_state_out": cs_out}
+    if keep:
+        out.update(u=u, r=r, i=i, ell=ell, a=a, m=m, h_prev=h_prev, y_exact=y)
+    return out
+
+
+def decode_step(x_t, conv_w, conv_b, conv_state, W_a, W_x, b_a, b_x, lam, h, c, io):
+    """One generation step with the fixed-size state ([BLOG] "Hawk": generation reads and
+    writes only the current token and a fixed-size state).
+
+    x_t [B,D]; conv_state [B,3,D] (x_{t-3}, x_{t-2}, x_{t-1}); h [B,D].  The step is the
+    forward above on a length-1 sequence with the carried state.
+    Returns (y_t [B,D], new conv_state [B,3,D], new h [B,D]).
+    """
+    o = forward(np.asarray(x_t, dtype=np.float64)[:, None, :], conv_w, conv_b, conv_state,
+                W_a, W_x, b_a, b_x, lam, h, c, io)
+    return o["y"][:, 0, :], o["conv_state_out"], o["h_T"]
+
+
+# ----------------------------------------------------------------------------------
+# Backward (chain rule through the same definitions; the pages state no backward)
+# ----------------------------------------------------------------------------------
+def backward(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, c, io,
+             dy, dh_T=None):
+    """Gradients of sum(dy * y) + sum(dh_T * h_T) with respect to every input.
+
+    R1 and R2 act as identity in the backward.  Let G_t be the total derivative with
+    respect to h_t: G_t = dy_t + a_{t+1} G_{t+1}, G_{T-1} = dy_{T-1} + dh_T, dh0 = a_0 G_0.
+      d(log a_t) = G_t (a_t h_{t-1} - (a_t^2 / m_t) i_t u_t)   [m-path term 0 where m_t=0]
+      dr = c L d(log a), dL = sum c r d(log a), dLambda = dL * sigma(-Lambda)
+      dzr = dr r (1-r), dzi = G m u i (1-i), db = sum dz, dW = sum dz (x) u
+      du = G m i + W_a^T dzr + W_x^T dzi
+      dconv_w[k] = sum du_t X_{t-k}, dconv_b = sum du, dx_tau = sum_k w[k] du_{tau+k}.
+    Returns dict dx [B,T,D], dconv_w [4,D], dconv_b [D], dW_a, dW_x [D,D], db_a, db_x,
+    dlambda [D], dh0 [B,D]; all fp64.
+    """
+    f = forward(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, c, io,
+                keep=True)
+    u, r, i, a, m, hp = f["u"], f["r"], f["i"], f["a"], f["m"], f["h_prev"]
+    B, T, D = u.shape
+    dy = np.asarray(dy, dtype=np.float64)
+    g = np.zeros((B, D)) if dh_T is None else np.asarray(dh_T, dtype=np.float64).copy()
+    G = np.empty((B, T, D))
+    for t in range(T - 1, -1, -1):                      # reverse-time recurrence
+        g = g + dy[:, t]
+        G[:, t] = g
+        g = a[:, t] * g
+    dh0 = g
+    L = log_sigmoid(lam)
+    safe_m = np.where(m > 0, m, 1.0)
+    m_term = np.where(m > 0, (a * a / safe_m) * i * u, 0.0)
+    dell = G * (a * hp - m_term)
+    dr = c * L * dell
+    dL = (c * r * dell).sum(axis=(0, 1))
+    dlam = dL * sigmoid(-np.asarray(lam, dtype=np.float64))
+    di = G * m * u
+    dzr = dr * r * (1.0 - r)
+    dzi = di * i * (1.0 - i)
+    Wa = np.asarray(W_a, dtype=np.float64)
+    Wx = np.asarray(W_x, dtype=np.float64)
+    dW_a = np.zeros((D, D))
+    dW_x = np.zeros((D, D))
+    du = G * m * i
+    for b in range(B):
+        dW_a += dzr[b].T @ u[b]
+        dW_x += dzi[b].T @ u[b]
+        du[b] += dzr[b] @ Wa + dzi[b] @ Wx
+    out = {"dW_a": dW_a, "dW_x": dW_x, "db_a": dzr.sum(axis=(0, 1)),
+           "db_x": dzi.sum(axis=(0, 1)), "dlambda": dlam, "dh0": dh0}
+    if conv_w is None:
+        out.update(dx=du, dconv_w=None, dconv_b=None)
+        return out
+    X = _history(x, conv_state_in)
+    w = np.asarray(conv_w, dtype=np.float64)
+    dconv_w = np.empty((4, D))
+    dx = np.zeros((B, T, D))
+    for k in range(4):
+        dconv_w[k] = (du * X[:, 3 - k:3 - k + T, :]).sum(axis=(0, 1))
+        dx[:, :T - k, :] += w[k] * du[:, k:, :]
+    out.update(dx=dx, dconv_w=dconv_w, dconv_b=du.sum(axis=(0, 1)))
+    return out
