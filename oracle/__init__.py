@@ -3,5 +3,5 @@
 Only tests/, the smoke check and the benchmark's CPU-baseline leg may import this
 package; the HIP library never does.
 """
-from .rglru_oracle import (round_io, sigmoid, log_sigmoid, gates, conv1d_causal4,  # noqa: F401
+from .rglru_oracle import (round_io, fma_f32, sigmoid, log_sigmoid, gates, conv1d_causal4,  # noqa: F401
                            forward, decode_step, backward)

@@ -32,7 +32,9 @@ Readings where the pages leave a step open (each also listed in the design notes
     conv state (x_{-3}, x_{-2}, x_{-1}) or zeros.
   * Rounding points of the I/O dtype: R1 - u is rounded to the I/O dtype (nearest-even)
     and that rounded u feeds both the gates and the scan; R2 - y_t is h_t rounded to the
-    I/O dtype.  The state h and h_T stay unrounded.
+    I/O dtype.  The state h and h_T stay unrounded.  R1 is a quantisation decision, so
+    the value it rounds is the conv sum in the kernels' precision (an fp32 fma chain);
+    everything else is fp64.
   * Backward (not on the pages): chain rule through the same definitions, R1 and R2
     treated as identity; where m_t = sqrt(1 - a_t^2) = 0 the m-path term of d(log a_t)
     is defined as 0.
@@ -123,12 +125,47 @@ def _history(x, conv_state_in):
     return np.concatenate([hist, np.asarray(x, dtype=np.float64)], axis=1)
 
 
+def fma_f32(a, b, c) -> np.ndarray:
+    """IEEE single-precision fused multiply-add round_f32(a*b + c), for fp32 inputs.
+
+    a*b is exact in fp64 (24 + 24 significant bits); the sum's fp64 rounding error e is
+    recovered exactly (Knuth's TwoSum), and rounding s + e to fp32 differs from rounding s
+    only when s is an exact fp32 halfway point, where the sign of e decides.  Results must
+    stay in fp32's normal range (checked).
+    """
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    c = np.asarray(c, dtype=np.float64)
+    p = a * b
+    s = p + c
+    bb = s - p
+    e = (p - (s - bb)) + (c - bb)
+    r = s.astype(np.float32).astype(np.float64)
+    bits = np.ascontiguousarray(s).view(np.uint64)
+    tie = (bits & np.uint64((1 << 29) - 1)) == np.uint64(1 << 28)
+    fix = tie & (e != 0)
+    if np.any(fix):
+        down = (bits & ~np.uint64((1 << 29) - 1)).view(np.float64)     # toward zero
+        away = np.where(down > 0, np.inf, -np.inf).astype(np.float32)
+        up = np.nextafter(down.astype(np.float32), away).astype(np.float64)   # away from zero
+        toward_larger = (e > 0) == (s > 0)                                # |s + e| > |s|
+        r = np.where(fix, np.where(toward_larger, up, down), r)
+    big = np.abs(r) >= 2.0 ** -126
+    if not np.all(big | (r == 0)):
+        raise ValueError("fp32 fma emulation left the normal range")
+    return r
+
+
 def conv1d_causal4(x, conv_w, conv_b, conv_state_in, io):
     """Causal depthwise Conv1D with temporal width 4 ([ARCH] "Recurrent block").
 
     u[b,t,d] = conv_b[d] + sum_{k=0..3} conv_w[k,d] * X[b,t-k,d], then u is rounded to
     the I/O dtype (R1).  Returns (u [B,T,D] fp64, conv_state_out [B,3,D] = the last three
     time rows of [conv_state_in || x]).
+
+    R1 quantises u, so the value it rounds is taken in the precision the kernels compute it
+    in: for fp32 and bf16 I/O the sum is the fp32 chain acc = b; acc = fma(w_k, x_{t-k},
+    acc) for k = 0..3, each step rounded once; io="f64" (gradient checks) sums in fp64.
     """
     x = np.asarray(x, dtype=np.float64)
     B, T, D = x.shape
@@ -137,7 +174,10 @@ def conv1d_causal4(x, conv_w, conv_b, conv_state_in, io):
     u = np.zeros((B, T, D)) if conv_b is None else np.broadcast_to(
         np.asarray(conv_b, dtype=np.float64), (B, T, D)).copy()
     for k in range(4):
-        u += w[k] * X[:, 3 - k:3 - k + T, :]
+        if io == "f64":
+            u += w[k] * X[:, 3 - k:3 - k + T, :]
+        else:
+            u = fma_f32(w[k], X[:, 3 - k:3 - k + T, :], u)
     return round_io(u, io), X[:, T:T + 3, :].copy()
 
 

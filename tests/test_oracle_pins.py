@@ -300,3 +300,46 @@ def test_output_rounding_points():
     o = _fwd(p, keep=True)
     np.testing.assert_array_equal(o["y"], oracle.round_io(o["y_exact"], "bf16"))
     np.testing.assert_array_equal(o["u"], oracle.round_io(o["u"], "bf16"))
+
+
+# ---------------------------------------------------------------- fp32 fma emulation (R1 input)
+def _round_f32_exact(fr):
+    """Nearest fp32 (ties to even) of an exact rational, by integer arithmetic."""
+    from fractions import Fraction
+    if fr == 0:
+        return 0.0
+    sign = -1.0 if fr < 0 else 1.0
+    mag = abs(fr)
+    e = mag.numerator.bit_length() - mag.denominator.bit_length()
+    if Fraction(2) ** e > mag:
+        e -= 1
+    ulp = Fraction(2) ** (e - 23)
+    q = mag / ulp
+    n = q.numerator // q.denominator
+    rem = q - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return sign * float(n * ulp)
+
+
+def test_fma_f32_matches_exact_rational_rounding():
+    from fractions import Fraction
+    rng = np.random.default_rng(40)
+    n = 3000
+    a = (rng.standard_normal(n) * 2.0 ** rng.integers(-20, 20, n)).astype(np.float32)
+    b = (rng.standard_normal(n) * 2.0 ** rng.integers(-20, 20, n)).astype(np.float32)
+    c = (rng.standard_normal(n) * 2.0 ** rng.integers(-40, 40, n)).astype(np.float32)
+    # constructed halfway cases: fp64 rounding of a*b + c lands exactly on an fp32 midpoint
+    # while the exact value lies just below (a naive double rounding picks the wrong side)
+    ta = np.array([1 + 2.0 ** -23, -(1 + 2.0 ** -23), 1 + 2.0 ** -23], dtype=np.float32)
+    tb = np.array([2.0 ** -24 * (1 - 2.0 ** -23), 2.0 ** -24 * (1 - 2.0 ** -23),
+                   -(2.0 ** -24) * (1 - 2.0 ** -23)], dtype=np.float32)
+    tc = np.array([1 + 2.0 ** -23, -(1 + 2.0 ** -23), 1 + 2.0 ** -21], dtype=np.float32)
+    a, b, c = np.concatenate([a, ta]), np.concatenate([b, tb]), np.concatenate([c, tc])
+    got = oracle.fma_f32(a, b, c)
+    want = np.array([_round_f32_exact(Fraction(float(x)) * Fraction(float(y)) + Fraction(float(z)))
+                     for x, y, z in zip(a, b, c)])
+    np.testing.assert_array_equal(got, want)
+    assert got[-3] == np.float32(1 + 2.0 ** -23)          # not the even neighbour 1 + 2^-22
+    naive = (a.astype(np.float64) * b + c).astype(np.float32)
+    assert np.any(naive != got)                             # the cases do discriminate
