@@ -1,0 +1,10 @@
+"""MI355X (gfx950) RG-LRU temporal branch: causal Conv1D (width 4) -> RG-LRU.
+
+The compute path is librglru.so (hand-written HIP kernels behind a C ABI, declared in
+include/rglru.h); this package is its thin ctypes binding.  Importing the package does not
+load the library; load() (or the first call) does, and raises if it is not built.
+"""
+from ._binding import (EXPORTS, LIB_PATH, RGLRU_BF16, RGLRU_F32, RgluError,  # noqa: F401
+                       backward, bwd_workspace_bytes, conv1d_causal4, decode_workspace_bytes,
+                       forward, fwd_workspace_bytes, io_code, load, rglru_bwd,
+                       rglru_decode_step, rglru_fwd, status_string, workspace)

@@ -1,0 +1,175 @@
+"""ctypes binding of librglru.so: the same entry points as include/rglru.h.
+
+Argument marshalling only: every step of the temporal branch runs in the HIP kernels of
+librglru.so.  Tensors are torch tensors already on the GPU (torch provides device memory
+and the stream); there is no fallback path: if the library is missing, load() raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librglru.so")
+
+RGLRU_F32, RGLRU_BF16 = 0, 1
+_IO = {torch.float32: RGLRU_F32, torch.bfloat16: RGLRU_BF16}
+
+# Symbols declared in include/rglru.h.
+EXPORTS = ("rglru_status_string", "conv1d_causal4", "rglru_fwd_workspace_bytes", "rglru_fwd",
+           "rglru_decode_workspace_bytes", "rglru_decode_step", "rglru_bwd_workspace_bytes",
+           "rglru_bwd")
+
+_lib = None
+_P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+
+class RgluError(RuntimeError):
+    pass
+
+
+def load(path: str = LIB_PATH):
+    """Load librglru.so (once) and declare every entry point's signature."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RgluError(f"{path} is not built; run `python -m gated_linear_rnn_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.rglru_status_string.argtypes = [_I]
+    lib.rglru_status_string.restype = ctypes.c_char_p
+    lib.conv1d_causal4.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]
+    lib.conv1d_causal4.restype = _I
+    lib.rglru_fwd_workspace_bytes.argtypes = [_I, _I, _I, _I]
+    lib.rglru_fwd_workspace_bytes.restype = _Z
+    lib.rglru_fwd.argtypes = [_I, _I, _I, _I, _F] + [_P] * 13 + [_P, _Z, _P]
+    lib.rglru_fwd.restype = _I
+    lib.rglru_decode_workspace_bytes.argtypes = [_I, _I, _I]
+    lib.rglru_decode_workspace_bytes.restype = _Z
+    lib.rglru_decode_step.argtypes = [_I, _I, _I, _F] + [_P] * 11 + [_P, _Z, _P]
+    lib.rglru_decode_step.restype = _I
+    lib.rglru_bwd_workspace_bytes.argtypes = [_I, _I, _I, _I]
+    lib.rglru_bwd_workspace_bytes.restype = _Z
+    lib.rglru_bwd.argtypes = [_I, _I, _I, _I, _F] + [_P] * 21 + [_P, _Z, _P]
+    lib.rglru_bwd.restype = _I
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load().rglru_status_string(int(code)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise RgluError(f"{what} failed: {status_string(code)} ({code})")
+
+
+def io_code(dtype) -> int:
+    if dtype not in _IO:
+        raise RgluError(f"unsupported I/O dtype {dtype}")
+    return _IO[dtype]
+
+
+# ------------------------------------------------------------------ workspace queries
+def fwd_workspace_bytes(B, T, D, dtype) -> int:
+    return int(load().rglru_fwd_workspace_bytes(B, T, D, io_code(dtype)))
+
+
+def decode_workspace_bytes(B, D, dtype) -> int:
+    return int(load().rglru_decode_workspace_bytes(B, D, io_code(dtype)))
+
+
+def bwd_workspace_bytes(B, T, D, dtype) -> int:
+    return int(load().rglru_bwd_workspace_bytes(B, T, D, io_code(dtype)))
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ entry points
+def conv1d_causal4(x, w, b, state_in, u, state_out, stream=None):
+    B, T, D = x.shape
+    _check(load().conv1d_causal4(B, T, D, io_code(x.dtype), _ptr(x), _ptr(w), _ptr(b),
+                                 _ptr(state_in), _ptr(u), _ptr(state_out), _stream(stream)),
+           "conv1d_causal4")
+
+
+def rglru_fwd(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, y, h_T,
+              conv_state_out, ws, c=8.0, stream=None):
+    B, T, D = x.shape
+    _check(load().rglru_fwd(B, T, D, io_code(x.dtype), float(c), _ptr(x), _ptr(conv_w),
+                            _ptr(conv_b), _ptr(conv_state_in), _ptr(W_a), _ptr(W_x), _ptr(b_a),
+                            _ptr(b_x), _ptr(lam), _ptr(h0), _ptr(y), _ptr(h_T),
+                            _ptr(conv_state_out), _ptr(ws), ws.numel(), _stream(stream)),
+           "rglru_fwd")
+
+
+def rglru_decode_step(x_t, conv_w, conv_b, conv_state, W_a, W_x, b_a, b_x, lam, h, y_t, ws,
+                      c=8.0, stream=None):
+    B, D = x_t.shape
+    _check(load().rglru_decode_step(B, D, io_code(x_t.dtype), float(c), _ptr(x_t), _ptr(conv_w),
+                                    _ptr(conv_b), _ptr(conv_state), _ptr(W_a), _ptr(W_x),
+                                    _ptr(b_a), _ptr(b_x), _ptr(lam), _ptr(h), _ptr(y_t),
+                                    _ptr(ws), ws.numel(), _stream(stream)),
+           "rglru_decode_step")
+
+
+def rglru_bwd(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, dy, dh_T, dx,
+              dconv_w, dconv_b, dW_a, dW_x, db_a, db_x, dlam, dh0, ws, c=8.0, stream=None):
+    B, T, D = x.shape
+    _check(load().rglru_bwd(B, T, D, io_code(x.dtype), float(c), _ptr(x), _ptr(conv_w),
+                            _ptr(conv_b), _ptr(conv_state_in), _ptr(W_a), _ptr(W_x), _ptr(b_a),
+                            _ptr(b_x), _ptr(lam), _ptr(h0), _ptr(dy), _ptr(dh_T), _ptr(dx),
+                            _ptr(dconv_w), _ptr(dconv_b), _ptr(dW_a), _ptr(dW_x), _ptr(db_a),
+                            _ptr(db_x), _ptr(dlam), _ptr(dh0), _ptr(ws), ws.numel(),
+                            _stream(stream)),
+           "rglru_bwd")
+
+
+# ------------------------------------------------------------------ allocating helpers
+def forward(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0=None, c=8.0,
+            ws=None, stream=None):
+    """Allocate y, h_T, conv_state_out (and the workspace unless given), run rglru_fwd."""
+    B, T, D = x.shape
+    y = torch.empty_like(x)
+    h_T = torch.empty((B, D), dtype=torch.float32, device=x.device)
+    cs_out = torch.empty((B, 3, D), dtype=x.dtype, device=x.device) if conv_w is not None else None
+    if ws is None:
+        ws = workspace(fwd_workspace_bytes(B, T, D, x.dtype), x.device)
+    rglru_fwd(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, y, h_T, cs_out, ws,
+              c, stream)
+    return y, h_T, cs_out
+
+
+def backward(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, dy, dh_T=None,
+             c=8.0, ws=None, stream=None):
+    """Allocate every gradient (fp32) and run rglru_bwd; returns a dict."""
+    B, T, D = x.shape
+    dev = x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"dx": torch.empty((B, T, D), **f32),
+         "dconv_w": torch.empty((4, D), **f32) if conv_w is not None else None,
+         "dconv_b": torch.empty((D,), **f32) if conv_w is not None else None,
+         "dW_a": torch.empty((D, D), **f32), "dW_x": torch.empty((D, D), **f32),
+         "db_a": torch.empty((D,), **f32), "db_x": torch.empty((D,), **f32),
+         "dlambda": torch.empty((D,), **f32), "dh0": torch.empty((B, D), **f32)}
+    if ws is None:
+        ws = workspace(bwd_workspace_bytes(B, T, D, x.dtype), dev)
+    rglru_bwd(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, dy, dh_T, g["dx"],
+              g["dconv_w"], g["dconv_b"], g["dW_a"], g["dW_x"], g["db_a"], g["db_x"],
+              g["dlambda"], g["dh0"], ws, c, stream)
+    return g

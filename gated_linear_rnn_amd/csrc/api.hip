@@ -1,0 +1,385 @@
+// C ABI of librglru.so: argument validation, workspace carving and launch orchestration
+// on the caller's stream.  Every entry point validates all arguments before the first
+// HIP call and never allocates device memory.  Declarations and the contract of each
+// entry point are in include/rglru.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/rglru.h"
+#include "kernels.h"
+#include "rglru_device.h"
+
+using namespace rglru;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t io_bytes(rglru_dtype io) { return io == RGLRU_BF16 ? 2 : 4; }
+bool io_ok(int io) { return io == RGLRU_F32 || io == RGLRU_BF16; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Bump allocator over the caller's workspace; with base == nullptr it only measures.
+struct Carver {
+  unsigned char* base;
+  size_t used = 0;
+  explicit Carver(void* b) : base(static_cast<unsigned char*>(b)) {}
+  template <typename T>
+  T* take(size_t count) {
+    used = (used + kAlign - 1) / kAlign * kAlign;
+    T* p = base ? reinterpret_cast<T*>(base + used) : nullptr;
+    used += count * sizeof(T);
+    return p;
+  }
+};
+
+int shape_status(int B, int T, int D) {
+  if (B <= 0 || T <= 0 || D <= 0) return RGLRU_EINVAL;
+  if (D % 64 != 0) return RGLRU_ESHAPE;
+  if (int64_t(B) * T * D >= (int64_t(1) << 31)) return RGLRU_ESHAPE;
+  return RGLRU_OK;
+}
+
+bool c_ok(float c) { return c >= 0.f && isfinite(c); }
+
+#define RG_CHECK(expr)                                   \
+  do {                                                   \
+    if ((expr) != hipSuccess) return RGLRU_EHIP;         \
+  } while (0)
+
+// ------------------------------------------------------------------ forward
+struct FwdWs {
+  void* u;
+  float* a;      // fp32 io: z^a, then a in place
+  float* beta;   // fp32 io: z^x, then beta in place
+  uint32_t* status;
+  uint32_t* counter;
+};
+
+FwdWs carve_fwd(Carver& cv, int B, int T, int D, rglru_dtype io) {
+  const size_t n = size_t(B) * T * D;
+  FwdWs w;
+  w.u = cv.take<unsigned char>(n * io_bytes(io));
+  w.a = cv.take<float>(n);
+  w.beta = cv.take<float>(n);
+  w.status = cv.take<uint32_t>(scan_status_words(B, T, D));
+  w.counter = cv.take<uint32_t>(64);
+  return w;
+}
+
+// The gate projection for M rows: out0/out1 per the epilogue kind.
+int gate_projection(rglru_dtype io, GateGemmArgs g, int epi, bool small_m, float* zscratch_a,
+                    float* zscratch_x, hipStream_t s) {
+  if (io == RGLRU_BF16) {
+    RG_CHECK(launch_gate_gemm_bf16(g, epi, small_m, s));
+    return RGLRU_OK;
+  }
+  PlainGemmArgs pa{};
+  pa.A = g.U; pa.Bm = g.Wa; pa.M = g.M; pa.N = g.N; pa.K = g.K;
+  pa.lda = g.K; pa.ldb = g.K; pa.ldc = g.N; pa.C = zscratch_a;
+  RG_CHECK(launch_plain_gemm_f32(pa, s));
+  pa.Bm = g.Wx; pa.C = zscratch_x;
+  RG_CHECK(launch_plain_gemm_f32(pa, s));
+  RG_CHECK(launch_gate_elementwise_f32(g, zscratch_a, zscratch_x, epi, s));
+  return RGLRU_OK;
+}
+
+// ------------------------------------------------------------------ backward
+struct BwdWs {
+  void* u;
+  float* r;
+  float* i;
+  float* h_all;
+  void* dz_hi;   // [M, 2D] (bf16) or fp32 dz
+  void* dz_lo;   // [M, 2D] bf16 (bf16 io only)
+  void* dzT_hi;  // [2D, Mp]
+  void* dzT_lo;
+  void* uT;      // [D, Mp]
+  void* WT;      // [D, 2D]
+  float* du;     // [M, D]
+  double* scan_part;
+  double* conv_part;
+  uint32_t* status;
+  uint32_t* counter;
+};
+
+BwdWs carve_bwd(Carver& cv, int B, int T, int D, rglru_dtype io) {
+  const size_t M = size_t(B) * T, n = M * D, Mp = (M + 63) / 64 * 64;
+  const size_t eb = io_bytes(io);
+  const size_t P = size_t(B) * scan_chunks(T);
+  BwdWs w;
+  w.u = cv.take<unsigned char>(n * eb);
+  w.r = cv.take<float>(n);
+  w.i = cv.take<float>(n);
+  w.h_all = cv.take<float>(n);
+  w.dz_hi = cv.take<unsigned char>(2 * n * eb);
+  w.dz_lo = io == RGLRU_BF16 ? cv.take<unsigned char>(2 * n * eb) : nullptr;
+  w.dzT_hi = cv.take<unsigned char>(2 * size_t(D) * Mp * eb);
+  w.dzT_lo = io == RGLRU_BF16 ? cv.take<unsigned char>(2 * size_t(D) * Mp * eb) : nullptr;
+  w.uT = cv.take<unsigned char>(size_t(D) * Mp * eb);
+  w.WT = cv.take<unsigned char>(2 * size_t(D) * D * eb);
+  w.du = cv.take<float>(n);
+  w.scan_part = cv.take<double>(P * 3 * D);
+  w.conv_part = cv.take<double>(P * 5 * D);
+  w.status = cv.take<uint32_t>(scan_status_words(B, T, D));
+  w.counter = cv.take<uint32_t>(64);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rglru_status_string(int status) {
+  switch (status) {
+    case RGLRU_OK: return "RGLRU_OK";
+    case RGLRU_EINVAL: return "RGLRU_EINVAL: invalid argument (null pointer, non-positive size, misaligned pointer or bad c)";
+    case RGLRU_ESHAPE: return "RGLRU_ESHAPE: unsupported shape (D % 64 != 0 or B*T*D >= 2^31)";
+    case RGLRU_EDTYPE: return "RGLRU_EDTYPE: unknown I/O dtype";
+    case RGLRU_EWORKSPACE: return "RGLRU_EWORKSPACE: workspace missing or too small";
+    case RGLRU_EHIP: return "RGLRU_EHIP: HIP launch or runtime error";
+    case RGLRU_EINTERNAL: return "RGLRU_EINTERNAL: internal error";
+    default: return "unknown rglru status";
+  }
+}
+
+int conv1d_causal4(int B, int T, int D, rglru_dtype io, const void* x, const void* w,
+                   const float* b, const void* state_in, void* u, void* state_out,
+                   hipStream_t stream) {
+  int st = shape_status(B, T, D);
+  if (st != RGLRU_OK) return st;
+  if (!io_ok(io)) return RGLRU_EDTYPE;
+  if (!x || !w || !u) return RGLRU_EINVAL;
+  for (const void* p : {x, w, (const void*)b, state_in, (const void*)u, (const void*)state_out})
+    if (p && !aligned16(p)) return RGLRU_EINVAL;
+  if (io == RGLRU_BF16) RG_CHECK(launch_conv_fwd<bf16_t>(B, T, D, x, w, b, state_in, u, state_out, stream));
+  else RG_CHECK(launch_conv_fwd<float>(B, T, D, x, w, b, state_in, u, state_out, stream));
+  return RGLRU_OK;
+}
+
+size_t rglru_fwd_workspace_bytes(int B, int T, int D, rglru_dtype io) {
+  if (shape_status(B, T, D) != RGLRU_OK || !io_ok(io)) return 0;
+  Carver cv(nullptr);
+  carve_fwd(cv, B, T, D, io);
+  return cv.used;
+}
+
+int rglru_fwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const void* conv_w,
+              const float* conv_b, const void* conv_state_in, const void* W_a, const void* W_x,
+              const float* b_a, const float* b_x, const float* lambda, const float* h0, void* y,
+              float* h_T, void* conv_state_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = shape_status(B, T, D);
+  if (st != RGLRU_OK) return st;
+  if (!io_ok(io)) return RGLRU_EDTYPE;
+  if (!x || !W_a || !W_x || !b_a || !b_x || !lambda || !y || !c_ok(c)) return RGLRU_EINVAL;
+  for (const void* p : {x, conv_w, (const void*)conv_b, conv_state_in, W_a, W_x, (const void*)b_a,
+                        (const void*)b_x, (const void*)lambda, (const void*)h0, (const void*)y,
+                        (const void*)h_T, (const void*)conv_state_out, (const void*)ws})
+    if (p && !aligned16(p)) return RGLRU_EINVAL;
+  if (!ws || ws_bytes < rglru_fwd_workspace_bytes(B, T, D, io)) return RGLRU_EWORKSPACE;
+
+  Carver cv(ws);
+  FwdWs w = carve_fwd(cv, B, T, D, io);
+  const int M = B * T;
+  const void* u = x;
+  if (conv_w) {
+    if (io == RGLRU_BF16)
+      RG_CHECK(launch_conv_fwd<bf16_t>(B, T, D, x, conv_w, conv_b, conv_state_in, w.u, conv_state_out, stream));
+    else
+      RG_CHECK(launch_conv_fwd<float>(B, T, D, x, conv_w, conv_b, conv_state_in, w.u, conv_state_out, stream));
+    u = w.u;
+  }
+  GateGemmArgs g{};
+  g.U = u; g.Wa = W_a; g.Wx = W_x; g.M = M; g.N = D; g.K = D;
+  g.ba = b_a; g.bx = b_x; g.lam = lambda; g.c = c;
+  g.out0 = w.a; g.out1 = w.beta;
+  st = gate_projection(io, g, kEpiAB, false, w.a, w.beta, stream);
+  if (st != RGLRU_OK) return st;
+
+  ScanFwdArgs sa{};
+  sa.B = B; sa.T = T; sa.D = D;
+  sa.x = x; sa.conv_w = conv_w; sa.conv_b = conv_b; sa.conv_state = conv_w ? conv_state_in : nullptr;
+  sa.a = w.a; sa.beta = w.beta; sa.from_ri = false; sa.lam = lambda; sa.c = c;
+  sa.h0 = h0; sa.y = y; sa.h_all = nullptr; sa.h_T = h_T;
+  sa.status = w.status; sa.counter = w.counter;
+  if (io == RGLRU_BF16) RG_CHECK(launch_scan_fwd<bf16_t>(sa, stream));
+  else RG_CHECK(launch_scan_fwd<float>(sa, stream));
+  return RGLRU_OK;
+}
+
+size_t rglru_decode_workspace_bytes(int B, int D, rglru_dtype io) {
+  if (shape_status(B, 1, D) != RGLRU_OK || !io_ok(io)) return 0;
+  Carver cv(nullptr);
+  cv.take<unsigned char>(size_t(B) * D * io_bytes(io));
+  if (io == RGLRU_F32) {
+    cv.take<float>(size_t(B) * D);
+    cv.take<float>(size_t(B) * D);
+  }
+  return cv.used;
+}
+
+int rglru_decode_step(int B, int D, rglru_dtype io, float c, const void* x_t, const void* conv_w,
+                      const float* conv_b, void* conv_state, const void* W_a, const void* W_x,
+                      const float* b_a, const float* b_x, const float* lambda, float* h,
+                      void* y_t, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = shape_status(B, 1, D);
+  if (st != RGLRU_OK) return st;
+  if (!io_ok(io)) return RGLRU_EDTYPE;
+  if (!x_t || !W_a || !W_x || !b_a || !b_x || !lambda || !h || !y_t || !c_ok(c)) return RGLRU_EINVAL;
+  if (conv_w && !conv_state) return RGLRU_EINVAL;
+  for (const void* p : {x_t, conv_w, (const void*)conv_b, (const void*)conv_state, W_a, W_x,
+                        (const void*)b_a, (const void*)b_x, (const void*)lambda, (const void*)h,
+                        (const void*)y_t, (const void*)ws})
+    if (p && !aligned16(p)) return RGLRU_EINVAL;
+  if (!ws || ws_bytes < rglru_decode_workspace_bytes(B, D, io)) return RGLRU_EWORKSPACE;
+
+  Carver cv(ws);
+  void* ubuf = cv.take<unsigned char>(size_t(B) * D * io_bytes(io));
+  float* za = io == RGLRU_F32 ? cv.take<float>(size_t(B) * D) : nullptr;
+  float* zx = io == RGLRU_F32 ? cv.take<float>(size_t(B) * D) : nullptr;
+  const void* u = x_t;
+  if (conv_w) {
+    if (io == RGLRU_BF16) RG_CHECK(launch_conv_decode<bf16_t>(B, D, x_t, conv_w, conv_b, conv_state, ubuf, stream));
+    else RG_CHECK(launch_conv_decode<float>(B, D, x_t, conv_w, conv_b, conv_state, ubuf, stream));
+    u = ubuf;
+  }
+  GateGemmArgs g{};
+  g.U = u; g.Wa = W_a; g.Wx = W_x; g.M = B; g.N = D; g.K = D;
+  g.ba = b_a; g.bx = b_x; g.lam = lambda; g.c = c;
+  g.u = u; g.h = h; g.y = y_t;
+  return gate_projection(io, g, kEpiDecode, B <= 1024, za, zx, stream);
+}
+
+size_t rglru_bwd_workspace_bytes(int B, int T, int D, rglru_dtype io) {
+  if (shape_status(B, T, D) != RGLRU_OK || !io_ok(io)) return 0;
+  Carver cv(nullptr);
+  carve_bwd(cv, B, T, D, io);
+  return cv.used;
+}
+
+int rglru_bwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const void* conv_w,
+              const float* conv_b, const void* conv_state_in, const void* W_a, const void* W_x,
+              const float* b_a, const float* b_x, const float* lambda, const float* h0,
+              const void* dy, const float* dh_T, float* dx, float* dconv_w, float* dconv_b,
+              float* dW_a, float* dW_x, float* db_a, float* db_x, float* dlambda, float* dh0,
+              void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = shape_status(B, T, D);
+  if (st != RGLRU_OK) return st;
+  if (!io_ok(io)) return RGLRU_EDTYPE;
+  if (!x || !W_a || !W_x || !b_a || !b_x || !lambda || !dy || !dx || !dW_a || !dW_x || !db_a ||
+      !db_x || !dlambda || !c_ok(c))
+    return RGLRU_EINVAL;
+  if (conv_w && (!dconv_w || !dconv_b)) return RGLRU_EINVAL;
+  for (const void* p : {x, conv_w, (const void*)conv_b, conv_state_in, W_a, W_x, (const void*)b_a,
+                        (const void*)b_x, (const void*)lambda, (const void*)h0, dy, (const void*)dh_T,
+                        (const void*)dx, (const void*)dconv_w, (const void*)dconv_b,
+                        (const void*)dW_a, (const void*)dW_x, (const void*)db_a, (const void*)db_x,
+                        (const void*)dlambda, (const void*)dh0, (const void*)ws})
+    if (p && !aligned16(p)) return RGLRU_EINVAL;
+  if (!ws || ws_bytes < rglru_bwd_workspace_bytes(B, T, D, io)) return RGLRU_EWORKSPACE;
+
+  Carver cv(ws);
+  BwdWs w = carve_bwd(cv, B, T, D, io);
+  const int M = B * T;
+  const int Mp = (M + 63) / 64 * 64;
+  const bool bf = io == RGLRU_BF16;
+  const void* cs = conv_w ? conv_state_in : nullptr;
+
+  // 1. recompute u, the gates (r, i) and every state h_t
+  const void* u = x;
+  if (conv_w) {
+    if (bf) RG_CHECK(launch_conv_fwd<bf16_t>(B, T, D, x, conv_w, conv_b, cs, w.u, nullptr, stream));
+    else RG_CHECK(launch_conv_fwd<float>(B, T, D, x, conv_w, conv_b, cs, w.u, nullptr, stream));
+    u = w.u;
+  }
+  GateGemmArgs g{};
+  g.U = u; g.Wa = W_a; g.Wx = W_x; g.M = M; g.N = D; g.K = D;
+  g.ba = b_a; g.bx = b_x; g.lam = lambda; g.c = c;
+  g.out0 = w.r; g.out1 = w.i;
+  st = gate_projection(io, g, kEpiRI, false, w.r, w.i, stream);
+  if (st != RGLRU_OK) return st;
+  ScanFwdArgs sf{};
+  sf.B = B; sf.T = T; sf.D = D;
+  sf.x = x; sf.conv_w = conv_w; sf.conv_b = conv_b; sf.conv_state = cs;
+  sf.a = w.r; sf.beta = w.i; sf.from_ri = true; sf.lam = lambda; sf.c = c;
+  sf.h0 = h0; sf.y = nullptr; sf.h_all = w.h_all; sf.h_T = nullptr;
+  sf.status = w.status; sf.counter = w.counter;
+  if (bf) RG_CHECK(launch_scan_fwd<bf16_t>(sf, stream));
+  else RG_CHECK(launch_scan_fwd<float>(sf, stream));
+
+  // 2. reverse scan: dz^a, dz^x, the direct du term, dh0, partial sums
+  float* du = conv_w ? w.du : dx;   // without the conv, du is dx
+  ScanBwdArgs sb{};
+  sb.B = B; sb.T = T; sb.D = D;
+  sb.u = u; sb.r = w.r; sb.i = w.i; sb.h_all = w.h_all; sb.h0 = h0;
+  sb.dy = dy; sb.dh_T = dh_T; sb.lam = lambda; sb.c = c;
+  sb.dz_hi = w.dz_hi; sb.dz_lo = w.dz_lo; sb.du = du; sb.dh0 = dh0;
+  sb.partial = w.scan_part; sb.status = w.status; sb.counter = w.counter;
+  if (bf) RG_CHECK(launch_scan_bwd<bf16_t>(sb, stream));
+  else RG_CHECK(launch_scan_bwd<float>(sb, stream));
+
+  // 3. du += [dz^a dz^x] [W_a; W_x]   (K = 2D; the B operand is [W_a; W_x]^T)
+  PlainGemmArgs pg{};
+  if (bf) {
+    const uint16_t* Wa16 = static_cast<const uint16_t*>(W_a);
+    const uint16_t* Wx16 = static_cast<const uint16_t*>(W_x);
+    uint16_t* WT = static_cast<uint16_t*>(w.WT);
+    RG_CHECK(launch_transpose<uint16_t>(Wa16, D, D, D, WT, 2 * D, D, stream));
+    RG_CHECK(launch_transpose<uint16_t>(Wx16, D, D, D, WT + D, 2 * D, D, stream));
+  } else {
+    float* WT = static_cast<float*>(w.WT);
+    RG_CHECK(launch_transpose<float>(static_cast<const float*>(W_a), D, D, D, WT, 2 * D, D, stream));
+    RG_CHECK(launch_transpose<float>(static_cast<const float*>(W_x), D, D, D, WT + D, 2 * D, D, stream));
+  }
+  pg.A = w.dz_hi; pg.A2 = bf ? w.dz_lo : nullptr; pg.Bm = w.WT;
+  pg.M = M; pg.N = D; pg.K = 2 * D; pg.lda = 2 * D; pg.ldb = 2 * D; pg.ldc = D;
+  pg.C = du; pg.addend = du;
+  if (bf) RG_CHECK(launch_plain_gemm_bf16(pg, stream));
+  else RG_CHECK(launch_plain_gemm_f32(pg, stream));
+
+  // 4. dW = dz^T u   (reduction over the B*T rows, zero-padded to Mp)
+  if (bf) {
+    RG_CHECK(launch_transpose<uint16_t>(static_cast<const uint16_t*>(w.dz_hi), M, 2 * D, 2 * D,
+                                        static_cast<uint16_t*>(w.dzT_hi), Mp, Mp, stream));
+    RG_CHECK(launch_transpose<uint16_t>(static_cast<const uint16_t*>(w.dz_lo), M, 2 * D, 2 * D,
+                                        static_cast<uint16_t*>(w.dzT_lo), Mp, Mp, stream));
+    RG_CHECK(launch_transpose<uint16_t>(static_cast<const uint16_t*>(u), M, D, D,
+                                        static_cast<uint16_t*>(w.uT), Mp, Mp, stream));
+  } else {
+    RG_CHECK(launch_transpose<float>(static_cast<const float*>(w.dz_hi), M, 2 * D, 2 * D,
+                                     static_cast<float*>(w.dzT_hi), Mp, Mp, stream));
+    RG_CHECK(launch_transpose<float>(static_cast<const float*>(u), M, D, D,
+                                     static_cast<float*>(w.uT), Mp, Mp, stream));
+  }
+  const size_t eb = io_bytes(io);
+  for (int gi = 0; gi < 2; ++gi) {
+    PlainGemmArgs q{};
+    q.A = static_cast<const unsigned char*>(w.dzT_hi) + size_t(gi) * D * Mp * eb;
+    q.A2 = bf ? static_cast<const unsigned char*>(w.dzT_lo) + size_t(gi) * D * Mp * eb : nullptr;
+    q.Bm = w.uT;
+    q.M = D; q.N = D; q.K = Mp; q.lda = Mp; q.ldb = Mp; q.ldc = D;
+    q.C = gi == 0 ? dW_a : dW_x;
+    q.addend = nullptr;
+    if (bf) RG_CHECK(launch_plain_gemm_bf16(q, stream));
+    else RG_CHECK(launch_plain_gemm_f32(q, stream));
+  }
+
+  // 5. conv backward and the fixed-order reductions
+  if (conv_w) {
+    ConvBwdArgs cb{};
+    cb.B = B; cb.T = T; cb.D = D; cb.x = x; cb.conv_w = conv_w; cb.conv_state = cs;
+    cb.du = w.du; cb.dx = dx; cb.partial = w.conv_part;
+    if (bf) RG_CHECK(launch_conv_bwd<bf16_t>(cb, stream));
+    else RG_CHECK(launch_conv_bwd<float>(cb, stream));
+  }
+  ReduceArgs ra{};
+  ra.D = D; ra.P = B * scan_chunks(T);
+  ra.scan_part = w.scan_part; ra.conv_part = conv_w ? w.conv_part : nullptr;
+  ra.lam = lambda; ra.c = c;
+  ra.db_a = db_a; ra.db_x = db_x; ra.dlambda = dlambda;
+  ra.dconv_w = dconv_w; ra.dconv_b = dconv_b;
+  RG_CHECK(launch_reduce(ra, stream));
+  return RGLRU_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,171 @@
+// Backward helpers of the RG-LRU temporal branch (the pages state no backward; these
+// are the chain rule through the "Recurrent block" Conv1D and the gate projections of
+// Eq. (1)-(2) of the Griffin model-architecture page).
+//   * tiled transposes that put the reduction axis of the weight-gradient and
+//     input-gradient products last, so both run on the same K-contiguous MFMA kernel;
+//   * the conv backward: dx_tau = sum_k w[k] du_{tau+k}, and per-tile partial sums of
+//     du_t x_{t-k} and du_t for dconv_w, dconv_b;
+//   * one fixed-order reduction of all per-tile partials (bitwise reproducible).
+#include "rglru_device.h"
+#include "kernels.h"
+
+namespace rglru {
+
+// dst[c * ldd + r] = src[r * lds + c] for r < R; zero for R <= r < Rp.
+template <typename E>
+__global__ __launch_bounds__(256) void transpose_kernel(const E* __restrict__ src, int R, int C,
+                                                        int lds, E* __restrict__ dst, int ldd,
+                                                        int Rp) {
+  __shared__ E tile[64][65];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < R && c < C) ? src[size_t(r) * lds + c] : E(0);
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < C && r < Rp) dst[size_t(c) * ldd + r] = tile[tx][i];
+  }
+}
+
+template <typename E>
+hipError_t launch_transpose(const E* src, int R, int C, int lds, E* dst, int ldd, int Rp,
+                            hipStream_t s) {
+  dim3 grid((Rp + 63) / 64, (C + 63) / 64);
+  transpose_kernel<E><<<grid, 256, 0, s>>>(src, R, C, lds, dst, ldd, Rp);
+  return hipGetLastError();
+}
+template hipError_t launch_transpose<uint16_t>(const uint16_t*, int, int, int, uint16_t*, int, int,
+                                               hipStream_t);
+template hipError_t launch_transpose<float>(const float*, int, int, int, float*, int, int,
+                                            hipStream_t);
+
+constexpr int kBSteps = 8, kBTG = 16, kBChunk = 128, kBCh = 64;
+
+template <typename IO>
+__global__ __launch_bounds__(256) void conv_bwd_kernel(ConvBwdArgs p) {
+  // du and x staging; after the time loop the same LDS holds the fp64 tile reduction
+  __shared__ __attribute__((aligned(16))) float smem[2 * (kBChunk + 3) * kBCh];
+  static_assert(sizeof(double) * kBTG * 5 * kBCh <= sizeof(float) * 2 * (kBChunk + 3) * kBCh, "");
+  float* dus = smem;
+  float* xs = smem + (kBChunk + 3) * kBCh;
+  double (*sRed)[5][kBCh] = reinterpret_cast<double (*)[5][kBCh]>(smem);
+  const int B = p.B, T = p.T, D = p.D;
+  const int nchunks = (T + kBChunk - 1) / kBChunk;
+  const int nq = D / kBCh;
+  const int blk = blockIdx.x % (B * nq);
+  const int chunk = blockIdx.x / (B * nq);
+  const int b = blk / nq, d0 = (blk % nq) * kBCh;
+  const int t0 = chunk * kBChunk;
+  const int tid = threadIdx.x, cg = tid & 15, tg = tid >> 4;
+  const int d = d0 + 4 * cg;
+  const IO* x = static_cast<const IO*>(p.x);
+  const IO* cs = static_cast<const IO*>(p.conv_state);
+  // du rows t0 .. t0+130 (zero past T); x rows t0-3 .. t0+127 (history for t < 0)
+  for (int idx = tid; idx < (kBChunk + 3) * 16; idx += 256) {
+    const int rr = idx >> 4, q = idx & 15;
+    const int tdu = t0 + rr;
+    float4 v = make_float4(0, 0, 0, 0);
+    if (tdu < T) v = *reinterpret_cast<const float4*>(p.du + (size_t(b) * T + tdu) * D + d0 + 4 * q);
+    *reinterpret_cast<float4*>(&dus[rr * kBCh + 4 * q]) = v;
+    const int tx = t0 - 3 + rr;
+    float4 xv = make_float4(0, 0, 0, 0);
+    if (tx >= 0 && tx < T) xv = Io<IO>::load4(x + (size_t(b) * T + tx) * D + d0 + 4 * q);
+    else if (tx < 0 && cs) xv = Io<IO>::load4(cs + (size_t(b) * 3 + 3 + tx) * D + d0 + 4 * q);
+    *reinterpret_cast<float4*>(&xs[rr * kBCh + 4 * q]) = xv;
+  }
+  const IO* w = static_cast<const IO*>(p.conv_w);
+  const float4 w0 = Io<IO>::load4(w + d), w1 = Io<IO>::load4(w + D + d),
+               w2 = Io<IO>::load4(w + 2 * D + d), w3 = Io<IO>::load4(w + 3 * D + d);
+  __syncthreads();
+  double pw[4][4] = {}, pb[4] = {};
+  for (int s = 0; s < kBSteps; ++s) {
+    const int lt = tg * kBSteps + s;         // local time
+    const int t = t0 + lt;
+    if (t >= T) break;
+    const float4 du0 = *reinterpret_cast<const float4*>(&dus[lt * kBCh + 4 * cg]);
+    const float4 du1 = *reinterpret_cast<const float4*>(&dus[(lt + 1) * kBCh + 4 * cg]);
+    const float4 du2 = *reinterpret_cast<const float4*>(&dus[(lt + 2) * kBCh + 4 * cg]);
+    const float4 du3 = *reinterpret_cast<const float4*>(&dus[(lt + 3) * kBCh + 4 * cg]);
+    const float4 x0 = *reinterpret_cast<const float4*>(&xs[(lt + 3) * kBCh + 4 * cg]);
+    const float4 x1 = *reinterpret_cast<const float4*>(&xs[(lt + 2) * kBCh + 4 * cg]);
+    const float4 x2 = *reinterpret_cast<const float4*>(&xs[(lt + 1) * kBCh + 4 * cg]);
+    const float4 x3 = *reinterpret_cast<const float4*>(&xs[lt * kBCh + 4 * cg]);
+    float4 dxv;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float acc = f4get(w0, j) * f4get(du0, j);
+      acc = fmaf(f4get(w1, j), f4get(du1, j), acc);
+      acc = fmaf(f4get(w2, j), f4get(du2, j), acc);
+      acc = fmaf(f4get(w3, j), f4get(du3, j), acc);
+      f4set(dxv, j, acc);
+      const double g = f4get(du0, j);
+      pw[0][j] = fma(g, double(f4get(x0, j)), pw[0][j]);
+      pw[1][j] = fma(g, double(f4get(x1, j)), pw[1][j]);
+      pw[2][j] = fma(g, double(f4get(x2, j)), pw[2][j]);
+      pw[3][j] = fma(g, double(f4get(x3, j)), pw[3][j]);
+      pb[j] += g;
+    }
+    *reinterpret_cast<float4*>(p.dx + (size_t(b) * T + t) * D + d) = dxv;
+  }
+  __syncthreads();   // staging reads done: the LDS is reused for the reduction
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sRed[tg][k][4 * cg + j] = pw[k][j];
+    sRed[tg][4][4 * cg + j] = pb[j];
+  }
+  __syncthreads();
+  for (int k = tid; k < 5 * kBCh; k += 256) {
+    const int qn = k / kBCh, c = k % kBCh;
+    double acc = 0.0;
+    for (int q = 0; q < kBTG; ++q) acc += sRed[q][qn][c];
+    p.partial[(size_t(b) * nchunks + chunk) * 5 * D + size_t(qn) * D + d0 + c] = acc;
+  }
+}
+
+template <typename IO>
+hipError_t launch_conv_bwd(const ConvBwdArgs& a, hipStream_t s) {
+  const int blocks = ((a.T + kBChunk - 1) / kBChunk) * a.B * (a.D / kBCh);
+  conv_bwd_kernel<IO><<<blocks, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+template hipError_t launch_conv_bwd<float>(const ConvBwdArgs&, hipStream_t);
+template hipError_t launch_conv_bwd<bf16_t>(const ConvBwdArgs&, hipStream_t);
+
+// Sums of per-tile partials in a fixed order (tile index ascending), in fp64.
+__global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs p) {
+  const int d = blockIdx.x * blockDim.x + threadIdx.x;
+  if (d >= p.D) return;
+  const size_t D = p.D;
+  double sa = 0, sx = 0, sl = 0;
+  for (int q = 0; q < p.P; ++q) {
+    const double* r = p.scan_part + size_t(q) * 3 * D;
+    sa += r[d];
+    sx += r[D + d];
+    sl += r[2 * D + d];
+  }
+  p.db_a[d] = float(sa);
+  p.db_x[d] = float(sx);
+  p.dlambda[d] = float(sl * double(sigmoid_negf(p.lam[d])));
+  if (p.conv_part) {
+    double sw[4] = {0, 0, 0, 0}, sb = 0;
+    for (int q = 0; q < p.P; ++q) {
+      const double* r = p.conv_part + size_t(q) * 5 * D;
+      for (int k = 0; k < 4; ++k) sw[k] += r[k * D + d];
+      sb += r[4 * D + d];
+    }
+    if (p.dconv_w)
+      for (int k = 0; k < 4; ++k) p.dconv_w[k * D + d] = float(sw[k]);
+    if (p.dconv_b) p.dconv_b[d] = float(sb);
+  }
+}
+
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
+  reduce_kernel<<<(a.D + 255) / 256, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace rglru

@@ -1,0 +1,144 @@
+// Causal depthwise Conv1D of temporal width 4 (Griffin model-architecture page, section
+// "Recurrent block": a small separable Conv1D with only 4*D parameters placed before the
+// RG-LRU).  Elementwise and HBM-bound: each thread owns four consecutive channels of one
+// sequence and walks a run of time steps with a three-row sliding window, so every x
+// element is read from HBM once and every u element written once (coalesced 8/16-byte
+// accesses along the channel axis).
+#include "rglru_device.h"
+#include "kernels.h"
+
+namespace rglru {
+
+constexpr int kConvSteps = 16;   // time steps per thread
+
+template <typename IO>
+__global__ __launch_bounds__(256) void conv_fwd_kernel(int B, int T, int D, const IO* __restrict__ x,
+                                                       const IO* __restrict__ w,
+                                                       const float* __restrict__ cb,
+                                                       const IO* __restrict__ state_in,
+                                                       IO* __restrict__ u,
+                                                       IO* __restrict__ state_out) {
+  const int nq = D / 4;
+  const int nt = (T + kConvSteps - 1) / kConvSteps;
+  const long item = long(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (item >= long(B) * nt * nq) return;
+  const int q = int(item % nq);
+  const int tc = int((item / nq) % nt);
+  const int b = int(item / (long(nq) * nt));
+  const int d = 4 * q;
+  const float4 w0 = Io<IO>::load4(w + d), w1 = Io<IO>::load4(w + D + d),
+               w2 = Io<IO>::load4(w + 2 * D + d), w3 = Io<IO>::load4(w + 3 * D + d);
+  const float4 bias = cb ? *reinterpret_cast<const float4*>(cb + d) : make_float4(0, 0, 0, 0);
+  // X(t) = x[b,t] for t >= 0, state_in[b,3+t] for t < 0 (zeros without a state)
+  auto X = [&](int t) -> float4 {
+    if (t >= 0) return Io<IO>::load4(x + (size_t(b) * T + t) * D + d);
+    if (state_in) return Io<IO>::load4(state_in + (size_t(b) * 3 + 3 + t) * D + d);
+    return make_float4(0, 0, 0, 0);
+  };
+  const int t0 = tc * kConvSteps;
+  float4 xm3 = X(t0 - 3), xm2 = X(t0 - 2), xm1 = X(t0 - 1);
+  const int t1 = min(T, t0 + kConvSteps);
+  for (int t = t0; t < t1; ++t) {
+    float4 x0 = X(t), o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      f4set(o, j, conv_u<IO>(f4get(bias, j), f4get(w0, j), f4get(w1, j), f4get(w2, j),
+                             f4get(w3, j), f4get(x0, j), f4get(xm1, j), f4get(xm2, j),
+                             f4get(xm3, j)));
+    Io<IO>::store4(u + (size_t(b) * T + t) * D + d, o);
+    xm3 = xm2; xm2 = xm1; xm1 = x0;
+  }
+  if (state_out && tc == 0) {
+    for (int j = 0; j < 3; ++j) Io<IO>::store4(state_out + (size_t(b) * 3 + j) * D + d, X(T - 3 + j));
+  }
+}
+
+// One decode step of the conv: u_t from x_t and the three-token history, then the
+// history is shifted in place (each thread touches only its own channels).
+template <typename IO>
+__global__ __launch_bounds__(256) void conv_decode_kernel(int B, int D, const IO* __restrict__ x,
+                                                          const IO* __restrict__ w,
+                                                          const float* __restrict__ cb,
+                                                          IO* __restrict__ hist,
+                                                          IO* __restrict__ u) {
+  const int nq = D / 4;
+  const long item = long(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (item >= long(B) * nq) return;
+  const int b = int(item / nq), d = 4 * int(item % nq);
+  const float4 w0 = Io<IO>::load4(w + d), w1 = Io<IO>::load4(w + D + d),
+               w2 = Io<IO>::load4(w + 2 * D + d), w3 = Io<IO>::load4(w + 3 * D + d);
+  const float4 bias = cb ? *reinterpret_cast<const float4*>(cb + d) : make_float4(0, 0, 0, 0);
+  IO* hb = hist + size_t(b) * 3 * D + d;
+  const float4 xm3 = Io<IO>::load4(hb), xm2 = Io<IO>::load4(hb + D), xm1 = Io<IO>::load4(hb + 2 * D);
+  const IO* xp = x + size_t(b) * D + d;
+  const float4 x0 = Io<IO>::load4(xp);
+  float4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    f4set(o, j, conv_u<IO>(f4get(bias, j), f4get(w0, j), f4get(w1, j), f4get(w2, j),
+                           f4get(w3, j), f4get(x0, j), f4get(xm1, j), f4get(xm2, j),
+                           f4get(xm3, j)));
+  Io<IO>::store4(u + size_t(b) * D + d, o);
+  // shift: (x_{t-3}, x_{t-2}, x_{t-1}) <- (x_{t-2}, x_{t-1}, x_t); stores are bit copies
+  const int nb = sizeof(IO) * 4;
+  if (nb == 8) {
+    const uint2 v1 = *reinterpret_cast<const uint2*>(hb + D), v2 = *reinterpret_cast<const uint2*>(hb + 2 * D),
+                v0 = *reinterpret_cast<const uint2*>(xp);
+    *reinterpret_cast<uint2*>(hb) = v1;
+    *reinterpret_cast<uint2*>(hb + D) = v2;
+    *reinterpret_cast<uint2*>(hb + 2 * D) = v0;
+  } else {
+    const uint4 v1 = *reinterpret_cast<const uint4*>(hb + D), v2 = *reinterpret_cast<const uint4*>(hb + 2 * D),
+                v0 = *reinterpret_cast<const uint4*>(xp);
+    *reinterpret_cast<uint4*>(hb) = v1;
+    *reinterpret_cast<uint4*>(hb + D) = v2;
+    *reinterpret_cast<uint4*>(hb + 2 * D) = v0;
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p, size_t n, uint32_t v) {
+  size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const size_t stride = size_t(gridDim.x) * blockDim.x;
+  for (; i < n; i += stride) p[i] = v;
+}
+
+// ------------------------------------------------------------------ launchers
+template <typename IO>
+hipError_t launch_conv_fwd(int B, int T, int D, const void* x, const void* w, const float* cb,
+                           const void* state_in, void* u, void* state_out, hipStream_t s) {
+  const long items = long(B) * ((T + kConvSteps - 1) / kConvSteps) * (D / 4);
+  const int blocks = int((items + 255) / 256);
+  conv_fwd_kernel<IO><<<blocks, 256, 0, s>>>(B, T, D, static_cast<const IO*>(x),
+                                             static_cast<const IO*>(w), cb,
+                                             static_cast<const IO*>(state_in), static_cast<IO*>(u),
+                                             static_cast<IO*>(state_out));
+  return hipGetLastError();
+}
+template hipError_t launch_conv_fwd<float>(int, int, int, const void*, const void*, const float*,
+                                           const void*, void*, void*, hipStream_t);
+template hipError_t launch_conv_fwd<bf16_t>(int, int, int, const void*, const void*, const float*,
+                                            const void*, void*, void*, hipStream_t);
+
+template <typename IO>
+hipError_t launch_conv_decode(int B, int D, const void* x, const void* w, const float* cb,
+                              void* hist, void* u, hipStream_t s) {
+  const long items = long(B) * (D / 4);
+  conv_decode_kernel<IO><<<int((items + 255) / 256), 256, 0, s>>>(
+      B, D, static_cast<const IO*>(x), static_cast<const IO*>(w), cb, static_cast<IO*>(hist),
+      static_cast<IO*>(u));
+  return hipGetLastError();
+}
+template hipError_t launch_conv_decode<float>(int, int, const void*, const void*, const float*,
+                                              void*, void*, hipStream_t);
+template hipError_t launch_conv_decode<bf16_t>(int, int, const void*, const void*, const float*,
+                                               void*, void*, hipStream_t);
+
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  fill_u32_kernel<<<int(blocks), 256, 0, s>>>(p, n, v);
+  return hipGetLastError();
+}
+
+}  // namespace rglru

@@ -1,0 +1,136 @@
+// Host-side launchers of the gfx950 kernels (internal to librglru.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rglru {
+
+// ---------------------------------------------------------------- conv.hip
+template <typename IO>
+hipError_t launch_conv_fwd(int B, int T, int D, const void* x, const void* w, const float* cb,
+                           const void* state_in, void* u, void* state_out, hipStream_t s);
+template <typename IO>
+hipError_t launch_conv_decode(int B, int D, const void* x, const void* w, const float* cb,
+                              void* hist, void* u, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
+
+// ---------------------------------------------------------------- gemm.hip
+// Epilogue kinds of the gate projection z = U [W_a; W_x]^T (Eq. (1)-(2)).
+enum GateEpi : int {
+  kEpiAB = 0,      // write a, beta = m i           (forward)
+  kEpiRI = 1,      // write r, i                    (backward recompute)
+  kEpiDecode = 2,  // h <- a h + beta u, y = RNE(h) (decode step)
+};
+
+struct GateGemmArgs {
+  const void* U;      // [M, K] io, row stride K
+  const void* Wa;     // [N, K] io
+  const void* Wx;     // [N, K] io
+  int M, N, K;        // N = K = D
+  const float* ba;
+  const float* bx;
+  const float* lam;
+  float c;
+  float* out0;        // kEpiAB: a  ; kEpiRI: r  [M, N]
+  float* out1;        // kEpiAB: beta; kEpiRI: i [M, N]
+  const void* u;      // kEpiDecode: u [M, N] io
+  float* h;           // kEpiDecode: state [M, N] in/out
+  void* y;            // kEpiDecode: y [M, N] io
+};
+
+// C[M,N] = A[M,K] B[N,K]^T (+ addend), fp32 output.  With A2 (bf16 only) the product
+// is (A + A2) B^T, evaluated as two bf16 MFMA passes over K.
+struct PlainGemmArgs {
+  const void* A;
+  const void* A2;
+  const void* Bm;
+  int M, N, K;
+  int lda, ldb, ldc;
+  float* C;
+  const float* addend;   // may equal C (read before write by the same thread) or NULL
+};
+
+hipError_t launch_gate_gemm_bf16(const GateGemmArgs& g, int epi, bool small_m, hipStream_t s);
+hipError_t launch_plain_gemm_bf16(const PlainGemmArgs& g, hipStream_t s);
+hipError_t launch_plain_gemm_f32(const PlainGemmArgs& g, hipStream_t s);
+// fp32 I/O: gate math from pre-activations za, zx [M, N] (already W u, bias not added).
+hipError_t launch_gate_elementwise_f32(const GateGemmArgs& g, const float* za, const float* zx,
+                                       int epi, hipStream_t s);
+
+// ---------------------------------------------------------------- scan.hip
+struct ScanFwdArgs {
+  int B, T, D;
+  const void* x;          // [B,T,D] io (conv input, or u itself when conv_w is NULL)
+  const void* conv_w;     // [4,D] io or NULL
+  const float* conv_b;
+  const void* conv_state; // [B,3,D] io or NULL
+  const float* a;         // [B,T,D] fp32   (kEpiAB layout) -- or r when from_ri
+  const float* beta;      // [B,T,D] fp32                   -- or i when from_ri
+  bool from_ri;           // gates given as (r, i): a, beta recomputed with lam, c
+  const float* lam;
+  float c;
+  const float* h0;        // [B,D] or NULL
+  void* y;                // [B,T,D] io or NULL
+  float* h_all;           // [B,T,D] fp32 or NULL: every h_t
+  float* h_T;             // [B,D] or NULL
+  uint32_t* status;       // look-back words, scan_status_words(B,T,D) of them
+  uint32_t* counter;      // one ticket counter (zeroed with the status words)
+};
+size_t scan_status_words(int B, int T, int D);
+template <typename IO> hipError_t launch_scan_fwd(const ScanFwdArgs& a, hipStream_t s);
+
+struct ScanBwdArgs {
+  int B, T, D;
+  const void* u;          // [B,T,D] io
+  const float* r;         // [B,T,D] fp32
+  const float* i;         // [B,T,D] fp32
+  const float* h_all;     // [B,T,D] fp32, h_t
+  const float* h0;        // [B,D] or NULL
+  const void* dy;         // [B,T,D] io
+  const float* dh_T;      // [B,D] or NULL
+  const float* lam;
+  float c;
+  // outputs
+  void* dz_hi;            // [B*T, 2D]: bf16 hi part (bf16 io) or fp32 dz (fp32 io)
+  void* dz_lo;            // [B*T, 2D] bf16 lo part (bf16 io only)
+  float* du;              // [B,T,D] fp32: G m i (the direct term of du)
+  float* dh0;             // [B,D] or NULL
+  double* partial;        // [B * nchunks, 3, D]: db_a, db_x, dL partial sums
+  uint32_t* status;
+  uint32_t* counter;
+};
+int scan_chunks(int T);
+template <typename IO> hipError_t launch_scan_bwd(const ScanBwdArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- bwd.hip
+template <typename E>
+hipError_t launch_transpose(const E* src, int R, int C, int lds_src, E* dst, int ldd, int Rp,
+                            hipStream_t s);
+struct ConvBwdArgs {
+  int B, T, D;
+  const void* x;
+  const void* conv_w;
+  const void* conv_state;
+  const float* du;       // [B,T,D]
+  float* dx;             // [B,T,D]
+  double* partial;       // [B * nchunks, 5, D]: dconv_w[0..3], dconv_b partial sums
+};
+template <typename IO> hipError_t launch_conv_bwd(const ConvBwdArgs& a, hipStream_t s);
+struct ReduceArgs {
+  int D;
+  int P;                   // number of partial rows per quantity
+  const double* scan_part;  // [P, 3, D]
+  const double* conv_part;  // [P, 5, D] or NULL
+  const float* lam;
+  float c;
+  float* db_a;
+  float* db_x;
+  float* dlambda;
+  float* dconv_w;          // [4, D] or NULL
+  float* dconv_b;          // [D] or NULL
+};
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
+
+}  // namespace rglru

@@ -1,0 +1,179 @@
+// Device helpers shared by the gfx950 kernels of the RG-LRU temporal branch.
+//
+// Definitions follow the Griffin model-architecture page: the "Recurrent block" section
+// (causal Conv1D of temporal width 4 before the RG-LRU) and the "Real-Gated Linear
+// Recurrent Unit (RG-LRU)" section, Eq. (1)-(4), with a = sigma(Lambda), c = 8 and
+// a^{c r_t} evaluated in log space.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rglru {
+
+// ------------------------------------------------------------------ element types
+typedef uint16_t bf16_t;   // raw bf16 bits; arithmetic is always fp32
+
+__device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return bf16_t(u >> 16);
+}
+
+// I/O element traits: load/store 4 consecutive channels as fp32.
+template <typename IO> struct Io;
+
+template <> struct Io<float> {
+  static constexpr int kBytes = 4;
+  __device__ __forceinline__ static float4 load4(const float* p) {
+    return *reinterpret_cast<const float4*>(p);
+  }
+  __device__ __forceinline__ static void store4(float* p, float4 v) {
+    *reinterpret_cast<float4*>(p) = v;
+  }
+  __device__ __forceinline__ static float round(float v) { return v; }
+  __device__ __forceinline__ static float load1(const float* p) { return *p; }
+  __device__ __forceinline__ static void store1(float* p, float v) { *p = v; }
+};
+
+template <> struct Io<bf16_t> {
+  static constexpr int kBytes = 2;
+  __device__ __forceinline__ static float4 load4(const bf16_t* p) {
+    uint2 r = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                       __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+  }
+  __device__ __forceinline__ static void store4(bf16_t* p, float4 v) {
+    uint2 r;
+    r.x = uint32_t(f2bf(v.x)) | (uint32_t(f2bf(v.y)) << 16);
+    r.y = uint32_t(f2bf(v.z)) | (uint32_t(f2bf(v.w)) << 16);
+    *reinterpret_cast<uint2*>(p) = r;
+  }
+  // value after rounding to bf16 (nearest even), as fp32
+  __device__ __forceinline__ static float round(float v) { return bf2f(f2bf(v)); }
+  __device__ __forceinline__ static float load1(const bf16_t* p) { return bf2f(*p); }
+  __device__ __forceinline__ static void store1(bf16_t* p, float v) { *p = f2bf(v); }
+};
+
+__device__ __forceinline__ float f4get(const float4& v, int j) {
+  return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+}
+__device__ __forceinline__ void f4set(float4& v, int j, float s) {
+  if (j == 0) v.x = s; else if (j == 1) v.y = s; else if (j == 2) v.z = s; else v.w = s;
+}
+
+// ------------------------------------------------------------------ conv (R1)
+// u = RNE_io(b + w0 x_t + w1 x_{t-1} + w2 x_{t-2} + w3 x_{t-3}), one fixed fma order so
+// every kernel that evaluates u produces the same bits.
+template <typename IO>
+__device__ __forceinline__ float conv_u(float b, float w0, float w1, float w2, float w3,
+                                        float x0, float x1, float x2, float x3) {
+  float acc = b;
+  acc = fmaf(w0, x0, acc);
+  acc = fmaf(w1, x1, acc);
+  acc = fmaf(w2, x2, acc);
+  acc = fmaf(w3, x3, acc);
+  return Io<IO>::round(acc);
+}
+
+// ------------------------------------------------------------------ gate math
+__device__ __forceinline__ float sigmoidf_stable(float z) {
+  if (z >= 0.f) return 1.f / (1.f + expf(-z));
+  float e = expf(z);
+  return e / (1.f + e);
+}
+
+// log sigma(Lambda) = -log(1 + e^{-Lambda}), without overflow or cancellation.
+__device__ __forceinline__ float log_sigmoidf(float lam) {
+  float t = log1pf(expf(-fabsf(lam)));
+  return lam >= 0.f ? -t : lam - t;
+}
+
+// sigma(-Lambda) = 1 - sigma(Lambda): derivative of log sigma(Lambda).
+__device__ __forceinline__ float sigmoid_negf(float lam) { return sigmoidf_stable(-lam); }
+
+// Eq. (3) in log space and the sqrt(1 - a^2) factor of Eq. (4):
+//   log a = c r L,  a = exp(log a),  m = sqrt(-expm1(2 log a)).
+struct Gate {
+  float r, i, a, m;
+};
+__device__ __forceinline__ Gate gate_from_ri(float r, float i, float L, float c) {
+  Gate g;
+  g.r = r;
+  g.i = i;
+  float ell = (c * r) * L;
+  g.a = expf(ell);
+  g.m = sqrtf(-expm1f(2.f * ell));
+  return g;
+}
+__device__ __forceinline__ Gate gate_from_z(float zr, float zi, float L, float c) {
+  return gate_from_ri(sigmoidf_stable(zr), sigmoidf_stable(zi), L, c);
+}
+
+// ------------------------------------------------------------------ scan look-back
+// Chunk summaries of the affine map h -> A h + H are published word by word with
+// agent-scope atomics.  A word holding kEmpty has not been written yet; a published
+// value that happens to have those bits is replaced by the canonical quiet NaN.
+constexpr uint32_t kEmpty = 0xffffffffu;
+
+__device__ __forceinline__ void publish(uint32_t* p, float v) {
+  uint32_t u = __float_as_uint(v);
+  if (u == kEmpty) u = 0x7fc00000u;
+  __hip_atomic_store(p, u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t peek(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Upper bound on polls of one predecessor word; beyond it the carry becomes NaN (the
+// output is then visibly wrong) instead of the kernel waiting forever.
+constexpr int kMaxPolls = 1 << 20;
+
+// Decoupled look-back for one channel, with a canonical result.  `incl`, `aggA`, `aggH`
+// are indexed by chain position (0 = first chunk of the chain) times `stride`.  Position
+// `pos` walks back over positions pos-1, pos-2, ... collecting published aggregates until
+// it meets a published inclusive state, then applies the collected aggregates forward in
+// chain order: h <- fmaf(A_j, h, H_j).  Every inclusive state is published as
+// fmaf(A, carry, H), so the carry equals, bit for bit, the one a strictly sequential chain
+// would compute, whatever the timing: results are reproducible run to run.  At most
+// kWindow aggregates are collected; past that the walk waits for an inclusive state.
+// `bufA`, `bufH` are kWindow floats of scratch (LDS) owned by the calling thread.
+constexpr int kWindow = 16;
+
+__device__ __forceinline__ float lookback_carry(const uint32_t* incl, const uint32_t* aggA,
+                                                const uint32_t* aggH, int pos, size_t stride,
+                                                float* bufA, float* bufH) {
+  int j = pos - 1;
+  int n = 0;
+  int polls = 0;
+  float h;
+  while (true) {
+    const uint32_t vi = peek(incl + size_t(j) * stride);
+    if (vi != kEmpty) {
+      h = __uint_as_float(vi);
+      break;
+    }
+    if (n < kWindow) {
+      const uint32_t va = peek(aggA + size_t(j) * stride);
+      const uint32_t vh = peek(aggH + size_t(j) * stride);
+      if (va != kEmpty && vh != kEmpty) {
+        bufA[n] = __uint_as_float(va);
+        bufH[n] = __uint_as_float(vh);
+        ++n;
+        --j;   // position 0 always publishes an inclusive state, so j stays >= 0
+        polls = 0;
+        continue;
+      }
+    }
+    if (++polls > kMaxPolls) return __uint_as_float(0x7fc00000u);
+    __builtin_amdgcn_s_sleep(1);
+  }
+  for (int k = n - 1; k >= 0; --k) h = fmaf(bufA[k], h, bufH[k]);
+  return h;
+}
+
+}  // namespace rglru

@@ -1,0 +1,422 @@
+// Diagonal linear scan of the RG-LRU, Eq. (4) of the Griffin model-architecture page
+// ("Real-Gated Linear Recurrent Unit (RG-LRU)" section):
+//     h_t = a_t h_{t-1} + beta_t u_t,   beta_t = sqrt(1 - a_t^2) i_t,   y_t = h_t,
+// evaluated as a chunked parallel scan (the blog page "Griffin's Compromise", "Term
+// explanation: Parallel scan": chunk subtotals computed in parallel, each chunk's summary
+// passed on to the next).  Every step is elementwise over channels and the kernel moves
+// 12 bytes per element at bf16 I/O (x 2, a 4, beta 4, y 2), so it is HBM-bound.
+//
+// Work decomposition (one workgroup = 256 threads = one tile of 128 time steps x 64
+// channels of one sequence):
+//   * thread (tg, cg): time group tg in [0,16) owns 8 consecutive steps, channel group cg
+//     in [0,16) owns 4 consecutive channels, so a wave's loads of a and beta cover four
+//     256-byte channel-contiguous row segments;
+//   * x rows t0-3 .. t0+127 are staged through LDS with coalesced loads and the width-4
+//     conv (the "Recurrent block" Conv1D) is recomputed from them with the same fma order
+//     as the stand-alone conv, so u is bit-identical to the u the gate projection used;
+//   * each thread scans its 8 steps from zero to the affine summary (A = prod a, H), the
+//     16 time-group summaries are combined in LDS, and the tile summary is chained across
+//     tiles with a decoupled look-back (tiles take tickets in time order from an atomic
+//     counter, so every tile a tile waits on has already started: no deadlock);
+//   * each thread then re-runs its 8 steps from its exact incoming state and writes y.
+#include "rglru_device.h"
+#include "kernels.h"
+
+namespace rglru {
+
+constexpr int kSteps = 8;                 // steps per thread
+constexpr int kTG = 16;                   // time groups per tile
+constexpr int kChunk = kSteps * kTG;      // 128 time steps per tile
+constexpr int kCh = 64;                   // channels per tile
+
+int scan_chunks(int T) { return (T + kChunk - 1) / kChunk; }
+size_t scan_status_words(int B, int T, int D) { return 3ull * scan_chunks(T) * size_t(B) * D; }
+
+template <typename IO>
+__global__ __launch_bounds__(256) void scan_fwd_kernel(ScanFwdArgs p) {
+  __shared__ uint32_t s_ticket;
+  __shared__ float xs[(kChunk + 3) * kCh];
+  __shared__ float sA[kTG][kCh], sH[kTG][kCh];
+  __shared__ float sCarry[kCh];
+  __shared__ float sLb[16][2][kWindow];
+
+  const int B = p.B, T = p.T, D = p.D;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_ticket = atomicAdd(p.counter, 1u);
+  __syncthreads();
+  const int nblk = B * (D / kCh);
+  const int nchunks = (T + kChunk - 1) / kChunk;
+  const int tk = int(s_ticket);
+  const int chunk = tk / nblk, blk = tk % nblk;
+  const int b = blk / (D / kCh), d0 = (blk % (D / kCh)) * kCh;
+  const int t0 = chunk * kChunk;
+  const int cg = tid & 15, tg = tid >> 4;
+  const int d = d0 + 4 * cg;
+  const size_t BD = size_t(B) * D;
+
+  // gates for this thread's steps (issued first: the longest-latency loads)
+  float4 ga[kSteps], gb[kSteps];
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const int t = t0 + tg * kSteps + s;
+    if (t < T) {
+      const size_t o = (size_t(b) * T + t) * D + d;
+      ga[s] = *reinterpret_cast<const float4*>(p.a + o);
+      gb[s] = *reinterpret_cast<const float4*>(p.beta + o);
+    } else {
+      ga[s] = p.from_ri ? make_float4(0, 0, 0, 0) : make_float4(1, 1, 1, 1);
+      gb[s] = make_float4(0, 0, 0, 0);
+    }
+  }
+  // stage x rows t0-3 .. t0+kChunk-1 (fp32 in LDS)
+  const IO* x = static_cast<const IO*>(p.x);
+  const IO* cs = static_cast<const IO*>(p.conv_state);
+  for (int idx = tid; idx < (kChunk + 3) * 16; idx += 256) {
+    const int rr = idx >> 4, q = idx & 15;
+    const int t = t0 - 3 + rr;
+    float4 v = make_float4(0, 0, 0, 0);
+    if (t >= 0 && t < T) v = Io<IO>::load4(x + (size_t(b) * T + t) * D + d0 + 4 * q);
+    else if (t < 0 && cs) v = Io<IO>::load4(cs + (size_t(b) * 3 + 3 + t) * D + d0 + 4 * q);
+    *reinterpret_cast<float4*>(&xs[rr * kCh + 4 * q]) = v;
+  }
+  float4 w0 = make_float4(0, 0, 0, 0), w1 = w0, w2 = w0, w3 = w0, cb = w0, Lv = w0;
+  const bool conv = p.conv_w != nullptr;
+  if (conv) {
+    const IO* w = static_cast<const IO*>(p.conv_w);
+    w0 = Io<IO>::load4(w + d); w1 = Io<IO>::load4(w + D + d);
+    w2 = Io<IO>::load4(w + 2 * D + d); w3 = Io<IO>::load4(w + 3 * D + d);
+    if (p.conv_b) cb = *reinterpret_cast<const float4*>(p.conv_b + d);
+  }
+  if (p.from_ri) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f4set(Lv, j, log_sigmoidf(p.lam[d + j]));
+  }
+  __syncthreads();
+
+  // a_t and beta_t u_t for each step
+  float4 bu[kSteps];
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const int rr = tg * kSteps + s + 3;
+    const float4 x0 = *reinterpret_cast<const float4*>(&xs[rr * kCh + 4 * cg]);
+    float4 u = x0;
+    if (conv) {
+      const float4 x1 = *reinterpret_cast<const float4*>(&xs[(rr - 1) * kCh + 4 * cg]);
+      const float4 x2 = *reinterpret_cast<const float4*>(&xs[(rr - 2) * kCh + 4 * cg]);
+      const float4 x3 = *reinterpret_cast<const float4*>(&xs[(rr - 3) * kCh + 4 * cg]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        f4set(u, j, conv_u<IO>(f4get(cb, j), f4get(w0, j), f4get(w1, j), f4get(w2, j),
+                               f4get(w3, j), f4get(x0, j), f4get(x1, j), f4get(x2, j),
+                               f4get(x3, j)));
+    }
+    if (p.from_ri) {
+      const bool valid = t0 + tg * kSteps + s < T;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const Gate g = gate_from_ri(f4get(ga[s], j), f4get(gb[s], j), f4get(Lv, j), p.c);
+        f4set(ga[s], j, valid ? g.a : 1.f);
+        f4set(gb[s], j, valid ? g.m * g.i : 0.f);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f4set(bu[s], j, f4get(gb[s], j) * f4get(u, j));
+  }
+
+  // local summary of this thread's steps: h -> A h + H
+  float4 A = make_float4(1, 1, 1, 1), H = make_float4(0, 0, 0, 0);
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f4set(H, j, fmaf(f4get(ga[s], j), f4get(H, j), f4get(bu[s], j)));
+      f4set(A, j, f4get(A, j) * f4get(ga[s], j));
+    }
+  *reinterpret_cast<float4*>(&sA[tg][4 * cg]) = A;
+  *reinterpret_cast<float4*>(&sH[tg][4 * cg]) = H;
+  __syncthreads();
+
+  if (tg == 0) {
+    // tile aggregate, publish, look back, publish the inclusive state
+    float4 Ag = make_float4(1, 1, 1, 1), Hg = make_float4(0, 0, 0, 0);
+    for (int q = 0; q < kTG; ++q) {
+      const float4 Aq = *reinterpret_cast<const float4*>(&sA[q][4 * cg]);
+      const float4 Hq = *reinterpret_cast<const float4*>(&sH[q][4 * cg]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f4set(Hg, j, fmaf(f4get(Aq, j), f4get(Hg, j), f4get(Hq, j)));
+        f4set(Ag, j, f4get(Aq, j) * f4get(Ag, j));
+      }
+    }
+    uint32_t* incl = p.status;
+    uint32_t* aggA = p.status + size_t(nchunks) * BD;
+    uint32_t* aggH = aggA + size_t(nchunks) * BD;
+    const size_t base = size_t(b) * D + d;
+    if (chunk > 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        publish(aggA + size_t(chunk) * BD + base + j, f4get(Ag, j));
+        publish(aggH + size_t(chunk) * BD + base + j, f4get(Hg, j));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float carry;
+      if (chunk == 0) carry = p.h0 ? p.h0[base + j] : 0.f;
+      else carry = lookback_carry(incl + base + j, aggA + base + j, aggH + base + j, chunk, BD,
+                                  sLb[cg][0], sLb[cg][1]);
+      publish(incl + size_t(chunk) * BD + base + j, fmaf(f4get(Ag, j), carry, f4get(Hg, j)));
+      sCarry[4 * cg + j] = carry;
+    }
+  }
+  // exclusive prefix of the time groups before this one
+  float4 Ap = make_float4(1, 1, 1, 1), Hp = make_float4(0, 0, 0, 0);
+  for (int q = 0; q < tg; ++q) {
+    const float4 Aq = *reinterpret_cast<const float4*>(&sA[q][4 * cg]);
+    const float4 Hq = *reinterpret_cast<const float4*>(&sH[q][4 * cg]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f4set(Hp, j, fmaf(f4get(Aq, j), f4get(Hp, j), f4get(Hq, j)));
+      f4set(Ap, j, f4get(Aq, j) * f4get(Ap, j));
+    }
+  }
+  __syncthreads();
+
+  float4 h;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f4set(h, j, fmaf(f4get(Ap, j), sCarry[4 * cg + j], f4get(Hp, j)));
+  IO* y = static_cast<IO*>(p.y);
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const int t = t0 + tg * kSteps + s;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f4set(h, j, fmaf(f4get(ga[s], j), f4get(h, j), f4get(bu[s], j)));
+    if (t < T) {
+      const size_t o = (size_t(b) * T + t) * D + d;
+      if (y) Io<IO>::store4(y + o, h);
+      if (p.h_all) *reinterpret_cast<float4*>(p.h_all + o) = h;
+      if (t == T - 1 && p.h_T) *reinterpret_cast<float4*>(p.h_T + size_t(b) * D + d) = h;
+    }
+  }
+}
+
+template <typename IO>
+hipError_t launch_scan_fwd(const ScanFwdArgs& a, hipStream_t s) {
+  hipError_t e = launch_fill_u32(a.status, scan_status_words(a.B, a.T, a.D), kEmpty, s);
+  if (e != hipSuccess) return e;
+  e = launch_fill_u32(a.counter, 1, 0u, s);
+  if (e != hipSuccess) return e;
+  const int tiles = scan_chunks(a.T) * a.B * (a.D / kCh);
+  scan_fwd_kernel<IO><<<tiles, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+template hipError_t launch_scan_fwd<float>(const ScanFwdArgs&, hipStream_t);
+template hipError_t launch_scan_fwd<bf16_t>(const ScanFwdArgs&, hipStream_t);
+
+// ------------------------------------------------------------------ reverse scan
+// Backward through Eq. (4) (the pages give no backward; chain rule).  With G_t the total
+// derivative of h_t and g_t = a_t G_t the part handed to step t-1:
+//     G_t = dy_t + g_{t+1},   g_t = a_t (dy_t + g_{t+1}),   g_T = dh_T,   dh0 = g_0,
+// the same affine recurrence run backwards in time, chunked and chained exactly like the
+// forward (tiles take tickets from the last time chunk to the first).  Per element it
+// then forms the local gradients:
+//     d(log a) = G (a h_{t-1} - (a^2/m) i u)   [m-path term 0 where m = 0]
+//     dz^a = c L d(log a) r (1-r),  dz^x = G m u i (1-i),  du_direct = G m i,
+// and per-tile partial sums of dz^a, dz^x and c r d(log a) (for db_a, db_x, dLambda).
+template <typename IO>
+__global__ __launch_bounds__(256) void scan_bwd_kernel(ScanBwdArgs p) {
+  __shared__ uint32_t s_ticket;
+  __shared__ float sA[kTG][kCh], sH[kTG][kCh];
+  __shared__ float sCarry[kCh];
+  __shared__ float sLb[16][2][kWindow];
+  __shared__ double sRed[kTG][3][kCh];
+
+  const int B = p.B, T = p.T, D = p.D;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_ticket = atomicAdd(p.counter, 1u);
+  __syncthreads();
+  const int nblk = B * (D / kCh);
+  const int nchunks = (T + kChunk - 1) / kChunk;
+  const int tk = int(s_ticket);
+  const int pos = tk / nblk, blk = tk % nblk;       // chain position 0 = last time chunk
+  const int chunk = nchunks - 1 - pos;
+  const int b = blk / (D / kCh), d0 = (blk % (D / kCh)) * kCh;
+  const int t0 = chunk * kChunk;
+  const int cg = tid & 15, tg = tid >> 4;
+  const int d = d0 + 4 * cg;
+  const size_t BD = size_t(B) * D;
+
+  float4 ra[kSteps], ia[kSteps], hp[kSteps], uu[kSteps], dyv[kSteps];
+  const IO* u = static_cast<const IO*>(p.u);
+  const IO* dy = static_cast<const IO*>(p.dy);
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const int t = t0 + tg * kSteps + s;
+    if (t < T) {
+      const size_t o = (size_t(b) * T + t) * D + d;
+      ra[s] = *reinterpret_cast<const float4*>(p.r + o);
+      ia[s] = *reinterpret_cast<const float4*>(p.i + o);
+      uu[s] = Io<IO>::load4(u + o);
+      dyv[s] = Io<IO>::load4(dy + o);
+      if (t > 0) hp[s] = *reinterpret_cast<const float4*>(p.h_all + o - D);
+      else hp[s] = p.h0 ? *reinterpret_cast<const float4*>(p.h0 + size_t(b) * D + d)
+                        : make_float4(0, 0, 0, 0);
+    } else {
+      ra[s] = ia[s] = hp[s] = uu[s] = dyv[s] = make_float4(0, 0, 0, 0);
+    }
+  }
+  float4 Lv;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f4set(Lv, j, log_sigmoidf(p.lam[d + j]));
+  // a_t, m_t per step (identity a = 1 on padded steps)
+  float4 av[kSteps], mv[kSteps];
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const bool valid = t0 + tg * kSteps + s < T;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const Gate g = gate_from_ri(f4get(ra[s], j), f4get(ia[s], j), f4get(Lv, j), p.c);
+      f4set(av[s], j, valid ? g.a : 1.f);
+      f4set(mv[s], j, valid ? g.m : 0.f);
+    }
+  }
+  // local summary, backwards over this thread's steps: g -> A g + H
+  float4 A = make_float4(1, 1, 1, 1), H = make_float4(0, 0, 0, 0);
+#pragma unroll
+  for (int s = kSteps - 1; s >= 0; --s)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = f4get(av[s], j);
+      f4set(H, j, a * (f4get(dyv[s], j) + f4get(H, j)));
+      f4set(A, j, f4get(A, j) * a);
+    }
+  *reinterpret_cast<float4*>(&sA[tg][4 * cg]) = A;
+  *reinterpret_cast<float4*>(&sH[tg][4 * cg]) = H;
+  __syncthreads();
+
+  if (tg == 0) {
+    float4 Ag = make_float4(1, 1, 1, 1), Hg = make_float4(0, 0, 0, 0);
+    for (int q = kTG - 1; q >= 0; --q) {
+      const float4 Aq = *reinterpret_cast<const float4*>(&sA[q][4 * cg]);
+      const float4 Hq = *reinterpret_cast<const float4*>(&sH[q][4 * cg]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f4set(Hg, j, fmaf(f4get(Aq, j), f4get(Hg, j), f4get(Hq, j)));
+        f4set(Ag, j, f4get(Aq, j) * f4get(Ag, j));
+      }
+    }
+    uint32_t* incl = p.status;
+    uint32_t* aggA = p.status + size_t(nchunks) * BD;
+    uint32_t* aggH = aggA + size_t(nchunks) * BD;
+    const size_t base = size_t(b) * D + d;
+    if (pos > 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        publish(aggA + size_t(pos) * BD + base + j, f4get(Ag, j));
+        publish(aggH + size_t(pos) * BD + base + j, f4get(Hg, j));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float carry;
+      if (pos == 0) carry = p.dh_T ? p.dh_T[base + j] : 0.f;
+      else carry = lookback_carry(incl + base + j, aggA + base + j, aggH + base + j, pos, BD,
+                                  sLb[cg][0], sLb[cg][1]);
+      publish(incl + size_t(pos) * BD + base + j, fmaf(f4get(Ag, j), carry, f4get(Hg, j)));
+      sCarry[4 * cg + j] = carry;
+    }
+  }
+  float4 Ap = make_float4(1, 1, 1, 1), Hp = make_float4(0, 0, 0, 0);
+  for (int q = kTG - 1; q > tg; --q) {
+    const float4 Aq = *reinterpret_cast<const float4*>(&sA[q][4 * cg]);
+    const float4 Hq = *reinterpret_cast<const float4*>(&sH[q][4 * cg]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f4set(Hp, j, fmaf(f4get(Aq, j), f4get(Hp, j), f4get(Hq, j)));
+      f4set(Ap, j, f4get(Aq, j) * f4get(Ap, j));
+    }
+  }
+  __syncthreads();
+
+  float4 g;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f4set(g, j, fmaf(f4get(Ap, j), sCarry[4 * cg + j], f4get(Hp, j)));
+  double sdza[4] = {0, 0, 0, 0}, sdzi[4] = {0, 0, 0, 0}, sdl[4] = {0, 0, 0, 0};
+  const size_t ld2 = size_t(2) * D;
+#pragma unroll
+  for (int s = kSteps - 1; s >= 0; --s) {
+    const int t = t0 + tg * kSteps + s;
+    float4 dza, dzi, dud;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = f4get(av[s], j), m = f4get(mv[s], j);
+      const float r = f4get(ra[s], j), ii = f4get(ia[s], j), uv = f4get(uu[s], j);
+      const float G = f4get(dyv[s], j) + f4get(g, j);
+      const float mterm = m > 0.f ? ((a * a) / m) * ii * uv : 0.f;
+      const float dl = G * (a * f4get(hp[s], j) - mterm);
+      const float zr = (p.c * f4get(Lv, j)) * dl * r * (1.f - r);
+      const float zi = (G * m * uv) * ii * (1.f - ii);
+      f4set(dza, j, zr);
+      f4set(dzi, j, zi);
+      f4set(dud, j, G * m * ii);
+      if (t < T) {
+        sdza[j] += double(zr);
+        sdzi[j] += double(zi);
+        sdl[j] += double(p.c * r * dl);
+      }
+      f4set(g, j, a * G);
+    }
+    if (t < T) {
+      const size_t row = size_t(b) * T + t;
+      *reinterpret_cast<float4*>(p.du + row * D + d) = dud;
+      if (sizeof(IO) == 2) {
+        float4 lo_a, lo_i;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f4set(lo_a, j, f4get(dza, j) - Io<bf16_t>::round(f4get(dza, j)));
+          f4set(lo_i, j, f4get(dzi, j) - Io<bf16_t>::round(f4get(dzi, j)));
+        }
+        bf16_t* hi = static_cast<bf16_t*>(p.dz_hi);
+        bf16_t* lo = static_cast<bf16_t*>(p.dz_lo);
+        Io<bf16_t>::store4(hi + row * ld2 + d, dza);
+        Io<bf16_t>::store4(hi + row * ld2 + D + d, dzi);
+        Io<bf16_t>::store4(lo + row * ld2 + d, lo_a);
+        Io<bf16_t>::store4(lo + row * ld2 + D + d, lo_i);
+      } else {
+        float* z = static_cast<float*>(p.dz_hi);
+        *reinterpret_cast<float4*>(z + row * ld2 + d) = dza;
+        *reinterpret_cast<float4*>(z + row * ld2 + D + d) = dzi;
+      }
+      if (t == 0 && p.dh0) *reinterpret_cast<float4*>(p.dh0 + size_t(b) * D + d) = g;
+    }
+  }
+  // fixed-order per-tile partial sums
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    sRed[tg][0][4 * cg + j] = sdza[j];
+    sRed[tg][1][4 * cg + j] = sdzi[j];
+    sRed[tg][2][4 * cg + j] = sdl[j];
+  }
+  __syncthreads();
+  if (tid < 3 * kCh) {
+    const int qn = tid / kCh, c = tid % kCh;
+    double acc = 0.0;
+    for (int q = 0; q < kTG; ++q) acc += sRed[q][qn][c];
+    p.partial[(size_t(b) * nchunks + chunk) * 3 * D + size_t(qn) * D + d0 + c] = acc;
+  }
+}
+
+template <typename IO>
+hipError_t launch_scan_bwd(const ScanBwdArgs& a, hipStream_t s) {
+  hipError_t e = launch_fill_u32(a.status, scan_status_words(a.B, a.T, a.D), kEmpty, s);
+  if (e != hipSuccess) return e;
+  e = launch_fill_u32(a.counter, 1, 0u, s);
+  if (e != hipSuccess) return e;
+  const int tiles = scan_chunks(a.T) * a.B * (a.D / kCh);
+  scan_bwd_kernel<IO><<<tiles, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+template hipError_t launch_scan_bwd<float>(const ScanBwdArgs&, hipStream_t);
+template hipError_t launch_scan_bwd<bf16_t>(const ScanBwdArgs&, hipStream_t);
+
+}  // namespace rglru

@@ -1,0 +1,139 @@
+/*
+ * rglru.h - C ABI of the MI355X (gfx950) RG-LRU temporal-branch library (librglru.so).
+ *
+ * The temporal branch of the Griffin/Hawk recurrent block: a causal depthwise Conv1D of
+ * temporal width 4 followed by the RG-LRU layer.  Definitions (the Griffin
+ * model-architecture page, sections "Recurrent block" and "Real-Gated Linear Recurrent
+ * Unit (RG-LRU)", Eq. (1)-(4)), with x_t in the equations read as the conv output u_t:
+ *
+ *   u_t = conv_b + sum_{k=0..3} conv_w[k] * x_{t-k}          (rounded to the I/O dtype)
+ *   r_t = sigma(W_a u_t + b_a)                                (recurrence gate, Eq. 1)
+ *   i_t = sigma(W_x u_t + b_x)                                (input gate, Eq. 2)
+ *   log a_t = c * r_t * log sigma(Lambda)                     (Eq. 3, in log space)
+ *   h_t = a_t * h_{t-1} + sqrt(1 - a_t^2) * (i_t * u_t)       (Eq. 4, diagonal)
+ *   y_t = h_t                                                 (rounded to the I/O dtype)
+ *
+ * Conventions shared by every entry point:
+ *   - Row-major, contiguous tensors, last dimension fastest.  B = batch, T = time,
+ *     D = D_RNN channels.  x, y, dy are [B,T,D]; W_a, W_x are [D,D] stored [out,in]
+ *     (z = W u); conv_w is [4,D] and tap k multiplies x_{t-k}; conv state tensors are
+ *     [B,3,D] holding (x_{t-3}, x_{t-2}, x_{t-1}); vectors b_a, b_x, lambda, conv_b are [D].
+ *   - The I/O dtype `io` applies to x, conv_w, W_a, W_x, y, the conv state and dy.
+ *     Always fp32: b_a, b_x, lambda, conv_b, h0, h_T, the decode state h and every
+ *     gradient output.
+ *   - Shapes: B >= 1, T >= 1, D >= 64 with D % 64 == 0, B*T*D < 2^31.
+ *   - Every pointer is a device pointer, 16-byte aligned, owned by the caller.  The
+ *     library never allocates or frees device memory and keeps no state between calls.
+ *     Scratch memory is passed in as `ws` of at least the size the matching
+ *     *_workspace_bytes query returns.
+ *   - No output may alias an input, except the declared in/out state of the decode step.
+ *   - Every call is asynchronous on `stream` (0 = the null stream).  Arguments are
+ *     validated before any HIP call; invalid arguments return a negative status and
+ *     launch nothing.  A launch failure returns RGLRU_EHIP.  Device faults surface at
+ *     the caller's next synchronisation.  No C++ exception crosses this interface.
+ *   - Calls that share a workspace must not overlap in time.
+ */
+#ifndef RGLRU_H
+#define RGLRU_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RGLRU_OK = 0,
+  RGLRU_EINVAL = -1,     /* null required pointer, B/T/D <= 0, misaligned pointer */
+  RGLRU_ESHAPE = -2,     /* D % 64 != 0 or B*T*D too large */
+  RGLRU_EDTYPE = -3,     /* unknown I/O dtype */
+  RGLRU_EWORKSPACE = -4, /* ws null or smaller than the query returns */
+  RGLRU_EHIP = -5,       /* a kernel launch or HIP runtime call failed */
+  RGLRU_EINTERNAL = -6
+} rglru_status;
+
+typedef enum { RGLRU_F32 = 0, RGLRU_BF16 = 1 } rglru_dtype;
+
+/* Human-readable name of a status code; never NULL. */
+const char* rglru_status_string(int status);
+
+/*
+ * Causal depthwise Conv1D, temporal width 4 (the "Recurrent block" section of the
+ * Griffin model-architecture page: a small separable Conv1D with 4*D parameters).
+ *   u[b,t,d] = RNE_io( b[d] + w[0,d] x[b,t,d] + w[1,d] x[b,t-1,d] + w[2,d] x[b,t-2,d]
+ *                      + w[3,d] x[b,t-3,d] ), evaluated in fp32,
+ * with x[b,t,d] for t < 0 taken from state_in[b,3+t,d] (zeros when state_in is NULL).
+ *   x [B,T,D] io; w [4,D] io; b [D] fp32 or NULL (zero); state_in [B,3,D] io or NULL;
+ *   u [B,T,D] io (output); state_out [B,3,D] io or NULL: the last three time rows of
+ *   [state_in || x].
+ */
+int conv1d_causal4(int B, int T, int D, rglru_dtype io, const void* x, const void* w,
+                   const float* b, const void* state_in, void* u, void* state_out,
+                   hipStream_t stream);
+
+/* Workspace bytes rglru_fwd needs for this shape (0 for invalid arguments). */
+size_t rglru_fwd_workspace_bytes(int B, int T, int D, rglru_dtype io);
+
+/*
+ * Forward of the temporal branch: conv (skipped when conv_w is NULL, then x is already
+ * the RG-LRU input), Eq. (1)-(4), y_t = h_t.
+ *   c: the scalar constant of Eq. (3) (8 on the pages; any value >= 0 accepted).
+ *   conv_b, conv_state_in: as in conv1d_causal4 (nullable).
+ *   W_a, W_x [D,D] io ([out,in]); b_a, b_x, lambda [D] fp32.
+ *   h0 [B,D] fp32, the state before the first token, or NULL (zeros).
+ *   y [B,T,D] io (output).  h_T [B,D] fp32 (output, nullable): the unrounded final
+ *   state.  conv_state_out [B,3,D] io (nullable): conv history after the last token.
+ */
+int rglru_fwd(int B, int T, int D, rglru_dtype io, float c, const void* x,
+              const void* conv_w, const float* conv_b, const void* conv_state_in,
+              const void* W_a, const void* W_x, const float* b_a, const float* b_x,
+              const float* lambda, const float* h0, void* y, float* h_T,
+              void* conv_state_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes rglru_decode_step needs (0 for invalid arguments). */
+size_t rglru_decode_workspace_bytes(int B, int D, rglru_dtype io);
+
+/*
+ * One generation step with the fixed-size state (the blog page "Griffin's Compromise",
+ * section "Hawk": generation reads and writes only the current token and a fixed-size
+ * state).  Equal to rglru_fwd on a length-1 sequence with carried state.
+ *   x_t [B,D] io; conv_state [B,3,D] io, in/out (shifted in place; ignored when conv_w
+ *   is NULL); h [B,D] fp32, in/out (the recurrent state, updated in place);
+ *   y_t [B,D] io (output).  Other arguments as in rglru_fwd.
+ */
+int rglru_decode_step(int B, int D, rglru_dtype io, float c, const void* x_t,
+                      const void* conv_w, const float* conv_b, void* conv_state,
+                      const void* W_a, const void* W_x, const float* b_a,
+                      const float* b_x, const float* lambda, float* h, void* y_t,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes rglru_bwd needs for this shape (0 for invalid arguments). */
+size_t rglru_bwd_workspace_bytes(int B, int T, int D, rglru_dtype io);
+
+/*
+ * Backward of rglru_fwd (the pages give no backward; it is the chain rule through the
+ * definitions above, with both I/O roundings treated as identity).  The forward is
+ * recomputed internally from the same inputs, so nothing is saved between calls.
+ *   dy [B,T,D] io: gradient of y.  dh_T [B,D] fp32 or NULL (zero): gradient of h_T.
+ *   Outputs, all fp32, all overwritten: dx [B,T,D]; dconv_w [4,D]; dconv_b [D];
+ *   dW_a, dW_x [D,D]; db_a, db_x, dlambda [D]; dh0 [B,D] or NULL.
+ *   When conv_w is NULL, dx is the gradient of the RG-LRU input and dconv_w, dconv_b
+ *   may be NULL (they are not written).
+ *   Where sqrt(1 - a_t^2) = 0 its contribution to d(log a_t) is taken as 0.
+ *   Reductions over batch and time run in a fixed order: results are bitwise
+ *   reproducible run to run.
+ */
+int rglru_bwd(int B, int T, int D, rglru_dtype io, float c, const void* x,
+              const void* conv_w, const float* conv_b, const void* conv_state_in,
+              const void* W_a, const void* W_x, const float* b_a, const float* b_x,
+              const float* lambda, const float* h0, const void* dy, const float* dh_T,
+              float* dx, float* dconv_w, float* dconv_b, float* dW_a, float* dW_x,
+              float* db_a, float* db_x, float* dlambda, float* dh0, void* ws,
+              size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RGLRU_H */

@@ -1,0 +1,105 @@
+"""The C ABI of librglru.so, checked without a GPU: the library loads, exports every
+symbol include/rglru.h declares, and rejects invalid arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_linear_rnn_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rglru.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w ]*?[\s\*]+([a-z_][a-z0-9_]*)\s*\(", src, re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return g.load()
+
+
+def test_header_declares_the_expected_entry_points():
+    assert _declared_functions() == sorted(g.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_cover_every_code(lib):
+    codes = {0: "RGLRU_OK", -1: "RGLRU_EINVAL", -2: "RGLRU_ESHAPE", -3: "RGLRU_EDTYPE",
+             -4: "RGLRU_EWORKSPACE", -5: "RGLRU_EHIP", -6: "RGLRU_EINTERNAL"}
+    for c, name in codes.items():
+        assert g.status_string(c).startswith(name)
+    assert "unknown" in g.status_string(7)
+
+
+def test_workspace_queries(lib):
+    assert lib.rglru_fwd_workspace_bytes(8, 2048, 2560, 1) > 8 * 2048 * 2560 * 10
+    assert lib.rglru_fwd_workspace_bytes(1, 1, 63, 1) == 0          # D % 64
+    assert lib.rglru_fwd_workspace_bytes(0, 1, 64, 1) == 0
+    assert lib.rglru_fwd_workspace_bytes(1, 1, 64, 7) == 0          # dtype
+    assert lib.rglru_bwd_workspace_bytes(4, 2048, 5376, 1) > lib.rglru_fwd_workspace_bytes(4, 2048, 5376, 1)
+    assert lib.rglru_decode_workspace_bytes(256, 2560, 1) >= 256 * 2560 * 2
+    assert lib.rglru_decode_workspace_bytes(256, 2560, 0) >= 3 * 256 * 2560 * 4
+
+
+# Fake, 16-byte aligned "device" addresses: validation must reject the call before any HIP
+# call would touch them.  These run only where no GPU is visible, so a validation bug can
+# never hand a fake address to a kernel.
+A = 1 << 20
+no_gpu = pytest.mark.skipif(__import__("torch").cuda.is_available(),
+                            reason="fake device addresses are only passed where no GPU exists")
+BAD = A + 4
+
+
+def _fwd(lib, B=1, T=4, D=64, io=1, c=8.0, **over):
+    args = dict(x=A, conv_w=None, conv_b=None, cs=None, Wa=A, Wx=A, ba=A, bx=A, lam=A, h0=None,
+                y=A, hT=None, cso=None, ws=A, wsb=1 << 40)
+    args.update(over)
+    return lib.rglru_fwd(B, T, D, io, c, *[args[k] for k in
+                         ("x", "conv_w", "conv_b", "cs", "Wa", "Wx", "ba", "bx", "lam", "h0", "y",
+                          "hT", "cso", "ws")], args["wsb"], None)
+
+
+@no_gpu
+def test_fwd_rejects_invalid_arguments(lib):
+    assert _fwd(lib, B=0) == -1
+    assert _fwd(lib, T=-3) == -1
+    assert _fwd(lib, D=96) == -2
+    assert _fwd(lib, B=1 << 12, T=1 << 12, D=1 << 7) == -2            # B*T*D >= 2^31
+    assert _fwd(lib, io=2) == -3
+    for k in ("x", "Wa", "Wx", "ba", "bx", "lam", "y"):
+        assert _fwd(lib, **{k: None}) == -1, k
+    assert _fwd(lib, x=BAD) == -1                                     # misaligned
+    assert _fwd(lib, h0=BAD) == -1
+    assert _fwd(lib, c=-1.0) == -1
+    assert _fwd(lib, c=float("nan")) == -1
+    assert _fwd(lib, ws=None) == -4
+    assert _fwd(lib, wsb=10) == -4
+
+
+@no_gpu
+def test_decode_and_conv_and_bwd_reject_invalid_arguments(lib):
+    r = lib.rglru_decode_step(1, 64, 1, 8.0, A, A, None, None, A, A, A, A, A, A, A, A, 1 << 40, None)
+    assert r == -1                                                    # conv_w without state
+    r = lib.rglru_decode_step(1, 64, 1, 8.0, A, None, None, None, A, A, A, A, A, None, A, A, 1 << 40, None)
+    assert r == -1                                                    # h missing
+    r = lib.rglru_decode_step(1, 64, 1, 8.0, A, None, None, None, A, A, A, A, A, A, A, A, 1, None)
+    assert r == -4
+    assert lib.conv1d_causal4(1, 4, 64, 1, None, A, None, None, A, None, None) == -1
+    assert lib.conv1d_causal4(1, 4, 65, 1, A, A, None, None, A, None, None) == -2
+    assert lib.conv1d_causal4(1, 4, 64, 5, A, A, None, None, A, None, None) == -3
+    bwd = [A] * 21
+    bwd[1] = None        # conv_w NULL
+    r = lib.rglru_bwd(1, 4, 64, 1, 8.0, *bwd, A, 10, None)
+    assert r == -4
+    bwd[10] = None       # dy
+    assert lib.rglru_bwd(1, 4, 64, 1, 8.0, *bwd, A, 1 << 40, None) == -1

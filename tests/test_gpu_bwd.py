@@ -1,0 +1,84 @@
+"""Backward parity (rglru_bwd) with the oracle's chain-rule gradients, element by element,
+at small shapes and at the full fwd+bwd training workload (4 x 2048 x 5376, bf16)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import TOL, device_inputs, err, host
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ["dx", "dconv_w", "dconv_b", "dW_a", "dW_x", "db_a", "db_x", "dlambda", "dh0"]
+
+
+def _check(g, p, dh_T=None, conv=True, what=""):
+    w = p["workload"]
+    d = device_inputs(p)
+    dhT_d = None if dh_T is None else torch.from_numpy(dh_T.astype(np.float32)).cuda()
+    got = g.backward(d["x"], d["conv_w"] if conv else None, d["conv_b"] if conv else None,
+                     d["conv_state"] if conv else None, d["W_a"], d["W_x"], d["b_a"], d["b_x"],
+                     d["lam"], d["h0"], d["dy"], dhT_d, p["c"])
+    torch.cuda.synchronize()
+    want = oracle.backward(p["x"], p["conv_w"] if conv else None, p["conv_b"] if conv else None,
+                           p["conv_state"] if conv else None, p["W_a"], p["W_x"], p["b_a"],
+                           p["b_x"], p["lam"], p["h0"], p["c"], w.io, p["dy"], dh_T)
+    errs = {}
+    for n in NAMES:
+        if want[n] is None:
+            continue
+        errs[n] = err(host(got[n]), want[n])
+    print(f"{what} io={w.io} shape={p['x'].shape} " +
+          " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e <= TOL[w.io], (n, e)
+    return got
+
+
+SMALL = [
+    (workloads.TINY_F32, 1, 64, 64),
+    (workloads.TINY_F32, 2, 200, 128),
+    (workloads.TRAIN_BWD, 2, 300, 192),
+    (workloads.TRAIN_BWD, 1, 130, 64),
+    (workloads.TRAIN_BWD, 3, 1, 64),
+]
+
+
+@pytest.mark.parametrize("w,B,T,D", SMALL, ids=[f"{w.io}-{B}x{T}x{D}" for w, B, T, D in SMALL])
+def test_backward_small_elementwise(lib, w, B, T, D):
+    p = workloads.make_inputs(w.with_shape(B=B, T=T, D=D, with_dy=True))
+    _check(lib, p, what="small")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_backward_with_state_h0_and_dhT(lib, io):
+    w = workloads.TRAIN_BWD.with_shape(B=2, T=257, D=128, io=io, h0="normal", history="normal")
+    p = workloads.make_inputs(w)
+    p["conv_b"] = np.random.default_rng(1).standard_normal(128).astype(np.float32) * 0.1
+    dh_T = np.random.default_rng(2).standard_normal((2, 128))
+    _check(lib, p, dh_T=dh_T, what="state")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_backward_without_conv(lib, io):
+    p = workloads.make_inputs(workloads.TRAIN_BWD.with_shape(B=2, T=150, D=128, io=io))
+    _check(lib, p, conv=False, what="noconv")
+
+
+def test_backward_is_bitwise_reproducible(lib):
+    p = workloads.make_inputs(workloads.TRAIN_BWD.with_shape(B=2, T=300, D=192))
+    d = device_inputs(p)
+    args = (d["x"], d["conv_w"], d["conv_b"], None, d["W_a"], d["W_x"], d["b_a"], d["b_x"],
+            d["lam"], None, d["dy"])
+    g1 = lib.backward(*args, c=p["c"])
+    g2 = lib.backward(*args, c=p["c"])
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert torch.equal(g1[n], g2[n]), n
+
+
+@pytest.mark.timeout(900)
+def test_backward_full_training_workload(lib):
+    p = workloads.make_inputs(workloads.TRAIN_BWD)
+    _check(lib, p, what="full")

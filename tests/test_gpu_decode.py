@@ -1,0 +1,100 @@
+"""Decode-step parity: the fixed-size state (conv history [B,3,D] and h [B,D]) carried
+through consecutive single-token steps (the blog page "Griffin's Compromise", section
+"Hawk": generation reads and writes only the current token and a fixed-size state)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import TOL, TORCH_IO, dev, err, host, sample_channels
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(g, p, steps, channels=None, conv=True):
+    """Run `steps` decode steps on the GPU; compare every y_t (and the final state) with the
+    oracle, restricted to `channels` when given."""
+    w = p["workload"]
+    io = TORCH_IO[w.io]
+    B, D = w.B, w.D
+    S = np.arange(D) if channels is None else channels
+    St = torch.from_numpy(S).cuda()
+    x = dev(p["x"][:steps], io)                        # [steps, B, D]
+    cw = dev(p["conv_w"], io) if conv else None
+    cb = dev(p["conv_b"]) if conv else None
+    hist = dev(p["conv_state"], io)
+    Wa, Wx, ba, bx, lam = (dev(p["W_a"], io), dev(p["W_x"], io), dev(p["b_a"]), dev(p["b_x"]),
+                           dev(p["lam"]))
+    h = dev(p["h0"])
+    ws = g.workspace(g.decode_workspace_bytes(B, D, io))
+    ys = torch.empty((steps, B, len(S)), dtype=torch.float32, device="cuda")
+    y_t = torch.empty((B, D), dtype=io, device="cuda")
+    for t in range(steps):
+        g.rglru_decode_step(x[t], cw, cb, hist, Wa, Wx, ba, bx, lam, h, y_t, ws, p["c"])
+        ys[t] = y_t.float().index_select(1, St)
+    torch.cuda.synchronize()
+    # oracle, channel subset: the conv history is kept for every channel (the gates read all
+    # of u), the state only matters on S
+    hist_o = p["conv_state"].astype(np.float64)
+    h_o = p["h0"].astype(np.float64).copy()
+    worst = 0.0
+    for t in range(steps):
+        o = oracle.forward(p["x"][t][:, None, :], p["conv_w"] if conv else None,
+                           p["conv_b"] if conv else None, hist_o if conv else None, p["W_a"],
+                           p["W_x"], p["b_a"], p["b_x"], p["lam"], h_o, p["c"], w.io, channels=S)
+        worst = max(worst, err(host(ys[t]), o["y"][:, 0, :]))
+        h_o[:, S] = o["h_T"]
+        if conv:
+            hist_o = o["conv_state_out"]
+    eh = err(host(h)[:, S], h_o[:, S])
+    print(f"decode io={w.io} B={B} D={D} steps={steps} err(y)={worst:.3e} err(h)={eh:.3e}", flush=True)
+    assert worst <= TOL[w.io] and eh <= TOL[w.io]
+    if conv:
+        np.testing.assert_array_equal(host(hist), hist_o)
+
+
+@pytest.mark.parametrize("io,B,D", [("f32", 3, 128), ("bf16", 16, 256), ("bf16", 5, 192),
+                                    ("bf16", 300, 64)])
+def test_decode_small_elementwise(lib, io, B, D):
+    p = workloads.make_inputs(workloads.DECODE.with_shape(B=B, D=D, T=40, io=io))
+    _run(lib, p, 40)
+
+
+def test_decode_without_conv(lib):
+    p = workloads.make_inputs(workloads.DECODE.with_shape(B=4, D=128, T=10))
+    _run(lib, p, 10, conv=False)
+
+
+def test_decode_continues_forward(lib):
+    """Prefill with rglru_fwd, then decode: equals one forward over the whole sequence
+    (state consistency on streaming input)."""
+    w = workloads.TRAIN_FWD.with_shape(B=2, T=150, D=128, h0="normal", history="normal")
+    p = workloads.make_inputs(w)
+    io = TORCH_IO[w.io]
+    T1 = 140
+    d = {k: dev(p[k], io) for k in ("x", "conv_w", "W_a", "W_x", "conv_state")}
+    f = {k: dev(p[k]) for k in ("conv_b", "b_a", "b_x", "lam", "h0")}
+    y1, hT, cso = lib.forward(d["x"][:, :T1].contiguous(), d["conv_w"], f["conv_b"], d["conv_state"],
+                              d["W_a"], d["W_x"], f["b_a"], f["b_x"], f["lam"], f["h0"], p["c"])
+    ws = lib.workspace(lib.decode_workspace_bytes(2, 128, io))
+    ys = []
+    y_t = torch.empty((2, 128), dtype=io, device="cuda")
+    for t in range(T1, w.T):
+        lib.rglru_decode_step(d["x"][:, t].contiguous(), d["conv_w"], f["conv_b"], cso, d["W_a"],
+                              d["W_x"], f["b_a"], f["b_x"], f["lam"], hT, y_t, ws, p["c"])
+        ys.append(host(y_t))
+    torch.cuda.synchronize()
+    o = oracle.forward(p["x"], p["conv_w"], p["conv_b"], p["conv_state"], p["W_a"], p["W_x"],
+                       p["b_a"], p["b_x"], p["lam"], p["h0"], p["c"], w.io)
+    assert err(host(y1), o["y"][:, :T1]) <= TOL[w.io]
+    assert err(np.stack(ys, 1), o["y"][:, T1:]) <= TOL[w.io]
+    assert err(host(hT), o["h_T"]) <= TOL[w.io]
+    np.testing.assert_array_equal(host(cso), o["conv_state_out"])
+
+
+@pytest.mark.timeout(900)
+def test_decode_full_workload_channel_subset(lib):
+    p = workloads.make_inputs(workloads.DECODE)
+    S = sample_channels(workloads.DECODE.D, 24, seed=5)
+    _run(lib, p, workloads.DECODE.T, channels=S)

@@ -1,0 +1,105 @@
+"""Properties the pages fix, re-checked on the HIP path itself.
+
+* Gate behaviour (Griffin model-architecture page, "Gate behaviour" with Eq. (3)-(4)):
+  r_t = 0 (b_a = -inf) or c = 0 gives a_t = 1 and sqrt(1 - a_t^2) = 0, so the state is
+  kept bit-exactly: y_t = RNE(h0), h_T = h0.
+* The sqrt(1 - a^2) normalisation: with constant gates, i = 1 and i.i.d. unit-variance
+  input, Var(h_t) = 1 at every t (statistical, N >= 2e5 channels).
+* Streaming input (the blog's checklist item on recurrent-state consistency): a forward
+  split in two with the state handed over equals one forward.
+* The stand-alone conv entry point against the oracle's conv, and bitwise determinism.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import TOL, TORCH_IO, dev, device_inputs, err, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["b_a=-inf", "c=0"])
+def test_closed_recurrence_gate_keeps_state_bit_exact(lib, io, mode):
+    w = workloads.TRAIN_FWD.with_shape(B=3, T=300, D=128, io=io, h0="normal", history="normal")
+    p = workloads.make_inputs(w)
+    d = device_inputs(p)
+    c = p["c"]
+    if mode == "b_a=-inf":
+        d["b_a"] = torch.full((128,), -math.inf, device="cuda")
+    else:
+        c = 0.0
+    y, hT, _ = lib.forward(d["x"], d["conv_w"], d["conv_b"], d["conv_state"], d["W_a"], d["W_x"],
+                           d["b_a"], d["b_x"], d["lam"], d["h0"], c)
+    torch.cuda.synchronize()
+    assert torch.equal(hT, d["h0"])
+    want = d["h0"].to(TORCH_IO[io])[:, None, :].expand_as(y)
+    assert torch.equal(y, want)
+
+
+def test_stationary_variance_is_one(lib):
+    B, T, D = 64, 64, 4096
+    N = B * D
+    rng = np.random.default_rng(31)
+    x = dev(rng.standard_normal((B, T, D)))
+    h0 = dev(rng.standard_normal((B, D)))
+    conv_w = torch.zeros((4, D), device="cuda"); conv_w[0] = 1.0
+    Z = torch.zeros((D, D), device="cuda")
+    lam = dev(rng.uniform(0.0, 5.0, D))
+    y, _, _ = lib.forward(x, conv_w, None, None, Z, Z, torch.zeros(D, device="cuda"),
+                          torch.full((D,), math.inf, device="cuda"), lam, h0, 8.0)
+    torch.cuda.synchronize()
+    var = (y.double() ** 2).mean(dim=(0, 2)).cpu().numpy()
+    assert np.all(np.abs(var - 1.0) < 5 * math.sqrt(2.0 / N)), var
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_split_forward_equals_forward(lib, io):
+    w = workloads.TRAIN_FWD.with_shape(B=2, T=700, D=192, io=io, h0="normal", history="normal")
+    p = workloads.make_inputs(w)
+    d = device_inputs(p)
+    args = (d["W_a"], d["W_x"], d["b_a"], d["b_x"], d["lam"])
+    y, hT, cso = lib.forward(d["x"], d["conv_w"], d["conv_b"], d["conv_state"], *args, d["h0"], p["c"])
+    t1 = 333
+    y1, h1, c1 = lib.forward(d["x"][:, :t1].contiguous(), d["conv_w"], d["conv_b"], d["conv_state"],
+                             *args, d["h0"], p["c"])
+    y2, h2, c2 = lib.forward(d["x"][:, t1:].contiguous(), d["conv_w"], d["conv_b"], c1, *args, h1,
+                             p["c"])
+    torch.cuda.synchronize()
+    assert err(host(torch.cat([y1, y2], 1)), host(y)) <= TOL[io]
+    assert err(host(h2), host(hT)) <= TOL[io]
+    assert torch.equal(c2, cso)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_conv_entry_point_matches_oracle(lib, io):
+    w = workloads.TRAIN_FWD.with_shape(B=3, T=77, D=192, io=io, history="normal")
+    p = workloads.make_inputs(w)
+    p["conv_b"] = np.random.default_rng(3).standard_normal(192).astype(np.float32)
+    d = device_inputs(p)
+    u = torch.empty_like(d["x"])
+    so = torch.empty_like(d["conv_state"])
+    lib.conv1d_causal4(d["x"], d["conv_w"], d["conv_b"], d["conv_state"], u, so)
+    torch.cuda.synchronize()
+    uo, soo = oracle.conv1d_causal4(p["x"], p["conv_w"], p["conv_b"], p["conv_state"], io)
+    # fp32 evaluation of four fmas: error <= 4 * 2^-24 * sum |terms|, then one rounding to
+    # the I/O dtype (half an ulp of each side)
+    mag, _ = oracle.conv1d_causal4(np.abs(p["x"]), np.abs(p["conv_w"]), np.abs(p["conv_b"]),
+                                   np.abs(p["conv_state"]), "f64")
+    ulp = 2.0 ** -23 if io == "f32" else 2.0 ** -7
+    assert np.all(np.abs(host(u) - uo) <= 4 * 2.0 ** -24 * mag + ulp * np.abs(uo))
+    np.testing.assert_array_equal(host(so), soo)
+
+
+def test_forward_is_bitwise_reproducible(lib):
+    p = workloads.make_inputs(workloads.TRAIN_FWD.with_shape(B=4, T=1000, D=256))
+    d = device_inputs(p)
+    outs = [lib.forward(d["x"], d["conv_w"], d["conv_b"], None, d["W_a"], d["W_x"], d["b_a"],
+                        d["b_x"], d["lam"], None, p["c"]) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o[0], outs[0][0]) and torch.equal(o[1], outs[0][1])
