@@ -16,6 +16,8 @@ namespace {
 constexpr size_t kAlign = 256;
 
 size_t io_bytes(rglru_dtype io) { return io == RGLRU_BF16 ? 2 : 4; }
+// Scan state precision: fp32 for bf16 I/O, fp64 for fp32 I/O.
+int acc_bytes(rglru_dtype io) { return io == RGLRU_BF16 ? 4 : 8; }
 bool io_ok(int io) { return io == RGLRU_F32 || io == RGLRU_BF16; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -52,7 +54,7 @@ struct FwdWs {
   void* u;
   float* a;      // fp32 io: z^a, then a in place
   float* beta;   // fp32 io: z^x, then beta in place
-  uint32_t* status;
+  void* status;
   uint32_t* counter;
 };
 
@@ -62,7 +64,7 @@ FwdWs carve_fwd(Carver& cv, int B, int T, int D, rglru_dtype io) {
   w.u = cv.take<unsigned char>(n * io_bytes(io));
   w.a = cv.take<float>(n);
   w.beta = cv.take<float>(n);
-  w.status = cv.take<uint32_t>(scan_status_words(B, T, D));
+  w.status = cv.take<unsigned char>(scan_status_bytes(B, T, D, acc_bytes(io)));
   w.counter = cv.take<uint32_t>(64);
   return w;
 }
@@ -89,7 +91,7 @@ struct BwdWs {
   void* u;
   float* r;
   float* i;
-  float* h_all;
+  void* h_all;   // scan state type
   void* dz_hi;   // [M, 2D] (bf16) or fp32 dz
   void* dz_lo;   // [M, 2D] bf16 (bf16 io only)
   void* dzT_hi;  // [2D, Mp]
@@ -99,7 +101,7 @@ struct BwdWs {
   float* du;     // [M, D]
   double* scan_part;
   double* conv_part;
-  uint32_t* status;
+  void* status;
   uint32_t* counter;
 };
 
@@ -111,7 +113,7 @@ BwdWs carve_bwd(Carver& cv, int B, int T, int D, rglru_dtype io) {
   w.u = cv.take<unsigned char>(n * eb);
   w.r = cv.take<float>(n);
   w.i = cv.take<float>(n);
-  w.h_all = cv.take<float>(n);
+  w.h_all = cv.take<unsigned char>(n * acc_bytes(io));
   w.dz_hi = cv.take<unsigned char>(2 * n * eb);
   w.dz_lo = io == RGLRU_BF16 ? cv.take<unsigned char>(2 * n * eb) : nullptr;
   w.dzT_hi = cv.take<unsigned char>(2 * size_t(D) * Mp * eb);
@@ -121,7 +123,7 @@ BwdWs carve_bwd(Carver& cv, int B, int T, int D, rglru_dtype io) {
   w.du = cv.take<float>(n);
   w.scan_part = cv.take<double>(P * 3 * D);
   w.conv_part = cv.take<double>(P * 5 * D);
-  w.status = cv.take<uint32_t>(scan_status_words(B, T, D));
+  w.status = cv.take<unsigned char>(scan_status_bytes(B, T, D, acc_bytes(io)));
   w.counter = cv.take<uint32_t>(64);
   return w;
 }
@@ -202,8 +204,8 @@ int rglru_fwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const
   sa.a = w.a; sa.beta = w.beta; sa.from_ri = false; sa.lam = lambda; sa.c = c;
   sa.h0 = h0; sa.y = y; sa.h_all = nullptr; sa.h_T = h_T;
   sa.status = w.status; sa.counter = w.counter;
-  if (io == RGLRU_BF16) RG_CHECK(launch_scan_fwd<bf16_t>(sa, stream));
-  else RG_CHECK(launch_scan_fwd<float>(sa, stream));
+  if (io == RGLRU_BF16) RG_CHECK((launch_scan_fwd<bf16_t, float>(sa, stream)));
+  else RG_CHECK((launch_scan_fwd<float, double>(sa, stream)));
   return RGLRU_OK;
 }
 
@@ -304,8 +306,8 @@ int rglru_bwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const
   sf.a = w.r; sf.beta = w.i; sf.from_ri = true; sf.lam = lambda; sf.c = c;
   sf.h0 = h0; sf.y = nullptr; sf.h_all = w.h_all; sf.h_T = nullptr;
   sf.status = w.status; sf.counter = w.counter;
-  if (bf) RG_CHECK(launch_scan_fwd<bf16_t>(sf, stream));
-  else RG_CHECK(launch_scan_fwd<float>(sf, stream));
+  if (bf) RG_CHECK((launch_scan_fwd<bf16_t, float>(sf, stream)));
+  else RG_CHECK((launch_scan_fwd<float, double>(sf, stream)));
 
   // 2. reverse scan: dz^a, dz^x, the direct du term, dh0, partial sums
   float* du = conv_w ? w.du : dx;   // without the conv, du is dx
@@ -315,8 +317,8 @@ int rglru_bwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const
   sb.dy = dy; sb.dh_T = dh_T; sb.lam = lambda; sb.c = c;
   sb.dz_hi = w.dz_hi; sb.dz_lo = w.dz_lo; sb.du = du; sb.dh0 = dh0;
   sb.partial = w.scan_part; sb.status = w.status; sb.counter = w.counter;
-  if (bf) RG_CHECK(launch_scan_bwd<bf16_t>(sb, stream));
-  else RG_CHECK(launch_scan_bwd<float>(sb, stream));
+  if (bf) RG_CHECK((launch_scan_bwd<bf16_t, float>(sb, stream)));
+  else RG_CHECK((launch_scan_bwd<float, double>(sb, stream)));
 
   // 3. du += [dz^a dz^x] [W_a; W_x]   (K = 2D; the B operand is [W_a; W_x]^T)
   PlainGemmArgs pg{};

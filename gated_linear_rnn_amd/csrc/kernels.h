@@ -73,20 +73,22 @@ struct ScanFwdArgs {
   float c;
   const float* h0;        // [B,D] or NULL
   void* y;                // [B,T,D] io or NULL
-  float* h_all;           // [B,T,D] fp32 or NULL: every h_t
+  void* h_all;            // [B,T,D] of the scan state type (Acc), or NULL: every h_t
   float* h_T;             // [B,D] or NULL
-  uint32_t* status;       // look-back words, scan_status_words(B,T,D) of them
+  void* status;           // look-back words, scan_status_bytes(B,T,D,sizeof(Acc)) bytes
   uint32_t* counter;      // one ticket counter (zeroed with the status words)
 };
-size_t scan_status_words(int B, int T, int D);
-template <typename IO> hipError_t launch_scan_fwd(const ScanFwdArgs& a, hipStream_t s);
+// Look-back status bytes of a scan whose state type has acc_bytes bytes (4 or 8).
+size_t scan_status_bytes(int B, int T, int D, int acc_bytes);
+// Acc = float for bf16 I/O, double for fp32 I/O.
+template <typename IO, typename Acc> hipError_t launch_scan_fwd(const ScanFwdArgs& a, hipStream_t s);
 
 struct ScanBwdArgs {
   int B, T, D;
   const void* u;          // [B,T,D] io
   const float* r;         // [B,T,D] fp32
   const float* i;         // [B,T,D] fp32
-  const float* h_all;     // [B,T,D] fp32, h_t
+  const void* h_all;      // [B,T,D] of the scan state type (Acc), h_t
   const float* h0;        // [B,D] or NULL
   const void* dy;         // [B,T,D] io
   const float* dh_T;      // [B,D] or NULL
@@ -98,11 +100,11 @@ struct ScanBwdArgs {
   float* du;              // [B,T,D] fp32: G m i (the direct term of du)
   float* dh0;             // [B,D] or NULL
   double* partial;        // [B * nchunks, 3, D]: db_a, db_x, dL partial sums
-  uint32_t* status;
+  void* status;
   uint32_t* counter;
 };
 int scan_chunks(int T);
-template <typename IO> hipError_t launch_scan_bwd(const ScanBwdArgs& a, hipStream_t s);
+template <typename IO, typename Acc> hipError_t launch_scan_bwd(const ScanBwdArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- bwd.hip
 template <typename E>

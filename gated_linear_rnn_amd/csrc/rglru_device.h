@@ -116,17 +116,38 @@ __device__ __forceinline__ Gate gate_from_z(float zr, float zi, float L, float c
 
 // ------------------------------------------------------------------ scan look-back
 // Chunk summaries of the affine map h -> A h + H are published word by word with
-// agent-scope atomics.  A word holding kEmpty has not been written yet; a published
-// value that happens to have those bits is replaced by the canonical quiet NaN.
-constexpr uint32_t kEmpty = 0xffffffffu;
+// agent-scope atomics, one word per value: 32-bit words for an fp32 scan state, 64-bit
+// words for an fp64 one.  A word holding all ones has not been written yet; a published
+// value with those bits is replaced by the canonical quiet NaN.
+template <typename Acc> struct Words;
+template <> struct Words<float> {
+  typedef uint32_t W;
+  static constexpr W kEmpty = 0xffffffffu;
+  static constexpr W kNaN = 0x7fc00000u;
+  __device__ __forceinline__ static W bits(float v) { return __float_as_uint(v); }
+  __device__ __forceinline__ static float val(W w) { return __uint_as_float(w); }
+};
+template <> struct Words<double> {
+  typedef unsigned long long W;
+  static constexpr W kEmpty = ~0ull;
+  static constexpr W kNaN = 0x7ff8000000000000ull;
+  __device__ __forceinline__ static W bits(double v) { return (W)__double_as_longlong(v); }
+  __device__ __forceinline__ static double val(W w) { return __longlong_as_double((long long)w); }
+};
 
-__device__ __forceinline__ void publish(uint32_t* p, float v) {
-  uint32_t u = __float_as_uint(v);
-  if (u == kEmpty) u = 0x7fc00000u;
+__device__ __forceinline__ float fmaA(float a, float b, float c) { return fmaf(a, b, c); }
+__device__ __forceinline__ double fmaA(double a, double b, double c) { return fma(a, b, c); }
+
+template <typename Acc>
+__device__ __forceinline__ void publish(typename Words<Acc>::W* p, Acc v) {
+  typename Words<Acc>::W u = Words<Acc>::bits(v);
+  if (u == Words<Acc>::kEmpty) u = Words<Acc>::kNaN;
   __hip_atomic_store(p, u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t peek(const uint32_t* p) {
-  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+template <typename Acc>
+__device__ __forceinline__ typename Words<Acc>::W peek(const typename Words<Acc>::W* p) {
+  return __hip_atomic_load(const_cast<typename Words<Acc>::W*>(p), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Upper bound on polls of one predecessor word; beyond it the carry becomes NaN (the
@@ -137,42 +158,45 @@ constexpr int kMaxPolls = 1 << 20;
 // are indexed by chain position (0 = first chunk of the chain) times `stride`.  Position
 // `pos` walks back over positions pos-1, pos-2, ... collecting published aggregates until
 // it meets a published inclusive state, then applies the collected aggregates forward in
-// chain order: h <- fmaf(A_j, h, H_j).  Every inclusive state is published as
-// fmaf(A, carry, H), so the carry equals, bit for bit, the one a strictly sequential chain
+// chain order: h <- fma(A_j, h, H_j).  Every inclusive state is published as
+// fma(A, carry, H), so the carry equals, bit for bit, the one a strictly sequential chain
 // would compute, whatever the timing: results are reproducible run to run.  At most
 // kWindow aggregates are collected; past that the walk waits for an inclusive state.
-// `bufA`, `bufH` are kWindow floats of scratch (LDS) owned by the calling thread.
+// `bufA`, `bufH` are kWindow values of scratch (LDS) owned by the calling thread.
 constexpr int kWindow = 16;
 
-__device__ __forceinline__ float lookback_carry(const uint32_t* incl, const uint32_t* aggA,
-                                                const uint32_t* aggH, int pos, size_t stride,
-                                                float* bufA, float* bufH) {
+template <typename Acc>
+__device__ __forceinline__ Acc lookback_carry(const typename Words<Acc>::W* incl,
+                                              const typename Words<Acc>::W* aggA,
+                                              const typename Words<Acc>::W* aggH, int pos,
+                                              size_t stride, Acc* bufA, Acc* bufH) {
+  typedef Words<Acc> Wd;
   int j = pos - 1;
   int n = 0;
   int polls = 0;
-  float h;
+  Acc h;
   while (true) {
-    const uint32_t vi = peek(incl + size_t(j) * stride);
-    if (vi != kEmpty) {
-      h = __uint_as_float(vi);
+    const typename Wd::W vi = peek<Acc>(incl + size_t(j) * stride);
+    if (vi != Wd::kEmpty) {
+      h = Wd::val(vi);
       break;
     }
     if (n < kWindow) {
-      const uint32_t va = peek(aggA + size_t(j) * stride);
-      const uint32_t vh = peek(aggH + size_t(j) * stride);
-      if (va != kEmpty && vh != kEmpty) {
-        bufA[n] = __uint_as_float(va);
-        bufH[n] = __uint_as_float(vh);
+      const typename Wd::W va = peek<Acc>(aggA + size_t(j) * stride);
+      const typename Wd::W vh = peek<Acc>(aggH + size_t(j) * stride);
+      if (va != Wd::kEmpty && vh != Wd::kEmpty) {
+        bufA[n] = Wd::val(va);
+        bufH[n] = Wd::val(vh);
         ++n;
         --j;   // position 0 always publishes an inclusive state, so j stays >= 0
         polls = 0;
         continue;
       }
     }
-    if (++polls > kMaxPolls) return __uint_as_float(0x7fc00000u);
+    if (++polls > kMaxPolls) return Wd::val(Wd::kNaN);
     __builtin_amdgcn_s_sleep(1);
   }
-  for (int k = n - 1; k >= 0; --k) h = fmaf(bufA[k], h, bufH[k]);
+  for (int k = n - 1; k >= 0; --k) h = fmaA(bufA[k], h, bufH[k]);
   return h;
 }
 

@@ -19,6 +19,7 @@
 //     tiles with a decoupled look-back (tiles take tickets in time order from an atomic
 //     counter, so every tile a tile waits on has already started: no deadlock);
 //   * each thread then re-runs its 8 steps from its exact incoming state and writes y.
+// The scan state type Acc is fp32 for bf16 I/O and fp64 for fp32 I/O.
 #include "rglru_device.h"
 #include "kernels.h"
 
@@ -30,15 +31,34 @@ constexpr int kChunk = kSteps * kTG;      // 128 time steps per tile
 constexpr int kCh = 64;                   // channels per tile
 
 int scan_chunks(int T) { return (T + kChunk - 1) / kChunk; }
-size_t scan_status_words(int B, int T, int D) { return 3ull * scan_chunks(T) * size_t(B) * D; }
+size_t scan_status_bytes(int B, int T, int D, int acc_bytes) {
+  return 3ull * scan_chunks(T) * size_t(B) * D * size_t(acc_bytes);
+}
 
-template <typename IO>
+// Compose the summaries of time groups [q0, q1) of this tile (ascending order of
+// application) for 4 channels: h -> A h + H.
+template <typename Acc>
+__device__ __forceinline__ void compose_groups(const Acc (*sA)[kCh], const Acc (*sH)[kCh], int c0,
+                                               int q0, int q1, int step, Acc* A, Acc* H) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { A[j] = Acc(1); H[j] = Acc(0); }
+  for (int q = q0; q != q1; q += step)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const Acc Aq = sA[q][c0 + j], Hq = sH[q][c0 + j];
+      H[j] = fmaA(Aq, H[j], Hq);
+      A[j] = Aq * A[j];
+    }
+}
+
+template <typename IO, typename Acc>
 __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanFwdArgs p) {
+  typedef typename Words<Acc>::W W;
   __shared__ uint32_t s_ticket;
   __shared__ float xs[(kChunk + 3) * kCh];
-  __shared__ float sA[kTG][kCh], sH[kTG][kCh];
-  __shared__ float sCarry[kCh];
-  __shared__ float sLb[16][2][kWindow];
+  __shared__ Acc sA[kTG][kCh], sH[kTG][kCh];
+  __shared__ Acc sCarry[kCh];
+  __shared__ Acc sLb[16][2][kWindow];
 
   const int B = p.B, T = p.T, D = p.D;
   const int tid = threadIdx.x;
@@ -94,7 +114,7 @@ __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanFwdArgs p) {
   __syncthreads();
 
   // a_t and beta_t u_t for each step
-  float4 bu[kSteps];
+  Acc av[kSteps][4], bu[kSteps][4];
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) {
     const int rr = tg * kSteps + s + 3;
@@ -110,108 +130,101 @@ __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanFwdArgs p) {
                                f4get(w3, j), f4get(x0, j), f4get(x1, j), f4get(x2, j),
                                f4get(x3, j)));
     }
-    if (p.from_ri) {
-      const bool valid = t0 + tg * kSteps + s < T;
+    const bool valid = t0 + tg * kSteps + s < T;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const Gate g = gate_from_ri(f4get(ga[s], j), f4get(gb[s], j), f4get(Lv, j), p.c);
-        f4set(ga[s], j, valid ? g.a : 1.f);
-        f4set(gb[s], j, valid ? g.m * g.i : 0.f);
+    for (int j = 0; j < 4; ++j) {
+      float a = f4get(ga[s], j), beta = f4get(gb[s], j);
+      if (p.from_ri) {
+        const Gate g = gate_from_ri(a, beta, f4get(Lv, j), p.c);
+        a = valid ? g.a : 1.f;
+        beta = valid ? g.m * g.i : 0.f;
       }
+      av[s][j] = Acc(a);
+      bu[s][j] = Acc(beta) * Acc(f4get(u, j));
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) f4set(bu[s], j, f4get(gb[s], j) * f4get(u, j));
   }
 
   // local summary of this thread's steps: h -> A h + H
-  float4 A = make_float4(1, 1, 1, 1), H = make_float4(0, 0, 0, 0);
+  Acc A[4], H[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { A[j] = Acc(1); H[j] = Acc(0); }
 #pragma unroll
   for (int s = 0; s < kSteps; ++s)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      f4set(H, j, fmaf(f4get(ga[s], j), f4get(H, j), f4get(bu[s], j)));
-      f4set(A, j, f4get(A, j) * f4get(ga[s], j));
+      H[j] = fmaA(av[s][j], H[j], bu[s][j]);
+      A[j] = A[j] * av[s][j];
     }
-  *reinterpret_cast<float4*>(&sA[tg][4 * cg]) = A;
-  *reinterpret_cast<float4*>(&sH[tg][4 * cg]) = H;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { sA[tg][4 * cg + j] = A[j]; sH[tg][4 * cg + j] = H[j]; }
   __syncthreads();
 
   if (tg == 0) {
     // tile aggregate, publish, look back, publish the inclusive state
-    float4 Ag = make_float4(1, 1, 1, 1), Hg = make_float4(0, 0, 0, 0);
-    for (int q = 0; q < kTG; ++q) {
-      const float4 Aq = *reinterpret_cast<const float4*>(&sA[q][4 * cg]);
-      const float4 Hq = *reinterpret_cast<const float4*>(&sH[q][4 * cg]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f4set(Hg, j, fmaf(f4get(Aq, j), f4get(Hg, j), f4get(Hq, j)));
-        f4set(Ag, j, f4get(Aq, j) * f4get(Ag, j));
-      }
-    }
-    uint32_t* incl = p.status;
-    uint32_t* aggA = p.status + size_t(nchunks) * BD;
-    uint32_t* aggH = aggA + size_t(nchunks) * BD;
+    Acc Ag[4], Hg[4];
+    compose_groups<Acc>(sA, sH, 4 * cg, 0, kTG, 1, Ag, Hg);
+    W* incl = static_cast<W*>(p.status);
+    W* aggA = incl + size_t(nchunks) * BD;
+    W* aggH = aggA + size_t(nchunks) * BD;
     const size_t base = size_t(b) * D + d;
     if (chunk > 0) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        publish(aggA + size_t(chunk) * BD + base + j, f4get(Ag, j));
-        publish(aggH + size_t(chunk) * BD + base + j, f4get(Hg, j));
+        publish<Acc>(aggA + size_t(chunk) * BD + base + j, Ag[j]);
+        publish<Acc>(aggH + size_t(chunk) * BD + base + j, Hg[j]);
       }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float carry;
-      if (chunk == 0) carry = p.h0 ? p.h0[base + j] : 0.f;
-      else carry = lookback_carry(incl + base + j, aggA + base + j, aggH + base + j, chunk, BD,
-                                  sLb[cg][0], sLb[cg][1]);
-      publish(incl + size_t(chunk) * BD + base + j, fmaf(f4get(Ag, j), carry, f4get(Hg, j)));
+      Acc carry;
+      if (chunk == 0) carry = p.h0 ? Acc(p.h0[base + j]) : Acc(0);
+      else carry = lookback_carry<Acc>(incl + base + j, aggA + base + j, aggH + base + j, chunk,
+                                       BD, sLb[cg][0], sLb[cg][1]);
+      publish<Acc>(incl + size_t(chunk) * BD + base + j, fmaA(Ag[j], carry, Hg[j]));
       sCarry[4 * cg + j] = carry;
     }
   }
   // exclusive prefix of the time groups before this one
-  float4 Ap = make_float4(1, 1, 1, 1), Hp = make_float4(0, 0, 0, 0);
-  for (int q = 0; q < tg; ++q) {
-    const float4 Aq = *reinterpret_cast<const float4*>(&sA[q][4 * cg]);
-    const float4 Hq = *reinterpret_cast<const float4*>(&sH[q][4 * cg]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f4set(Hp, j, fmaf(f4get(Aq, j), f4get(Hp, j), f4get(Hq, j)));
-      f4set(Ap, j, f4get(Aq, j) * f4get(Ap, j));
-    }
-  }
+  Acc Ap[4], Hp[4];
+  compose_groups<Acc>(sA, sH, 4 * cg, 0, tg, 1, Ap, Hp);
   __syncthreads();
 
-  float4 h;
+  Acc h[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f4set(h, j, fmaf(f4get(Ap, j), sCarry[4 * cg + j], f4get(Hp, j)));
+  for (int j = 0; j < 4; ++j) h[j] = fmaA(Ap[j], sCarry[4 * cg + j], Hp[j]);
   IO* y = static_cast<IO*>(p.y);
+  Acc* h_all = static_cast<Acc*>(p.h_all);
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) {
     const int t = t0 + tg * kSteps + s;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) f4set(h, j, fmaf(f4get(ga[s], j), f4get(h, j), f4get(bu[s], j)));
+    for (int j = 0; j < 4; ++j) h[j] = fmaA(av[s][j], h[j], bu[s][j]);
     if (t < T) {
       const size_t o = (size_t(b) * T + t) * D + d;
-      if (y) Io<IO>::store4(y + o, h);
-      if (p.h_all) *reinterpret_cast<float4*>(p.h_all + o) = h;
-      if (t == T - 1 && p.h_T) *reinterpret_cast<float4*>(p.h_T + size_t(b) * D + d) = h;
+      const float4 hf = make_float4(float(h[0]), float(h[1]), float(h[2]), float(h[3]));
+      if (y) Io<IO>::store4(y + o, hf);
+      if (h_all) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) h_all[o + j] = h[j];
+      }
+      if (t == T - 1 && p.h_T) *reinterpret_cast<float4*>(p.h_T + size_t(b) * D + d) = hf;
     }
   }
 }
 
-template <typename IO>
+template <typename IO, typename Acc>
 hipError_t launch_scan_fwd(const ScanFwdArgs& a, hipStream_t s) {
-  hipError_t e = launch_fill_u32(a.status, scan_status_words(a.B, a.T, a.D), kEmpty, s);
+  hipError_t e = launch_fill_u32(static_cast<uint32_t*>(a.status),
+                                 scan_status_bytes(a.B, a.T, a.D, sizeof(Acc)) / 4, 0xffffffffu, s);
   if (e != hipSuccess) return e;
   e = launch_fill_u32(a.counter, 1, 0u, s);
   if (e != hipSuccess) return e;
   const int tiles = scan_chunks(a.T) * a.B * (a.D / kCh);
-  scan_fwd_kernel<IO><<<tiles, 256, 0, s>>>(a);
+  scan_fwd_kernel<IO, Acc><<<tiles, 256, 0, s>>>(a);
   return hipGetLastError();
 }
-template hipError_t launch_scan_fwd<float>(const ScanFwdArgs&, hipStream_t);
-template hipError_t launch_scan_fwd<bf16_t>(const ScanFwdArgs&, hipStream_t);
+template hipError_t launch_scan_fwd<float, double>(const ScanFwdArgs&, hipStream_t);
+template hipError_t launch_scan_fwd<bf16_t, float>(const ScanFwdArgs&, hipStream_t);
 
 // ------------------------------------------------------------------ reverse scan
 // Backward through Eq. (4) (the pages give no backward; chain rule).  With G_t the total
@@ -222,13 +235,14 @@ template hipError_t launch_scan_fwd<bf16_t>(const ScanFwdArgs&, hipStream_t);
 // then forms the local gradients:
 //     d(log a) = G (a h_{t-1} - (a^2/m) i u)   [m-path term 0 where m = 0]
 //     dz^a = c L d(log a) r (1-r),  dz^x = G m u i (1-i),  du_direct = G m i,
-// and per-tile partial sums of dz^a, dz^x and c r d(log a) (for db_a, db_x, dLambda).
-template <typename IO>
+// and per-tile fp64 partial sums of dz^a, dz^x and c r d(log a) (for db_a, db_x, dLambda).
+template <typename IO, typename Acc>
 __global__ __launch_bounds__(256) void scan_bwd_kernel(ScanBwdArgs p) {
+  typedef typename Words<Acc>::W W;
   __shared__ uint32_t s_ticket;
-  __shared__ float sA[kTG][kCh], sH[kTG][kCh];
-  __shared__ float sCarry[kCh];
-  __shared__ float sLb[16][2][kWindow];
+  __shared__ Acc sA[kTG][kCh], sH[kTG][kCh];
+  __shared__ Acc sCarry[kCh];
+  __shared__ Acc sLb[16][2][kWindow];
   __shared__ double sRed[kTG][3][kCh];
 
   const int B = p.B, T = p.T, D = p.D;
@@ -246,9 +260,11 @@ __global__ __launch_bounds__(256) void scan_bwd_kernel(ScanBwdArgs p) {
   const int d = d0 + 4 * cg;
   const size_t BD = size_t(B) * D;
 
-  float4 ra[kSteps], ia[kSteps], hp[kSteps], uu[kSteps], dyv[kSteps];
+  float4 ra[kSteps], ia[kSteps], uu[kSteps], dyv[kSteps];
+  Acc hp[kSteps][4];
   const IO* u = static_cast<const IO*>(p.u);
   const IO* dy = static_cast<const IO*>(p.dy);
+  const Acc* h_all = static_cast<const Acc*>(p.h_all);
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) {
     const int t = t0 + tg * kSteps + s;
@@ -258,113 +274,105 @@ __global__ __launch_bounds__(256) void scan_bwd_kernel(ScanBwdArgs p) {
       ia[s] = *reinterpret_cast<const float4*>(p.i + o);
       uu[s] = Io<IO>::load4(u + o);
       dyv[s] = Io<IO>::load4(dy + o);
-      if (t > 0) hp[s] = *reinterpret_cast<const float4*>(p.h_all + o - D);
-      else hp[s] = p.h0 ? *reinterpret_cast<const float4*>(p.h0 + size_t(b) * D + d)
-                        : make_float4(0, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (t > 0) hp[s][j] = h_all[o - D + j];
+        else hp[s][j] = p.h0 ? Acc(p.h0[size_t(b) * D + d + j]) : Acc(0);
+      }
     } else {
-      ra[s] = ia[s] = hp[s] = uu[s] = dyv[s] = make_float4(0, 0, 0, 0);
+      ra[s] = ia[s] = uu[s] = dyv[s] = make_float4(0, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hp[s][j] = Acc(0);
     }
   }
   float4 Lv;
 #pragma unroll
   for (int j = 0; j < 4; ++j) f4set(Lv, j, log_sigmoidf(p.lam[d + j]));
   // a_t, m_t per step (identity a = 1 on padded steps)
-  float4 av[kSteps], mv[kSteps];
+  float av[kSteps][4], mv[kSteps][4];
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) {
     const bool valid = t0 + tg * kSteps + s < T;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const Gate g = gate_from_ri(f4get(ra[s], j), f4get(ia[s], j), f4get(Lv, j), p.c);
-      f4set(av[s], j, valid ? g.a : 1.f);
-      f4set(mv[s], j, valid ? g.m : 0.f);
+      av[s][j] = valid ? g.a : 1.f;
+      mv[s][j] = valid ? g.m : 0.f;
     }
   }
   // local summary, backwards over this thread's steps: g -> A g + H
-  float4 A = make_float4(1, 1, 1, 1), H = make_float4(0, 0, 0, 0);
+  Acc A[4], H[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { A[j] = Acc(1); H[j] = Acc(0); }
 #pragma unroll
   for (int s = kSteps - 1; s >= 0; --s)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float a = f4get(av[s], j);
-      f4set(H, j, a * (f4get(dyv[s], j) + f4get(H, j)));
-      f4set(A, j, f4get(A, j) * a);
+      const Acc a = av[s][j];
+      H[j] = a * (Acc(f4get(dyv[s], j)) + H[j]);
+      A[j] = A[j] * a;
     }
-  *reinterpret_cast<float4*>(&sA[tg][4 * cg]) = A;
-  *reinterpret_cast<float4*>(&sH[tg][4 * cg]) = H;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { sA[tg][4 * cg + j] = A[j]; sH[tg][4 * cg + j] = H[j]; }
   __syncthreads();
 
   if (tg == 0) {
-    float4 Ag = make_float4(1, 1, 1, 1), Hg = make_float4(0, 0, 0, 0);
-    for (int q = kTG - 1; q >= 0; --q) {
-      const float4 Aq = *reinterpret_cast<const float4*>(&sA[q][4 * cg]);
-      const float4 Hq = *reinterpret_cast<const float4*>(&sH[q][4 * cg]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f4set(Hg, j, fmaf(f4get(Aq, j), f4get(Hg, j), f4get(Hq, j)));
-        f4set(Ag, j, f4get(Aq, j) * f4get(Ag, j));
-      }
-    }
-    uint32_t* incl = p.status;
-    uint32_t* aggA = p.status + size_t(nchunks) * BD;
-    uint32_t* aggH = aggA + size_t(nchunks) * BD;
+    Acc Ag[4], Hg[4];
+    compose_groups<Acc>(sA, sH, 4 * cg, kTG - 1, -1, -1, Ag, Hg);
+    W* incl = static_cast<W*>(p.status);
+    W* aggA = incl + size_t(nchunks) * BD;
+    W* aggH = aggA + size_t(nchunks) * BD;
     const size_t base = size_t(b) * D + d;
     if (pos > 0) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        publish(aggA + size_t(pos) * BD + base + j, f4get(Ag, j));
-        publish(aggH + size_t(pos) * BD + base + j, f4get(Hg, j));
+        publish<Acc>(aggA + size_t(pos) * BD + base + j, Ag[j]);
+        publish<Acc>(aggH + size_t(pos) * BD + base + j, Hg[j]);
       }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float carry;
-      if (pos == 0) carry = p.dh_T ? p.dh_T[base + j] : 0.f;
-      else carry = lookback_carry(incl + base + j, aggA + base + j, aggH + base + j, pos, BD,
-                                  sLb[cg][0], sLb[cg][1]);
-      publish(incl + size_t(pos) * BD + base + j, fmaf(f4get(Ag, j), carry, f4get(Hg, j)));
+      Acc carry;
+      if (pos == 0) carry = p.dh_T ? Acc(p.dh_T[base + j]) : Acc(0);
+      else carry = lookback_carry<Acc>(incl + base + j, aggA + base + j, aggH + base + j, pos, BD,
+                                       sLb[cg][0], sLb[cg][1]);
+      publish<Acc>(incl + size_t(pos) * BD + base + j, fmaA(Ag[j], carry, Hg[j]));
       sCarry[4 * cg + j] = carry;
     }
   }
-  float4 Ap = make_float4(1, 1, 1, 1), Hp = make_float4(0, 0, 0, 0);
-  for (int q = kTG - 1; q > tg; --q) {
-    const float4 Aq = *reinterpret_cast<const float4*>(&sA[q][4 * cg]);
-    const float4 Hq = *reinterpret_cast<const float4*>(&sH[q][4 * cg]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f4set(Hp, j, fmaf(f4get(Aq, j), f4get(Hp, j), f4get(Hq, j)));
-      f4set(Ap, j, f4get(Aq, j) * f4get(Ap, j));
-    }
-  }
+  Acc Ap[4], Hp[4];
+  compose_groups<Acc>(sA, sH, 4 * cg, kTG - 1, tg, -1, Ap, Hp);
   __syncthreads();
 
-  float4 g;
+  Acc g[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f4set(g, j, fmaf(f4get(Ap, j), sCarry[4 * cg + j], f4get(Hp, j)));
+  for (int j = 0; j < 4; ++j) g[j] = fmaA(Ap[j], sCarry[4 * cg + j], Hp[j]);
   double sdza[4] = {0, 0, 0, 0}, sdzi[4] = {0, 0, 0, 0}, sdl[4] = {0, 0, 0, 0};
   const size_t ld2 = size_t(2) * D;
+  const Acc cL[4] = {Acc(p.c) * Acc(f4get(Lv, 0)), Acc(p.c) * Acc(f4get(Lv, 1)),
+                     Acc(p.c) * Acc(f4get(Lv, 2)), Acc(p.c) * Acc(f4get(Lv, 3))};
 #pragma unroll
   for (int s = kSteps - 1; s >= 0; --s) {
     const int t = t0 + tg * kSteps + s;
     float4 dza, dzi, dud;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float a = f4get(av[s], j), m = f4get(mv[s], j);
-      const float r = f4get(ra[s], j), ii = f4get(ia[s], j), uv = f4get(uu[s], j);
-      const float G = f4get(dyv[s], j) + f4get(g, j);
-      const float mterm = m > 0.f ? ((a * a) / m) * ii * uv : 0.f;
-      const float dl = G * (a * f4get(hp[s], j) - mterm);
-      const float zr = (p.c * f4get(Lv, j)) * dl * r * (1.f - r);
-      const float zi = (G * m * uv) * ii * (1.f - ii);
-      f4set(dza, j, zr);
-      f4set(dzi, j, zi);
-      f4set(dud, j, G * m * ii);
+      const Acc a = av[s][j], m = mv[s][j];
+      const Acc r = f4get(ra[s], j), ii = f4get(ia[s], j), uv = f4get(uu[s], j);
+      const Acc G = Acc(f4get(dyv[s], j)) + g[j];
+      const Acc mterm = m > Acc(0) ? ((a * a) / m) * ii * uv : Acc(0);
+      const Acc dl = G * (a * hp[s][j] - mterm);
+      const Acc zr = cL[j] * dl * r * (Acc(1) - r);
+      const Acc zi = (G * m * uv) * ii * (Acc(1) - ii);
+      f4set(dza, j, float(zr));
+      f4set(dzi, j, float(zi));
+      f4set(dud, j, float(G * m * ii));
       if (t < T) {
         sdza[j] += double(zr);
         sdzi[j] += double(zi);
-        sdl[j] += double(p.c * r * dl);
+        sdl[j] += double(Acc(p.c) * r * dl);
       }
-      f4set(g, j, a * G);
+      g[j] = a * G;
     }
     if (t < T) {
       const size_t row = size_t(b) * T + t;
@@ -387,7 +395,9 @@ __global__ __launch_bounds__(256) void scan_bwd_kernel(ScanBwdArgs p) {
         *reinterpret_cast<float4*>(z + row * ld2 + d) = dza;
         *reinterpret_cast<float4*>(z + row * ld2 + D + d) = dzi;
       }
-      if (t == 0 && p.dh0) *reinterpret_cast<float4*>(p.dh0 + size_t(b) * D + d) = g;
+      if (t == 0 && p.dh0)
+        *reinterpret_cast<float4*>(p.dh0 + size_t(b) * D + d) =
+            make_float4(float(g[0]), float(g[1]), float(g[2]), float(g[3]));
     }
   }
   // fixed-order per-tile partial sums
@@ -406,17 +416,18 @@ __global__ __launch_bounds__(256) void scan_bwd_kernel(ScanBwdArgs p) {
   }
 }
 
-template <typename IO>
+template <typename IO, typename Acc>
 hipError_t launch_scan_bwd(const ScanBwdArgs& a, hipStream_t s) {
-  hipError_t e = launch_fill_u32(a.status, scan_status_words(a.B, a.T, a.D), kEmpty, s);
+  hipError_t e = launch_fill_u32(static_cast<uint32_t*>(a.status),
+                                 scan_status_bytes(a.B, a.T, a.D, sizeof(Acc)) / 4, 0xffffffffu, s);
   if (e != hipSuccess) return e;
   e = launch_fill_u32(a.counter, 1, 0u, s);
   if (e != hipSuccess) return e;
   const int tiles = scan_chunks(a.T) * a.B * (a.D / kCh);
-  scan_bwd_kernel<IO><<<tiles, 256, 0, s>>>(a);
+  scan_bwd_kernel<IO, Acc><<<tiles, 256, 0, s>>>(a);
   return hipGetLastError();
 }
-template hipError_t launch_scan_bwd<float>(const ScanBwdArgs&, hipStream_t);
-template hipError_t launch_scan_bwd<bf16_t>(const ScanBwdArgs&, hipStream_t);
+template hipError_t launch_scan_bwd<float, double>(const ScanBwdArgs&, hipStream_t);
+template hipError_t launch_scan_bwd<bf16_t, float>(const ScanBwdArgs&, hipStream_t);
 
 }  // namespace rglru
