@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Benchmark of the RG-LRU temporal branch (conv width 4 -> RG-LRU) on one MI355X.
+
+Headline workload: the training-shape forward B=8, T=2048, D_RNN=2560, bf16 I/O with
+fp32 scan state.  One step is one pass of the whole forward hot path over one batch:
+    conv1d_causal4 (K0) -> rglru_gates (K1: MFMA gate GEMM + fused epilogue)
+    -> rglru_scan (K2: fused conv + chunked scan)
+which is exactly what rglru_fwd launches (rglru_fwd folds the scan's status
+initialisation into K0; here rglru_scan launches it itself).  Inputs are resident in HBM
+before the timed region; three input sets rotate so consecutive steps do not re-read the
+same x from the 256 MB Infinity Cache.  HIP events on the library's stream (the torch
+current stream) bracket every launch, giving per-kernel durations over the timed region.
+
+Prints ONE JSON line.  With --gpus N > 1 it exits with a message: the build runs on one
+GPU (no cross-GPU path exists).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "RG-LRU block tokens/sec + achieved HBM GB/s (B=8,T=2048,D_RNN=2560 bf16)"
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+GEMM_PROFILE = os.path.join(ROOT, "profiles", "gate_gemm_train_fwd_B8_T2048_D2560_pmc.md")
+GEMM_SOURCE = os.path.join(ROOT, "gated_linear_rnn_amd", "csrc", "gemm.hip")
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-extras", action="store_true", help="skip the decode and fwd+bwd timings")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _gemm_traffic():
+    """HBM bytes per gate-GEMM launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; otherwise None."""
+    try:
+        txt = open(GEMM_PROFILE).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", txt, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    if rec.get("gemm_source_sha256") != src:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n,
+                      "launches": 3}))
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs the RG-LRU "
+              f"temporal branch on one GPU only (no cross-GPU path exists).", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    import gated_linear_rnn_amd as g
+    import workloads
+
+    g.load()
+    torch.cuda.set_device(0)
+    w = workloads.TRAIN_FWD
+    B, T, D = w.B, w.T, w.D
+    M = B * T
+    bf = torch.bfloat16
+    dev = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dt)
+
+    _log("drawing inputs")
+    p = workloads.make_inputs(w)
+    xs = [dev(p["x"], bf)] + [dev(workloads.extra_inputs_x(w, k), bf) for k in (1, 2)]
+    conv_w, conv_b = dev(p["conv_w"], bf), dev(p["conv_b"])
+    W_a, W_x = dev(p["W_a"], bf), dev(p["W_x"], bf)
+    b_a, b_x, lam = dev(p["b_a"]), dev(p["b_x"]), dev(p["lam"])
+    u = torch.empty((B, T, D), dtype=bf, device="cuda")
+    a = torch.empty((B, T, D), dtype=torch.float32, device="cuda")
+    beta = torch.empty_like(a)
+    y = torch.empty((B, T, D), dtype=bf, device="cuda")
+    hT = torch.empty((B, D), dtype=torch.float32, device="cuda")
+    ws = g.workspace(g.scan_workspace_bytes(B, T, D, bf))
+    c = p["c"]
+
+    def step(k, ev=None):
+        x = xs[k % len(xs)]
+        if ev is not None:
+            ev[0].record()
+        g.conv1d_causal4(x, conv_w, conv_b, None, u, None)
+        if ev is not None:
+            ev[1].record()
+        g.rglru_gates(u, W_a, W_x, b_a, b_x, lam, a, beta, c)
+        if ev is not None:
+            ev[2].record()
+        g.rglru_scan(x, conv_w, conv_b, None, a, beta, None, y, hT, ws)
+        if ev is not None:
+            ev[3].record()
+
+    _log(f"warmup {args.warmup} steps")
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    _log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k, evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    ms = lambda i, j: float(np.mean([e[i].elapsed_time(e[j]) for e in evs]))
+    conv_ms, gates_ms, scan_ms = ms(0, 1), ms(1, 2), ms(2, 3)
+    tokens_per_s = M * args.steps / wall
+
+    gemm_flop = 2.0 * M * (2 * D) * D
+    gemm_tflops = gemm_flop / (gates_ms * 1e-3) / 1e12
+    scan_bytes = M * D * (2 + 4 + 4 + 2)            # x, a, beta in; y out
+    scan_gbps = scan_bytes / (scan_ms * 1e-3) / 1e9
+    conv_bytes = M * D * (2 + 2)
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "T": T, "D_RNN": D, "io": "bf16",
+                   "scan_state": "fp32", "c": c},
+        "roofline": {
+            "kernel": "gemm_bf16_kernel<256,128,2,2,kEpiAB> (rglru_gates: gate GEMM + epilogue)",
+            "bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": gemm_tflops / PEAK_BF16_TFLOPS, "traffic": _gemm_traffic(),
+            "flop_per_launch": gemm_flop, "avg_launch_ms": gates_ms,
+        },
+        "scan_hbm": {
+            "kernel": "scan_fwd_kernel<bf16,float> (rglru_scan: fused conv + chunked scan)",
+            "bound": "hbm", "achieved": scan_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": scan_gbps / PEAK_HBM_GBPS, "bytes_per_launch": scan_bytes,
+            "avg_launch_ms": scan_ms,
+            "note": "interval includes the look-back status initialisation launch",
+        },
+        "per_kernel_ms": {"conv": conv_ms, "gates": gates_ms, "scan": scan_ms},
+        "block_tokens_per_s_kernels": M / ((conv_ms + gates_ms + scan_ms) * 1e-3),
+        "conv_hbm_GBps": conv_bytes / (conv_ms * 1e-3) / 1e9,
+    }
+    del xs, u, a, beta, y, ws
+    torch.cuda.empty_cache()
+
+    if not args.no_extras:
+        out["decode"] = bench_decode(g, torch, np, workloads)
+        out["train_fwd_bwd"] = bench_fwd_bwd(g, torch, np, workloads)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(p, np)
+    print(json.dumps(out))
+
+
+def bench_decode(g, torch, np, workloads):
+    """1024 dependent decode steps at B=256, D=2560 (eager launches and one hipGraph)."""
+    w = workloads.DECODE.with_shape(T=64)     # 64 distinct seeded tokens, cycled
+    p = workloads.make_inputs(w)
+    bf = torch.bfloat16
+    dev = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dt)
+    B, D, steps = w.B, w.D, workloads.DECODE.T
+    toks = dev(p["x"], bf)
+    cw, cb = dev(p["conv_w"], bf), dev(p["conv_b"])
+    Wa, Wx, ba, bx, lam = dev(p["W_a"], bf), dev(p["W_x"], bf), dev(p["b_a"]), dev(p["b_x"]), dev(p["lam"])
+    hist0, h0 = dev(p["conv_state"], bf), dev(p["h0"])
+    hist, h = hist0.clone(), h0.clone()
+    y = torch.empty((B, D), dtype=bf, device="cuda")
+    ws = g.workspace(g.decode_workspace_bytes(B, D, bf))
+
+    def run():
+        for t in range(steps):
+            g.rglru_decode_step(toks[t % w.T], cw, cb, hist, Wa, Wx, ba, bx, lam, h, y, ws, p["c"])
+
+    _log("decode: eager")
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run()
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1)
+    _log("decode: graph")
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            run()
+    torch.cuda.current_stream().wait_stream(s)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1)
+    state_bytes = B * D * (4 + 4 + 6 + 6 + 2 + 2)   # h r/w, history r/w, x_t, y_t
+    w_bytes = 2 * D * D * 2
+    best = min(eager_ms, graph_ms)
+    return {
+        "workload": workloads.DECODE.name, "steps": steps,
+        "tokens_per_s_eager": B * steps / (eager_ms * 1e-3),
+        "tokens_per_s_graph": B * steps / (graph_ms * 1e-3),
+        "us_per_step_eager": eager_ms * 1e3 / steps, "us_per_step_graph": graph_ms * 1e3 / steps,
+        "state_update_GBps": state_bytes * steps / (best * 1e-3) / 1e9,
+        "state_plus_weights_GBps": (state_bytes + w_bytes) * steps / (best * 1e-3) / 1e9,
+        "note": "W (26 MB) and the state (16 MB) stay resident in the 256 MB Infinity Cache",
+    }
+
+
+def bench_fwd_bwd(g, torch, np, workloads):
+    """rglru_fwd + rglru_bwd on the fwd+bwd training workload B=4, T=2048, D=5376."""
+    w = workloads.TRAIN_BWD
+    p = workloads.make_inputs(w)
+    bf = torch.bfloat16
+    dev = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dt)
+    B, T, D = w.B, w.T, w.D
+    x, dy = dev(p["x"], bf), dev(p["dy"], bf)
+    cw, cb = dev(p["conv_w"], bf), dev(p["conv_b"])
+    Wa, Wx, ba, bx, lam = dev(p["W_a"], bf), dev(p["W_x"], bf), dev(p["b_a"]), dev(p["b_x"]), dev(p["lam"])
+    wsf = g.workspace(g.fwd_workspace_bytes(B, T, D, bf))
+    wsb = g.workspace(g.bwd_workspace_bytes(B, T, D, bf))
+    _log("fwd+bwd")
+
+    def once():
+        y, hT, _ = g.forward(x, cw, cb, None, Wa, Wx, ba, bx, lam, None, p["c"], ws=wsf)
+        e_mid.record()
+        g.backward(x, cw, cb, None, Wa, Wx, ba, bx, lam, None, dy, None, p["c"], ws=wsb)
+
+    e0, e_mid, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    once()
+    torch.cuda.synchronize()
+    fwd, bwd = [], []
+    for _ in range(3):
+        e0.record()
+        once()
+        e1.record()
+        torch.cuda.synchronize()
+        fwd.append(e0.elapsed_time(e_mid))
+        bwd.append(e_mid.elapsed_time(e1))
+    f, b = float(np.median(fwd)), float(np.median(bwd))
+    return {"workload": w.name, "fwd_ms": f, "bwd_ms": b,
+            "tokens_per_s_fwd_bwd": B * T / ((f + b) * 1e-3)}
+
+
+def cpu_baseline(p, np):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+    Bs = p["x"].shape[0]
+    cores = len(os.sched_getaffinity(0))
+    _log(f"cpu baseline: oracle forward on {Bs} sequences ({cores} cores)")
+    t0 = time.perf_counter()
+    oracle.forward(p["x"][:Bs], p["conv_w"], p["conv_b"], None, p["W_a"], p["W_x"], p["b_a"],
+                   p["b_x"], p["lam"], None, p["c"], "bf16")
+    dt = time.perf_counter() - t0
+    T = p["x"].shape[1]
+    return {"value": Bs * T / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"oracle forward (fp64 NumPy, BLAS threads = cores) over the whole "
+                      f"{Bs}x{T}x{p['x'].shape[2]} workload ({Bs * T} tokens, {dt:.1f} s)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -86,6 +86,34 @@ int gate_projection(rglru_dtype io, GateGemmArgs g, int epi, bool small_m, float
   return RGLRU_OK;
 }
 
+// The forward scan over (a, beta): K2.  `prefilled` when the conv launch before it on the
+// stream already initialised the look-back status.
+int forward_scan(rglru_dtype io, int B, int T, int D, const void* x, const void* conv_w,
+                 const float* conv_b, const void* conv_state_in, const float* a, const float* beta,
+                 const float* h0, void* y, float* h_T, void* status, uint32_t* counter,
+                 bool prefilled, hipStream_t stream) {
+  ScanFwdArgs sa{};
+  sa.B = B; sa.T = T; sa.D = D;
+  sa.x = x; sa.conv_w = conv_w; sa.conv_b = conv_b; sa.conv_state = conv_w ? conv_state_in : nullptr;
+  sa.a = a; sa.beta = beta; sa.from_ri = false; sa.lam = nullptr; sa.c = 0.f;
+  sa.h0 = h0; sa.y = y; sa.h_all = nullptr; sa.h_T = h_T;
+  sa.status = status; sa.counter = counter; sa.prefilled = prefilled;
+  if (io == RGLRU_BF16) RG_CHECK((launch_scan_fwd<bf16_t, float>(sa, stream)));
+  else RG_CHECK((launch_scan_fwd<float, double>(sa, stream)));
+  return RGLRU_OK;
+}
+
+struct ScanWs {
+  void* status;
+  uint32_t* counter;
+};
+ScanWs carve_scan(Carver& cv, int B, int T, int D, rglru_dtype io) {
+  ScanWs w;
+  w.status = cv.take<unsigned char>(scan_status_bytes(B, T, D, acc_bytes(io)));
+  w.counter = cv.take<uint32_t>(64);
+  return w;
+}
+
 // ------------------------------------------------------------------ backward
 struct BwdWs {
   void* u;
@@ -184,12 +212,19 @@ int rglru_fwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const
   FwdWs w = carve_fwd(cv, B, T, D, io);
   const int M = B * T;
   const void* u = x;
+  bool prefilled = false;
   if (conv_w) {
+    // the conv launch also initialises the scan's look-back status
+    uint32_t* fill = static_cast<uint32_t*>(w.status);
+    const size_t words = scan_status_bytes(B, T, D, acc_bytes(io)) / 4;
     if (io == RGLRU_BF16)
-      RG_CHECK(launch_conv_fwd<bf16_t>(B, T, D, x, conv_w, conv_b, conv_state_in, w.u, conv_state_out, stream));
+      RG_CHECK(launch_conv_fwd<bf16_t>(B, T, D, x, conv_w, conv_b, conv_state_in, w.u, conv_state_out,
+                                       stream, fill, words, w.counter));
     else
-      RG_CHECK(launch_conv_fwd<float>(B, T, D, x, conv_w, conv_b, conv_state_in, w.u, conv_state_out, stream));
+      RG_CHECK(launch_conv_fwd<float>(B, T, D, x, conv_w, conv_b, conv_state_in, w.u, conv_state_out,
+                                      stream, fill, words, w.counter));
     u = w.u;
+    prefilled = true;
   }
   GateGemmArgs g{};
   g.U = u; g.Wa = W_a; g.Wx = W_x; g.M = M; g.N = D; g.K = D;
@@ -197,16 +232,50 @@ int rglru_fwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const
   g.out0 = w.a; g.out1 = w.beta;
   st = gate_projection(io, g, kEpiAB, false, w.a, w.beta, stream);
   if (st != RGLRU_OK) return st;
+  return forward_scan(io, B, T, D, x, conv_w, conv_b, conv_state_in, w.a, w.beta, h0, y, h_T,
+                      w.status, w.counter, prefilled, stream);
+}
 
-  ScanFwdArgs sa{};
-  sa.B = B; sa.T = T; sa.D = D;
-  sa.x = x; sa.conv_w = conv_w; sa.conv_b = conv_b; sa.conv_state = conv_w ? conv_state_in : nullptr;
-  sa.a = w.a; sa.beta = w.beta; sa.from_ri = false; sa.lam = lambda; sa.c = c;
-  sa.h0 = h0; sa.y = y; sa.h_all = nullptr; sa.h_T = h_T;
-  sa.status = w.status; sa.counter = w.counter;
-  if (io == RGLRU_BF16) RG_CHECK((launch_scan_fwd<bf16_t, float>(sa, stream)));
-  else RG_CHECK((launch_scan_fwd<float, double>(sa, stream)));
-  return RGLRU_OK;
+int rglru_gates(int B, int T, int D, rglru_dtype io, float c, const void* u, const void* W_a,
+                const void* W_x, const float* b_a, const float* b_x, const float* lambda, float* a,
+                float* beta, hipStream_t stream) {
+  int st = shape_status(B, T, D);
+  if (st != RGLRU_OK) return st;
+  if (!io_ok(io)) return RGLRU_EDTYPE;
+  if (!u || !W_a || !W_x || !b_a || !b_x || !lambda || !a || !beta || !c_ok(c)) return RGLRU_EINVAL;
+  for (const void* p : {u, W_a, W_x, (const void*)b_a, (const void*)b_x, (const void*)lambda,
+                        (const void*)a, (const void*)beta})
+    if (!aligned16(p)) return RGLRU_EINVAL;
+  GateGemmArgs g{};
+  g.U = u; g.Wa = W_a; g.Wx = W_x; g.M = B * T; g.N = D; g.K = D;
+  g.ba = b_a; g.bx = b_x; g.lam = lambda; g.c = c;
+  g.out0 = a; g.out1 = beta;
+  return gate_projection(io, g, kEpiAB, false, a, beta, stream);
+}
+
+size_t rglru_scan_workspace_bytes(int B, int T, int D, rglru_dtype io) {
+  if (shape_status(B, T, D) != RGLRU_OK || !io_ok(io)) return 0;
+  Carver cv(nullptr);
+  carve_scan(cv, B, T, D, io);
+  return cv.used;
+}
+
+int rglru_scan(int B, int T, int D, rglru_dtype io, const void* x, const void* conv_w,
+               const float* conv_b, const void* conv_state_in, const float* a, const float* beta,
+               const float* h0, void* y, float* h_T, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = shape_status(B, T, D);
+  if (st != RGLRU_OK) return st;
+  if (!io_ok(io)) return RGLRU_EDTYPE;
+  if (!x || !a || !beta || !y) return RGLRU_EINVAL;
+  for (const void* p : {x, conv_w, (const void*)conv_b, conv_state_in, (const void*)a,
+                        (const void*)beta, (const void*)h0, (const void*)y, (const void*)h_T,
+                        (const void*)ws})
+    if (p && !aligned16(p)) return RGLRU_EINVAL;
+  if (!ws || ws_bytes < rglru_scan_workspace_bytes(B, T, D, io)) return RGLRU_EWORKSPACE;
+  Carver cv(ws);
+  ScanWs w = carve_scan(cv, B, T, D, io);
+  return forward_scan(io, B, T, D, x, conv_w, conv_b, conv_state_in, a, beta, h0, y, h_T,
+                      w.status, w.counter, false, stream);
 }
 
 size_t rglru_decode_workspace_bytes(int B, int D, rglru_dtype io) {

@@ -11,13 +11,24 @@ namespace rglru {
 
 constexpr int kConvSteps = 16;   // time steps per thread
 
+// Blocks past `conv_blocks` do not convolve: they set `fill_words` words at `fill` to all
+// ones and zero `counter` (the look-back status of the scan that follows on the stream),
+// which saves the scan a separate initialisation launch.
 template <typename IO>
 __global__ __launch_bounds__(256) void conv_fwd_kernel(int B, int T, int D, const IO* __restrict__ x,
                                                        const IO* __restrict__ w,
                                                        const float* __restrict__ cb,
                                                        const IO* __restrict__ state_in,
                                                        IO* __restrict__ u,
-                                                       IO* __restrict__ state_out) {
+                                                       IO* __restrict__ state_out, int conv_blocks,
+                                                       uint32_t* __restrict__ fill, size_t fill_words,
+                                                       uint32_t* __restrict__ counter) {
+  if (int(blockIdx.x) >= conv_blocks) {
+    const size_t fb = blockIdx.x - conv_blocks, nfb = gridDim.x - conv_blocks;
+    for (size_t i = fb * 256 + threadIdx.x; i < fill_words; i += nfb * 256) fill[i] = 0xffffffffu;
+    if (fb == 0 && threadIdx.x == 0 && counter) *counter = 0u;
+    return;
+  }
   const int nq = D / 4;
   const int nt = (T + kConvSteps - 1) / kConvSteps;
   const long item = long(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -105,19 +116,25 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p,
 // ------------------------------------------------------------------ launchers
 template <typename IO>
 hipError_t launch_conv_fwd(int B, int T, int D, const void* x, const void* w, const float* cb,
-                           const void* state_in, void* u, void* state_out, hipStream_t s) {
+                           const void* state_in, void* u, void* state_out, hipStream_t s,
+                           uint32_t* fill, size_t fill_words, uint32_t* counter) {
   const long items = long(B) * ((T + kConvSteps - 1) / kConvSteps) * (D / 4);
   const int blocks = int((items + 255) / 256);
-  conv_fwd_kernel<IO><<<blocks, 256, 0, s>>>(B, T, D, static_cast<const IO*>(x),
-                                             static_cast<const IO*>(w), cb,
-                                             static_cast<const IO*>(state_in), static_cast<IO*>(u),
-                                             static_cast<IO*>(state_out));
+  size_t fill_blocks = (fill_words + 255) / 256;
+  if (fill_blocks > 1024) fill_blocks = 1024;
+  if (fill_blocks == 0 && counter) fill_blocks = 1;
+  conv_fwd_kernel<IO><<<blocks + int(fill_blocks), 256, 0, s>>>(
+      B, T, D, static_cast<const IO*>(x), static_cast<const IO*>(w), cb,
+      static_cast<const IO*>(state_in), static_cast<IO*>(u), static_cast<IO*>(state_out), blocks,
+      fill, fill_words, counter);
   return hipGetLastError();
 }
 template hipError_t launch_conv_fwd<float>(int, int, int, const void*, const void*, const float*,
-                                           const void*, void*, void*, hipStream_t);
+                                           const void*, void*, void*, hipStream_t, uint32_t*, size_t,
+                                           uint32_t*);
 template hipError_t launch_conv_fwd<bf16_t>(int, int, int, const void*, const void*, const float*,
-                                            const void*, void*, void*, hipStream_t);
+                                            const void*, void*, void*, hipStream_t, uint32_t*,
+                                            size_t, uint32_t*);
 
 template <typename IO>
 hipError_t launch_conv_decode(int B, int D, const void* x, const void* w, const float* cb,

@@ -8,9 +8,13 @@
 namespace rglru {
 
 // ---------------------------------------------------------------- conv.hip
+// With fill/counter, the same launch also prepares the look-back status of a following
+// scan (fill_words words set to all ones, *counter = 0).
 template <typename IO>
 hipError_t launch_conv_fwd(int B, int T, int D, const void* x, const void* w, const float* cb,
-                           const void* state_in, void* u, void* state_out, hipStream_t s);
+                           const void* state_in, void* u, void* state_out, hipStream_t s,
+                           uint32_t* fill = nullptr, size_t fill_words = 0,
+                           uint32_t* counter = nullptr);
 template <typename IO>
 hipError_t launch_conv_decode(int B, int D, const void* x, const void* w, const float* cb,
                               void* hist, void* u, hipStream_t s);
@@ -77,6 +81,7 @@ struct ScanFwdArgs {
   float* h_T;             // [B,D] or NULL
   void* status;           // look-back words, scan_status_bytes(B,T,D,sizeof(Acc)) bytes
   uint32_t* counter;      // one ticket counter (zeroed with the status words)
+  bool prefilled;         // status and counter already initialised on this stream
 };
 // Look-back status bytes of a scan whose state type has acc_bytes bytes (4 or 8).
 size_t scan_status_bytes(int B, int T, int D, int acc_bytes);

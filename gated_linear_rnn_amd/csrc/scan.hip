@@ -214,11 +214,13 @@ __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanFwdArgs p) {
 
 template <typename IO, typename Acc>
 hipError_t launch_scan_fwd(const ScanFwdArgs& a, hipStream_t s) {
-  hipError_t e = launch_fill_u32(static_cast<uint32_t*>(a.status),
-                                 scan_status_bytes(a.B, a.T, a.D, sizeof(Acc)) / 4, 0xffffffffu, s);
-  if (e != hipSuccess) return e;
-  e = launch_fill_u32(a.counter, 1, 0u, s);
-  if (e != hipSuccess) return e;
+  if (!a.prefilled) {
+    hipError_t e = launch_fill_u32(static_cast<uint32_t*>(a.status),
+                                   scan_status_bytes(a.B, a.T, a.D, sizeof(Acc)) / 4, 0xffffffffu, s);
+    if (e != hipSuccess) return e;
+    e = launch_fill_u32(a.counter, 1, 0u, s);
+    if (e != hipSuccess) return e;
+  }
   const int tiles = scan_chunks(a.T) * a.B * (a.D / kCh);
   scan_fwd_kernel<IO, Acc><<<tiles, 256, 0, s>>>(a);
   return hipGetLastError();

@@ -83,13 +83,47 @@ size_t rglru_fwd_workspace_bytes(int B, int T, int D, rglru_dtype io);
  *   W_a, W_x [D,D] io ([out,in]); b_a, b_x, lambda [D] fp32.
  *   h0 [B,D] fp32, the state before the first token, or NULL (zeros).
  *   y [B,T,D] io (output).  h_T [B,D] fp32 (output, nullable): the unrounded final
- *   state.  conv_state_out [B,3,D] io (nullable): conv history after the last token.
+ *   state.  conv_state_out [B,3,D] io (nullable): conv history after the last token
+ *   (conv_state_in and conv_state_out are ignored when conv_w is NULL).
+ *   Results are bitwise reproducible run to run.
  */
 int rglru_fwd(int B, int T, int D, rglru_dtype io, float c, const void* x,
               const void* conv_w, const float* conv_b, const void* conv_state_in,
               const void* W_a, const void* W_x, const float* b_a, const float* b_x,
               const float* lambda, const float* h0, void* y, float* h_T,
               void* conv_state_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The forward in two halves, for callers that produce or consume the gates themselves
+ * (rglru_fwd is conv1d_causal4, then rglru_gates, then rglru_scan on the same stream).
+ *
+ * rglru_gates: Eq. (1)-(3) and the input scale of Eq. (4) for every (batch, time) row:
+ *   r = sigma(W_a u + b_a), i = sigma(W_x u + b_x), a = exp(c r log sigma(Lambda)),
+ *   beta = sqrt(1 - a^2) i.
+ *   u [B,T,D] io (the RG-LRU input, i.e. the conv output); W_a, W_x [D,D] io; b_a, b_x,
+ *   lambda [D] fp32; a, beta [B,T,D] fp32 (outputs).  No workspace.
+ */
+int rglru_gates(int B, int T, int D, rglru_dtype io, float c, const void* u, const void* W_a,
+                const void* W_x, const float* b_a, const float* b_x, const float* lambda,
+                float* a, float* beta, hipStream_t stream);
+
+/* Workspace bytes rglru_scan needs (0 for invalid arguments). */
+size_t rglru_scan_workspace_bytes(int B, int T, int D, rglru_dtype io);
+
+/*
+ * rglru_scan: the conv (recomputed from x when conv_w is not NULL, as in conv1d_causal4)
+ * fused with the diagonal recurrence of Eq. (4): h_t = a_t h_{t-1} + beta_t u_t, y_t = h_t
+ * (rounded to io), evaluated as a chunked parallel scan (the blog page "Griffin's
+ * Compromise", "Term explanation: Parallel scan").
+ *   x [B,T,D] io; conv_w, conv_b, conv_state_in as in rglru_fwd (nullable); a, beta
+ *   [B,T,D] fp32 as written by rglru_gates; h0 [B,D] fp32 or NULL; y [B,T,D] io (output);
+ *   h_T [B,D] fp32 (output, nullable).  The state is fp32 for bf16 I/O and fp64 for fp32
+ *   I/O.  Results are bitwise reproducible run to run.
+ */
+int rglru_scan(int B, int T, int D, rglru_dtype io, const void* x, const void* conv_w,
+               const float* conv_b, const void* conv_state_in, const float* a,
+               const float* beta, const float* h0, void* y, float* h_T, void* ws,
+               size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes rglru_decode_step needs (0 for invalid arguments). */
 size_t rglru_decode_workspace_bytes(int B, int D, rglru_dtype io);

@@ -98,3 +98,42 @@ def test_decode_full_workload_channel_subset(lib):
     p = workloads.make_inputs(workloads.DECODE)
     S = sample_channels(workloads.DECODE.D, 24, seed=5)
     _run(lib, p, workloads.DECODE.T, channels=S)
+
+
+def test_decode_graph_replays_match_eager(lib):
+    """A captured hipGraph of decode steps, replayed several times with eager work and
+    synchronisations in between; every replay equals the eager run from the same state."""
+    w = workloads.DECODE.with_shape(B=32, D=256, T=8)
+    p = workloads.make_inputs(w)
+    io = TORCH_IO[w.io]
+    toks = dev(p["x"], io)
+    cw, cb = dev(p["conv_w"], io), dev(p["conv_b"])
+    Wa, Wx, ba, bx, lam = dev(p["W_a"], io), dev(p["W_x"], io), dev(p["b_a"]), dev(p["b_x"]), dev(p["lam"])
+    hist0, h0 = dev(p["conv_state"], io), dev(p["h0"])
+    hist, h = hist0.clone(), h0.clone()
+    y = torch.empty((w.B, w.D), dtype=io, device="cuda")
+    ws = lib.workspace(lib.decode_workspace_bytes(w.B, w.D, io))
+
+    def run():
+        for t in range(w.T):
+            lib.rglru_decode_step(toks[t], cw, cb, hist, Wa, Wx, ba, bx, lam, h, y, ws, p["c"])
+
+    run()                                           # eager reference from (hist0, h0)
+    torch.cuda.synchronize()
+    ref = (hist.clone(), h.clone(), y.clone())
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            run()
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        hist.copy_(hist0)
+        h.copy_(h0)
+        y.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(hist, ref[0]) and torch.equal(h, ref[1]) and torch.equal(y, ref[2]), rep
+        _ = (toks.float() * 2).sum().item()         # unrelated eager work between replays

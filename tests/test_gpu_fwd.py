@@ -73,3 +73,29 @@ def test_forward_full_size_channel_subset(lib, w):
     p = workloads.make_inputs(w)
     S = sample_channels(w.D, 40, seed=w.seed)
     _check(lib, p, channels=S, what=w.name)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_forward_as_conv_gates_scan(lib, io):
+    """rglru_fwd split into its three entry points (the benchmark's timed step)."""
+    import oracle
+    import torch
+    from gpu_util import host
+    p = make(workloads.TRAIN_FWD, B=2, T=500, D=192, io=io, h0="normal", history="normal")
+    d = device_inputs(p)
+    u = torch.empty_like(d["x"])
+    a = torch.empty(d["x"].shape, dtype=torch.float32, device="cuda")
+    beta = torch.empty_like(a)
+    y = torch.empty_like(d["x"])
+    hT = torch.empty_like(d["h0"])
+    ws = lib.workspace(lib.scan_workspace_bytes(2, 500, 192, d["x"].dtype))
+    lib.conv1d_causal4(d["x"], d["conv_w"], d["conv_b"], d["conv_state"], u, None)
+    lib.rglru_gates(u, d["W_a"], d["W_x"], d["b_a"], d["b_x"], d["lam"], a, beta, p["c"])
+    lib.rglru_scan(d["x"], d["conv_w"], d["conv_b"], d["conv_state"], a, beta, d["h0"], y, hT, ws)
+    torch.cuda.synchronize()
+    o = oracle_forward(p)
+    ok = oracle_forward(p, keep=True)
+    assert err(host(a), ok["a"]) <= 1e-5 and err(host(beta), ok["m"] * ok["i"]) <= 1e-5
+    ey, eh = err(host(y), o["y"]), err(host(hT), o["h_T"])
+    print(f"split io={io} err(a)={err(host(a), ok['a']):.2e} err(y)={ey:.2e} err(h_T)={eh:.2e}")
+    assert ey <= TOL[io] and eh <= TOL[io]

@@ -120,3 +120,10 @@ def make_inputs(w: Workload, c: float = C_DEFAULT) -> dict:
         out["x"] = _normal(rng, (T, B, D), 1.0, io)        # one token per sequence per step
     out["dy"] = _normal(rng, (B, T, D), 1.0, io) if w.with_dy else None
     return out
+
+
+def extra_inputs_x(w: Workload, k: int) -> np.ndarray:
+    """Input set k >= 1 of workload w for rotation in timing loops: x only, drawn the same
+    way as x from default_rng(w.seed + 1000 k) (set 0 is make_inputs(w)["x"])."""
+    rng = np.random.default_rng(w.seed + 1000 * k)
+    return _normal(rng, (w.B, w.T, w.D), 1.0, w.io)
