@@ -7,5 +7,5 @@ load the library; load() (or the first call) does, and raises if it is not built
 from ._binding import (EXPORTS, LIB_PATH, RGLRU_BF16, RGLRU_F32, RgluError,  # noqa: F401
                        backward, bwd_workspace_bytes, conv1d_causal4, decode_workspace_bytes,
                        forward, fwd_workspace_bytes, io_code, load, rglru_bwd,
-                       rglru_decode_step, rglru_fwd, rglru_gates, rglru_scan,
-                       scan_workspace_bytes, status_string, workspace)
+                       rglru_decode_step, rglru_fwd, rglru_gates, rglru_lru, rglru_scan,
+                       lru_workspace_bytes, scan_workspace_bytes, status_string, workspace)

@@ -19,7 +19,8 @@ _IO = {torch.float32: RGLRU_F32, torch.bfloat16: RGLRU_BF16}
 
 # Symbols declared in include/rglru.h.
 EXPORTS = ("rglru_status_string", "conv1d_causal4", "rglru_fwd_workspace_bytes", "rglru_fwd",
-           "rglru_gates", "rglru_scan_workspace_bytes", "rglru_scan",
+           "rglru_lru_workspace_bytes", "rglru_lru", "rglru_gates", "rglru_scan_workspace_bytes",
+           "rglru_scan",
            "rglru_decode_workspace_bytes", "rglru_decode_step", "rglru_bwd_workspace_bytes",
            "rglru_bwd")
 
@@ -47,6 +48,10 @@ def load(path: str = LIB_PATH):
     lib.rglru_fwd_workspace_bytes.restype = _Z
     lib.rglru_fwd.argtypes = [_I, _I, _I, _I, _F] + [_P] * 13 + [_P, _Z, _P]
     lib.rglru_fwd.restype = _I
+    lib.rglru_lru_workspace_bytes.argtypes = [_I, _I, _I, _I]
+    lib.rglru_lru_workspace_bytes.restype = _Z
+    lib.rglru_lru.argtypes = [_I, _I, _I, _I, _F] + [_P] * 9 + [_P, _Z, _P]
+    lib.rglru_lru.restype = _I
     lib.rglru_gates.argtypes = [_I, _I, _I, _I, _F] + [_P] * 8 + [_P]
     lib.rglru_gates.restype = _I
     lib.rglru_scan_workspace_bytes.argtypes = [_I, _I, _I, _I]
@@ -95,6 +100,10 @@ def fwd_workspace_bytes(B, T, D, dtype) -> int:
     return int(load().rglru_fwd_workspace_bytes(B, T, D, io_code(dtype)))
 
 
+def lru_workspace_bytes(B, T, D, dtype) -> int:
+    return int(load().rglru_lru_workspace_bytes(B, T, D, io_code(dtype)))
+
+
 def scan_workspace_bytes(B, T, D, dtype) -> int:
     return int(load().rglru_scan_workspace_bytes(B, T, D, io_code(dtype)))
 
@@ -127,6 +136,14 @@ def rglru_fwd(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, y, 
                             _ptr(b_x), _ptr(lam), _ptr(h0), _ptr(y), _ptr(h_T),
                             _ptr(conv_state_out), _ptr(ws), ws.numel(), _stream(stream)),
            "rglru_fwd")
+
+
+def rglru_lru(u, W_a, W_x, b_a, b_x, lam, h0, y, h_T, ws, c=8.0, stream=None):
+    B, T, D = u.shape
+    _check(load().rglru_lru(B, T, D, io_code(u.dtype), float(c), _ptr(u), _ptr(W_a), _ptr(W_x),
+                            _ptr(b_a), _ptr(b_x), _ptr(lam), _ptr(h0), _ptr(y), _ptr(h_T),
+                            _ptr(ws), ws.numel(), _stream(stream)),
+           "rglru_lru")
 
 
 def rglru_gates(u, W_a, W_x, b_a, b_x, lam, a, beta, c=8.0, stream=None):

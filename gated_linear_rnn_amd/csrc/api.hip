@@ -50,6 +50,8 @@ bool c_ok(float c) { return c >= 0.f && isfinite(c); }
   } while (0)
 
 // ------------------------------------------------------------------ forward
+// bf16 I/O: u, then the fused RG-LRU kernel's look-back status and counters.
+// fp32 I/O: u, a, beta (the unfused gates) and the scan's look-back status and counter.
 struct FwdWs {
   void* u;
   float* a;      // fp32 io: z^a, then a in place
@@ -58,15 +60,30 @@ struct FwdWs {
   uint32_t* counter;
 };
 
+// The RG-LRU layer's scratch (everything after u).
+void carve_lru(Carver& cv, FwdWs& w, int B, int T, int D, rglru_dtype io) {
+  const size_t n = size_t(B) * T * D;
+  if (io == RGLRU_BF16) {
+    w.a = w.beta = nullptr;
+    w.status = cv.take<unsigned char>(lru_status_bytes(B, T, D));
+  } else {
+    w.a = cv.take<float>(n);
+    w.beta = cv.take<float>(n);
+    w.status = cv.take<unsigned char>(scan_status_bytes(B, T, D, acc_bytes(io)));
+  }
+  w.counter = cv.take<uint32_t>(64);
+}
+
 FwdWs carve_fwd(Carver& cv, int B, int T, int D, rglru_dtype io) {
   const size_t n = size_t(B) * T * D;
   FwdWs w;
   w.u = cv.take<unsigned char>(n * io_bytes(io));
-  w.a = cv.take<float>(n);
-  w.beta = cv.take<float>(n);
-  w.status = cv.take<unsigned char>(scan_status_bytes(B, T, D, acc_bytes(io)));
-  w.counter = cv.take<uint32_t>(64);
+  carve_lru(cv, w, B, T, D, io);
   return w;
+}
+
+size_t status_fill_words(int B, int T, int D, rglru_dtype io) {
+  return (io == RGLRU_BF16 ? lru_status_bytes(B, T, D) : scan_status_bytes(B, T, D, acc_bytes(io))) / 4;
 }
 
 // The gate projection for M rows: out0/out1 per the epilogue kind.
@@ -101,6 +118,30 @@ int forward_scan(rglru_dtype io, int B, int T, int D, const void* x, const void*
   if (io == RGLRU_BF16) RG_CHECK((launch_scan_fwd<bf16_t, float>(sa, stream)));
   else RG_CHECK((launch_scan_fwd<float, double>(sa, stream)));
   return RGLRU_OK;
+}
+
+// The RG-LRU layer on the conv output u (Eq. (1)-(4)): the fused kernel for bf16 I/O, the
+// gate projection then the scan for fp32 I/O.  `prefilled`: the launch before it on the
+// stream already initialised the look-back status and counters.
+int lru_layer(rglru_dtype io, int B, int T, int D, float c, const void* u, const void* W_a,
+              const void* W_x, const float* b_a, const float* b_x, const float* lambda,
+              const float* h0, void* y, float* h_T, FwdWs& w, bool prefilled, hipStream_t stream) {
+  if (io == RGLRU_BF16) {
+    LruArgs la{};
+    la.u = u; la.Wa = W_a; la.Wx = W_x; la.ba = b_a; la.bx = b_x; la.lam = lambda; la.c = c;
+    la.h0 = h0; la.y = y; la.hT = h_T; la.B = B; la.T = T; la.D = D;
+    la.status = static_cast<uint32_t*>(w.status); la.counters = w.counter;
+    RG_CHECK(launch_lru_fused(la, prefilled, stream));
+    return RGLRU_OK;
+  }
+  GateGemmArgs g{};
+  g.U = u; g.Wa = W_a; g.Wx = W_x; g.M = B * T; g.N = D; g.K = D;
+  g.ba = b_a; g.bx = b_x; g.lam = lambda; g.c = c;
+  g.out0 = w.a; g.out1 = w.beta;
+  int st = gate_projection(io, g, kEpiAB, false, w.a, w.beta, stream);
+  if (st != RGLRU_OK) return st;
+  return forward_scan(io, B, T, D, u, nullptr, nullptr, nullptr, w.a, w.beta, h0, y, h_T,
+                      w.status, w.counter, prefilled, stream);
 }
 
 struct ScanWs {
@@ -210,13 +251,12 @@ int rglru_fwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const
 
   Carver cv(ws);
   FwdWs w = carve_fwd(cv, B, T, D, io);
-  const int M = B * T;
   const void* u = x;
   bool prefilled = false;
   if (conv_w) {
-    // the conv launch also initialises the scan's look-back status
+    // the conv launch also initialises the layer's look-back status and counters
     uint32_t* fill = static_cast<uint32_t*>(w.status);
-    const size_t words = scan_status_bytes(B, T, D, acc_bytes(io)) / 4;
+    const size_t words = status_fill_words(B, T, D, io);
     if (io == RGLRU_BF16)
       RG_CHECK(launch_conv_fwd<bf16_t>(B, T, D, x, conv_w, conv_b, conv_state_in, w.u, conv_state_out,
                                        stream, fill, words, w.counter));
@@ -226,14 +266,33 @@ int rglru_fwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const
     u = w.u;
     prefilled = true;
   }
-  GateGemmArgs g{};
-  g.U = u; g.Wa = W_a; g.Wx = W_x; g.M = M; g.N = D; g.K = D;
-  g.ba = b_a; g.bx = b_x; g.lam = lambda; g.c = c;
-  g.out0 = w.a; g.out1 = w.beta;
-  st = gate_projection(io, g, kEpiAB, false, w.a, w.beta, stream);
+  return lru_layer(io, B, T, D, c, u, W_a, W_x, b_a, b_x, lambda, h0, y, h_T, w, prefilled, stream);
+}
+
+size_t rglru_lru_workspace_bytes(int B, int T, int D, rglru_dtype io) {
+  if (shape_status(B, T, D) != RGLRU_OK || !io_ok(io)) return 0;
+  Carver cv(nullptr);
+  FwdWs w;
+  carve_lru(cv, w, B, T, D, io);
+  return cv.used;
+}
+
+int rglru_lru(int B, int T, int D, rglru_dtype io, float c, const void* u, const void* W_a,
+              const void* W_x, const float* b_a, const float* b_x, const float* lambda,
+              const float* h0, void* y, float* h_T, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = shape_status(B, T, D);
   if (st != RGLRU_OK) return st;
-  return forward_scan(io, B, T, D, x, conv_w, conv_b, conv_state_in, w.a, w.beta, h0, y, h_T,
-                      w.status, w.counter, prefilled, stream);
+  if (!io_ok(io)) return RGLRU_EDTYPE;
+  if (!u || !W_a || !W_x || !b_a || !b_x || !lambda || !y || !c_ok(c)) return RGLRU_EINVAL;
+  for (const void* p : {u, W_a, W_x, (const void*)b_a, (const void*)b_x, (const void*)lambda,
+                        (const void*)h0, (const void*)y, (const void*)h_T, (const void*)ws})
+    if (p && !aligned16(p)) return RGLRU_EINVAL;
+  if (!ws || ws_bytes < rglru_lru_workspace_bytes(B, T, D, io)) return RGLRU_EWORKSPACE;
+  Carver cv(ws);
+  FwdWs w;
+  w.u = nullptr;
+  carve_lru(cv, w, B, T, D, io);
+  return lru_layer(io, B, T, D, c, u, W_a, W_x, b_a, b_x, lambda, h0, y, h_T, w, false, stream);
 }
 
 int rglru_gates(int B, int T, int D, rglru_dtype io, float c, const void* u, const void* W_a,

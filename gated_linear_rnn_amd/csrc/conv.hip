@@ -12,7 +12,8 @@ namespace rglru {
 constexpr int kConvSteps = 16;   // time steps per thread
 
 // Blocks past `conv_blocks` do not convolve: they set `fill_words` words at `fill` to all
-// ones and zero `counter` (the look-back status of the scan that follows on the stream),
+// ones and zero the 64 words at `counter` (the look-back status and ticket counters of
+// the scan that follows on the stream),
 // which saves the scan a separate initialisation launch.
 template <typename IO>
 __global__ __launch_bounds__(256) void conv_fwd_kernel(int B, int T, int D, const IO* __restrict__ x,
@@ -26,7 +27,7 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(int B, int T, int D, cons
   if (int(blockIdx.x) >= conv_blocks) {
     const size_t fb = blockIdx.x - conv_blocks, nfb = gridDim.x - conv_blocks;
     for (size_t i = fb * 256 + threadIdx.x; i < fill_words; i += nfb * 256) fill[i] = 0xffffffffu;
-    if (fb == 0 && threadIdx.x == 0 && counter) *counter = 0u;
+    if (fb == 0 && threadIdx.x < 64 && counter) counter[threadIdx.x] = 0u;
     return;
   }
   const int nq = D / 4;

@@ -13,13 +13,10 @@
 // global_load_lds_dwordx4 (no VGPR staging) into a double buffer; rows of 128 bytes are
 // XOR-swizzled in 16-byte chunks so the ds_read_b128 operand fetches are conflict-free.
 // The workgroup -> tile map groups tiles sharing U and W panels on one XCD for L2 reuse.
-#include "rglru_device.h"
+#include "gemm_core.h"
 #include "kernels.h"
 
 namespace rglru {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 enum : int { kModePlain = 3 };
 
@@ -45,8 +42,6 @@ struct GemmParams {
   const float* addend;
 };
 
-__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 // Map the linear workgroup id to a (tile_m, tile_n) pair.  Consecutive workgroup ids are
 // dispatched round-robin over the 8 XCDs; the remap gives every XCD a contiguous range of
 // the grouped tile order, so the tiles one XCD runs together share U and W panels in its L2.
@@ -63,135 +58,39 @@ __device__ __forceinline__ void tile_coords(int MT, int NT, int& tm, int& tn) {
   tn = in / gsize;
 }
 
-template <int BM, int BC, int WM, int WN, int MODE, bool DUAL>
-__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmParams p) {
-  constexpr int NW = WM * WN;
-  constexpr int BNR = 2 * BC;                  // B-tile rows
-  constexpr int WTM = BM / WM, WTNR = BNR / WN;
-  constexpr int MF = WTM / 32, NF = WTNR / 32;
-  constexpr int ROWS = BM + BNR;
-  constexpr int STAGE = ROWS * 128;            // bytes per stage (BK = 64 bf16 per row)
-  constexpr int QPW = ROWS / 8 / NW;           // DMA instructions per wave per stage
-  constexpr int QA = BM / 8 / NW;              // ... of which load U rows
-  constexpr int QB1 = (BM + BC) / 8 / NW;      // gate modes: index of the first W_x load
-  static_assert(WTM % 32 == 0 && WTNR % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert((ROWS / 8) % NW == 0 && (BM / 8) % NW == 0 && ((BM + BC) / 8) % NW == 0, "");
-  static_assert(MODE == kModePlain || (BC / WN) % 32 == 0, "");
-  static_assert(2 * STAGE <= 160 * 1024, "LDS");
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * STAGE];
-
+template <class C, int MODE, bool DUAL>
+__global__ __launch_bounds__(C::NW * 64, C::NW >= 8 ? 2 : 1) void gemm_bf16_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS_BYTES];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave / WN, wn = wave % WN;
-
-  const int MT = (p.M + BM - 1) / BM;
-  const int NT = MODE == kModePlain ? (p.N + BNR - 1) / BNR : (p.N + BC - 1) / BC;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int MT = (p.M + C::BM - 1) / C::BM;
+  const int NT = MODE == kModePlain ? (p.N + C::BNR - 1) / C::BNR : (p.N + C::BC - 1) / C::BC;
   int tm, tn;
   tile_coords(MT, NT, tm, tn);
-  const int m0 = tm * BM;
-  const int n0 = tn * (MODE == kModePlain ? BNR : BC);
+  const int m0 = tm * C::BM;
+  const int n0 = tn * (MODE == kModePlain ? C::BNR : C::BC);
 
-  // per-lane source offsets (elements) of this wave's DMA loads
-  uint32_t off[QPW];
-#pragma unroll
-  for (int q = 0; q < QPW; ++q) {
-    const int r = (q * NW + wave) * 8 + (lane >> 3);
-    const int pchunk = lane & 7;
-    if (q < QA) {
-      const int gm = min(m0 + r, p.M - 1);
-      off[q] = uint32_t(gm) * uint32_t(p.lda) + uint32_t((pchunk ^ ((r >> 1) & 7)) * 8);
-    } else {
-      const int rb = r - BM;
-      int gn;
-      if (MODE == kModePlain) gn = min(n0 + rb, p.N - 1);
-      else gn = min(n0 + (rb % BC), p.N - 1);
-      off[q] = uint32_t(gn) * uint32_t(p.ldb) + uint32_t((pchunk ^ ((rb >> 1) & 7)) * 8);
-    }
-  }
-  const int KT1 = p.K / 64;                    // k tiles per pass
-  const int KT = DUAL ? 2 * KT1 : KT1;
-
-  auto issue = [&](int stage, int kt) {
-    const bf16_t* abase = (DUAL && kt >= KT1) ? p.A2 : p.A;
-    const int kofs = (DUAL && kt >= KT1 ? kt - KT1 : kt) * 64;
-    unsigned char* sbase = lds + stage * STAGE;
-#pragma unroll
-    for (int q = 0; q < QPW; ++q) {
-      const bf16_t* base = q < QA ? abase : ((MODE != kModePlain && q >= QB1) ? p.B1 : p.B0);
-      const bf16_t* gp = base + off[q] + kofs;
-      __builtin_amdgcn_global_load_lds(
-          (void*)gp, (void*)(sbase + (q * NW + wave) * 1024), 16, 0, 0);
-    }
-  };
-
-  // LDS rows of this lane's operand fragments
-  int arow[MF], brow[NF];
-#pragma unroll
-  for (int mf = 0; mf < MF; ++mf) arow[mf] = wm * WTM + mf * 32 + (lane & 31);
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    int base;
-    if (MODE == kModePlain) {
-      base = wn * WTNR + f * 32;
-    } else {
-      const int half = NF / 2;
-      const int g = f / half, jc = f % half;
-      base = g * BC + wn * (BC / WN) + jc * 32;
-    }
-    brow[f] = BM + base + (lane & 31);
-  }
-  const int swz = ((lane & 31) >> 1) & 7;
-  const int khalf = lane >> 5;
-
-  f32x16_t acc[MF][NF];
-#pragma unroll
-  for (int mf = 0; mf < MF; ++mf)
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mf][f][v] = 0.f;
-
-  issue(0, 0);
-  wait_vmem_all();
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < KT) issue(st ^ 1, kt + 1);
-    const unsigned char* sb = lds + st * STAGE;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int coff = (((kk * 2 + khalf) ^ swz) * 16);
-      bf16x8_t af[MF], bfr[NF];
-#pragma unroll
-      for (int mf = 0; mf < MF; ++mf)
-        af[mf] = *reinterpret_cast<const bf16x8_t*>(sb + arow[mf] * 128 + coff);
-#pragma unroll
-      for (int f = 0; f < NF; ++f)
-        bfr[f] = *reinterpret_cast<const bf16x8_t*>(sb + brow[f] * 128 + coff);
-#pragma unroll
-      for (int mf = 0; mf < MF; ++mf)
-#pragma unroll
-        for (int f = 0; f < NF; ++f)
-          acc[mf][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mf], bfr[f], acc[mf][f], 0, 0, 0);
-    }
-    wait_vmem_all();
-    __syncthreads();
-  }
+  TileOperands op;
+  op.A = p.A; op.A2 = p.A2; op.B0 = p.B0; op.B1 = p.B1;
+  op.lda = p.lda; op.ldb = p.ldb; op.K = p.K;
+  op.a_row0 = m0; op.a_rows = p.M - m0;
+  op.b_row0 = n0; op.b_rows = p.N - n0;
+  f32x16_t acc[C::MF][C::NF];
+  gemm_mainloop<C, DUAL>(op, lds, lane, wave, acc);
 
   // ---------------------------------------------------------------- epilogue
-  // accumulator slot v of lane l holds row 8*(v/4) + 4*(l/32) + v%4, column l%32
   const int col = lane & 31;
-  const int rbase = 4 * (lane >> 5);
   if (MODE == kModePlain) {
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int n = n0 + wn * WTNR + f * 32 + col;
+    for (int f = 0; f < C::NF; ++f) {
+      const int n = n0 + wn * C::WTNR + f * 32 + col;
       if (n >= p.N) continue;
 #pragma unroll
-      for (int mf = 0; mf < MF; ++mf)
+      for (int mf = 0; mf < C::MF; ++mf)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int m = m0 + wm * WTM + mf * 32 + 8 * (v >> 2) + rbase + (v & 3);
+          const int m = m0 + wm * C::WTM + mf * 32 + acc_row(v, lane);
           if (m < p.M) {
             const size_t o = size_t(m) * p.ldc + n;
             float val = acc[mf][f][v];
@@ -201,32 +100,36 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmParams p
         }
     }
   } else {
-    constexpr int HALF = NF / 2;
+    constexpr int HALF = C::NF / 2;
 #pragma unroll
     for (int jc = 0; jc < HALF; ++jc) {
-      const int ch = n0 + wn * (BC / WN) + jc * 32 + col;
+      const int ch = n0 + wn * (C::BC / C::WN) + jc * 32 + col;
       if (ch >= p.N) continue;
-      const float ba = p.ba[ch], bx = p.bx[ch];
-      const float L = log_sigmoidf(p.lam[ch]);
+      const GateChan k = gate_chan(p.ba[ch], p.bx[ch], p.lam[ch], p.c);
 #pragma unroll
-      for (int mf = 0; mf < MF; ++mf)
+      for (int mf = 0; mf < C::MF; ++mf)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int m = m0 + wm * WTM + mf * 32 + 8 * (v >> 2) + rbase + (v & 3);
+          const int m = m0 + wm * C::WTM + mf * 32 + acc_row(v, lane);
           if (m >= p.M) continue;
           const size_t o = size_t(m) * p.N + ch;
-          const Gate g = gate_from_z(acc[mf][jc][v] + ba, acc[mf][jc + HALF][v] + bx, L, p.c);
-          if (MODE == kEpiAB) {
-            p.out0[o] = g.a;
-            p.out1[o] = g.m * g.i;
-          } else if (MODE == kEpiRI) {
-            p.out0[o] = g.r;
-            p.out1[o] = g.i;
-          } else {  // kEpiDecode
-            const float uu = bf2f(p.u[o]);
-            const float hn = fmaf(g.a, p.h[o], (g.m * g.i) * uu);
-            p.h[o] = hn;
-            p.y[o] = f2bf(hn);
+          const float za = acc[mf][jc][v], zx = acc[mf][jc + HALF][v];
+          if (MODE == kEpiRI) {
+            float r, i;
+            gate_fast_ri(za, zx, k, r, i);
+            p.out0[o] = r;
+            p.out1[o] = i;
+          } else {
+            float a, beta;
+            gate_fast(za, zx, k, a, beta);
+            if (MODE == kEpiAB) {
+              p.out0[o] = a;
+              p.out1[o] = beta;
+            } else {  // kEpiDecode
+              const float hn = fmaf(a, p.h[o], beta * bf2f(p.u[o]));
+              p.h[o] = hn;
+              p.y[o] = f2bf(hn);
+            }
           }
         }
     }
@@ -234,12 +137,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmParams p
 }
 
 // ---------------------------------------------------------------- launchers (bf16)
-template <int BM, int BC, int WM, int WN, int MODE, bool DUAL>
+// Large tiles: 256 x 256, 8 waves of 128 x 64, BK = 64, double-buffered.
+typedef GemmCfg<256, 128, 2, 4, false, 64, 2> CfgGate;
+typedef GemmCfg<256, 128, 2, 4, true, 64, 2> CfgPlain;
+// Small-M tiles (decode): 64 x 64, 2 waves of 32 x 64.
+typedef GemmCfg<64, 32, 2, 1, false, 32, 4> CfgGateSmall;
+
+template <class C, int MODE, bool DUAL>
 static hipError_t run_bf16(const GemmParams& p, hipStream_t s) {
-  const int BNR = 2 * BC;
-  const int MT = (p.M + BM - 1) / BM;
-  const int NT = MODE == kModePlain ? (p.N + BNR - 1) / BNR : (p.N + BC - 1) / BC;
-  gemm_bf16_kernel<BM, BC, WM, WN, MODE, DUAL><<<MT * NT, WM * WN * 64, 0, s>>>(p);
+  const int MT = (p.M + C::BM - 1) / C::BM;
+  const int NT = MODE == kModePlain ? (p.N + C::BNR - 1) / C::BNR : (p.N + C::BC - 1) / C::BC;
+  gemm_bf16_kernel<C, MODE, DUAL><<<MT * NT, C::NW * 64, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -257,15 +165,15 @@ hipError_t launch_gate_gemm_bf16(const GateGemmArgs& g, int epi, bool small_m, h
   p.y = static_cast<bf16_t*>(g.y);
   if (small_m) {
     switch (epi) {
-      case kEpiAB: return run_bf16<64, 32, 2, 1, kEpiAB, false>(p, s);
-      case kEpiRI: return run_bf16<64, 32, 2, 1, kEpiRI, false>(p, s);
-      case kEpiDecode: return run_bf16<64, 32, 2, 1, kEpiDecode, false>(p, s);
+      case kEpiAB: return run_bf16<CfgGateSmall, kEpiAB, false>(p, s);
+      case kEpiRI: return run_bf16<CfgGateSmall, kEpiRI, false>(p, s);
+      case kEpiDecode: return run_bf16<CfgGateSmall, kEpiDecode, false>(p, s);
     }
   } else {
     switch (epi) {
-      case kEpiAB: return run_bf16<256, 128, 2, 2, kEpiAB, false>(p, s);
-      case kEpiRI: return run_bf16<256, 128, 2, 2, kEpiRI, false>(p, s);
-      case kEpiDecode: return run_bf16<256, 128, 2, 2, kEpiDecode, false>(p, s);
+      case kEpiAB: return run_bf16<CfgGate, kEpiAB, false>(p, s);
+      case kEpiRI: return run_bf16<CfgGate, kEpiRI, false>(p, s);
+      case kEpiDecode: return run_bf16<CfgGate, kEpiDecode, false>(p, s);
     }
   }
   return hipErrorInvalidValue;
@@ -279,8 +187,8 @@ hipError_t launch_plain_gemm_bf16(const PlainGemmArgs& g, hipStream_t s) {
   p.M = g.M; p.N = g.N; p.K = g.K;
   p.lda = g.lda; p.ldb = g.ldb; p.ldc = g.ldc;
   p.C = g.C; p.addend = g.addend;
-  if (g.A2) return run_bf16<256, 128, 2, 2, kModePlain, true>(p, s);
-  return run_bf16<256, 128, 2, 2, kModePlain, false>(p, s);
+  if (g.A2) return run_bf16<CfgPlain, kModePlain, true>(p, s);
+  return run_bf16<CfgPlain, kModePlain, false>(p, s);
 }
 
 // ---------------------------------------------------------------- fp32 VALU GEMM

@@ -9,7 +9,7 @@ namespace rglru {
 
 // ---------------------------------------------------------------- conv.hip
 // With fill/counter, the same launch also prepares the look-back status of a following
-// scan (fill_words words set to all ones, *counter = 0).
+// scan (fill_words words set to all ones, counter[0..63] = 0).
 template <typename IO>
 hipError_t launch_conv_fwd(int B, int T, int D, const void* x, const void* w, const float* cb,
                            const void* state_in, void* u, void* state_out, hipStream_t s,
@@ -62,6 +62,28 @@ hipError_t launch_plain_gemm_f32(const PlainGemmArgs& g, hipStream_t s);
 // fp32 I/O: gate math from pre-activations za, zx [M, N] (already W u, bias not added).
 hipError_t launch_gate_elementwise_f32(const GateGemmArgs& g, const float* za, const float* zx,
                                        int epi, hipStream_t s);
+
+// ---------------------------------------------------------------- lru.hip
+// The fused RG-LRU layer (gate GEMM + log-space gates + chunked scan) for bf16 I/O.
+struct LruArgs {
+  const void* u;          // [B,T,D] bf16 (the conv output)
+  const void* Wa;
+  const void* Wx;
+  const float* ba;
+  const float* bx;
+  const float* lam;
+  float c;
+  const float* h0;        // [B,D] or NULL
+  void* y;                // [B,T,D] bf16
+  float* hT;              // [B,D] or NULL
+  int B, T, D;
+  uint32_t* status;       // lru_status_bytes(B,T,D) bytes of look-back words
+  uint32_t* counters;     // 64 ticket counters (zeroed with the status words)
+  int groups;             // set by the launcher
+};
+int lru_chunks(int T);
+size_t lru_status_bytes(int B, int T, int D);
+hipError_t launch_lru_fused(const LruArgs& a, bool prefilled, hipStream_t s);
 
 // ---------------------------------------------------------------- scan.hip
 struct ScanFwdArgs {

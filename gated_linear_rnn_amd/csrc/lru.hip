@@ -1,0 +1,236 @@
+// The RG-LRU layer in one kernel for bf16 I/O: the gate projections of Eq. (1)-(2) on the
+// matrix cores, the log-space gates of Eq. (3), and the diagonal recurrence of Eq. (4)
+// evaluated in the GEMM epilogue (Griffin model-architecture page, section "Real-Gated
+// Linear Recurrent Unit (RG-LRU)").  The input is u, the conv output.
+//
+// A workgroup owns 256 consecutive time steps of one sequence x 128 channels.  After the
+// K loop each lane holds z^a and z^x for one channel and 64 of the tile's time steps (16
+// groups of 4 consecutive steps; the partner lane l^32 holds the interleaved groups, the
+// other row half lives in the other wave row).  The epilogue turns them into a_t and
+// beta_t u_t, scans each group to an affine summary (A = prod a, H), combines the summaries
+// along time - partner lanes by a lane exchange, the two wave rows through LDS - and
+// chains tiles along time with the decoupled look-back of the chunked scan (the blog page
+// "Griffin's Compromise", "Term explanation: Parallel scan").  Only y (bf16) and h_T leave
+// the kernel: a_t and beta_t never touch HBM.
+//
+// Tiles of one chain (sequence b, channel tile) must be started in time order: every
+// workgroup takes a ticket from the counter of its group g = blockIdx % G; group g owns
+// the chains c = g, g + G, ... (so all tiles of a chain share one counter), and tickets
+// enumerate its tiles time-level by time-level.  A tile only waits on tiles with lower
+// tickets of its own counter, which have already started: no deadlock.  G = 8 matches the
+// round-robin dispatch of workgroups over the 8 XCDs, so a chain stays on one XCD's L2.
+#include "gemm_core.h"
+#include "kernels.h"
+
+namespace rglru {
+
+typedef GemmCfg<256, 128, 2, 4, false, 64, 2> CfgLru;
+constexpr int kLruRows = CfgLru::BM;   // time steps per tile
+constexpr int kLruCh = CfgLru::BC;     // channels per tile
+
+int lru_chunks(int T) { return (T + kLruRows - 1) / kLruRows; }
+size_t lru_status_bytes(int B, int T, int D) { return 3ull * lru_chunks(T) * size_t(B) * D * 4; }
+
+static int lru_groups(int chains) {
+  int g = 8;
+  while (chains % g) g >>= 1;
+  return g;
+}
+
+// The scan epilogue of lru_fused_kernel (see the file comment).  EDGE: the tile may have
+// fewer than 256 valid rows or hold the sequence's final step.
+template <bool EDGE>
+__device__ __forceinline__ void lru_epilogue(const LruArgs& p, unsigned char* lds,
+                                             f32x16_t (&acc)[CfgLru::MF][CfgLru::NF], int lane,
+                                             int wave, int b, int tn, int tt, int t0, int rows) {
+  typedef CfgLru C;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int B = p.B, T = p.T, D = p.D;
+  const bf16_t* u = static_cast<const bf16_t*>(p.u);
+  // LDS after the K loop: [0, 64 KB) the tile's u (then y) as 256 rows x 128 bf16 channels;
+  // then per-channel aggregates, carries and the look-back scratch.
+  __syncthreads();   // every wave is done with the GEMM stages: the LDS is reused below
+  bf16_t* tileU = reinterpret_cast<bf16_t*>(lds);
+  float* eA = reinterpret_cast<float*>(lds + kLruRows * kLruCh * 2);
+  float* eH = eA + kLruCh;
+  float* eC = eH + kLruCh;
+  float* eLb = eC + kLruCh;                          // look-back scratch, 2 kWindow per channel
+  const int chv = min(kLruCh, D - tn * kLruCh);      // valid channels of the tile (64 or 128)
+  const size_t rowbase = size_t(b) * T + t0;
+  {
+    // u rows of the tile -> LDS, 16 bytes per lane (4 rows of 256 B per wave instruction);
+    // rows past the sequence and chunks past D are clamped to valid addresses (unused)
+    const bf16_t* ug = u + rowbase * D + tn * kLruCh;
+#pragma unroll
+    for (int it = 0; it < kLruRows / 4 / C::NW; ++it) {
+      const int r = (it * C::NW + wave) * 4 + (lane >> 4);
+      const int chunk = min(lane & 15, chv / 8 - 1);
+      const bf16_t* gp = ug + size_t(min(r, rows - 1)) * D + chunk * 8;
+      __builtin_amdgcn_global_load_lds((void*)gp, (void*)(lds + (it * C::NW + wave) * 1024), 16, 0, 0);
+    }
+  }
+  const int c = lane & 31, half = lane >> 5;
+  const int chl = wn * 32 + c;                       // channel within the tile
+  const int ch = tn * kLruCh + chl;
+  const bool chok = chl < chv;
+  const GateChan kc = gate_chan(p.ba[chok ? ch : tn * kLruCh], p.bx[chok ? ch : tn * kLruCh],
+                                p.lam[chok ? ch : tn * kLruCh], p.c);
+  // Group q = 4 mf + gq of this lane covers tile rows wm*128 + 32 mf + 8 gq + 4 half + rr,
+  // rr = 0..3 (consecutive time steps).  a_t and beta_t first (the u tile is in flight).
+  float av[16][4], bu[16][4];
+#pragma unroll
+  for (int mf = 0; mf < C::MF; ++mf)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int lr = wm * C::WTM + mf * 32 + 8 * gq + 4 * half + rr;
+        float a, beta;
+        gate_fast(acc[mf][0][gq * 4 + rr], acc[mf][1][gq * 4 + rr], kc, a, beta);
+        const bool ok = !EDGE || lr < rows;
+        av[mf * 4 + gq][rr] = ok ? a : 1.f;
+        bu[mf * 4 + gq][rr] = ok ? beta : 0.f;
+      }
+  wait_dma_barrier<0>();                             // the u tile is in LDS
+  // this lane's rows of the LDS tile: tb[(32 mf + 8 gq + rr) * kLruCh] (constant offsets)
+  bf16_t* tb = tileU + (wm * C::WTM + 4 * half) * kLruCh + chl;
+  const int partner = (lane ^ 32) << 2;               // ds_bpermute byte address
+  // Per group: beta_t u_t, the group's summary (A = prod a, H), and the running composition
+  // over the 32 groups of the wave's 128 rows in time order (for each gq the lower-half
+  // lane's group comes first, then the upper-half lane's).  pre[q] is the map in front of
+  // this lane's group q.
+  float preA[16], preH[16];
+  float RA = 1.f, RH = 0.f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    float Aq = 1.f, Hq = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      bu[q][rr] *= bf2f(tb[((q >> 2) * 32 + 8 * (q & 3) + rr) * kLruCh]);
+      Hq = fmaf(av[q][rr], Hq, bu[q][rr]);
+      Aq = Aq * av[q][rr];
+    }
+    const float Ap = __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(Aq)));
+    const float Hp = __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(Hq)));
+    const float A0 = half ? Ap : Aq, H0 = half ? Hp : Hq;   // rows 8gq .. 8gq+3
+    const float A1 = half ? Aq : Ap, H1 = half ? Hq : Hp;   // rows 8gq+4 .. 8gq+7
+    const float R0A = RA, R0H = RH;
+    RH = fmaf(A0, RH, H0);
+    RA = A0 * RA;
+    preA[q] = half ? RA : R0A;
+    preH[q] = half ? RH : R0H;
+    RH = fmaf(A1, RH, H1);
+    RA = A1 * RA;
+  }
+  if (wm == 0 && half == 0) { eA[chl] = RA; eH[chl] = RH; }
+  __syncthreads();                                   // also: every wave is done reading u
+  float A0w = 1.f, H0w = 0.f;
+  if (wm == 1) { A0w = eA[chl]; H0w = eH[chl]; }
+  if (wm == 1 && half == 0) {
+    // tile aggregate: the upper 128 rows, then the lower 128
+    const float At = RA * A0w, Ht = fmaf(RA, H0w, RH);
+    float carry = 0.f;
+    if (chok) {
+      const int nchunks = (T + kLruRows - 1) / kLruRows;
+      const size_t BD = size_t(B) * D, base = size_t(b) * D + ch;
+      uint32_t* incl = p.status;
+      uint32_t* aggA = incl + size_t(nchunks) * BD;
+      uint32_t* aggH = aggA + size_t(nchunks) * BD;
+      if (tt > 0) {
+        publish<float>(aggA + size_t(tt) * BD + base, At);
+        publish<float>(aggH + size_t(tt) * BD + base, Ht);
+        carry = lookback_carry<float>(incl + base, aggA + base, aggH + base, tt, BD,
+                                      eLb + chl * 2 * kWindow, eLb + chl * 2 * kWindow + kWindow);
+      } else {
+        carry = p.h0 ? p.h0[base] : 0.f;
+      }
+      publish<float>(incl + size_t(tt) * BD + base, fmaf(At, carry, Ht));
+    }
+    eC[chl] = carry;
+  }
+  __syncthreads();
+  const float carry = eC[chl];
+  const float hin = wm == 0 ? carry : fmaf(A0w, carry, H0w);
+  const int lastrow = T - 1 - t0;                    // tile row of the final step, if in tile
+  float hlast = 0.f;
+  bool haslast = false;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    float h = fmaf(preA[q], hin, preH[q]);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      h = fmaf(av[q][rr], h, bu[q][rr]);
+      const int lr = wm * C::WTM + (q >> 2) * 32 + 8 * (q & 3) + 4 * half + rr;
+      tb[((q >> 2) * 32 + 8 * (q & 3) + rr) * kLruCh] = f2bf(h);
+      if (EDGE) {
+        hlast = lr == lastrow ? h : hlast;
+        haslast = haslast || lr == lastrow;
+      }
+    }
+  }
+  if (EDGE && haslast && chok && p.hT) p.hT[size_t(b) * D + ch] = hlast;
+  __syncthreads();
+  // y rows of the tile -> HBM, 16 bytes per lane
+  bf16_t* yg = static_cast<bf16_t*>(p.y) + rowbase * D + tn * kLruCh;
+#pragma unroll
+  for (int it = 0; it < kLruRows / 4 / C::NW; ++it) {
+    const int r = (it * C::NW + wave) * 4 + (lane >> 4);
+    const int chunk = lane & 15;
+    if ((!EDGE || r < rows) && chunk * 8 < chv)
+      *reinterpret_cast<uint4*>(yg + size_t(r) * D + chunk * 8) =
+          *reinterpret_cast<const uint4*>(tileU + r * kLruCh + chunk * 8);
+  }
+}
+
+__global__ __launch_bounds__(CfgLru::NW * 64, 2) void lru_fused_kernel(LruArgs p) {
+  typedef CfgLru C;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS_BYTES];
+  __shared__ uint32_t s_ticket;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int G = p.groups, g = blockIdx.x % G;
+  if (tid == 0) s_ticket = atomicAdd(p.counters + g, 1u);
+  __syncthreads();
+  const int B = p.B, T = p.T, D = p.D;
+  const int NT = (D + kLruCh - 1) / kLruCh;
+  const int per_level = B * NT / G;
+  const int k = int(s_ticket);
+  const int tt = k / per_level;
+  const int chain = g + G * (k % per_level);
+  const int b = chain / NT, tn = chain % NT;
+  const int t0 = tt * kLruRows;
+  const int rows = min(kLruRows, T - t0);
+  const bf16_t* u = static_cast<const bf16_t*>(p.u);
+
+  TileOperands op;
+  op.A = u; op.A2 = nullptr;
+  op.B0 = static_cast<const bf16_t*>(p.Wa);
+  op.B1 = static_cast<const bf16_t*>(p.Wx);
+  op.lda = D; op.ldb = D; op.K = D;
+  op.a_row0 = b * T + t0; op.a_rows = rows;
+  op.b_row0 = tn * kLruCh; op.b_rows = min(kLruCh, D - tn * kLruCh);
+  f32x16_t acc[C::MF][C::NF];
+  gemm_mainloop<C, false>(op, lds, lane, wave, acc);
+
+  // ---------------------------------------------------------------- scan epilogue
+  lru_epilogue<true>(p, lds, acc, lane, wave, b, tn, tt, t0, rows);
+}
+
+hipError_t launch_lru_fused(const LruArgs& a_in, bool prefilled, hipStream_t s) {
+  LruArgs a = a_in;
+  const int NT = (a.D + kLruCh - 1) / kLruCh;
+  const int chains = a.B * NT;
+  a.groups = lru_groups(chains);
+  if (!prefilled) {
+    hipError_t e = launch_fill_u32(a.status, lru_status_bytes(a.B, a.T, a.D) / 4, 0xffffffffu, s);
+    if (e != hipSuccess) return e;
+    e = launch_fill_u32(a.counters, 64, 0u, s);
+    if (e != hipSuccess) return e;
+  }
+  const int tiles = chains * lru_chunks(a.T);
+  lru_fused_kernel<<<tiles, CfgLru::NW * 64, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace rglru

@@ -16,13 +16,8 @@ typedef uint16_t bf16_t;   // raw bf16 bits; arithmetic is always fp32
 
 __device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float(uint32_t(v) << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return bf16_t(u >> 16);
-}
+// fp32 -> bf16, round to nearest even (gfx950 v_cvt_pk_bf16_f32); NaN stays NaN.
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 // I/O element traits: load/store 4 consecutive channels as fp32.
 template <typename IO> struct Io;
@@ -112,6 +107,56 @@ __device__ __forceinline__ Gate gate_from_ri(float r, float i, float L, float c)
 }
 __device__ __forceinline__ Gate gate_from_z(float zr, float zi, float L, float c) {
   return gate_from_ri(sigmoidf_stable(zr), sigmoidf_stable(zi), L, c);
+}
+
+// Fast form of the same gate math for the bf16 MFMA epilogue, on the hardware
+// transcendentals (v_exp_f32 = 2^x, v_rcp_f32, v_sqrt_f32; about 1 ulp each):
+//   sigma(z) = 1 / (1 + 2^(-z log2 e)), with the bias folded into the exp2 argument;
+//   log2 a = r * (c log2 sigma(Lambda)),  a = 2^(log2 a);
+//   1 - a^2 = -expm1(x), x = 2 ln2 log2 a <= 0: a degree-8 Taylor series of -expm1 for
+//   x > -ln2 (truncation below 1.6e-7 relative), 1 - a*a otherwise (no cancellation there).
+// r = 0 or c = 0 still gives a = 1 and sqrt(1 - a^2) = 0 exactly.
+struct GateChan {
+  float nba;   // -b_a log2 e
+  float nbx;   // -b_x log2 e
+  float cl2;   // c log2 sigma(Lambda)
+};
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ GateChan gate_chan(float ba, float bx, float lam, float c) {
+  GateChan k;
+  k.nba = -ba * kLog2e;
+  k.nbx = -bx * kLog2e;
+  k.cl2 = c * (log_sigmoidf(lam) * kLog2e);
+  return k;
+}
+
+// returns a and beta = sqrt(1 - a^2) * i from the accumulated W_a u and W_x u
+__device__ __forceinline__ void gate_fast(float za, float zx, const GateChan& k, float& a,
+                                          float& beta) {
+  const float r = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(fmaf(za, -kLog2e, k.nba)));
+  const float i = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(fmaf(zx, -kLog2e, k.nbx)));
+  const float l2 = r * k.cl2;
+  a = __builtin_amdgcn_exp2f(l2);
+  const float x = l2 * (2.f * kLn2);
+  float q = 2.4801587301587302e-05f;                  // 1/8!
+  q = fmaf(q, x, 1.9841269841269841e-04f);            // 1/7!
+  q = fmaf(q, x, 1.3888888888888889e-03f);            // 1/6!
+  q = fmaf(q, x, 8.3333333333333333e-03f);            // 1/5!
+  q = fmaf(q, x, 4.1666666666666667e-02f);            // 1/4!
+  q = fmaf(q, x, 1.6666666666666667e-01f);            // 1/3!
+  q = fmaf(q, x, 0.5f);                               // 1/2!
+  q = fmaf(q, x, 1.f);
+  const float m2 = x > -kLn2 ? -x * q : fmaf(-a, a, 1.f);
+  beta = __builtin_amdgcn_sqrtf(m2) * i;
+}
+
+// r and i only (the backward's recompute)
+__device__ __forceinline__ void gate_fast_ri(float za, float zx, const GateChan& k, float& r,
+                                             float& i) {
+  r = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(fmaf(za, -kLog2e, k.nba)));
+  i = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(fmaf(zx, -kLog2e, k.nbx)));
 }
 
 // ------------------------------------------------------------------ scan look-back

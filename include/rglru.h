@@ -93,9 +93,26 @@ int rglru_fwd(int B, int T, int D, rglru_dtype io, float c, const void* x,
               const float* lambda, const float* h0, void* y, float* h_T,
               void* conv_state_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Workspace bytes rglru_lru needs (0 for invalid arguments). */
+size_t rglru_lru_workspace_bytes(int B, int T, int D, rglru_dtype io);
+
 /*
- * The forward in two halves, for callers that produce or consume the gates themselves
- * (rglru_fwd is conv1d_causal4, then rglru_gates, then rglru_scan on the same stream).
+ * The RG-LRU layer alone (Eq. (1)-(4) of the RG-LRU section) on an input u that is
+ * already the conv output: rglru_fwd is conv1d_causal4 followed by rglru_lru on the same
+ * stream, and equals rglru_lru when conv_w is NULL.  For bf16 I/O one fused kernel runs
+ * the gate GEMM on the matrix cores and the chunked scan in its epilogue (a_t and beta_t
+ * never reach HBM); for fp32 I/O it is rglru_gates followed by rglru_scan.
+ *   u [B,T,D] io; W_a, W_x [D,D] io; b_a, b_x, lambda [D] fp32; h0 [B,D] fp32 or NULL;
+ *   y [B,T,D] io (output); h_T [B,D] fp32 (output, nullable).  Bitwise reproducible.
+ */
+int rglru_lru(int B, int T, int D, rglru_dtype io, float c, const void* u, const void* W_a,
+              const void* W_x, const float* b_a, const float* b_x, const float* lambda,
+              const float* h0, void* y, float* h_T, void* ws, size_t ws_bytes,
+              hipStream_t stream);
+
+/*
+ * The unfused halves of the RG-LRU layer, for callers that produce or consume the gates
+ * themselves (rglru_lru for fp32 I/O is rglru_gates, then rglru_scan on the same stream).
  *
  * rglru_gates: Eq. (1)-(3) and the input scale of Eq. (4) for every (batch, time) row:
  *   r = sigma(W_a u + b_a), i = sigma(W_x u + b_x), a = exp(c r log sigma(Lambda)),

@@ -99,3 +99,24 @@ def test_forward_as_conv_gates_scan(lib, io):
     ey, eh = err(host(y), o["y"]), err(host(hT), o["h_T"])
     print(f"split io={io} err(a)={err(host(a), ok['a']):.2e} err(y)={ey:.2e} err(h_T)={eh:.2e}")
     assert ey <= TOL[io] and eh <= TOL[io]
+
+
+@pytest.mark.parametrize("io,B,T,D", [("bf16", 2, 700, 384), ("bf16", 3, 257, 192), ("bf16", 1, 1, 64),
+                                      ("bf16", 2, 513, 320), ("f32", 2, 300, 128)])
+def test_lru_layer_on_conv_output(lib, io, B, T, D):
+    """conv1d_causal4 then rglru_lru (the RG-LRU layer alone) equals the full forward."""
+    import torch
+    from gpu_util import host
+    p = make(workloads.TRAIN_FWD, B=B, T=T, D=D, io=io, h0="normal", history="normal")
+    d = device_inputs(p)
+    u = torch.empty_like(d["x"])
+    y = torch.empty_like(d["x"])
+    hT = torch.empty_like(d["h0"])
+    ws = lib.workspace(lib.lru_workspace_bytes(B, T, D, d["x"].dtype))
+    lib.conv1d_causal4(d["x"], d["conv_w"], d["conv_b"], d["conv_state"], u, None)
+    lib.rglru_lru(u, d["W_a"], d["W_x"], d["b_a"], d["b_x"], d["lam"], d["h0"], y, hT, ws, p["c"])
+    torch.cuda.synchronize()
+    o = oracle_forward(p)
+    ey, eh = err(host(y), o["y"]), err(host(hT), o["h_T"])
+    print(f"lru io={io} shape={(B, T, D)} err(y)={ey:.2e} err(h_T)={eh:.2e}")
+    assert ey <= TOL[io] and eh <= TOL[io]
