@@ -3,13 +3,15 @@
 
 Headline workload: the training-shape forward B=8, T=2048, D_RNN=2560, bf16 I/O with
 fp32 scan state.  One step is one pass of the whole forward hot path over one batch:
-    conv1d_causal4 (K0) -> rglru_gates (K1: MFMA gate GEMM + fused epilogue)
-    -> rglru_scan (K2: fused conv + chunked scan)
-which is exactly what rglru_fwd launches (rglru_fwd folds the scan's status
-initialisation into K0; here rglru_scan launches it itself).  Inputs are resident in HBM
-before the timed region; three input sets rotate so consecutive steps do not re-read the
-same x from the 256 MB Infinity Cache.  HIP events on the library's stream (the torch
-current stream) bracket every launch, giving per-kernel durations over the timed region.
+    conv1d_causal4 (K0: width-4 causal conv)
+    -> rglru_lru (K1: MFMA gate GEMM with the log-space gates and the chunked scan fused
+       into its epilogue)
+which is what rglru_fwd launches (rglru_fwd folds the look-back status initialisation
+into K0; rglru_lru launches it itself, so the K1 interval includes that small fill).
+Inputs are resident in HBM before the timed region; three input sets rotate so
+consecutive steps do not re-read the same x from the 256 MB Infinity Cache.  HIP events
+on the library's stream (the torch current stream) bracket every launch, giving
+per-kernel durations over the timed region.
 
 Prints ONE JSON line.  With --gpus N > 1 it exits with a message: the build runs on one
 GPU (no cross-GPU path exists).
@@ -30,8 +32,9 @@ sys.path.insert(0, ROOT)
 METRIC = "RG-LRU block tokens/sec + achieved HBM GB/s (B=8,T=2048,D_RNN=2560 bf16)"
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
-GEMM_PROFILE = os.path.join(ROOT, "profiles", "gate_gemm_train_fwd_B8_T2048_D2560_pmc.md")
-GEMM_SOURCE = os.path.join(ROOT, "gated_linear_rnn_amd", "csrc", "gemm.hip")
+LRU_PROFILE = os.path.join(ROOT, "profiles", "lru_fused_train_fwd_B8_T2048_D2560_pmc.md")
+LRU_SOURCES = [os.path.join(ROOT, "gated_linear_rnn_amd", "csrc", f)
+               for f in ("lru.hip", "gemm_core.h", "rglru_device.h")]
 
 
 def _parse():
@@ -50,19 +53,27 @@ def _log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def _gemm_traffic():
-    """HBM bytes per gate-GEMM launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; otherwise None."""
+def kernel_source_sha256():
+    """SHA-256 over the sources of the fused RG-LRU kernel (lru.hip, gemm_core.h,
+    rglru_device.h, in that order)."""
+    h = hashlib.sha256()
+    for f in LRU_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def _lru_traffic():
+    """HBM bytes per fused-kernel launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; otherwise None."""
     try:
-        txt = open(GEMM_PROFILE).read()
+        txt = open(LRU_PROFILE).read()
     except OSError:
         return None
     m = re.search(r"```json\n(.*?)\n```", txt, re.S)
     if not m:
         return None
     rec = json.loads(m.group(1))
-    src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
-    if rec.get("gemm_source_sha256") != src:
+    if rec.get("kernel_source_sha256") != kernel_source_sha256():
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -112,11 +123,9 @@ def main():
     W_a, W_x = dev(p["W_a"], bf), dev(p["W_x"], bf)
     b_a, b_x, lam = dev(p["b_a"]), dev(p["b_x"]), dev(p["lam"])
     u = torch.empty((B, T, D), dtype=bf, device="cuda")
-    a = torch.empty((B, T, D), dtype=torch.float32, device="cuda")
-    beta = torch.empty_like(a)
     y = torch.empty((B, T, D), dtype=bf, device="cuda")
     hT = torch.empty((B, D), dtype=torch.float32, device="cuda")
-    ws = g.workspace(g.scan_workspace_bytes(B, T, D, bf))
+    ws = g.workspace(g.lru_workspace_bytes(B, T, D, bf))
     c = p["c"]
 
     def step(k, ev=None):
@@ -126,18 +135,15 @@ def main():
         g.conv1d_causal4(x, conv_w, conv_b, None, u, None)
         if ev is not None:
             ev[1].record()
-        g.rglru_gates(u, W_a, W_x, b_a, b_x, lam, a, beta, c)
+        g.rglru_lru(u, W_a, W_x, b_a, b_x, lam, None, y, hT, ws, c)
         if ev is not None:
             ev[2].record()
-        g.rglru_scan(x, conv_w, conv_b, None, a, beta, None, y, hT, ws)
-        if ev is not None:
-            ev[3].record()
 
     _log(f"warmup {args.warmup} steps")
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     _log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -147,14 +153,15 @@ def main():
     t1 = time.perf_counter()
     wall = t1 - t0
     ms = lambda i, j: float(np.mean([e[i].elapsed_time(e[j]) for e in evs]))
-    conv_ms, gates_ms, scan_ms = ms(0, 1), ms(1, 2), ms(2, 3)
+    conv_ms, lru_ms = ms(0, 1), ms(1, 2)
     tokens_per_s = M * args.steps / wall
 
     gemm_flop = 2.0 * M * (2 * D) * D
-    gemm_tflops = gemm_flop / (gates_ms * 1e-3) / 1e12
-    scan_bytes = M * D * (2 + 4 + 4 + 2)            # x, a, beta in; y out
-    scan_gbps = scan_bytes / (scan_ms * 1e-3) / 1e9
+    lru_tflops = gemm_flop / (lru_ms * 1e-3) / 1e12
+    block_bytes = M * D * (2 + 2) + 2 * D * D * 2      # x in, y out, W_a and W_x once
+    block_gbps = block_bytes / (wall / args.steps) / 1e9
     conv_bytes = M * D * (2 + 2)
+    lru_bytes = M * D * (2 + 2 + 2) + 2 * D * D * 2    # u (GEMM operand), u (scan), y, W once
     out = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -171,23 +178,24 @@ def main():
         "config": {"workload": w.name, "B": B, "T": T, "D_RNN": D, "io": "bf16",
                    "scan_state": "fp32", "c": c},
         "roofline": {
-            "kernel": "gemm_bf16_kernel<256,128,2,2,kEpiAB> (rglru_gates: gate GEMM + epilogue)",
-            "bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": gemm_tflops / PEAK_BF16_TFLOPS, "traffic": _gemm_traffic(),
-            "flop_per_launch": gemm_flop, "avg_launch_ms": gates_ms,
-        },
-        "scan_hbm": {
-            "kernel": "scan_fwd_kernel<bf16,float> (rglru_scan: fused conv + chunked scan)",
-            "bound": "hbm", "achieved": scan_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": scan_gbps / PEAK_HBM_GBPS, "bytes_per_launch": scan_bytes,
-            "avg_launch_ms": scan_ms,
+            "kernel": "lru_fused_kernel (rglru_lru: gate GEMM + gates + chunked scan)",
+            "bound": "mfma", "achieved": lru_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": lru_tflops / PEAK_BF16_TFLOPS, "traffic": _lru_traffic(),
+            "flop_per_launch": gemm_flop, "avg_launch_ms": lru_ms,
             "note": "interval includes the look-back status initialisation launch",
         },
-        "per_kernel_ms": {"conv": conv_ms, "gates": gates_ms, "scan": scan_ms},
-        "block_tokens_per_s_kernels": M / ((conv_ms + gates_ms + scan_ms) * 1e-3),
-        "conv_hbm_GBps": conv_bytes / (conv_ms * 1e-3) / 1e9,
+        "hbm": {
+            "block_achieved_GBps": block_bytes / (wall / args.steps) / 1e9,
+            "block_bytes_per_step": block_bytes,
+            "block_frac_of_peak": block_gbps / PEAK_HBM_GBPS,
+            "conv_kernel_GBps": conv_bytes / (conv_ms * 1e-3) / 1e9,
+            "lru_kernel_GBps": lru_bytes / (lru_ms * 1e-3) / 1e9,
+            "peak_GBps": PEAK_HBM_GBPS,
+        },
+        "per_kernel_ms": {"conv": conv_ms, "lru_fused": lru_ms},
+        "block_tokens_per_s_kernels": M / ((conv_ms + lru_ms) * 1e-3),
     }
-    del xs, u, a, beta, y, ws
+    del xs, u, y, ws
     torch.cuda.empty_cache()
 
     if not args.no_extras:

@@ -103,3 +103,27 @@ def test_forward_is_bitwise_reproducible(lib):
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert torch.equal(o[0], outs[0][0]) and torch.equal(o[1], outs[0][1])
+
+
+def test_bf16_rounding_of_halfway_sums_is_exact(lib):
+    """R1 on halfway cases: with conv taps (1, 1, 0, 0) the fp32 sum x_t + x_{t-1} of two
+    bf16 values lands exactly halfway between bf16 neighbours; the GPU's rounding must
+    equal the oracle's round-to-nearest-even bit for bit."""
+    D, T = 64, 48
+    k = np.arange(T)[:, None] % 16
+    x = np.zeros((1, T, D))
+    x[0, 0::2] = 1.0 + (k[0::2] + np.arange(D)[None, :] % 8) * 2.0 ** -7   # even steps: 1 + j 2^-7
+    x[0, 1::2] = 2.0 ** -8 * (1 + (np.arange(D)[None, :] % 3 == 0))         # odd: 2^-8 or 2^-7
+    x[0, 1::2] *= np.where(np.arange(D) % 2 == 0, 1, -1)[None, :]
+    w = np.zeros((4, D)); w[0] = 1.0; w[1] = 1.0
+    xd = dev(x, torch.bfloat16)
+    assert np.array_equal(host(xd), x)
+    wd = dev(w, torch.bfloat16)
+    u = torch.empty_like(xd)
+    lib.conv1d_causal4(xd, wd, None, None, u, None)
+    torch.cuda.synchronize()
+    uo, _ = oracle.conv1d_causal4(x, w, None, None, "bf16")
+    np.testing.assert_array_equal(host(u), uo)
+    # and the ties really occur (half of the odd-step sums sit exactly between neighbours)
+    s = x[0, 1:] + x[0, :-1]
+    assert np.sum(oracle.round_io(s, "bf16") != s) > 100
