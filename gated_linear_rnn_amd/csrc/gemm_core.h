@@ -25,6 +25,12 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // vmcnt(0)); the "memory" clobber keeps the compiler from moving memory accesses across.
 template <int N>
 __device__ __forceinline__ void wait_dma_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // The builtin wait (vmcnt(N) lgkmcnt(0), expcnt left at its maximum 7) is the one that
+  // counts; it also tells the compiler's wait-count tracking what has completed (it cannot
+  // see into asm), so later LDS reads get exact waits.  The asm adds the barrier, and its
+  // memory clobber keeps memory accesses from moving across.
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
@@ -64,6 +70,48 @@ struct TileOperands {
   int a_row0, a_rows;   // first global A row of the tile and valid rows (>= 1)
   int b_row0, b_rows;   // first global B row (gate: channel) and valid rows (>= 1)
 };
+
+// MFMAs LO .. HI-1 of a k-slice (fragment mf x fragment f, f fastest).
+template <class C, int LO, int HI>
+__device__ __forceinline__ void mfma_range(f32x16_t (&acc)[C::MF][C::NF], const bf16x8_t* af,
+                                           const bf16x8_t* bfr) {
+#pragma unroll
+  for (int i = LO; i < HI; ++i) {
+    const int mf = i / C::NF, f = i % C::NF;
+    acc[mf][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mf], bfr[f], acc[mf][f], 0, 0, 0);
+  }
+}
+
+// Scheduling groups for a region holding NM MFMAs and NR LDS reads: one MFMA, then reads
+// and MFMAs alternating, then whatever is left of either.
+template <int NM, int NR>
+__device__ __forceinline__ void sched_reads_after_first_mfma() {
+  constexpr int P = NR < NM - 1 ? NR : NM - 1;
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+  if constexpr (NR > P) __builtin_amdgcn_sched_group_barrier(0x100, NR - P, 0);
+  if constexpr (NM - 1 > P) __builtin_amdgcn_sched_group_barrier(0x008, NM - 1 - P, 0);
+}
+
+// Scheduling groups for NM MFMAs with NR LDS reads spread in front of them.
+template <int NM, int NR>
+__device__ __forceinline__ void sched_reads_spread() {
+  constexpr int Q = NR / NM, RM = NR % NM;
+#pragma unroll
+  for (int i = 0; i < RM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, Q + 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+#pragma unroll
+  for (int i = RM; i < NM; ++i) {
+    if constexpr (Q > 0) __builtin_amdgcn_sched_group_barrier(0x100, Q, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+}
 
 // Accumulate the tile into acc.  lds must hold C::LDS_BYTES; wave = wave index in the WG.
 template <class C, bool DUAL>
@@ -133,19 +181,17 @@ __device__ __forceinline__ void gemm_mainloop(const TileOperands& op, unsigned c
 #pragma unroll
     for (int f = 0; f < C::NF; ++f) bfr[f] = *reinterpret_cast<const bf16x8_t*>(sb + brow[f] + coff);
   };
-  auto mfmas = [&](const bf16x8_t* af, const bf16x8_t* bfr) {
-#pragma unroll
-    for (int mf = 0; mf < C::MF; ++mf)
-#pragma unroll
-      for (int f = 0; f < C::NF; ++f)
-        acc[mf][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mf], bfr[f], acc[mf][f], 0, 0, 0);
-  };
-
   // Software pipeline: the fragments of the next k-slice are read from LDS while the MFMAs
-  // of the current one run; the barrier that hands over the next k-step sits before the
-  // last slice's MFMAs, so the matrix core stays busy across it.  After the barrier every
-  // wave is done with k-step kt's buffer, which is refilled with k-step kt + STAGES.
+  // of the current one run; the scheduling groups below pin the order (one MFMA first, then
+  // reads and MFMAs alternating) so that the wait for a slice's fragments only covers reads
+  // issued a whole slice earlier.  The barrier that hands over the next k-step sits in the
+  // middle of the last slice's MFMAs, so the matrix core stays busy across it; after the
+  // barrier every wave is done with k-step kt's buffer, which is refilled with k-step
+  // kt + STAGES.  The final k-step is peeled off so that the loop body is the same on every
+  // trip (a conditional tail inside the loop makes the compiler drain all LDS reads at the
+  // loop header).
   constexpr int S = C::STAGES;
+  constexpr int NM = C::MF * C::NF, NR = C::MF + C::NF, NM1 = NM / 2;
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
     if (s < KT) issue(s);
@@ -154,20 +200,35 @@ __device__ __forceinline__ void gemm_mainloop(const TileOperands& op, unsigned c
   if (S - 1 < KT) issue(S - 1);
   bf16x8_t fa[2][C::MF], fb[2][C::NF];
   load_frags(0, 0, fa[0], fb[0]);
-  for (int kt = 0; kt < KT; ++kt) {
+  for (int kt = 0; kt < KT - 1; ++kt) {
 #pragma unroll
     for (int kk = 0; kk < C::KK; ++kk) {
       const int cur = kk & 1;   // KK is even: slice 0 of every k-step lives in buffer 0
       if (kk + 1 < C::KK) {
+        mfma_range<C, 0, NM>(acc, fa[cur], fb[cur]);
         load_frags(kt, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
-      } else if (kt + 1 < KT) {
+        sched_reads_after_first_mfma<NM, NR>();
+      } else {
+        mfma_range<C, 0, NM1>(acc, fa[cur], fb[cur]);
+        __builtin_amdgcn_sched_barrier(0);
         // k-step kt+1 has landed once at most min(S-2, KT-2-kt) newer k-steps pend
         if (kt + S - 1 < KT) wait_dma_barrier<(S - 2) * C::QPW>();
         else wait_dma_barrier<0>();
         if (kt + S < KT) issue(kt + S);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_range<C, NM1, NM>(acc, fa[cur], fb[cur]);
         load_frags(kt + 1, 0, fa[cur ^ 1], fb[cur ^ 1]);
+        sched_reads_spread<NM - NM1, NR>();
       }
-      mfmas(fa[cur], fb[cur]);
+    }
+  }
+#pragma unroll
+  for (int kk = 0; kk < C::KK; ++kk) {
+    const int cur = kk & 1;
+    mfma_range<C, 0, NM>(acc, fa[cur], fb[cur]);
+    if (kk + 1 < C::KK) {
+      load_frags(KT - 1, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
+      sched_reads_after_first_mfma<NM, NR>();
     }
   }
 }

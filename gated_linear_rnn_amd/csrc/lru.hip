@@ -75,30 +75,19 @@ __device__ __forceinline__ void lru_epilogue(const LruArgs& p, unsigned char* ld
   const bool chok = chl < chv;
   const GateChan kc = gate_chan(p.ba[chok ? ch : tn * kLruCh], p.bx[chok ? ch : tn * kLruCh],
                                 p.lam[chok ? ch : tn * kLruCh], p.c);
-  // Group q = 4 mf + gq of this lane covers tile rows wm*128 + 32 mf + 8 gq + 4 half + rr,
-  // rr = 0..3 (consecutive time steps).  a_t and beta_t first (the u tile is in flight).
-  float av[16][4], bu[16][4];
-#pragma unroll
-  for (int mf = 0; mf < C::MF; ++mf)
-#pragma unroll
-    for (int gq = 0; gq < 4; ++gq)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int lr = wm * C::WTM + mf * 32 + 8 * gq + 4 * half + rr;
-        float a, beta;
-        gate_fast(acc[mf][0][gq * 4 + rr], acc[mf][1][gq * 4 + rr], kc, a, beta);
-        const bool ok = !EDGE || lr < rows;
-        av[mf * 4 + gq][rr] = ok ? a : 1.f;
-        bu[mf * 4 + gq][rr] = ok ? beta : 0.f;
-      }
   wait_dma_barrier<0>();                             // the u tile is in LDS
-  // this lane's rows of the LDS tile: tb[(32 mf + 8 gq + rr) * kLruCh] (constant offsets)
+  // Group q = 4 mf + gq of this lane covers tile rows wm*128 + 32 mf + 8 gq + 4 half + rr,
+  // rr = 0..3 (consecutive time steps); tb[(32 mf + 8 gq + rr) * kLruCh] is the LDS element
+  // of row rr (constant offsets).  The first pass turns the accumulator pair (z^a, z^x) of
+  // each element into (a_t, beta_t u_t) in place, so the second pass finds them there.
   bf16_t* tb = tileU + (wm * C::WTM + 4 * half) * kLruCh + chl;
+  // rows of this lane's groups are lrow0 + 32 mf + 8 gq + rr; those >= lim are past the end
+  const int lrow0 = wm * C::WTM + 4 * half;
+  const int lim = rows - lrow0;
   const int partner = (lane ^ 32) << 2;               // ds_bpermute byte address
-  // Per group: beta_t u_t, the group's summary (A = prod a, H), and the running composition
-  // over the 32 groups of the wave's 128 rows in time order (for each gq the lower-half
-  // lane's group comes first, then the upper-half lane's).  pre[q] is the map in front of
-  // this lane's group q.
+  // Per group: the summary (A = prod a, H) and the running composition over the 32 groups
+  // of the wave's 128 rows in time order (for each gq the lower-half lane's group comes
+  // first, then the upper-half lane's).  pre[q] is the map in front of this lane's group q.
   float preA[16], preH[16];
   float RA = 1.f, RH = 0.f;
 #pragma unroll
@@ -106,9 +95,18 @@ __device__ __forceinline__ void lru_epilogue(const LruArgs& p, unsigned char* ld
     float Aq = 1.f, Hq = 0.f;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      bu[q][rr] *= bf2f(tb[((q >> 2) * 32 + 8 * (q & 3) + rr) * kLruCh]);
-      Hq = fmaf(av[q][rr], Hq, bu[q][rr]);
-      Aq = Aq * av[q][rr];
+      const int mf = q >> 2, gq = q & 3, v = gq * 4 + rr;
+      const int rel = mf * 32 + 8 * gq + rr;
+      float a, beta;
+      gate_fast(acc[mf][0][v], acc[mf][1][v], kc, a, beta);
+      const float uv = bf2f(tb[rel * kLruCh]);      // rows past the end hold clamped copies
+      const bool ok = !EDGE || rel < lim;
+      a = ok ? a : 1.f;
+      const float bu = ok ? beta * uv : 0.f;
+      acc[mf][0][v] = a;
+      acc[mf][1][v] = bu;
+      Hq = fmaf(a, Hq, bu);
+      Aq = Aq * a;
     }
     const float Ap = __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(Aq)));
     const float Hp = __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(Hq)));
@@ -121,6 +119,7 @@ __device__ __forceinline__ void lru_epilogue(const LruArgs& p, unsigned char* ld
     preH[q] = half ? RH : R0H;
     RH = fmaf(A1, RH, H1);
     RA = A1 * RA;
+    __builtin_amdgcn_sched_barrier(0);   // one group at a time: bounds the live registers
   }
   if (wm == 0 && half == 0) { eA[chl] = RA; eH[chl] = RH; }
   __syncthreads();                                   // also: every wave is done reading u
@@ -151,7 +150,7 @@ __device__ __forceinline__ void lru_epilogue(const LruArgs& p, unsigned char* ld
   __syncthreads();
   const float carry = eC[chl];
   const float hin = wm == 0 ? carry : fmaf(A0w, carry, H0w);
-  const int lastrow = T - 1 - t0;                    // tile row of the final step, if in tile
+  const int lastrel = T - 1 - t0 - lrow0;            // the final step, if in this lane's rows
   float hlast = 0.f;
   bool haslast = false;
 #pragma unroll
@@ -159,12 +158,12 @@ __device__ __forceinline__ void lru_epilogue(const LruArgs& p, unsigned char* ld
     float h = fmaf(preA[q], hin, preH[q]);
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      h = fmaf(av[q][rr], h, bu[q][rr]);
-      const int lr = wm * C::WTM + (q >> 2) * 32 + 8 * (q & 3) + 4 * half + rr;
+      h = fmaf(acc[q >> 2][0][(q & 3) * 4 + rr], h, acc[q >> 2][1][(q & 3) * 4 + rr]);
+      const int rel = (q >> 2) * 32 + 8 * (q & 3) + rr;
       tb[((q >> 2) * 32 + 8 * (q & 3) + rr) * kLruCh] = f2bf(h);
       if (EDGE) {
-        hlast = lr == lastrow ? h : hlast;
-        haslast = haslast || lr == lastrow;
+        hlast = rel == lastrel ? h : hlast;
+        haslast = haslast || rel == lastrel;
       }
     }
   }
@@ -185,17 +184,16 @@ __device__ __forceinline__ void lru_epilogue(const LruArgs& p, unsigned char* ld
 __global__ __launch_bounds__(CfgLru::NW * 64, 2) void lru_fused_kernel(LruArgs p) {
   typedef CfgLru C;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS_BYTES];
-  __shared__ uint32_t s_ticket;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / C::WN, wn = wave % C::WN;
+  __shared__ uint32_t s_ticket;
   const int G = p.groups, g = blockIdx.x % G;
   if (tid == 0) s_ticket = atomicAdd(p.counters + g, 1u);
   __syncthreads();
+  const int k = __builtin_amdgcn_readfirstlane(int(s_ticket));
   const int B = p.B, T = p.T, D = p.D;
   const int NT = (D + kLruCh - 1) / kLruCh;
   const int per_level = B * NT / G;
-  const int k = int(s_ticket);
   const int tt = k / per_level;
   const int chain = g + G * (k % per_level);
   const int b = chain / NT, tn = chain % NT;
