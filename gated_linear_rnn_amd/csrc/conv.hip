@@ -1,9 +1,9 @@
 // Causal depthwise Conv1D of temporal width 4 (Griffin model-architecture page, section
 // "Recurrent block": a small separable Conv1D with only 4*D parameters placed before the
 // RG-LRU).  Elementwise and HBM-bound: each thread owns four consecutive channels of one
-// sequence and walks a run of time steps with a three-row sliding window, so every x
-// element is read from HBM once and every u element written once (coalesced 8/16-byte
-// accesses along the channel axis).
+// sequence and a run of 16 time steps; it loads the run's 19 input rows at once (the loads
+// are in flight together) and writes the 16 output rows, so x is read about once (3 halo
+// rows per 16) and u written once, with coalesced 8/16-byte accesses along the channels.
 #include "rglru_device.h"
 #include "kernels.h"
 
@@ -48,17 +48,25 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(int B, int T, int D, cons
     return make_float4(0, 0, 0, 0);
   };
   const int t0 = tc * kConvSteps;
-  float4 xm3 = X(t0 - 3), xm2 = X(t0 - 2), xm1 = X(t0 - 1);
-  const int t1 = min(T, t0 + kConvSteps);
-  for (int t = t0; t < t1; ++t) {
-    float4 x0 = X(t), o;
+  // all kConvSteps + 3 input rows are loaded before any arithmetic, so the loads are in
+  // flight together; rows past the end are clamped to the last row (their outputs are not
+  // stored)
+  float4 xs[kConvSteps + 3];
+#pragma unroll
+  for (int j = 0; j < kConvSteps + 3; ++j) {
+    const int t = t0 - 3 + j;
+    xs[j] = (j < 3 && t0 == 0) ? X(t) : Io<IO>::load4(x + (size_t(b) * T + min(t, T - 1)) * D + d);
+  }
+#pragma unroll
+  for (int i = 0; i < kConvSteps; ++i) {
+    const int t = t0 + i;
+    float4 o;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       f4set(o, j, conv_u<IO>(f4get(bias, j), f4get(w0, j), f4get(w1, j), f4get(w2, j),
-                             f4get(w3, j), f4get(x0, j), f4get(xm1, j), f4get(xm2, j),
-                             f4get(xm3, j)));
-    Io<IO>::store4(u + (size_t(b) * T + t) * D + d, o);
-    xm3 = xm2; xm2 = xm1; xm1 = x0;
+                             f4get(w3, j), f4get(xs[i + 3], j), f4get(xs[i + 2], j),
+                             f4get(xs[i + 1], j), f4get(xs[i], j)));
+    if (t < T) Io<IO>::store4(u + (size_t(b) * T + t) * D + d, o);
   }
   if (state_out && tc == 0) {
     for (int j = 0; j < 3; ++j) Io<IO>::store4(state_out + (size_t(b) * 3 + j) * D + d, X(T - 3 + j));
