@@ -40,8 +40,8 @@ LRU_SOURCES = [os.path.join(ROOT, "gated_linear_rnn_amd", "csrc", f)
 def _parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-extras", action="store_true", help="skip the decode and fwd+bwd timings")
     ap.add_argument("--copy-calibration", action="store_true",
