@@ -344,6 +344,8 @@ size_t rglru_decode_workspace_bytes(int B, int D, rglru_dtype io) {
   if (io == RGLRU_F32) {
     cv.take<float>(size_t(B) * D);
     cv.take<float>(size_t(B) * D);
+  } else {
+    cv.take<unsigned char>(decode_partial_bytes(B, D));
   }
   return cv.used;
 }
@@ -367,11 +369,20 @@ int rglru_decode_step(int B, int D, rglru_dtype io, float c, const void* x_t, co
   void* ubuf = cv.take<unsigned char>(size_t(B) * D * io_bytes(io));
   float* za = io == RGLRU_F32 ? cv.take<float>(size_t(B) * D) : nullptr;
   float* zx = io == RGLRU_F32 ? cv.take<float>(size_t(B) * D) : nullptr;
+  float* partial = io == RGLRU_BF16 ? reinterpret_cast<float*>(cv.take<unsigned char>(decode_partial_bytes(B, D)))
+                                    : nullptr;
   const void* u = x_t;
   if (conv_w) {
     if (io == RGLRU_BF16) RG_CHECK(launch_conv_decode<bf16_t>(B, D, x_t, conv_w, conv_b, conv_state, ubuf, stream));
     else RG_CHECK(launch_conv_decode<float>(B, D, x_t, conv_w, conv_b, conv_state, ubuf, stream));
     u = ubuf;
+  }
+  if (io == RGLRU_BF16) {
+    DecodeArgs d{};
+    d.u = u; d.Wa = W_a; d.Wx = W_x; d.ba = b_a; d.bx = b_x; d.lam = lambda; d.c = c;
+    d.h = h; d.y = y_t; d.partial = partial; d.B = B; d.D = D;
+    RG_CHECK(launch_decode_bf16(d, stream));
+    return RGLRU_OK;
   }
   GateGemmArgs g{};
   g.U = u; g.Wa = W_a; g.Wx = W_x; g.M = B; g.N = D; g.K = D;

@@ -1,0 +1,145 @@
+// One decode step of the RG-LRU for bf16 I/O (Griffin model-architecture page, section
+// "Real-Gated Linear Recurrent Unit (RG-LRU)", Eq. (1)-(4) at a single time step; the blog
+// page "Griffin's Compromise", section "Hawk: Redesigning RNN State with Gates": a step
+// reads and writes only the current token and a fixed-size state).
+//
+// The gate projection of a step is a small-M GEMM (M = batch) whose cost is streaming the
+// weights, so its K loop is split S ways to put enough workgroups on the chip: every
+// workgroup accumulates z^a and z^x of its (row tile, channel tile) over one K range on the
+// matrix cores and writes the raw sums to a partial buffer.  A second kernel adds the S
+// partials of each (row, channel) in a fixed order (so the result does not depend on
+// scheduling), applies the gates of Eq. (1)-(3) with the biases, and updates the state in
+// place: h <- a h + sqrt(1 - a^2) (i u), y = RNE_bf16(h).
+#include "gemm_core.h"
+#include "kernels.h"
+
+namespace rglru {
+
+// 128 rows x 64 channels (64 rows of W_a + the same 64 of W_x), 4 waves of 64 x (32 + 32),
+// K steps of 64, double-buffered: 64 KB of LDS, so two workgroups fit on a CU.
+typedef GemmCfg<128, 64, 2, 2, false, 64, 2> CfgDecode;
+
+constexpr int kMaxSplits = 8;
+
+int decode_splits(int B, int D) {
+  const int MT = (B + CfgDecode::BM - 1) / CfgDecode::BM;
+  const int NT = (D + CfgDecode::BC - 1) / CfgDecode::BC;
+  const int ksteps = D / CfgDecode::BK;
+  // the smallest divisor of the K steps that gives at least one workgroup per CU
+  int best = 1;
+  for (int s = 1; s <= ksteps && s <= kMaxSplits; ++s) {
+    if (ksteps % s) continue;
+    best = s;
+    if (MT * NT * s >= 256) break;
+  }
+  return best;
+}
+
+size_t decode_partial_bytes(int B, int D) {
+  return size_t(decode_splits(B, D)) * 2 * size_t(B) * D * sizeof(float);
+}
+
+// partial[s][0][m][ch] = sum over k in split s of u[m,k] W_a[ch,k]; partial[s][1] for W_x
+__global__ __launch_bounds__(CfgDecode::NW * 64, 2) void decode_partial_kernel(DecodeArgs p) {
+  typedef CfgDecode C;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS_BYTES];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int B = p.B, D = p.D, S = p.splits;
+  const int MT = (B + C::BM - 1) / C::BM;
+  // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so that each XCD
+  // runs a contiguous range of L = tm + MT (s + S tn): the row tiles that share a W panel
+  // then share that XCD's L2, and W streams from the Infinity Cache once per step.
+  const int G = gridDim.x;
+  const int L = (G & 7) == 0 ? int(blockIdx.x & 7) * (G >> 3) + int(blockIdx.x >> 3) : int(blockIdx.x);
+  const int tm = L % MT;
+  const int s = (L / MT) % S;
+  const int tn = L / (MT * S);
+  const int kc = D / S;                            // K columns per split (a multiple of 64)
+  const int m0 = tm * C::BM, n0 = tn * C::BC;
+
+  TileOperands op;
+  op.A = static_cast<const bf16_t*>(p.u) + size_t(s) * kc;
+  op.A2 = nullptr;
+  op.B0 = static_cast<const bf16_t*>(p.Wa) + size_t(s) * kc;
+  op.B1 = static_cast<const bf16_t*>(p.Wx) + size_t(s) * kc;
+  op.lda = D; op.ldb = D; op.K = kc;
+  op.a_row0 = m0; op.a_rows = B - m0;
+  op.b_row0 = n0; op.b_rows = D - n0;
+  f32x16_t acc[C::MF][C::NF];
+  gemm_mainloop<C, false>(op, lds, lane, wave, acc);
+
+  const size_t BD = size_t(B) * D;
+  float* pa = p.partial + size_t(s) * 2 * BD;
+  float* px = pa + BD;
+  constexpr int HALF = C::NF / 2;
+  const int col = lane & 31;
+#pragma unroll
+  for (int jc = 0; jc < HALF; ++jc) {
+    const int ch = n0 + wn * (C::BC / C::WN) + jc * 32 + col;
+    if (ch >= D) continue;
+#pragma unroll
+    for (int mf = 0; mf < C::MF; ++mf)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + wm * C::WTM + mf * 32 + acc_row(v, lane);
+        if (m >= B) continue;
+        pa[size_t(m) * D + ch] = acc[mf][jc][v];
+        px[size_t(m) * D + ch] = acc[mf][jc + HALF][v];
+      }
+  }
+}
+
+// Sum the splits in order s = 0..S-1, then the gates and the state update; 4 channels per
+// thread (16-byte loads along the channel axis).
+__global__ __launch_bounds__(256) void decode_update_kernel(DecodeArgs p) {
+  const int B = p.B, D = p.D, S = p.splits;
+  const size_t BD = size_t(B) * D;
+  const size_t q = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (q >= BD / 4) return;
+  const size_t o = q * 4;
+  const int ch0 = int(o % D);
+  const float* pp = p.partial + o;
+  auto ld = [&](int s, int half) { return *reinterpret_cast<const float4*>(pp + (size_t(s) * 2 + half) * BD); };
+  auto add = [](float4& acc, const float4& v) { acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w; };
+  // up to kMaxSplits partials are loaded before any addition (their loads overlap)
+  float4 va[kMaxSplits], vx[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s)
+    if (s < S) { va[s] = ld(s, 0); vx[s] = ld(s, 1); }
+  float4 za = va[0], zx = vx[0];
+#pragma unroll
+  for (int s = 1; s < kMaxSplits; ++s)
+    if (s < S) { add(za, va[s]); add(zx, vx[s]); }
+  const float4 h = *reinterpret_cast<const float4*>(p.h + o);
+  const float4 u = Io<bf16_t>::load4(static_cast<const bf16_t*>(p.u) + o);
+  const float4 ba = *reinterpret_cast<const float4*>(p.ba + ch0);
+  const float4 bx = *reinterpret_cast<const float4*>(p.bx + ch0);
+  const float4 lam = *reinterpret_cast<const float4*>(p.lam + ch0);
+  float4 hn;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const GateChan k = gate_chan(f4get(ba, j), f4get(bx, j), f4get(lam, j), p.c);
+    float a, beta;
+    gate_fast(f4get(za, j), f4get(zx, j), k, a, beta);
+    f4set(hn, j, fmaf(a, f4get(h, j), beta * f4get(u, j)));
+  }
+  *reinterpret_cast<float4*>(p.h + o) = hn;
+  Io<bf16_t>::store4(static_cast<bf16_t*>(p.y) + o, hn);
+}
+
+hipError_t launch_decode_bf16(const DecodeArgs& a_in, hipStream_t s) {
+  DecodeArgs a = a_in;
+  a.splits = decode_splits(a.B, a.D);
+  const int MT = (a.B + CfgDecode::BM - 1) / CfgDecode::BM;
+  const int NT = (a.D + CfgDecode::BC - 1) / CfgDecode::BC;
+  decode_partial_kernel<<<MT * NT * a.splits, CfgDecode::NW * 64, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t quads = size_t(a.B) * a.D / 4;
+  decode_update_kernel<<<int((quads + 255) / 256), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace rglru

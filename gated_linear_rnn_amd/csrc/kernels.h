@@ -44,6 +44,26 @@ struct GateGemmArgs {
   void* y;            // kEpiDecode: y [M, N] io
 };
 
+// One bf16 decode step after the conv: split-K gate projection into `partial`, then the
+// fixed-order sum, the gates and the state update (decode.hip).
+struct DecodeArgs {
+  const void* u;      // [B, D] bf16, the conv output of the step
+  const void* Wa;     // [D, D] bf16
+  const void* Wx;     // [D, D] bf16
+  const float* ba;
+  const float* bx;
+  const float* lam;
+  float c;
+  float* h;           // [B, D] state, in/out
+  void* y;            // [B, D] bf16
+  float* partial;     // decode_partial_bytes(B, D)
+  int B, D;
+  int splits;         // set by the launcher
+};
+int decode_splits(int B, int D);
+size_t decode_partial_bytes(int B, int D);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+
 // C[M,N] = A[M,K] B[N,K]^T (+ addend), fp32 output.  With A2 (bf16 only) the product
 // is (A + A2) B^T, evaluated as two bf16 MFMA passes over K.
 struct PlainGemmArgs {

@@ -142,13 +142,16 @@ int rglru_scan(int B, int T, int D, rglru_dtype io, const void* x, const void* c
                const float* beta, const float* h0, void* y, float* h_T, void* ws,
                size_t ws_bytes, hipStream_t stream);
 
-/* Workspace bytes rglru_decode_step needs (0 for invalid arguments). */
+/* Workspace bytes rglru_decode_step needs (0 for invalid arguments): the conv output of
+ * the step and, for bf16 I/O, the fp32 partial sums of the split gate projection. */
 size_t rglru_decode_workspace_bytes(int B, int D, rglru_dtype io);
 
 /*
  * One generation step with the fixed-size state (the blog page "Griffin's Compromise",
  * section "Hawk": generation reads and writes only the current token and a fixed-size
- * state).  Equal to rglru_fwd on a length-1 sequence with carried state.
+ * state).  Computes rglru_fwd on a length-1 sequence with carried state (the same value
+ * up to the fp32 summation order of the gate projection, which is fixed, so repeated
+ * calls give identical bits).
  *   x_t [B,D] io; conv_state [B,3,D] io, in/out (shifted in place; ignored when conv_w
  *   is NULL); h [B,D] fp32, in/out (the recurrent state, updated in place);
  *   y_t [B,D] io (output).  Other arguments as in rglru_fwd.
