@@ -30,11 +30,56 @@ __global__ __launch_bounds__(256) void transpose_kernel(const E* __restrict__ sr
   }
 }
 
+// The same with 16-byte accesses on both sides (V = 16 / sizeof(E) elements per access):
+// a 64 x 64 tile goes through LDS, each thread loading one 16-byte run of a source row and
+// storing one 16-byte run of a destination row.  Needs C, lds, ldd and Rp multiples of V and
+// 16-byte aligned rows.
+template <typename E>
+__global__ __launch_bounds__(256) void transpose_vec_kernel(const E* __restrict__ src, int R, int C,
+                                                            int lds, E* __restrict__ dst, int ldd,
+                                                            int Rp) {
+  constexpr int V = 16 / sizeof(E);
+  constexpr int VPR = 64 / V;                       // 16-byte runs per 64-element tile row
+  __shared__ E tile[64][64 + 2];                    // padded: column reads spread over banks
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  for (int idx = tid; idx < 64 * VPR; idx += 256) {
+    const int i = idx / VPR, cv = (idx % VPR) * V;
+    const int r = r0 + i, c = c0 + cv;
+    E v[V];
+    if (r < R && c < C) {
+      const uint4 w = *reinterpret_cast<const uint4*>(src + size_t(r) * lds + c);
+      __builtin_memcpy(v, &w, 16);
+    } else {
+#pragma unroll
+      for (int j = 0; j < V; ++j) v[j] = E(0);
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j) tile[i][cv + j] = v[j];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < 64 * VPR; idx += 256) {
+    const int i = idx / VPR, rv = (idx % VPR) * V;   // destination row c0 + i, columns r0 + rv ..
+    const int c = c0 + i, r = r0 + rv;
+    if (c >= C || r >= Rp) continue;
+    E v[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) v[j] = tile[rv + j][i];
+    uint4 w;
+    __builtin_memcpy(&w, v, 16);
+    *reinterpret_cast<uint4*>(dst + size_t(c) * ldd + r) = w;
+  }
+}
+
 template <typename E>
 hipError_t launch_transpose(const E* src, int R, int C, int lds, E* dst, int ldd, int Rp,
                             hipStream_t s) {
+  constexpr int V = 16 / sizeof(E);
   dim3 grid((Rp + 63) / 64, (C + 63) / 64);
-  transpose_kernel<E><<<grid, 256, 0, s>>>(src, R, C, lds, dst, ldd, Rp);
+  const bool vec = C % V == 0 && lds % V == 0 && ldd % V == 0 && Rp % V == 0 &&
+                   (reinterpret_cast<uintptr_t>(src) & 15) == 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
+  if (vec) transpose_vec_kernel<E><<<grid, 256, 0, s>>>(src, R, C, lds, dst, ldd, Rp);
+  else transpose_kernel<E><<<grid, 256, 0, s>>>(src, R, C, lds, dst, ldd, Rp);
   return hipGetLastError();
 }
 template hipError_t launch_transpose<uint16_t>(const uint16_t*, int, int, int, uint16_t*, int, int,
