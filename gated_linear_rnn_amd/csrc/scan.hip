@@ -262,58 +262,48 @@ __global__ __launch_bounds__(256) void scan_bwd_kernel(ScanBwdArgs p) {
   const int d = d0 + 4 * cg;
   const size_t BD = size_t(B) * D;
 
-  float4 ra[kSteps], ia[kSteps], uu[kSteps], dyv[kSteps];
-  Acc hp[kSteps][4];
+  // Inputs stream through registers one step at a time (the next step's loads are in
+  // flight while the current one is computed), which keeps the kernel near 128 VGPRs so
+  // that four workgroups share a CU.
   const IO* u = static_cast<const IO*>(p.u);
   const IO* dy = static_cast<const IO*>(p.dy);
   const Acc* h_all = static_cast<const Acc*>(p.h_all);
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    const int t = t0 + tg * kSteps + s;
-    if (t < T) {
-      const size_t o = (size_t(b) * T + t) * D + d;
-      ra[s] = *reinterpret_cast<const float4*>(p.r + o);
-      ia[s] = *reinterpret_cast<const float4*>(p.i + o);
-      uu[s] = Io<IO>::load4(u + o);
-      dyv[s] = Io<IO>::load4(dy + o);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (t > 0) hp[s][j] = h_all[o - D + j];
-        else hp[s][j] = p.h0 ? Acc(p.h0[size_t(b) * D + d + j]) : Acc(0);
-      }
-    } else {
-      ra[s] = ia[s] = uu[s] = dyv[s] = make_float4(0, 0, 0, 0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) hp[s][j] = Acc(0);
-    }
-  }
   float4 Lv;
 #pragma unroll
   for (int j = 0; j < 4; ++j) f4set(Lv, j, log_sigmoidf(p.lam[d + j]));
-  // a_t, m_t per step (identity a = 1 on padded steps)
-  float av[kSteps][4], mv[kSteps][4];
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    const bool valid = t0 + tg * kSteps + s < T;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const Gate g = gate_from_ri(f4get(ra[s], j), f4get(ia[s], j), f4get(Lv, j), p.c);
-      av[s][j] = valid ? g.a : 1.f;
-      mv[s][j] = valid ? g.m : 0.f;
-    }
-  }
-  // local summary, backwards over this thread's steps: g -> A g + H
+  auto row_of = [&](int s) { return size_t(b) * T + (t0 + tg * kSteps + s); };
+  auto valid = [&](int s) { return t0 + tg * kSteps + s < T; };
+  // a_t of 4 channels from r_t (identity a = 1 on padded steps)
+  auto gate_a = [&](const float4& r, bool ok, int j) {
+    return ok ? gate_from_ri(f4get(r, j), 0.f, f4get(Lv, j), p.c).a : 1.f;
+  };
+
+  // pass 1: local summary, backwards over this thread's steps: g -> A g + H
   Acc A[4], H[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) { A[j] = Acc(1); H[j] = Acc(0); }
-#pragma unroll
-  for (int s = kSteps - 1; s >= 0; --s)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const Acc a = av[s][j];
-      H[j] = a * (Acc(f4get(dyv[s], j)) + H[j]);
-      A[j] = A[j] * a;
+  {
+    float4 rn = make_float4(0, 0, 0, 0), dn = rn;
+    if (valid(kSteps - 1)) {
+      rn = *reinterpret_cast<const float4*>(p.r + row_of(kSteps - 1) * D + d);
+      dn = Io<IO>::load4(dy + row_of(kSteps - 1) * D + d);
     }
+#pragma unroll 1
+    for (int s = kSteps - 1; s >= 0; --s) {
+      const float4 rc = rn, dc = dn;
+      const bool ok = valid(s);
+      if (s > 0 && valid(s - 1)) {
+        rn = *reinterpret_cast<const float4*>(p.r + row_of(s - 1) * D + d);
+        dn = Io<IO>::load4(dy + row_of(s - 1) * D + d);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const Acc a = gate_a(rc, ok, j);
+        H[j] = a * (Acc(f4get(dc, j)) + H[j]);
+        A[j] = A[j] * a;
+      }
+    }
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) { sA[tg][4 * cg + j] = A[j]; sH[tg][4 * cg + j] = H[j]; }
   __syncthreads();
@@ -346,6 +336,7 @@ __global__ __launch_bounds__(256) void scan_bwd_kernel(ScanBwdArgs p) {
   compose_groups<Acc>(sA, sH, 4 * cg, kTG - 1, tg, -1, Ap, Hp);
   __syncthreads();
 
+  // pass 2: the local gradients, backwards from the exact incoming g
   Acc g[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) g[j] = fmaA(Ap[j], sCarry[4 * cg + j], Hp[j]);
@@ -353,30 +344,61 @@ __global__ __launch_bounds__(256) void scan_bwd_kernel(ScanBwdArgs p) {
   const size_t ld2 = size_t(2) * D;
   const Acc cL[4] = {Acc(p.c) * Acc(f4get(Lv, 0)), Acc(p.c) * Acc(f4get(Lv, 1)),
                      Acc(p.c) * Acc(f4get(Lv, 2)), Acc(p.c) * Acc(f4get(Lv, 3))};
-#pragma unroll
-  for (int s = kSteps - 1; s >= 0; --s) {
+  struct StepIn {
+    float4 r, i, u, dy;
+    Acc hp[4];
+  };
+  auto load_step = [&](int s, StepIn& in) {
     const int t = t0 + tg * kSteps + s;
+    if (t < T) {
+      const size_t o = (size_t(b) * T + t) * D + d;
+      in.r = *reinterpret_cast<const float4*>(p.r + o);
+      in.i = *reinterpret_cast<const float4*>(p.i + o);
+      in.u = Io<IO>::load4(u + o);
+      in.dy = Io<IO>::load4(dy + o);
+      if (t > 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) in.hp[j] = h_all[o - D + j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) in.hp[j] = p.h0 ? Acc(p.h0[size_t(b) * D + d + j]) : Acc(0);
+      }
+    } else {
+      in.r = in.i = in.u = in.dy = make_float4(0, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) in.hp[j] = Acc(0);
+    }
+  };
+  StepIn cur, nxt;
+  load_step(kSteps - 1, nxt);
+#pragma unroll 1
+  for (int s = kSteps - 1; s >= 0; --s) {
+    cur = nxt;
+    if (s > 0) load_step(s - 1, nxt);
+    const int t = t0 + tg * kSteps + s;
+    const bool ok = t < T;
     float4 dza, dzi, dud;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const Acc a = av[s][j], m = mv[s][j];
-      const Acc r = f4get(ra[s], j), ii = f4get(ia[s], j), uv = f4get(uu[s], j);
-      const Acc G = Acc(f4get(dyv[s], j)) + g[j];
+      const Gate gt = gate_from_ri(f4get(cur.r, j), f4get(cur.i, j), f4get(Lv, j), p.c);
+      const Acc a = ok ? gt.a : 1.f, m = ok ? gt.m : 0.f;
+      const Acc r = f4get(cur.r, j), ii = f4get(cur.i, j), uv = f4get(cur.u, j);
+      const Acc G = Acc(f4get(cur.dy, j)) + g[j];
       const Acc mterm = m > Acc(0) ? ((a * a) / m) * ii * uv : Acc(0);
-      const Acc dl = G * (a * hp[s][j] - mterm);
+      const Acc dl = G * (a * cur.hp[j] - mterm);
       const Acc zr = cL[j] * dl * r * (Acc(1) - r);
       const Acc zi = (G * m * uv) * ii * (Acc(1) - ii);
       f4set(dza, j, float(zr));
       f4set(dzi, j, float(zi));
       f4set(dud, j, float(G * m * ii));
-      if (t < T) {
+      if (ok) {
         sdza[j] += double(zr);
         sdzi[j] += double(zi);
         sdl[j] += double(Acc(p.c) * r * dl);
       }
       g[j] = a * G;
     }
-    if (t < T) {
+    if (ok) {
       const size_t row = size_t(b) * T + t;
       *reinterpret_cast<float4*>(p.du + row * D + d) = dud;
       if (sizeof(IO) == 2) {
