@@ -87,10 +87,10 @@ size_t status_fill_words(int B, int T, int D, rglru_dtype io) {
 }
 
 // The gate projection for M rows: out0/out1 per the epilogue kind.
-int gate_projection(rglru_dtype io, GateGemmArgs g, int epi, bool small_m, float* zscratch_a,
+int gate_projection(rglru_dtype io, GateGemmArgs g, int epi, float* zscratch_a,
                     float* zscratch_x, hipStream_t s) {
   if (io == RGLRU_BF16) {
-    RG_CHECK(launch_gate_gemm_bf16(g, epi, small_m, s));
+    RG_CHECK(launch_gate_gemm_bf16(g, epi, s));
     return RGLRU_OK;
   }
   PlainGemmArgs pa{};
@@ -138,7 +138,7 @@ int lru_layer(rglru_dtype io, int B, int T, int D, float c, const void* u, const
   g.U = u; g.Wa = W_a; g.Wx = W_x; g.M = B * T; g.N = D; g.K = D;
   g.ba = b_a; g.bx = b_x; g.lam = lambda; g.c = c;
   g.out0 = w.a; g.out1 = w.beta;
-  int st = gate_projection(io, g, kEpiAB, false, w.a, w.beta, stream);
+  int st = gate_projection(io, g, kEpiAB, w.a, w.beta, stream);
   if (st != RGLRU_OK) return st;
   return forward_scan(io, B, T, D, u, nullptr, nullptr, nullptr, w.a, w.beta, h0, y, h_T,
                       w.status, w.counter, prefilled, stream);
@@ -309,7 +309,7 @@ int rglru_gates(int B, int T, int D, rglru_dtype io, float c, const void* u, con
   g.U = u; g.Wa = W_a; g.Wx = W_x; g.M = B * T; g.N = D; g.K = D;
   g.ba = b_a; g.bx = b_x; g.lam = lambda; g.c = c;
   g.out0 = a; g.out1 = beta;
-  return gate_projection(io, g, kEpiAB, false, a, beta, stream);
+  return gate_projection(io, g, kEpiAB, a, beta, stream);
 }
 
 size_t rglru_scan_workspace_bytes(int B, int T, int D, rglru_dtype io) {
@@ -388,7 +388,7 @@ int rglru_decode_step(int B, int D, rglru_dtype io, float c, const void* x_t, co
   g.U = u; g.Wa = W_a; g.Wx = W_x; g.M = B; g.N = D; g.K = D;
   g.ba = b_a; g.bx = b_x; g.lam = lambda; g.c = c;
   g.u = u; g.h = h; g.y = y_t;
-  return gate_projection(io, g, kEpiDecode, B <= 1024, za, zx, stream);
+  return gate_projection(io, g, kEpiDecode, za, zx, stream);
 }
 
 size_t rglru_bwd_workspace_bytes(int B, int T, int D, rglru_dtype io) {
@@ -437,7 +437,7 @@ int rglru_bwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const
   g.U = u; g.Wa = W_a; g.Wx = W_x; g.M = M; g.N = D; g.K = D;
   g.ba = b_a; g.bx = b_x; g.lam = lambda; g.c = c;
   g.out0 = w.r; g.out1 = w.i;
-  st = gate_projection(io, g, kEpiRI, false, w.r, w.i, stream);
+  st = gate_projection(io, g, kEpiRI, w.r, w.i, stream);
   if (st != RGLRU_OK) return st;
   ScanFwdArgs sf{};
   sf.B = B; sf.T = T; sf.D = D;

@@ -34,7 +34,7 @@ struct GemmParams {
   float c;
   float* out0;
   float* out1;
-  const bf16_t* u;
+  const bf16_t* u;   // fp32 decode (as raw bytes of the io type)
   float* h;
   bf16_t* y;
   // plain epilogue
@@ -119,17 +119,11 @@ __global__ __launch_bounds__(C::NW * 64, C::NW >= 8 ? 2 : 1) void gemm_bf16_kern
             gate_fast_ri(za, zx, k, r, i);
             p.out0[o] = r;
             p.out1[o] = i;
-          } else {
+          } else {  // kEpiAB
             float a, beta;
             gate_fast(za, zx, k, a, beta);
-            if (MODE == kEpiAB) {
-              p.out0[o] = a;
-              p.out1[o] = beta;
-            } else {  // kEpiDecode
-              const float hn = fmaf(a, p.h[o], beta * bf2f(p.u[o]));
-              p.h[o] = hn;
-              p.y[o] = f2bf(hn);
-            }
+            p.out0[o] = a;
+            p.out1[o] = beta;
           }
         }
     }
@@ -137,11 +131,9 @@ __global__ __launch_bounds__(C::NW * 64, C::NW >= 8 ? 2 : 1) void gemm_bf16_kern
 }
 
 // ---------------------------------------------------------------- launchers (bf16)
-// Large tiles: 256 x 256, 8 waves of 128 x 64, BK = 64, double-buffered.
+// 256 x 256 tiles, 8 waves of 128 x 64, BK = 64, double-buffered.
 typedef GemmCfg<256, 128, 2, 4, false, 64, 2> CfgGate;
 typedef GemmCfg<256, 128, 2, 4, true, 64, 2> CfgPlain;
-// Small-M tiles (decode): 64 x 64, 2 waves of 32 x 64.
-typedef GemmCfg<64, 32, 2, 1, false, 32, 4> CfgGateSmall;
 
 template <class C, int MODE, bool DUAL>
 static hipError_t run_bf16(const GemmParams& p, hipStream_t s) {
@@ -151,7 +143,7 @@ static hipError_t run_bf16(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gate_gemm_bf16(const GateGemmArgs& g, int epi, bool small_m, hipStream_t s) {
+hipError_t launch_gate_gemm_bf16(const GateGemmArgs& g, int epi, hipStream_t s) {
   GemmParams p{};
   p.A = static_cast<const bf16_t*>(g.U);
   p.B0 = static_cast<const bf16_t*>(g.Wa);
@@ -160,23 +152,11 @@ hipError_t launch_gate_gemm_bf16(const GateGemmArgs& g, int epi, bool small_m, h
   p.lda = g.K; p.ldb = g.K; p.ldc = g.N;
   p.ba = g.ba; p.bx = g.bx; p.lam = g.lam; p.c = g.c;
   p.out0 = g.out0; p.out1 = g.out1;
-  p.u = static_cast<const bf16_t*>(g.u);
-  p.h = g.h;
-  p.y = static_cast<bf16_t*>(g.y);
-  if (small_m) {
-    switch (epi) {
-      case kEpiAB: return run_bf16<CfgGateSmall, kEpiAB, false>(p, s);
-      case kEpiRI: return run_bf16<CfgGateSmall, kEpiRI, false>(p, s);
-      case kEpiDecode: return run_bf16<CfgGateSmall, kEpiDecode, false>(p, s);
-    }
-  } else {
-    switch (epi) {
-      case kEpiAB: return run_bf16<CfgGate, kEpiAB, false>(p, s);
-      case kEpiRI: return run_bf16<CfgGate, kEpiRI, false>(p, s);
-      case kEpiDecode: return run_bf16<CfgGate, kEpiDecode, false>(p, s);
-    }
+  switch (epi) {
+    case kEpiAB: return run_bf16<CfgGate, kEpiAB, false>(p, s);
+    case kEpiRI: return run_bf16<CfgGate, kEpiRI, false>(p, s);
   }
-  return hipErrorInvalidValue;
+  return hipErrorInvalidValue;   // the bf16 decode step has its own kernels (decode.hip)
 }
 
 hipError_t launch_plain_gemm_bf16(const PlainGemmArgs& g, hipStream_t s) {

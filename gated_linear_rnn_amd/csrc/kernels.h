@@ -25,7 +25,7 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 enum GateEpi : int {
   kEpiAB = 0,      // write a, beta = m i           (forward)
   kEpiRI = 1,      // write r, i                    (backward recompute)
-  kEpiDecode = 2,  // h <- a h + beta u, y = RNE(h) (decode step)
+  kEpiDecode = 2,  // h <- a h + beta u, y = RNE(h) (fp32 decode step)
 };
 
 struct GateGemmArgs {
@@ -76,7 +76,7 @@ struct PlainGemmArgs {
   const float* addend;   // may equal C (read before write by the same thread) or NULL
 };
 
-hipError_t launch_gate_gemm_bf16(const GateGemmArgs& g, int epi, bool small_m, hipStream_t s);
+hipError_t launch_gate_gemm_bf16(const GateGemmArgs& g, int epi, hipStream_t s);   // kEpiAB, kEpiRI
 hipError_t launch_plain_gemm_bf16(const PlainGemmArgs& g, hipStream_t s);
 hipError_t launch_plain_gemm_f32(const PlainGemmArgs& g, hipStream_t s);
 // fp32 I/O: gate math from pre-activations za, zx [M, N] (already W u, bias not added).
