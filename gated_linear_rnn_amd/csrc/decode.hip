@@ -9,7 +9,9 @@
 // matrix cores and writes the raw sums to a partial buffer.  A second kernel adds the S
 // partials of each (row, channel) in a fixed order (so the result does not depend on
 // scheduling), applies the gates of Eq. (1)-(3) with the biases, and updates the state in
-// place: h <- a h + sqrt(1 - a^2) (i u), y = RNE_bf16(h).
+// place: h <- a h + sqrt(1 - a^2) (i u), y = RNE_bf16(h).  The per-channel gate constants
+// (biases in the exp2 domain, c log2 sigma(Lambda)) are computed once per channel by the
+// first kernel rather than once per (row, channel) by the second.
 #include "gemm_core.h"
 #include "kernels.h"
 
@@ -36,7 +38,7 @@ int decode_splits(int B, int D) {
 }
 
 size_t decode_partial_bytes(int B, int D) {
-  return size_t(decode_splits(B, D)) * 2 * size_t(B) * D * sizeof(float);
+  return size_t(decode_splits(B, D)) * 2 * size_t(B) * D * sizeof(float) + 3 * size_t(D) * sizeof(float);
 }
 
 // partial[s][0][m][ch] = sum over k in split s of u[m,k] W_a[ch,k]; partial[s][1] for W_x
@@ -58,6 +60,13 @@ __global__ __launch_bounds__(CfgDecode::NW * 64, 2) void decode_partial_kernel(D
   const int tn = L / (MT * S);
   const int kc = D / S;                            // K columns per split (a multiple of 64)
   const int m0 = tm * C::BM, n0 = tn * C::BC;
+  if (tm == 0 && s == 0 && int(threadIdx.x) < C::BC && n0 + int(threadIdx.x) < D) {
+    const int ch = n0 + threadIdx.x;
+    const GateChan k = gate_chan(p.ba[ch], p.bx[ch], p.lam[ch], p.c);
+    p.chan[ch] = k.nba;
+    p.chan[D + ch] = k.nbx;
+    p.chan[2 * D + ch] = k.cl2;
+  }
 
   TileOperands op;
   op.A = static_cast<const bf16_t*>(p.u) + size_t(s) * kc;
@@ -114,13 +123,16 @@ __global__ __launch_bounds__(256) void decode_update_kernel(DecodeArgs p) {
     if (s < S) { add(za, va[s]); add(zx, vx[s]); }
   const float4 h = *reinterpret_cast<const float4*>(p.h + o);
   const float4 u = Io<bf16_t>::load4(static_cast<const bf16_t*>(p.u) + o);
-  const float4 ba = *reinterpret_cast<const float4*>(p.ba + ch0);
-  const float4 bx = *reinterpret_cast<const float4*>(p.bx + ch0);
-  const float4 lam = *reinterpret_cast<const float4*>(p.lam + ch0);
+  const float4 nba = *reinterpret_cast<const float4*>(p.chan + ch0);
+  const float4 nbx = *reinterpret_cast<const float4*>(p.chan + D + ch0);
+  const float4 cl2 = *reinterpret_cast<const float4*>(p.chan + 2 * D + ch0);
   float4 hn;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const GateChan k = gate_chan(f4get(ba, j), f4get(bx, j), f4get(lam, j), p.c);
+    GateChan k;
+    k.nba = f4get(nba, j);
+    k.nbx = f4get(nbx, j);
+    k.cl2 = f4get(cl2, j);
     float a, beta;
     gate_fast(f4get(za, j), f4get(zx, j), k, a, beta);
     f4set(hn, j, fmaf(a, f4get(h, j), beta * f4get(u, j)));
@@ -132,6 +144,7 @@ __global__ __launch_bounds__(256) void decode_update_kernel(DecodeArgs p) {
 hipError_t launch_decode_bf16(const DecodeArgs& a_in, hipStream_t s) {
   DecodeArgs a = a_in;
   a.splits = decode_splits(a.B, a.D);
+  a.chan = a.partial + size_t(a.splits) * 2 * size_t(a.B) * a.D;
   const int MT = (a.B + CfgDecode::BM - 1) / CfgDecode::BM;
   const int NT = (a.D + CfgDecode::BC - 1) / CfgDecode::BC;
   decode_partial_kernel<<<MT * NT * a.splits, CfgDecode::NW * 64, 0, s>>>(a);

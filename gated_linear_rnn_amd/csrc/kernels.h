@@ -56,9 +56,10 @@ struct DecodeArgs {
   float c;
   float* h;           // [B, D] state, in/out
   void* y;            // [B, D] bf16
-  float* partial;     // decode_partial_bytes(B, D)
+  float* partial;     // decode_partial_bytes(B, D): the split sums, then 3 D gate constants
   int B, D;
   int splits;         // set by the launcher
+  float* chan;        // set by the launcher: [3, D] per-channel gate constants
 };
 int decode_splits(int B, int D);
 size_t decode_partial_bytes(int B, int D);
