@@ -127,3 +127,38 @@ def test_bf16_rounding_of_halfway_sums_is_exact(lib):
     # and the ties really occur (half of the odd-step sums sit exactly between neighbours)
     s = x[0, 1:] + x[0, :-1]
     assert np.sum(oracle.round_io(s, "bf16") != s) > 100
+
+
+def test_maximum_size_matches_geometric_closed_form(lib):
+    """The largest shape the ABI accepts (B T D just under 2^31 elements, T ragged: 4096 tiles
+    of 256 steps with 255 in the last) on the fused bf16 path.  With W_a = W_x = 0, an
+    identity conv and x constant over time, r, i and a are constant per channel and Eq. (4)
+    has the closed form h_t = (1 - a^t) / (1 - a) m i x (h0 = 0, t steps done), checked at
+    sampled steps and for h_T."""
+    B, T, D = 8, 1048575, 256
+    assert B * T * D < 2 ** 31
+    rng = np.random.default_rng(11)
+    xi = torch.from_numpy(rng.standard_normal(D).astype(np.float32)).to(torch.bfloat16)
+    b_a = rng.normal(0.0, 0.5, D).astype(np.float32)
+    b_x = rng.normal(0.0, 0.5, D).astype(np.float32)
+    U = rng.uniform(0.9, 0.999, D)
+    c = 8.0
+    lam = np.log(U ** (1 / c) / (1 - U ** (1 / c))).astype(np.float32)
+    x = xi.cuda()[None, None, :].expand(B, T, D).contiguous()
+    conv_w = torch.zeros((4, D), dtype=torch.bfloat16, device="cuda")
+    conv_w[0] = 1.0
+    Wz = torch.zeros((D, D), dtype=torch.bfloat16, device="cuda")
+    y, hT, _ = lib.forward(x, conv_w, None, None, Wz, Wz, dev(b_a), dev(b_x), dev(lam), None, c)
+    torch.cuda.synchronize()
+    del x
+    _, i, _, a, m = oracle.gates(b_a.astype(np.float64), b_x.astype(np.float64),
+                                 lam.astype(np.float64), c)
+    xv = xi.float().numpy().astype(np.float64)
+    steady = m * i * xv / (1.0 - a)
+    ts = np.array([0, 1, 2, 255, 256, 257, 4095, T // 2, T - 256, T - 255, T - 2, T - 1])
+    want = (1.0 - a[None, :] ** (ts[:, None] + 1.0)) * steady[None, :]      # [len(ts), D]
+    got = host(y[:, torch.from_numpy(ts).cuda(), :])                          # [B, len(ts), D]
+    e_y = err(got, np.broadcast_to(want, got.shape))
+    e_h = err(host(hT), np.broadcast_to(want[-1], (B, D)))
+    print(f"max size B={B} T={T} D={D}: err(y)={e_y:.3e} err(h_T)={e_h:.3e}", flush=True)
+    assert e_y <= TOL["bf16"] and e_h <= TOL["bf16"]
