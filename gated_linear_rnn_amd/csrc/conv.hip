@@ -159,6 +159,26 @@ template hipError_t launch_conv_decode<float>(int, int, const void*, const void*
 template hipError_t launch_conv_decode<bf16_t>(int, int, const void*, const void*, const float*,
                                                void*, void*, hipStream_t);
 
+// Look-back status words to all ones (empty) and ncounters ticket counters to zero, in one
+// launch.
+__global__ __launch_bounds__(256) void fill_status_kernel(uint32_t* __restrict__ status, size_t n,
+                                                          uint32_t* __restrict__ counters,
+                                                          int ncounters) {
+  size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < size_t(ncounters)) counters[i] = 0u;
+  const size_t stride = size_t(gridDim.x) * blockDim.x;
+  for (; i < n; i += stride) status[i] = 0xffffffffu;
+}
+
+hipError_t launch_fill_status(uint32_t* status, size_t words, uint32_t* counters, int ncounters,
+                              hipStream_t s) {
+  size_t blocks = (words + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks == 0) blocks = 1;
+  fill_status_kernel<<<int(blocks), 256, 0, s>>>(status, words, counters, ncounters);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s) {
   if (n == 0) return hipSuccess;
   size_t blocks = (n + 255) / 256;

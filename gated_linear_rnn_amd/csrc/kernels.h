@@ -19,6 +19,9 @@ template <typename IO>
 hipError_t launch_conv_decode(int B, int D, const void* x, const void* w, const float* cb,
                               void* hist, void* u, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
+// status[0..words) = all ones, counters[0..ncounters) = 0 (ncounters <= 256), one launch
+hipError_t launch_fill_status(uint32_t* status, size_t words, uint32_t* counters, int ncounters,
+                              hipStream_t s);
 
 // ---------------------------------------------------------------- gemm.hip
 // Epilogue kinds of the gate projection z = U [W_a; W_x]^T (Eq. (1)-(2)).

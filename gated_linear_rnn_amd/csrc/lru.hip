@@ -221,9 +221,7 @@ hipError_t launch_lru_fused(const LruArgs& a_in, bool prefilled, hipStream_t s) 
   const int chains = a.B * NT;
   a.groups = lru_groups(chains);
   if (!prefilled) {
-    hipError_t e = launch_fill_u32(a.status, lru_status_bytes(a.B, a.T, a.D) / 4, 0xffffffffu, s);
-    if (e != hipSuccess) return e;
-    e = launch_fill_u32(a.counters, 64, 0u, s);
+    const hipError_t e = launch_fill_status(a.status, lru_status_bytes(a.B, a.T, a.D) / 4, a.counters, 64, s);
     if (e != hipSuccess) return e;
   }
   const int tiles = chains * lru_chunks(a.T);

@@ -215,10 +215,8 @@ __global__ __launch_bounds__(256) void scan_fwd_kernel(ScanFwdArgs p) {
 template <typename IO, typename Acc>
 hipError_t launch_scan_fwd(const ScanFwdArgs& a, hipStream_t s) {
   if (!a.prefilled) {
-    hipError_t e = launch_fill_u32(static_cast<uint32_t*>(a.status),
-                                   scan_status_bytes(a.B, a.T, a.D, sizeof(Acc)) / 4, 0xffffffffu, s);
-    if (e != hipSuccess) return e;
-    e = launch_fill_u32(a.counter, 1, 0u, s);
+    const hipError_t e = launch_fill_status(static_cast<uint32_t*>(a.status),
+                                            scan_status_bytes(a.B, a.T, a.D, sizeof(Acc)) / 4, a.counter, 1, s);
     if (e != hipSuccess) return e;
   }
   const int tiles = scan_chunks(a.T) * a.B * (a.D / kCh);
@@ -442,10 +440,8 @@ __global__ __launch_bounds__(256) void scan_bwd_kernel(ScanBwdArgs p) {
 
 template <typename IO, typename Acc>
 hipError_t launch_scan_bwd(const ScanBwdArgs& a, hipStream_t s) {
-  hipError_t e = launch_fill_u32(static_cast<uint32_t*>(a.status),
-                                 scan_status_bytes(a.B, a.T, a.D, sizeof(Acc)) / 4, 0xffffffffu, s);
-  if (e != hipSuccess) return e;
-  e = launch_fill_u32(a.counter, 1, 0u, s);
+  const hipError_t e = launch_fill_status(static_cast<uint32_t*>(a.status),
+                                          scan_status_bytes(a.B, a.T, a.D, sizeof(Acc)) / 4, a.counter, 1, s);
   if (e != hipSuccess) return e;
   const int tiles = scan_chunks(a.T) * a.B * (a.D / kCh);
   scan_bwd_kernel<IO, Acc><<<tiles, 256, 0, s>>>(a);
