@@ -162,3 +162,41 @@ def test_maximum_size_matches_geometric_closed_form(lib):
     e_h = err(host(hT), np.broadcast_to(want[-1], (B, D)))
     print(f"max size B={B} T={T} D={D}: err(y)={e_y:.3e} err(h_T)={e_h:.3e}", flush=True)
     assert e_y <= TOL["bf16"] and e_h <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_forward_graph_replays_match_eager(lib, io):
+    """rglru_fwd captured in a hipGraph (its look-back status is initialised by kernels, not
+    memset nodes), replayed several times with eager work and synchronisations in between;
+    every replay equals the eager result bit for bit."""
+    w = workloads.TRAIN_FWD.with_shape(B=2, T=700, D=320, io=io, h0="normal", history="normal")
+    p = workloads.make_inputs(w)
+    d = device_inputs(p)
+    B, T, D = w.B, w.T, w.D
+    y = torch.empty((B, T, D), dtype=TORCH_IO[io], device="cuda")
+    hT = torch.empty((B, D), device="cuda")
+    cso = torch.empty((B, 3, D), dtype=TORCH_IO[io], device="cuda")
+    ws = lib.workspace(lib.fwd_workspace_bytes(B, T, D, TORCH_IO[io]))
+
+    def run():
+        lib.rglru_fwd(d["x"], d["conv_w"], d["conv_b"], d["conv_state"], d["W_a"], d["W_x"],
+                      d["b_a"], d["b_x"], d["lam"], d["h0"], y, hT, cso, ws, p["c"])
+
+    run()
+    torch.cuda.synchronize()
+    ref = (y.clone(), hT.clone(), cso.clone())
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            run()
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        y.zero_()
+        hT.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref[0]) and torch.equal(hT, ref[1]) and torch.equal(cso, ref[2]), rep
+        _ = (d["x"].float() * 3).sum().item()       # unrelated eager work between replays
