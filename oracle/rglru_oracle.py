@@ -39,12 +39,21 @@ Readings where the pages leave a step open (each also listed in the design notes
     treated as identity; where m_t = sqrt(1 - a_t^2) = 0 the m-path term of d(log a_t)
     is defined as 0.
 
+The recurrent block around the branch ([ARCH] "Recurrent block", Fig. 2(c)): two linear
+layers D -> D_RNN in parallel, Conv1D + RG-LRU on the first branch, GeLU on the second,
+elementwise product, linear D_RNN -> D.  Readings: the linears have no bias (the pages
+give none); GeLU is the exact form q Phi(q); rounding points of the I/O dtype are the
+branch input p = RNE(x W_in1^T), g = RNE(GeLU(x W_in2^T)), the product z = RNE(h_t g_t)
+of the unrounded RG-LRU state and g, and the block output RNE(z W_out^T).
+
 Parity pins: every function here is pinned by a test against closed forms, invariants,
-brute force or library routines (tests/test_oracle_pins.py, tests/test_oracle_grad.py).
+brute force or library routines (tests/test_oracle_pins.py, tests/test_oracle_grad.py,
+tests/test_oracle_block.py).
 """
 from __future__ import annotations
 
 import numpy as np
+from scipy.special import erf as _erf
 
 _BF16_MAX = 3.3895313892515355e38   # largest finite bf16
 _BF16_MIN_ULP_EXP = -133            # exponent of the smallest bf16 subnormal
@@ -305,3 +314,38 @@ def backward(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, c, i
         dx[:, :T - k, :] += w[k] * du[:, k:, :]
     out.update(dx=dx, dconv_w=dconv_w, dconv_b=du.sum(axis=(0, 1)))
     return out
+
+
+# ----------------------------------------------------------------------------------
+# The recurrent block around the branch ([ARCH] "Recurrent block", Fig. 2(c))
+# ----------------------------------------------------------------------------------
+def gelu(q) -> np.ndarray:
+    """GeLU of the block's second branch, exact form: q Phi(q) = q (1 + erf(q / sqrt 2)) / 2."""
+    q = np.asarray(q, dtype=np.float64)
+    return 0.5 * q * (1.0 + _erf(q / np.sqrt(2.0)))
+
+
+def block_forward(x, W_in, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, W_out,
+                  c, io, keep=False):
+    """The recurrent block: out = W_out (RG-LRU(conv(W_in1 x)) * GeLU(W_in2 x)).
+
+    x [B,T,D]; W_in [2R, D] ([out, in]: rows 0..R-1 the recurrence branch, rows R..2R-1
+    the GeLU branch); conv and RG-LRU arguments as in forward() with width R; W_out [D, R].
+    Rounding points (I/O dtype, nearest even): p = RNE(x W_in1^T), g = RNE(GeLU(x W_in2^T)),
+    z = RNE(h_t * g_t) with h_t the unrounded RG-LRU state, out = RNE(z W_out^T).
+    Returns dict with out [B,T,D], h_T [B,R], conv_state_out [B,3,R]; with keep=True also
+    p, g, z.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    W_in = np.asarray(W_in, dtype=np.float64)
+    R = W_in.shape[0] // 2
+    pq = x @ W_in.T                                        # the two input linears
+    p = round_io(pq[..., :R], io)
+    g = round_io(gelu(pq[..., R:]), io)
+    f = forward(p, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, c, io, keep=True)
+    z = round_io(f["y_exact"] * g, io)
+    out = round_io(z @ np.asarray(W_out, dtype=np.float64).T, io)
+    res = {"out": out, "h_T": f["h_T"], "conv_state_out": f["conv_state_out"]}
+    if keep:
+        res.update(p=p, g=g, z=z)
+    return res
