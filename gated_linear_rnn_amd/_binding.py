@@ -22,7 +22,7 @@ EXPORTS = ("rglru_status_string", "conv1d_causal4", "rglru_fwd_workspace_bytes",
            "rglru_lru_workspace_bytes", "rglru_lru", "rglru_gates", "rglru_scan_workspace_bytes",
            "rglru_scan",
            "rglru_decode_workspace_bytes", "rglru_decode_step", "rglru_bwd_workspace_bytes",
-           "rglru_bwd")
+           "rglru_bwd", "rglru_block_fwd_workspace_bytes", "rglru_block_fwd")
 
 _lib = None
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -66,6 +66,10 @@ def load(path: str = LIB_PATH):
     lib.rglru_bwd_workspace_bytes.restype = _Z
     lib.rglru_bwd.argtypes = [_I, _I, _I, _I, _F] + [_P] * 21 + [_P, _Z, _P]
     lib.rglru_bwd.restype = _I
+    lib.rglru_block_fwd_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+    lib.rglru_block_fwd_workspace_bytes.restype = _Z
+    lib.rglru_block_fwd.argtypes = [_I, _I, _I, _I, _I, _F] + [_P] * 15 + [_P, _Z, _P]
+    lib.rglru_block_fwd.restype = _I
     _lib = lib
     return lib
 
@@ -114,6 +118,10 @@ def decode_workspace_bytes(B, D, dtype) -> int:
 
 def bwd_workspace_bytes(B, T, D, dtype) -> int:
     return int(load().rglru_bwd_workspace_bytes(B, T, D, io_code(dtype)))
+
+
+def block_fwd_workspace_bytes(B, T, D, R, dtype) -> int:
+    return int(load().rglru_block_fwd_workspace_bytes(B, T, D, R, io_code(dtype)))
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
@@ -184,6 +192,18 @@ def rglru_bwd(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, dy,
            "rglru_bwd")
 
 
+def rglru_block_fwd(x, W_in, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, W_out,
+                    out, h_T, conv_state_out, ws, c=8.0, stream=None):
+    B, T, D = x.shape
+    R = W_in.shape[0] // 2
+    _check(load().rglru_block_fwd(B, T, D, R, io_code(x.dtype), float(c), _ptr(x), _ptr(W_in),
+                                  _ptr(conv_w), _ptr(conv_b), _ptr(conv_state_in), _ptr(W_a),
+                                  _ptr(W_x), _ptr(b_a), _ptr(b_x), _ptr(lam), _ptr(h0),
+                                  _ptr(W_out), _ptr(out), _ptr(h_T), _ptr(conv_state_out),
+                                  _ptr(ws), ws.numel(), _stream(stream)),
+           "rglru_block_fwd")
+
+
 # ------------------------------------------------------------------ allocating helpers
 def forward(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0=None, c=8.0,
             ws=None, stream=None):
@@ -217,3 +237,18 @@ def backward(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, dy, 
               g["dconv_w"], g["dconv_b"], g["dW_a"], g["dW_x"], g["db_a"], g["db_x"],
               g["dlambda"], g["dh0"], ws, c, stream)
     return g
+
+
+def block_forward(x, W_in, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, W_out,
+                  c=8.0, ws=None, stream=None):
+    """Allocate out, h_T, conv_state_out (and the workspace unless given), run rglru_block_fwd."""
+    B, T, D = x.shape
+    R = W_in.shape[0] // 2
+    out = torch.empty_like(x)
+    h_T = torch.empty((B, R), dtype=torch.float32, device=x.device)
+    cs_out = torch.empty((B, 3, R), dtype=x.dtype, device=x.device) if conv_w is not None else None
+    if ws is None:
+        ws = workspace(block_fwd_workspace_bytes(B, T, D, R, x.dtype), x.device)
+    rglru_block_fwd(x, W_in, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, W_out,
+                    out, h_T, cs_out, ws, c, stream)
+    return out, h_T, cs_out

@@ -197,6 +197,38 @@ BwdWs carve_bwd(Carver& cv, int B, int T, int D, rglru_dtype io) {
   return w;
 }
 
+// ------------------------------------------------------------------ recurrent block
+// bf16 I/O: p, g, u, then the fused RG-LRU layer's scratch; z goes over p (or u).
+// fp32 I/O: the [M, 2R] input product, p, g, u, y (later z in place), the layer's scratch.
+struct BlockWs {
+  float* pq;
+  void* p;
+  void* g;
+  void* y;
+  FwdWs lru;
+};
+
+BlockWs carve_block(Carver& cv, int B, int T, int R, rglru_dtype io) {
+  const size_t n = size_t(B) * T * R;
+  BlockWs w;
+  w.pq = io == RGLRU_F32 ? cv.take<float>(2 * n) : nullptr;
+  w.p = cv.take<unsigned char>(n * io_bytes(io));
+  w.g = cv.take<unsigned char>(n * io_bytes(io));
+  w.y = io == RGLRU_F32 ? cv.take<unsigned char>(n * io_bytes(io)) : nullptr;
+  w.lru.u = cv.take<unsigned char>(n * io_bytes(io));
+  carve_lru(cv, w.lru, B, T, R, io);
+  return w;
+}
+
+int block_shape_status(int B, int T, int D, int R) {
+  if (B <= 0 || T <= 0 || D <= 0 || R <= 0) return RGLRU_EINVAL;
+  if (D % 64 != 0 || R % 64 != 0) return RGLRU_ESHAPE;
+  const int64_t M = int64_t(B) * T;
+  if (M * D >= (int64_t(1) << 31) || M * R >= (int64_t(1) << 31)) return RGLRU_ESHAPE;
+  if (int64_t(2) * R * D >= (int64_t(1) << 31)) return RGLRU_ESHAPE;
+  return RGLRU_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -520,6 +552,96 @@ int rglru_bwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const
   ra.db_a = db_a; ra.db_x = db_x; ra.dlambda = dlambda;
   ra.dconv_w = dconv_w; ra.dconv_b = dconv_b;
   RG_CHECK(launch_reduce(ra, stream));
+  return RGLRU_OK;
+}
+
+size_t rglru_block_fwd_workspace_bytes(int B, int T, int D, int R, rglru_dtype io) {
+  if (block_shape_status(B, T, D, R) != RGLRU_OK || !io_ok(io)) return 0;
+  Carver cv(nullptr);
+  carve_block(cv, B, T, R, io);
+  return cv.used;
+}
+
+int rglru_block_fwd(int B, int T, int D, int R, rglru_dtype io, float c, const void* x,
+                    const void* W_in, const void* conv_w, const float* conv_b,
+                    const void* conv_state_in, const void* W_a, const void* W_x,
+                    const float* b_a, const float* b_x, const float* lambda, const float* h0,
+                    const void* W_out, void* out, float* h_T, void* conv_state_out, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
+  int st = block_shape_status(B, T, D, R);
+  if (st != RGLRU_OK) return st;
+  if (!io_ok(io)) return RGLRU_EDTYPE;
+  if (!x || !W_in || !W_a || !W_x || !b_a || !b_x || !lambda || !W_out || !out || !c_ok(c))
+    return RGLRU_EINVAL;
+  for (const void* p : {x, W_in, conv_w, (const void*)conv_b, conv_state_in, W_a, W_x,
+                        (const void*)b_a, (const void*)b_x, (const void*)lambda, (const void*)h0,
+                        W_out, (const void*)out, (const void*)h_T, (const void*)conv_state_out,
+                        (const void*)ws})
+    if (p && !aligned16(p)) return RGLRU_EINVAL;
+  if (!ws || ws_bytes < rglru_block_fwd_workspace_bytes(B, T, D, R, io)) return RGLRU_EWORKSPACE;
+
+  Carver cv(ws);
+  BlockWs w = carve_block(cv, B, T, R, io);
+  const int M = B * T;
+  const bool bf = io == RGLRU_BF16;
+
+  // 1. the two input linears: p and g = GeLU(.)
+  if (bf) {
+    BlockGemmArgs gi{};
+    gi.A = x; gi.Bm = W_in; gi.M = M; gi.N = 2 * R; gi.K = D; gi.ldc = R;
+    gi.C = w.p; gi.G = w.g; gi.split = R;
+    RG_CHECK(launch_block_gemm_bf16(gi, stream));
+  } else {
+    PlainGemmArgs pa{};
+    pa.A = x; pa.Bm = W_in; pa.M = M; pa.N = 2 * R; pa.K = D;
+    pa.lda = D; pa.ldb = D; pa.ldc = 2 * R; pa.C = w.pq;
+    RG_CHECK(launch_plain_gemm_f32(pa, stream));
+    RG_CHECK(launch_split_gelu_f32(w.pq, M, R, static_cast<float*>(w.p), static_cast<float*>(w.g), stream));
+  }
+
+  // 2. the temporal branch on p (the conv launch also initialises the look-back status)
+  const void* u = w.p;
+  bool prefilled = false;
+  if (conv_w) {
+    uint32_t* fill = static_cast<uint32_t*>(w.lru.status);
+    const size_t words = status_fill_words(B, T, R, io);
+    if (bf)
+      RG_CHECK(launch_conv_fwd<bf16_t>(B, T, R, w.p, conv_w, conv_b, conv_state_in, w.lru.u,
+                                       conv_state_out, stream, fill, words, w.lru.counter));
+    else
+      RG_CHECK(launch_conv_fwd<float>(B, T, R, w.p, conv_w, conv_b, conv_state_in, w.lru.u,
+                                      conv_state_out, stream, fill, words, w.lru.counter));
+    u = w.lru.u;
+    prefilled = true;
+  }
+  if (bf) {
+    // the fused layer multiplies by g before rounding: z = RNE(h g).  z goes over p once
+    // the conv has consumed it; without the conv p is the layer's input, whose rows every
+    // channel tile reads, so z goes to the (then unused) u buffer.
+    w.y = conv_w ? w.p : w.lru.u;
+    LruArgs la{};
+    la.u = u; la.Wa = W_a; la.Wx = W_x; la.ba = b_a; la.bx = b_x; la.lam = lambda; la.c = c;
+    la.h0 = h0; la.y = w.y; la.hT = h_T; la.gate = w.g; la.B = B; la.T = T; la.D = R;
+    la.status = static_cast<uint32_t*>(w.lru.status); la.counters = w.lru.counter;
+    RG_CHECK(launch_lru_fused(la, prefilled, stream));
+  } else {
+    st = lru_layer(io, B, T, R, c, u, W_a, W_x, b_a, b_x, lambda, h0, w.y, h_T, w.lru, prefilled, stream);
+    if (st != RGLRU_OK) return st;
+    RG_CHECK(launch_mul_f32(static_cast<float*>(w.y), static_cast<const float*>(w.g), size_t(M) * R, stream));
+  }
+
+  // 3. the output linear on z
+  if (bf) {
+    BlockGemmArgs go{};
+    go.A = w.y; go.Bm = W_out; go.M = M; go.N = D; go.K = R; go.ldc = D;
+    go.C = out; go.G = nullptr; go.split = 0;
+    RG_CHECK(launch_block_gemm_bf16(go, stream));
+  } else {
+    PlainGemmArgs po{};
+    po.A = w.y; po.Bm = W_out; po.M = M; po.N = D; po.K = R;
+    po.lda = R; po.ldb = R; po.ldc = D; po.C = static_cast<float*>(out);
+    RG_CHECK(launch_plain_gemm_f32(po, stream));
+  }
   return RGLRU_OK;
 }
 

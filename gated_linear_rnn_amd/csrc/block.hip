@@ -1,0 +1,48 @@
+// Elementwise steps of the recurrent block for fp32 I/O (Griffin model-architecture page,
+// section "Recurrent block", Fig. 2(c)): the two input linears arrive as one [M, 2R]
+// product; its first R columns are the branch input p, GeLU of the other R columns is the
+// multiplier g; after the temporal branch, z = y g feeds the output linear.  The bf16 path
+// fuses both steps into the matrix-core kernels (the input-linear GEMM epilogue and the
+// fused RG-LRU kernel), so these only serve the fp32 reference-precision path.
+#include "kernels.h"
+#include "rglru_device.h"
+
+namespace rglru {
+
+// p[m, r] = pq[m, r], g[m, r] = RNE_f32(GeLU(pq[m, R + r])) with GeLU evaluated in fp64.
+__global__ __launch_bounds__(256) void split_gelu_f32_kernel(const float* __restrict__ pq, int M,
+                                                             int R, float* __restrict__ p,
+                                                             float* __restrict__ g) {
+  const size_t n = size_t(M) * R;
+  for (size_t o = size_t(blockIdx.x) * blockDim.x + threadIdx.x; o < n;
+       o += size_t(gridDim.x) * blockDim.x) {
+    const size_t m = o / R, r = o - m * R;
+    p[o] = pq[m * 2 * R + r];
+    g[o] = float(gelu_d(double(pq[m * 2 * R + R + r])));
+  }
+}
+
+// y[i] = RNE_f32(y[i] * g[i])
+__global__ __launch_bounds__(256) void mul_f32_kernel(float* __restrict__ y,
+                                                      const float* __restrict__ g, size_t n) {
+  for (size_t o = size_t(blockIdx.x) * blockDim.x + threadIdx.x; o < n;
+       o += size_t(gridDim.x) * blockDim.x)
+    y[o] = y[o] * g[o];
+}
+
+static int grid_for(size_t n) {
+  const size_t blocks = (n + 255) / 256;
+  return int(blocks > 8192 ? 8192 : blocks);
+}
+
+hipError_t launch_split_gelu_f32(const float* pq, int M, int R, float* p, float* g, hipStream_t s) {
+  split_gelu_f32_kernel<<<grid_for(size_t(M) * R), 256, 0, s>>>(pq, M, R, p, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_mul_f32(float* y, const float* g, size_t n, hipStream_t s) {
+  mul_f32_kernel<<<grid_for(n), 256, 0, s>>>(y, g, n);
+  return hipGetLastError();
+}
+
+}  // namespace rglru

@@ -18,7 +18,10 @@
 
 namespace rglru {
 
-enum : int { kModePlain = 3 };
+// kModePlain: fp32 C (+ addend).  kModeInProj: the two input linears of the recurrent
+// block, N = 2R columns; columns [0, R) are written to C16 as bf16 (the branch input p),
+// columns [R, 2R) go through GeLU and to G16 as bf16.  kModeOut: bf16 C16.
+enum : int { kModePlain = 3, kModeInProj = 4, kModeOut = 5 };
 
 struct GemmParams {
   const bf16_t* A;
@@ -40,6 +43,9 @@ struct GemmParams {
   // plain epilogue
   float* C;
   const float* addend;
+  bf16_t* C16;        // kModeInProj (p), kModeOut
+  bf16_t* G16;        // kModeInProj (GeLU branch)
+  int split;          // kModeInProj: R
 };
 
 // Map the linear workgroup id to a (tile_m, tile_n) pair.  Consecutive workgroup ids are
@@ -65,11 +71,12 @@ __global__ __launch_bounds__(C::NW * 64, C::NW >= 8 ? 2 : 1) void gemm_bf16_kern
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int MT = (p.M + C::BM - 1) / C::BM;
-  const int NT = MODE == kModePlain ? (p.N + C::BNR - 1) / C::BNR : (p.N + C::BC - 1) / C::BC;
+  constexpr bool kPlainTile = MODE >= kModePlain;
+  const int NT = kPlainTile ? (p.N + C::BNR - 1) / C::BNR : (p.N + C::BC - 1) / C::BC;
   int tm, tn;
   tile_coords(MT, NT, tm, tn);
   const int m0 = tm * C::BM;
-  const int n0 = tn * (MODE == kModePlain ? C::BNR : C::BC);
+  const int n0 = tn * (kPlainTile ? C::BNR : C::BC);
 
   TileOperands op;
   op.A = p.A; op.A2 = p.A2; op.B0 = p.B0; op.B1 = p.B1;
@@ -98,6 +105,42 @@ __global__ __launch_bounds__(C::NW * 64, C::NW >= 8 ? 2 : 1) void gemm_bf16_kern
             p.C[o] = val;
           }
         }
+    }
+  } else if (MODE == kModeInProj || MODE == kModeOut) {
+    // bf16 output through LDS: each wave rounds its 128 x 64 block into its own 16 KB of
+    // the (now idle) operand ring, then writes whole 128-byte row segments, 16 bytes per
+    // lane.  In LDS a block row is 8 chunks of 16 bytes; rows r and r + 4 (the two lane
+    // halves of one accumulator write) sit 64 bytes apart in the bank space (chunk XOR 4)
+    // so the 2-byte writes of the two halves use disjoint banks.
+    static_assert(C::WTNR == 64 && C::NW * C::WTM * C::WTNR * 2 <= C::LDS_BYTES, "staging");
+    __syncthreads();   // every wave is done reading the last operand stage
+    bf16_t* st = reinterpret_cast<bf16_t*>(lds) + wave * (C::WTM * C::WTNR);
+    const int nb = n0 + wn * C::WTNR;   // first column of the wave's block
+    // the split is a multiple of 64 and so is nb: a block lies on one side of it
+    const bool gelu_side = MODE == kModeInProj && nb >= p.split;
+#pragma unroll
+    for (int mf = 0; mf < C::MF; ++mf)
+#pragma unroll
+      for (int f = 0; f < C::NF; ++f)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = mf * 32 + acc_row(v, lane);
+          const int chunk = (f * 4 + (col >> 3)) ^ (((r >> 2) & 1) << 2);
+          const float val = acc[mf][f][v];
+          st[r * 64 + chunk * 8 + (col & 7)] = f2bf(gelu_side ? gelu_f(val) : val);
+        }
+    // LDS operations of a wave complete in order; the fence keeps the compiler from
+    // moving the reads below above the writes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    bf16_t* const dst0 = gelu_side ? p.G16 - p.split : p.C16;
+#pragma unroll
+    for (int it = 0; it < C::WTM / 8; ++it) {
+      const int r = it * 8 + (lane >> 3), ck = lane & 7;
+      const int m = m0 + wm * C::WTM + r, n = nb + ck * 8;
+      const uint4 val = *reinterpret_cast<const uint4*>(st + r * 64 + ((ck ^ (((r >> 2) & 1) << 2)) * 8));
+      if (m < p.M && n < p.N) *reinterpret_cast<uint4*>(dst0 + size_t(m) * p.ldc + n) = val;
     }
   } else {
     constexpr int HALF = C::NF / 2;
@@ -138,7 +181,7 @@ typedef GemmCfg<256, 128, 2, 4, true, 64, 2> CfgPlain;
 template <class C, int MODE, bool DUAL>
 static hipError_t run_bf16(const GemmParams& p, hipStream_t s) {
   const int MT = (p.M + C::BM - 1) / C::BM;
-  const int NT = MODE == kModePlain ? (p.N + C::BNR - 1) / C::BNR : (p.N + C::BC - 1) / C::BC;
+  const int NT = MODE >= kModePlain ? (p.N + C::BNR - 1) / C::BNR : (p.N + C::BC - 1) / C::BC;
   gemm_bf16_kernel<C, MODE, DUAL><<<MT * NT, C::NW * 64, 0, s>>>(p);
   return hipGetLastError();
 }
@@ -169,6 +212,19 @@ hipError_t launch_plain_gemm_bf16(const PlainGemmArgs& g, hipStream_t s) {
   p.C = g.C; p.addend = g.addend;
   if (g.A2) return run_bf16<CfgPlain, kModePlain, true>(p, s);
   return run_bf16<CfgPlain, kModePlain, false>(p, s);
+}
+
+hipError_t launch_block_gemm_bf16(const BlockGemmArgs& g, hipStream_t s) {
+  GemmParams p{};
+  p.A = static_cast<const bf16_t*>(g.A);
+  p.B0 = static_cast<const bf16_t*>(g.Bm);
+  p.M = g.M; p.N = g.N; p.K = g.K;
+  p.lda = g.K; p.ldb = g.K; p.ldc = g.ldc;
+  p.C16 = static_cast<bf16_t*>(g.C);
+  p.G16 = static_cast<bf16_t*>(g.G);
+  p.split = g.split;
+  if (g.G) return run_bf16<CfgPlain, kModeInProj, false>(p, s);
+  return run_bf16<CfgPlain, kModeOut, false>(p, s);
 }
 
 // ---------------------------------------------------------------- fp32 VALU GEMM

@@ -80,12 +80,32 @@ struct PlainGemmArgs {
   const float* addend;   // may equal C (read before write by the same thread) or NULL
 };
 
+// The linears of the recurrent block, bf16 in and out, C = A Bm^T with row strides K.
+// With G: N = 2 split columns, C[M, split] = the first split columns, G[M, split] = GeLU of
+// the rest (ldc = split); without G: C[M, N] (ldc = N).
+struct BlockGemmArgs {
+  const void* A;
+  const void* Bm;
+  int M, N, K;
+  int ldc;
+  void* C;
+  void* G;
+  int split;
+};
+hipError_t launch_block_gemm_bf16(const BlockGemmArgs& g, hipStream_t s);
+
 hipError_t launch_gate_gemm_bf16(const GateGemmArgs& g, int epi, hipStream_t s);   // kEpiAB, kEpiRI
 hipError_t launch_plain_gemm_bf16(const PlainGemmArgs& g, hipStream_t s);
 hipError_t launch_plain_gemm_f32(const PlainGemmArgs& g, hipStream_t s);
 // fp32 I/O: gate math from pre-activations za, zx [M, N] (already W u, bias not added).
 hipError_t launch_gate_elementwise_f32(const GateGemmArgs& g, const float* za, const float* zx,
                                        int epi, hipStream_t s);
+
+// ---------------------------------------------------------------- block.hip
+// fp32 I/O steps of the recurrent block: pq [M, 2R] -> p = pq[:, :R], g = GeLU(pq[:, R:]);
+// y *= g elementwise.
+hipError_t launch_split_gelu_f32(const float* pq, int M, int R, float* p, float* g, hipStream_t s);
+hipError_t launch_mul_f32(float* y, const float* g, size_t n, hipStream_t s);
 
 // ---------------------------------------------------------------- lru.hip
 // The fused RG-LRU layer (gate GEMM + log-space gates + chunked scan) for bf16 I/O.
@@ -98,12 +118,13 @@ struct LruArgs {
   const float* lam;
   float c;
   const float* h0;        // [B,D] or NULL
-  void* y;                // [B,T,D] bf16
+  void* y;                // [B,T,D] bf16: RNE(h), or RNE(h * gate) with a gate
   float* hT;              // [B,D] or NULL
   int B, T, D;
   uint32_t* status;       // lru_status_bytes(B,T,D) bytes of look-back words
   uint32_t* counters;     // 64 ticket counters (zeroed with the status words)
   int groups;             // set by the launcher
+  const void* gate;       // [B,T,D] bf16 multiplier of the output (the block's GeLU branch) or NULL
 };
 int lru_chunks(int T);
 size_t lru_status_bytes(int B, int T, int D);

@@ -13,6 +13,12 @@
 // "Griffin's Compromise", "Term explanation: Parallel scan").  Only y (bf16) and h_T leave
 // the kernel: a_t and beta_t never touch HBM.
 //
+// With a gate tensor g (the recurrent block's GeLU branch, same layout as u) the kernel
+// writes RNE(h_t g_t) instead of RNE(h_t): the g tile is fetched into LDS right behind the
+// u tile (the gated kernel takes 146 KB of LDS instead of 128 KB; one workgroup per CU
+// either way) and lands during the first pass; the second pass multiplies each state by
+// its g before rounding.
+//
 // Tiles of one chain (sequence b, channel tile) must be started in time order: every
 // workgroup takes a ticket from the counter of its group g = blockIdx % G; group g owns
 // the chains c = g, g + G, ... (so all tiles of a chain share one counter), and tickets
@@ -27,6 +33,14 @@ namespace rglru {
 typedef GemmCfg<256, 128, 2, 4, false, 64, 2> CfgLru;
 constexpr int kLruRows = CfgLru::BM;   // time steps per tile
 constexpr int kLruCh = CfgLru::BC;     // channels per tile
+constexpr int kTileBytes = kLruRows * kLruCh * 2;                  // one bf16 [rows x channels] tile
+constexpr int kEpiScratch = (3 * kLruCh + 2 * kWindow * kLruCh) * 4;  // aggregates, carries, look-back
+template <bool GATED>
+constexpr int lru_lds_bytes() {
+  return GATED ? 2 * kTileBytes + kEpiScratch : CfgLru::LDS_BYTES;
+}
+static_assert(kTileBytes + kEpiScratch <= CfgLru::LDS_BYTES, "epilogue LDS");
+static_assert(2 * kTileBytes + kEpiScratch + 1024 <= 160 * 1024, "gated epilogue LDS");
 
 int lru_chunks(int T) { return (T + kLruRows - 1) / kLruRows; }
 size_t lru_status_bytes(int B, int T, int D) { return 3ull * lru_chunks(T) * size_t(B) * D * 4; }
@@ -38,8 +52,8 @@ static int lru_groups(int chains) {
 }
 
 // The scan epilogue of lru_fused_kernel (see the file comment).  EDGE: the tile may have
-// fewer than 256 valid rows or hold the sequence's final step.
-template <bool EDGE>
+// fewer than 256 valid rows or hold the sequence's final step.  GATED: multiply by p.gate.
+template <bool EDGE, bool GATED>
 __device__ __forceinline__ void lru_epilogue(const LruArgs& p, unsigned char* lds,
                                              f32x16_t (&acc)[CfgLru::MF][CfgLru::NF], int lane,
                                              int wave, int b, int tn, int tt, int t0, int rows) {
@@ -48,34 +62,43 @@ __device__ __forceinline__ void lru_epilogue(const LruArgs& p, unsigned char* ld
   const int B = p.B, T = p.T, D = p.D;
   const bf16_t* u = static_cast<const bf16_t*>(p.u);
   // LDS after the K loop: [0, 64 KB) the tile's u (then y) as 256 rows x 128 bf16 channels;
-  // then per-channel aggregates, carries and the look-back scratch.
+  // with a gate, [64 KB, 128 KB) its g tile; then per-channel aggregates, carries and the
+  // look-back scratch.
   __syncthreads();   // every wave is done with the GEMM stages: the LDS is reused below
   bf16_t* tileU = reinterpret_cast<bf16_t*>(lds);
-  float* eA = reinterpret_cast<float*>(lds + kLruRows * kLruCh * 2);
+  float* eA = reinterpret_cast<float*>(lds + (GATED ? 2 : 1) * kTileBytes);
   float* eH = eA + kLruCh;
   float* eC = eH + kLruCh;
   float* eLb = eC + kLruCh;                          // look-back scratch, 2 kWindow per channel
   const int chv = min(kLruCh, D - tn * kLruCh);      // valid channels of the tile (64 or 128)
   const size_t rowbase = size_t(b) * T + t0;
-  {
-    // u rows of the tile -> LDS, 16 bytes per lane (4 rows of 256 B per wave instruction);
-    // rows past the sequence and chunks past D are clamped to valid addresses (unused)
-    const bf16_t* ug = u + rowbase * D + tn * kLruCh;
+  // A [256 rows x 128 channels] bf16 tile of src -> LDS [dst, dst + 64 KB), 16 bytes per
+  // lane (4 rows of 256 B per wave instruction, kFetch instructions per wave); rows past the
+  // sequence and chunks past D are clamped to valid addresses (their values are never used).
+  constexpr int kFetch = kLruRows / 4 / C::NW;
+  auto fetch_tile = [&](const bf16_t* src, int dst) {
+    const bf16_t* sg = src + rowbase * D + tn * kLruCh;
 #pragma unroll
-    for (int it = 0; it < kLruRows / 4 / C::NW; ++it) {
+    for (int it = 0; it < kFetch; ++it) {
       const int r = (it * C::NW + wave) * 4 + (lane >> 4);
       const int chunk = min(lane & 15, chv / 8 - 1);
-      const bf16_t* gp = ug + size_t(min(r, rows - 1)) * D + chunk * 8;
-      __builtin_amdgcn_global_load_lds((void*)gp, (void*)(lds + (it * C::NW + wave) * 1024), 16, 0, 0);
+      const bf16_t* gp = sg + size_t(min(r, rows - 1)) * D + chunk * 8;
+      __builtin_amdgcn_global_load_lds((void*)gp, (void*)(lds + dst + (it * C::NW + wave) * 1024), 16, 0, 0);
     }
-  }
+  };
+  fetch_tile(u, 0);
   const int c = lane & 31, half = lane >> 5;
   const int chl = wn * 32 + c;                       // channel within the tile
   const int ch = tn * kLruCh + chl;
   const bool chok = chl < chv;
   const GateChan kc = gate_chan(p.ba[chok ? ch : tn * kLruCh], p.bx[chok ? ch : tn * kLruCh],
                                 p.lam[chok ? ch : tn * kLruCh], p.c);
-  wait_dma_barrier<0>();                             // the u tile is in LDS
+  if (GATED) {
+    fetch_tile(static_cast<const bf16_t*>(p.gate), kTileBytes);
+    wait_dma_barrier<kFetch>();                      // the u tile is in LDS (g may still land)
+  } else {
+    wait_dma_barrier<0>();                           // the u tile is in LDS
+  }
   // Group q = 4 mf + gq of this lane covers tile rows wm*128 + 32 mf + 8 gq + 4 half + rr,
   // rr = 0..3 (consecutive time steps); tb[(32 mf + 8 gq + rr) * kLruCh] is the LDS element
   // of row rr (constant offsets).  The first pass turns the accumulator pair (z^a, z^x) of
@@ -147,7 +170,8 @@ __device__ __forceinline__ void lru_epilogue(const LruArgs& p, unsigned char* ld
     }
     eC[chl] = carry;
   }
-  __syncthreads();
+  if (GATED) wait_dma_barrier<0>();                  // the g tile is in LDS too
+  else __syncthreads();
   const float carry = eC[chl];
   const float hin = wm == 0 ? carry : fmaf(A0w, carry, H0w);
   const int lastrel = T - 1 - t0 - lrow0;            // the final step, if in this lane's rows
@@ -160,7 +184,8 @@ __device__ __forceinline__ void lru_epilogue(const LruArgs& p, unsigned char* ld
     for (int rr = 0; rr < 4; ++rr) {
       h = fmaf(acc[q >> 2][0][(q & 3) * 4 + rr], h, acc[q >> 2][1][(q & 3) * 4 + rr]);
       const int rel = (q >> 2) * 32 + 8 * (q & 3) + rr;
-      tb[((q >> 2) * 32 + 8 * (q & 3) + rr) * kLruCh] = f2bf(h);
+      const float o = GATED ? h * bf2f(tb[kTileBytes / 2 + rel * kLruCh]) : h;
+      tb[rel * kLruCh] = f2bf(o);
       if (EDGE) {
         hlast = rel == lastrel ? h : hlast;
         haslast = haslast || rel == lastrel;
@@ -181,9 +206,10 @@ __device__ __forceinline__ void lru_epilogue(const LruArgs& p, unsigned char* ld
   }
 }
 
+template <bool GATED>
 __global__ __launch_bounds__(CfgLru::NW * 64, 2) void lru_fused_kernel(LruArgs p) {
   typedef CfgLru C;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[lru_lds_bytes<GATED>()];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   __shared__ uint32_t s_ticket;
@@ -212,7 +238,7 @@ __global__ __launch_bounds__(CfgLru::NW * 64, 2) void lru_fused_kernel(LruArgs p
   gemm_mainloop<C, false>(op, lds, lane, wave, acc);
 
   // ---------------------------------------------------------------- scan epilogue
-  lru_epilogue<true>(p, lds, acc, lane, wave, b, tn, tt, t0, rows);
+  lru_epilogue<true, GATED>(p, lds, acc, lane, wave, b, tn, tt, t0, rows);
 }
 
 hipError_t launch_lru_fused(const LruArgs& a_in, bool prefilled, hipStream_t s) {
@@ -225,7 +251,8 @@ hipError_t launch_lru_fused(const LruArgs& a_in, bool prefilled, hipStream_t s) 
     if (e != hipSuccess) return e;
   }
   const int tiles = chains * lru_chunks(a.T);
-  lru_fused_kernel<<<tiles, CfgLru::NW * 64, 0, s>>>(a);
+  if (a.gate) lru_fused_kernel<true><<<tiles, CfgLru::NW * 64, 0, s>>>(a);
+  else lru_fused_kernel<false><<<tiles, CfgLru::NW * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 

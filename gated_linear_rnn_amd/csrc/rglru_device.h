@@ -75,6 +75,13 @@ __device__ __forceinline__ float conv_u(float b, float w0, float w1, float w2, f
   return Io<IO>::round(acc);
 }
 
+// ------------------------------------------------------------------ GeLU
+// The exact GeLU of the recurrent block's second branch, q Phi(q), written with the
+// complementary error function, Phi(q) = erfc(-q / sqrt 2) / 2, which keeps its relative
+// accuracy in the lower tail where 1 + erf(q / sqrt 2) would cancel.
+__device__ __forceinline__ float gelu_f(float q) { return 0.5f * q * erfcf(-0.70710678118654752f * q); }
+__device__ __forceinline__ double gelu_d(double q) { return 0.5 * q * erfc(-0.70710678118654752440 * q); }
+
 // ------------------------------------------------------------------ gate math
 __device__ __forceinline__ float sigmoidf_stable(float z) {
   if (z >= 0.f) return 1.f / (1.f + expf(-z));

@@ -186,6 +186,35 @@ int rglru_bwd(int B, int T, int D, rglru_dtype io, float c, const void* x,
               float* db_a, float* db_x, float* dlambda, float* dh0, void* ws,
               size_t ws_bytes, hipStream_t stream);
 
+/* Workspace bytes rglru_block_fwd needs (0 for invalid arguments). */
+size_t rglru_block_fwd_workspace_bytes(int B, int T, int D, int R, rglru_dtype io);
+
+/*
+ * Forward of the whole recurrent block around the temporal branch (the Griffin
+ * model-architecture page, section "Recurrent block", Fig. 2(c)): the model-width input x
+ * goes through two linear layers D -> R (R = D_RNN) in parallel; the first feeds the
+ * temporal branch (rglru_fwd), GeLU is applied to the second, the two are multiplied
+ * elementwise, and a linear layer R -> D gives the output:
+ *   p = RNE_io(x W_in[0:R]^T),  g = RNE_io(GeLU(x W_in[R:2R]^T)),  GeLU(q) = q Phi(q) (exact)
+ *   (y, h_T, conv_state_out) = rglru_fwd(p, ...)  with y kept unrounded,
+ *   out = RNE_io(RNE_io(y g) W_out^T).
+ * The linears have no bias.  For bf16 I/O the products accumulate in fp32 on the matrix
+ * cores; for fp32 I/O they accumulate in fp64.
+ *   x [B,T,D] io; W_in [2R,D] io ([out,in], the branch rows first, then the GeLU rows);
+ *   conv_w [4,R] io or NULL (no conv), conv_b [R] fp32 or NULL, conv_state_in [B,3,R] io
+ *   or NULL; W_a, W_x [R,R] io; b_a, b_x, lambda [R] fp32; h0 [B,R] fp32 or NULL;
+ *   W_out [D,R] io; out [B,T,D] io (output); h_T [B,R] fp32 (output, nullable);
+ *   conv_state_out [B,3,R] io (output, nullable).
+ *   Shapes: D % 64 == 0 and R % 64 == 0, B*T*max(D,R) < 2^31; otherwise RGLRU_ESHAPE.
+ *   Results are bitwise reproducible run to run.
+ */
+int rglru_block_fwd(int B, int T, int D, int R, rglru_dtype io, float c, const void* x,
+                    const void* W_in, const void* conv_w, const float* conv_b,
+                    const void* conv_state_in, const void* W_a, const void* W_x,
+                    const float* b_a, const float* b_x, const float* lambda, const float* h0,
+                    const void* W_out, void* out, float* h_T, void* conv_state_out, void* ws,
+                    size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -105,3 +105,38 @@ def test_decode_and_conv_and_bwd_reject_invalid_arguments(lib):
     assert r == -4
     bwd[10] = None       # dy
     assert lib.rglru_bwd(1, 4, 64, 1, 8.0, *bwd, A, 1 << 40, None) == -1
+
+
+def test_block_workspace_query(lib):
+    n = 8 * 2048 * 2560
+    assert lib.rglru_block_fwd_workspace_bytes(8, 2048, 2560, 2560, 1) >= 3 * n * 2   # p, g, u
+    assert lib.rglru_block_fwd_workspace_bytes(8, 2048, 2560, 2560, 0) >= 6 * n * 4   # pq, p, g, y, u
+    assert lib.rglru_block_fwd_workspace_bytes(1, 1, 64, 96, 1) == 0     # R % 64
+    assert lib.rglru_block_fwd_workspace_bytes(1, 1, 96, 64, 1) == 0     # D % 64
+    assert lib.rglru_block_fwd_workspace_bytes(1, 1, 64, 64, 3) == 0     # dtype
+    assert lib.rglru_block_fwd_workspace_bytes(1 << 12, 1 << 12, 64, 128, 1) == 0   # B*T*R >= 2^31
+
+
+def _block(lib, B=1, T=4, D=64, R=128, io=1, c=8.0, **over):
+    names = ("x", "W_in", "conv_w", "conv_b", "cs", "Wa", "Wx", "ba", "bx", "lam", "h0", "W_out",
+             "out", "hT", "cso", "ws")
+    args = dict.fromkeys(names, A)
+    args.update(conv_w=None, conv_b=None, cs=None, h0=None, hT=None, cso=None, wsb=1 << 40)
+    args.update(over)
+    return lib.rglru_block_fwd(B, T, D, R, io, c, *[args[k] for k in names], args["wsb"], None)
+
+
+@no_gpu
+def test_block_rejects_invalid_arguments(lib):
+    assert _block(lib, B=0) == -1
+    assert _block(lib, R=0) == -1
+    assert _block(lib, R=96) == -2
+    assert _block(lib, D=32) == -2
+    assert _block(lib, B=1 << 12, T=1 << 12, D=1 << 7) == -2
+    assert _block(lib, io=2) == -3
+    for k in ("x", "W_in", "Wa", "Wx", "ba", "bx", "lam", "W_out", "out"):
+        assert _block(lib, **{k: None}) == -1, k
+    assert _block(lib, W_out=BAD) == -1
+    assert _block(lib, c=-2.0) == -1
+    assert _block(lib, ws=None) == -4
+    assert _block(lib, wsb=100) == -4

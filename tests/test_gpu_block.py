@@ -1,0 +1,119 @@
+"""Parity of the recurrent block (rglru_block_fwd: the two input linears, the GeLU branch,
+the temporal branch, the product and the output linear of Fig. 2(c) on the Griffin
+model-architecture page) with the oracle's block_forward.
+
+Element by element at sizes the oracle finishes in seconds: ragged row tiles (M = B*T not
+a multiple of 256), ragged column tiles of both linears (2R and D not multiples of 256,
+the p/GeLU split inside a tile), an RG-LRU channel tile of 64 valid channels, T = 1, and
+model width different from the branch width.  At the full training shape every output of
+one whole sequence is compared (sequences are independent, so the oracle runs on that
+sequence alone) together with its final state.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import TOL, TORCH_IO, dev, device_inputs, err, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _device(p):
+    io = TORCH_IO[p["workload"].io]
+    d = device_inputs(p)
+    d.update(x_block=dev(p["x_block"], io), W_in=dev(p["W_in"], io), W_out=dev(p["W_out"], io))
+    return d
+
+
+def _gpu(g, d, p, conv=True):
+    out, hT, cso = g.block_forward(d["x_block"], d["W_in"], d["conv_w"] if conv else None,
+                                   d["conv_b"] if conv else None, d["conv_state"] if conv else None,
+                                   d["W_a"], d["W_x"], d["b_a"], d["b_x"], d["lam"], d["h0"],
+                                   d["W_out"], p["c"])
+    torch.cuda.synchronize()
+    return host(out), host(hT), host(cso)
+
+
+def _oracle(p, conv=True, rows=slice(None)):
+    sel = lambda a: None if a is None else a[rows]
+    return oracle.block_forward(
+        x=p["x_block"][rows], W_in=p["W_in"], conv_w=p["conv_w"] if conv else None,
+        conv_b=p["conv_b"] if conv else None, conv_state_in=sel(p["conv_state"]) if conv else None,
+        W_a=p["W_a"], W_x=p["W_x"], b_a=p["b_a"], b_x=p["b_x"], lam=p["lam"], h0=sel(p["h0"]),
+        W_out=p["W_out"], c=p["c"], io=p["workload"].io)
+
+
+def _check(g, p, conv=True, what=""):
+    io = p["workload"].io
+    out, hT, cso = _gpu(g, _device(p), p, conv)
+    o = _oracle(p, conv)
+    eo, eh = err(out, o["out"]), err(hT, o["h_T"])
+    print(f"{what} io={io} x={p['x_block'].shape} R={p['W_in'].shape[0] // 2} "
+          f"err(out)={eo:.3e} err(h_T)={eh:.3e}", flush=True)
+    assert eo <= TOL[io] and eh <= TOL[io]
+    if conv:
+        np.testing.assert_array_equal(cso, o["conv_state_out"])   # a copy of p rows: exact
+
+
+SMALL = [
+    # (workload recipe, B, T, model width D, branch width R)
+    (workloads.TINY_F32, 1, 256, 256, 256),
+    (workloads.TINY_F32, 2, 300, 192, 320),
+    (workloads.TINY_F32, 1, 1, 64, 64),
+    (workloads.TRAIN_FWD, 2, 700, 320, 384),
+    (workloads.TRAIN_FWD, 3, 257, 448, 192),
+    (workloads.TRAIN_FWD, 1, 1, 64, 64),
+    (workloads.TRAIN_FWD, 1, 300, 128, 640),
+    (workloads.LONG_FWD, 1, 1500, 256, 256),
+]
+
+
+@pytest.mark.parametrize("w,B,T,D,R", SMALL, ids=[f"{w.io}-{B}x{T}-D{D}-R{R}" for w, B, T, D, R in SMALL])
+def test_block_small_elementwise(lib, w, B, T, D, R):
+    p = workloads.make_block_inputs(w.with_shape(B=B, T=T, D=R), d_model=D)
+    _check(lib, p, what=w.name)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_block_with_conv_state_h0_and_bias(lib, io):
+    w = workloads.TRAIN_FWD.with_shape(B=2, T=333, D=192, io=io, h0="normal", history="normal")
+    p = workloads.make_block_inputs(w, d_model=256)
+    p["conv_b"] = np.random.default_rng(0).standard_normal(192).astype(np.float32) * 0.1
+    _check(lib, p, what="state")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_block_without_conv(lib, io):
+    # without the conv the branch input p is the layer input; the output must not overwrite
+    # it while other channel tiles of the same rows still read it (R = 384: 3 channel tiles)
+    w = workloads.TRAIN_FWD.with_shape(B=2, T=520, D=384, io=io)
+    p = workloads.make_block_inputs(w, d_model=192)
+    _check(lib, p, conv=False, what="noconv")
+
+
+def test_block_repeat_is_bitwise_identical(lib):
+    w = workloads.TRAIN_FWD.with_shape(B=2, T=600, D=256)
+    p = workloads.make_block_inputs(w, d_model=320)
+    d = _device(p)
+    first = _gpu(lib, d, p)
+    for _ in range(3):
+        again = _gpu(lib, d, p)
+        for a, b in zip(first, again):
+            np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.timeout(600)
+def test_block_full_training_shape_one_sequence(lib):
+    """B=8, T=2048, D = D_RNN = 2560 in the launch configuration the benchmark times; every
+    output and the final state of the last sequence against the oracle on that sequence."""
+    w = workloads.TRAIN_FWD
+    p = workloads.make_block_inputs(w)
+    out, hT, _ = _gpu(lib, _device(p), p)
+    b = w.B - 1
+    o = _oracle(p, rows=slice(b, b + 1))
+    eo, eh = err(out[b:b + 1], o["out"]), err(hT[b:b + 1], o["h_T"])
+    print(f"full block b={b} err(out)={eo:.3e} err(h_T)={eh:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
+    assert np.all(np.isfinite(out))

@@ -48,12 +48,8 @@ def test_gelu_against_simpson_integral_of_the_normal_density():
 # ---------------------------------------------------------------- the block
 def _block_params(rng, B, T, D, R, io="f32"):
     w = workloads.TINY_F32.with_shape(B=B, T=T, D=R, io=io, h0="normal", history="normal",
-                                      seed=int(rng.integers(1 << 30)))
-    p = workloads.make_inputs(w)
-    p["x_block"] = oracle.round_io(rng.standard_normal((B, T, D)), io)
-    p["W_in"] = oracle.round_io(rng.standard_normal((2 * R, D)) / math.sqrt(D), io)
-    p["W_out"] = oracle.round_io(rng.standard_normal((D, R)) / math.sqrt(R), io)
-    return p
+                                      bias_std=0.3, seed=int(rng.integers(1 << 30)))
+    return workloads.make_block_inputs(w, d_model=D)
 
 
 def _block(p, **kw):

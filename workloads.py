@@ -1,4 +1,5 @@
-"""Seeded synthetic inputs for the RG-LRU temporal branch (Conv1D width 4 -> RG-LRU).
+"""Seeded synthetic inputs for the RG-LRU temporal branch (Conv1D width 4 -> RG-LRU) and
+the recurrent block around it.
 
 This module holds no arithmetic of the layer itself: it only draws the inputs that
 both the CPU oracle and the HIP path consume, so that the two sides see the very same
@@ -127,3 +128,23 @@ def extra_inputs_x(w: Workload, k: int) -> np.ndarray:
     way as x from default_rng(w.seed + 1000 k) (set 0 is make_inputs(w)["x"])."""
     rng = np.random.default_rng(w.seed + 1000 * k)
     return _normal(rng, (w.B, w.T, w.D), 1.0, w.io)
+
+
+def make_block_inputs(w: Workload, d_model: int | None = None, c: float = C_DEFAULT) -> dict:
+    """Inputs of the whole recurrent block around the branch of workload ``w`` (R = w.D is
+    D_RNN, the branch width; d_model is the model width D, default D_RNN).
+
+    The branch parameters are make_inputs(w)'s; the block's own arrays come from a second
+    stream, default_rng(w.seed + 7919), in this order: x_block [B,T,D] ~ N(0,1),
+    W_in [2R, D] ~ N(0, 1/D) (LeCun, fan_in = D; rows 0..R-1 feed the branch, rows R..2R-1
+    the GeLU side), W_out [D, R] ~ N(0, 1/R) (LeCun, fan_in = R).  All io-exact fp32.
+    """
+    D = int(d_model or w.D)
+    R = w.D
+    out = make_inputs(w, c)
+    rng = np.random.default_rng(w.seed + 7919)
+    out["d_model"] = D
+    out["x_block"] = _normal(rng, (w.B, w.T, D), 1.0, w.io)
+    out["W_in"] = _normal(rng, (2 * R, D), 1.0 / np.sqrt(D), w.io)
+    out["W_out"] = _normal(rng, (D, R), 1.0 / np.sqrt(R), w.io)
+    return out
