@@ -201,6 +201,7 @@ def main():
     if not args.no_extras:
         out["decode"] = bench_decode(g, torch, np, workloads)
         out["train_fwd_bwd"] = bench_fwd_bwd(g, torch, np, workloads)
+        out["recurrent_block_fwd"] = bench_block(g, torch, np, workloads)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, np)
     print(json.dumps(out))
@@ -296,6 +297,44 @@ def bench_fwd_bwd(g, torch, np, workloads):
     f, b = float(np.median(fwd)), float(np.median(bwd))
     return {"workload": w.name, "fwd_ms": f, "bwd_ms": b,
             "tokens_per_s_fwd_bwd": B * T / ((f + b) * 1e-3)}
+
+
+def bench_block(g, torch, np, workloads, steps=50):
+    """rglru_block_fwd (input linears + GeLU branch + conv + RG-LRU + product + output
+    linear) at B=8, T=2048, D = D_RNN = 2560, bf16, inputs resident, warm clocks."""
+    w = workloads.TRAIN_FWD
+    p = workloads.make_block_inputs(w)
+    bf = torch.bfloat16
+    dev = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dt)
+    B, T, R = w.B, w.T, w.D
+    D = p["d_model"]
+    xb, W_in, W_out = dev(p["x_block"], bf), dev(p["W_in"], bf), dev(p["W_out"], bf)
+    cw, cb = dev(p["conv_w"], bf), dev(p["conv_b"])
+    Wa, Wx, ba, bx, lam = dev(p["W_a"], bf), dev(p["W_x"], bf), dev(p["b_a"]), dev(p["b_x"]), dev(p["lam"])
+    out = torch.empty_like(xb)
+    hT = torch.empty((B, R), dtype=torch.float32, device="cuda")
+    ws = g.workspace(g.block_fwd_workspace_bytes(B, T, D, R, bf))
+    _log("recurrent block")
+
+    def once():
+        g.rglru_block_fwd(xb, W_in, cw, cb, None, Wa, Wx, ba, bx, lam, None, W_out, out, hT, None,
+                          ws, p["c"])
+
+    for _ in range(steps):
+        once()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        once()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    M = B * T
+    flop = 2.0 * M * (2 * R * D + 2 * R * R + D * R)
+    return {"workload": f"block_fwd_bf16_B{B}_T{T}_D{D}_R{R}", "ms_per_step": ms,
+            "tokens_per_s": M / (ms * 1e-3), "TFLOPs": flop / (ms * 1e-3) / 1e12,
+            "flop_per_step": flop, "steps": steps}
 
 
 def cpu_baseline(p, np):
