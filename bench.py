@@ -202,6 +202,7 @@ def main():
         out["decode"] = bench_decode(g, torch, np, workloads)
         out["train_fwd_bwd"] = bench_fwd_bwd(g, torch, np, workloads)
         out["recurrent_block_fwd"] = bench_block(g, torch, np, workloads)
+        out["prefill_decode_latency"] = bench_latency(g, torch, np, workloads)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, np)
     print(json.dumps(out))
@@ -337,20 +338,80 @@ def bench_block(g, torch, np, workloads, steps=50):
             "flop_per_step": flop, "steps": steps}
 
 
-def cpu_baseline(p, np):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload."""
+def bench_latency(g, torch, np, workloads):
+    """Prefill latency (one rglru_fwd call) by context length and batch, decode latency per
+    step by batch, and the fixed state carried per sequence, at D = 2560 with the headline
+    workload's parameters (the pages' checklist: prefill and decode latency by context
+    length and batch size, state memory)."""
+    w = workloads.TRAIN_FWD
+    p = workloads.make_inputs(w.with_shape(B=1, T=1))
+    bf = torch.bfloat16
+    dev = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dt)
+    D = w.D
+    cw, cb = dev(p["conv_w"], bf), dev(p["conv_b"])
+    Wa, Wx, ba, bx, lam = dev(p["W_a"], bf), dev(p["W_x"], bf), dev(p["b_a"]), dev(p["b_x"]), dev(p["lam"])
+    gen = torch.Generator(device="cuda").manual_seed(17)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    _log("prefill/decode latency")
+    prefill = []
+    for B in (1, 8, 32):
+        for T in (512, 2048, 8192):
+            x = torch.randn((B, T, D), generator=gen, device="cuda").to(bf)
+            y = torch.empty_like(x)
+            hT = torch.empty((B, D), device="cuda")
+            cso = torch.empty((B, 3, D), dtype=bf, device="cuda")
+            ws = g.workspace(g.fwd_workspace_bytes(B, T, D, bf))
+            ms = timed(lambda: g.rglru_fwd(x, cw, cb, None, Wa, Wx, ba, bx, lam, None, y, hT, cso, ws,
+                                           p["c"]), 10)
+            prefill.append({"B": B, "T": T, "ms": ms, "tokens_per_s": B * T / (ms * 1e-3)})
+            del x, y, ws
+    decode = []
+    for B in (1, 8, 64, 256):
+        xt = torch.randn((B, D), generator=gen, device="cuda").to(bf)
+        hist = torch.randn((B, 3, D), generator=gen, device="cuda").to(bf)
+        h = torch.randn((B, D), generator=gen, device="cuda")
+        yt = torch.empty((B, D), dtype=bf, device="cuda")
+        ws = g.workspace(g.decode_workspace_bytes(B, D, bf))
+        ms = timed(lambda: g.rglru_decode_step(xt, cw, cb, hist, Wa, Wx, ba, bx, lam, h, yt, ws,
+                                               p["c"]), 200)
+        decode.append({"B": B, "us_per_step": ms * 1e3, "tokens_per_s": B / (ms * 1e-3)})
+    torch.cuda.empty_cache()
+    return {"D": D, "prefill_rglru_fwd": prefill, "decode_step_eager": decode,
+            "state_bytes_per_sequence": D * 4 + 3 * D * 2,
+            "note": "the state (h fp32 + 3-token bf16 conv history) does not grow with context"}
+
+
+def cpu_baseline(p, np, min_seconds=10.0):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload: its forward
+    over the whole headline batch, repeated until at least min_seconds have passed."""
     import oracle
     Bs = p["x"].shape[0]
     cores = len(os.sched_getaffinity(0))
     _log(f"cpu baseline: oracle forward on {Bs} sequences ({cores} cores)")
-    t0 = time.perf_counter()
-    oracle.forward(p["x"][:Bs], p["conv_w"], p["conv_b"], None, p["W_a"], p["W_x"], p["b_a"],
-                   p["b_x"], p["lam"], None, p["c"], "bf16")
-    dt = time.perf_counter() - t0
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(p["x"][:Bs], p["conv_w"], p["conv_b"], None, p["W_a"], p["W_x"], p["b_a"],
+                       p["b_x"], p["lam"], None, p["c"], "bf16")
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
     T = p["x"].shape[1]
-    return {"value": Bs * T / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": reps * Bs * T / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"oracle forward (fp64 NumPy, BLAS threads = cores) over the whole "
-                      f"{Bs}x{T}x{p['x'].shape[2]} workload ({Bs * T} tokens, {dt:.1f} s)"}
+                      f"{Bs}x{T}x{p['x'].shape[2]} workload, {reps} times ({reps * Bs * T} tokens, "
+                      f"{dt:.1f} s)"}
 
 
 if __name__ == "__main__":
