@@ -4,4 +4,5 @@ Only tests/, the smoke check and the benchmark's CPU-baseline leg may import thi
 package; the HIP library never does.
 """
 from .rglru_oracle import (round_io, fma_f32, sigmoid, log_sigmoid, gates, conv1d_causal4,  # noqa: F401
-                           forward, decode_step, backward, gelu, block_forward)
+                           forward, decode_step, backward, gelu, block_forward,
+                           gated_mlp_forward)

@@ -46,9 +46,16 @@ give none); GeLU is the exact form q Phi(q); rounding points of the I/O dtype ar
 branch input p = RNE(x W_in1^T), g = RNE(GeLU(x W_in2^T)), the product z = RNE(h_t g_t)
 of the unrounded RG-LRU state and g, and the block output RNE(z W_out^T).
 
+The gated MLP block ([ARCH] "MLP block", Fig. 2(b)): two linear layers D -> M*D on the
+same input (M = 3 on the pages), GeLU on the first branch, elementwise product with the
+second, a final linear M*D -> D.  Readings: no biases; exact GeLU; which branch carries
+the GeLU is not fixed by the pages, W_1 (the first argument) is the GeLU branch; the two
+branch outputs are not rounded on their own, the product h = RNE(GeLU(x W_1^T) (x W_2^T))
+is (one rounding point, where the product is formed), and the output RNE(h W_3^T).
+
 Parity pins: every function here is pinned by a test against closed forms, invariants,
 brute force or library routines (tests/test_oracle_pins.py, tests/test_oracle_grad.py,
-tests/test_oracle_block.py).
+tests/test_oracle_block.py, tests/test_oracle_mlp.py).
 """
 from __future__ import annotations
 
@@ -349,3 +356,21 @@ def block_forward(x, W_in, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, la
     if keep:
         res.update(p=p, g=g, z=z)
     return res
+
+
+def gated_mlp_forward(x, W_1, W_2, W_3, io, keep=False):
+    """The gated MLP block of [ARCH] "MLP block" (Fig. 2(b)): two branches of width M*D from
+    the same input, GeLU on the first, merged by an elementwise product, then a linear layer
+    back to width D.
+
+    x [..., D]; W_1, W_2 [MD, D] and W_3 [D, MD], all [out, in].  Returns out [..., D]
+    (rounded to io); with keep=True a dict that also holds h = RNE(GeLU(x W_1^T) (x W_2^T)).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    q1 = x @ np.asarray(W_1, dtype=np.float64).T
+    q2 = x @ np.asarray(W_2, dtype=np.float64).T
+    h = round_io(gelu(q1) * q2, io)
+    out = round_io(h @ np.asarray(W_3, dtype=np.float64).T, io)
+    if keep:
+        return {"out": out, "h": h}
+    return out

@@ -148,3 +148,18 @@ def make_block_inputs(w: Workload, d_model: int | None = None, c: float = C_DEFA
     out["W_in"] = _normal(rng, (2 * R, D), 1.0 / np.sqrt(D), w.io)
     out["W_out"] = _normal(rng, (D, R), 1.0 / np.sqrt(R), w.io)
     return out
+
+
+def make_mlp_inputs(w: Workload, expansion: int = 3) -> dict:
+    """Inputs of the gated MLP block at model width D = w.D with hidden width
+    expansion * D (M = 3 on the pages), from default_rng(w.seed + 104729) in this order:
+    x [B,T,D] ~ N(0,1), W_1 and W_2 [MD, D] ~ N(0, 1/D), W_3 [D, MD] ~ N(0, 1/(MD))
+    (LeCun, fan_in = D resp. MD).  All io-exact fp32."""
+    D = w.D
+    MD = expansion * D
+    rng = np.random.default_rng(w.seed + 104729)
+    return {"workload": w, "expansion": expansion,
+            "x": _normal(rng, (w.B, w.T, D), 1.0, w.io),
+            "W_1": _normal(rng, (MD, D), 1.0 / np.sqrt(D), w.io),
+            "W_2": _normal(rng, (MD, D), 1.0 / np.sqrt(D), w.io),
+            "W_3": _normal(rng, (D, MD), 1.0 / np.sqrt(MD), w.io)}
