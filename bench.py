@@ -203,6 +203,7 @@ def main():
         out["train_fwd_bwd"] = bench_fwd_bwd(g, torch, np, workloads)
         out["recurrent_block_fwd"] = bench_block(g, torch, np, workloads)
         out["prefill_decode_latency"] = bench_latency(g, torch, np, workloads)
+        out["gated_mlp_fwd"] = bench_mlp(g, torch, np, workloads)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, np)
     print(json.dumps(out))
@@ -334,6 +335,36 @@ def bench_block(g, torch, np, workloads, steps=50):
     M = B * T
     flop = 2.0 * M * (2 * R * D + 2 * R * R + D * R)
     return {"workload": f"block_fwd_bf16_B{B}_T{T}_D{D}_R{R}", "ms_per_step": ms,
+            "tokens_per_s": M / (ms * 1e-3), "TFLOPs": flop / (ms * 1e-3) / 1e12,
+            "flop_per_step": flop, "steps": steps}
+
+
+def bench_mlp(g, torch, np, workloads, steps=30):
+    """gated_mlp_fwd (two D -> 3D linears, GeLU product, 3D -> D linear) at B=8, T=2048,
+    D=2560, bf16, inputs resident, warm clocks."""
+    w = workloads.TRAIN_FWD
+    p = workloads.make_mlp_inputs(w)
+    bf = torch.bfloat16
+    dev = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dt)
+    x, W1, W2, W3 = (dev(p[k], bf) for k in ("x", "W_1", "W_2", "W_3"))
+    B, T, D = w.B, w.T, w.D
+    MD = W1.shape[0]
+    out = torch.empty_like(x)
+    ws = g.workspace(g.mlp_fwd_workspace_bytes(B, T, D, MD, bf))
+    _log("gated MLP")
+    for _ in range(steps):
+        g.gated_mlp_fwd(x, W1, W2, W3, out, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.gated_mlp_fwd(x, W1, W2, W3, out, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    M = B * T
+    flop = 2.0 * M * (2 * MD * D + MD * D)
+    return {"workload": f"mlp_fwd_bf16_B{B}_T{T}_D{D}_MD{MD}", "ms_per_step": ms,
             "tokens_per_s": M / (ms * 1e-3), "TFLOPs": flop / (ms * 1e-3) / 1e12,
             "flop_per_step": flop, "steps": steps}
 

@@ -22,7 +22,8 @@ EXPORTS = ("rglru_status_string", "conv1d_causal4", "rglru_fwd_workspace_bytes",
            "rglru_lru_workspace_bytes", "rglru_lru", "rglru_gates", "rglru_scan_workspace_bytes",
            "rglru_scan",
            "rglru_decode_workspace_bytes", "rglru_decode_step", "rglru_bwd_workspace_bytes",
-           "rglru_bwd", "rglru_block_fwd_workspace_bytes", "rglru_block_fwd")
+           "rglru_bwd", "rglru_block_fwd_workspace_bytes", "rglru_block_fwd",
+           "gated_mlp_fwd_workspace_bytes", "gated_mlp_fwd")
 
 _lib = None
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -70,6 +71,10 @@ def load(path: str = LIB_PATH):
     lib.rglru_block_fwd_workspace_bytes.restype = _Z
     lib.rglru_block_fwd.argtypes = [_I, _I, _I, _I, _I, _F] + [_P] * 15 + [_P, _Z, _P]
     lib.rglru_block_fwd.restype = _I
+    lib.gated_mlp_fwd_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+    lib.gated_mlp_fwd_workspace_bytes.restype = _Z
+    lib.gated_mlp_fwd.argtypes = [_I, _I, _I, _I, _I] + [_P] * 5 + [_P, _Z, _P]
+    lib.gated_mlp_fwd.restype = _I
     _lib = lib
     return lib
 
@@ -122,6 +127,10 @@ def bwd_workspace_bytes(B, T, D, dtype) -> int:
 
 def block_fwd_workspace_bytes(B, T, D, R, dtype) -> int:
     return int(load().rglru_block_fwd_workspace_bytes(B, T, D, R, io_code(dtype)))
+
+
+def mlp_fwd_workspace_bytes(B, T, D, MD, dtype) -> int:
+    return int(load().gated_mlp_fwd_workspace_bytes(B, T, D, MD, io_code(dtype)))
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
@@ -204,6 +213,14 @@ def rglru_block_fwd(x, W_in, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, 
            "rglru_block_fwd")
 
 
+def gated_mlp_fwd(x, W_1, W_2, W_3, out, ws, stream=None):
+    B, T, D = x.shape
+    MD = W_1.shape[0]
+    _check(load().gated_mlp_fwd(B, T, D, MD, io_code(x.dtype), _ptr(x), _ptr(W_1), _ptr(W_2),
+                                _ptr(W_3), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
+           "gated_mlp_fwd")
+
+
 # ------------------------------------------------------------------ allocating helpers
 def forward(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0=None, c=8.0,
             ws=None, stream=None):
@@ -252,3 +269,13 @@ def block_forward(x, W_in, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, la
     rglru_block_fwd(x, W_in, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, W_out,
                     out, h_T, cs_out, ws, c, stream)
     return out, h_T, cs_out
+
+
+def mlp_forward(x, W_1, W_2, W_3, ws=None, stream=None):
+    """Allocate out (and the workspace unless given), run gated_mlp_fwd."""
+    B, T, D = x.shape
+    out = torch.empty_like(x)
+    if ws is None:
+        ws = workspace(mlp_fwd_workspace_bytes(B, T, D, W_1.shape[0], x.dtype), x.device)
+    gated_mlp_fwd(x, W_1, W_2, W_3, out, ws, stream)
+    return out

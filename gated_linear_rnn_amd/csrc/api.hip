@@ -229,6 +229,29 @@ int block_shape_status(int B, int T, int D, int R) {
   return RGLRU_OK;
 }
 
+// ------------------------------------------------------------------ gated MLP block
+int mlp_shape_status(int B, int T, int D, int MD) {
+  if (B <= 0 || T <= 0 || D <= 0 || MD <= 0) return RGLRU_EINVAL;
+  if (D % 64 != 0 || MD % 64 != 0) return RGLRU_ESHAPE;
+  const int64_t M = int64_t(B) * T;
+  if (M * D >= (int64_t(1) << 31) || M * MD >= (int64_t(1) << 31)) return RGLRU_ESHAPE;
+  if (int64_t(MD) * D >= (int64_t(1) << 31)) return RGLRU_ESHAPE;
+  return RGLRU_OK;
+}
+
+// bf16: h [M, MD] bf16.  fp32: q1 (then h in place) and q2, [M, MD] fp32 each.
+struct MlpWs {
+  void* h;
+  float* q2;
+};
+MlpWs carve_mlp(Carver& cv, int B, int T, int MD, rglru_dtype io) {
+  const size_t n = size_t(B) * T * MD;
+  MlpWs w;
+  w.h = cv.take<unsigned char>(n * io_bytes(io));
+  w.q2 = io == RGLRU_F32 ? cv.take<float>(n) : nullptr;
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -642,6 +665,51 @@ int rglru_block_fwd(int B, int T, int D, int R, rglru_dtype io, float c, const v
     po.lda = R; po.ldb = R; po.ldc = D; po.C = static_cast<float*>(out);
     RG_CHECK(launch_plain_gemm_f32(po, stream));
   }
+  return RGLRU_OK;
+}
+
+size_t gated_mlp_fwd_workspace_bytes(int B, int T, int D, int MD, rglru_dtype io) {
+  if (mlp_shape_status(B, T, D, MD) != RGLRU_OK || !io_ok(io)) return 0;
+  Carver cv(nullptr);
+  carve_mlp(cv, B, T, MD, io);
+  return cv.used;
+}
+
+int gated_mlp_fwd(int B, int T, int D, int MD, rglru_dtype io, const void* x, const void* W_1,
+                  const void* W_2, const void* W_3, void* out, void* ws, size_t ws_bytes,
+                  hipStream_t stream) {
+  int st = mlp_shape_status(B, T, D, MD);
+  if (st != RGLRU_OK) return st;
+  if (!io_ok(io)) return RGLRU_EDTYPE;
+  if (!x || !W_1 || !W_2 || !W_3 || !out) return RGLRU_EINVAL;
+  for (const void* p : {x, W_1, W_2, W_3, (const void*)out, (const void*)ws})
+    if (p && !aligned16(p)) return RGLRU_EINVAL;
+  if (!ws || ws_bytes < gated_mlp_fwd_workspace_bytes(B, T, D, MD, io)) return RGLRU_EWORKSPACE;
+  Carver cv(ws);
+  MlpWs w = carve_mlp(cv, B, T, MD, io);
+  const int M = B * T;
+  if (io == RGLRU_BF16) {
+    GegluGemmArgs g1{};
+    g1.A = x; g1.W1 = W_1; g1.W2 = W_2; g1.M = M; g1.N = MD; g1.K = D; g1.H = w.h;
+    RG_CHECK(launch_geglu_gemm_bf16(g1, stream));
+    BlockGemmArgs g3{};
+    g3.A = w.h; g3.Bm = W_3; g3.M = M; g3.N = D; g3.K = MD; g3.ldc = D;
+    g3.C = out; g3.G = nullptr; g3.split = 0;
+    RG_CHECK(launch_block_gemm_bf16(g3, stream));
+    return RGLRU_OK;
+  }
+  float* q1 = static_cast<float*>(w.h);
+  PlainGemmArgs pa{};
+  pa.A = x; pa.Bm = W_1; pa.M = M; pa.N = MD; pa.K = D; pa.lda = D; pa.ldb = D; pa.ldc = MD;
+  pa.C = q1;
+  RG_CHECK(launch_plain_gemm_f32(pa, stream));
+  pa.Bm = W_2; pa.C = w.q2;
+  RG_CHECK(launch_plain_gemm_f32(pa, stream));
+  RG_CHECK(launch_geglu_f32(q1, w.q2, q1, size_t(M) * MD, stream));
+  PlainGemmArgs po{};
+  po.A = q1; po.Bm = W_3; po.M = M; po.N = D; po.K = MD; po.lda = MD; po.ldb = MD; po.ldc = D;
+  po.C = static_cast<float*>(out);
+  RG_CHECK(launch_plain_gemm_f32(po, stream));
   return RGLRU_OK;
 }
 

@@ -1,9 +1,11 @@
-// Elementwise steps of the recurrent block for fp32 I/O (Griffin model-architecture page,
-// section "Recurrent block", Fig. 2(c)): the two input linears arrive as one [M, 2R]
-// product; its first R columns are the branch input p, GeLU of the other R columns is the
-// multiplier g; after the temporal branch, z = y g feeds the output linear.  The bf16 path
-// fuses both steps into the matrix-core kernels (the input-linear GEMM epilogue and the
-// fused RG-LRU kernel), so these only serve the fp32 reference-precision path.
+// Elementwise steps of the recurrent block and of the gated MLP block for fp32 I/O
+// (Griffin model-architecture page, sections "Recurrent block", Fig. 2(c), and "MLP block",
+// Fig. 2(b)).  In the recurrent block the two input linears arrive as one [M, 2R] product:
+// its first R columns are the branch input p, GeLU of the other R columns is the
+// multiplier g; after the temporal branch, z = y g feeds the output linear.  In the MLP the
+// product GeLU(q1) q2 of its two branch outputs feeds its last linear.  The bf16 path fuses
+// these steps into the matrix-core kernels (GEMM epilogues and the fused RG-LRU kernel), so
+// these only serve the fp32 reference-precision path.
 #include "kernels.h"
 #include "rglru_device.h"
 
@@ -30,6 +32,15 @@ __global__ __launch_bounds__(256) void mul_f32_kernel(float* __restrict__ y,
     y[o] = y[o] * g[o];
 }
 
+// h[i] = RNE_f32(GeLU(q1[i]) * q2[i]), the product evaluated in fp64
+__global__ __launch_bounds__(256) void geglu_f32_kernel(const float* __restrict__ q1,
+                                                        const float* __restrict__ q2,
+                                                        float* __restrict__ h, size_t n) {
+  for (size_t o = size_t(blockIdx.x) * blockDim.x + threadIdx.x; o < n;
+       o += size_t(gridDim.x) * blockDim.x)
+    h[o] = float(gelu_d(double(q1[o])) * double(q2[o]));
+}
+
 static int grid_for(size_t n) {
   const size_t blocks = (n + 255) / 256;
   return int(blocks > 8192 ? 8192 : blocks);
@@ -42,6 +53,11 @@ hipError_t launch_split_gelu_f32(const float* pq, int M, int R, float* p, float*
 
 hipError_t launch_mul_f32(float* y, const float* g, size_t n, hipStream_t s) {
   mul_f32_kernel<<<grid_for(n), 256, 0, s>>>(y, g, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_geglu_f32(const float* q1, const float* q2, float* h, size_t n, hipStream_t s) {
+  geglu_f32_kernel<<<grid_for(n), 256, 0, s>>>(q1, q2, h, n);
   return hipGetLastError();
 }
 

@@ -21,7 +21,9 @@ namespace rglru {
 // kModePlain: fp32 C (+ addend).  kModeInProj: the two input linears of the recurrent
 // block, N = 2R columns; columns [0, R) are written to C16 as bf16 (the branch input p),
 // columns [R, 2R) go through GeLU and to G16 as bf16.  kModeOut: bf16 C16.
-enum : int { kModePlain = 3, kModeInProj = 4, kModeOut = 5 };
+// kModeGeglu (gate tile: B0 rows and the same B1 rows paired): the first layer of the
+// gated MLP block, C16 = RNE(GeLU(A B0^T) * (A B1^T)).
+enum : int { kModePlain = 3, kModeInProj = 4, kModeOut = 5, kModeGeglu = 6 };
 
 struct GemmParams {
   const bf16_t* A;
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(C::NW * 64, C::NW >= 8 ? 2 : 1) void gemm_bf16_kern
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int MT = (p.M + C::BM - 1) / C::BM;
-  constexpr bool kPlainTile = MODE >= kModePlain;
+  constexpr bool kPlainTile = C::PLAIN;   // plain tiles span BNR columns, gate tiles BC channels
   const int NT = kPlainTile ? (p.N + C::BNR - 1) / C::BNR : (p.N + C::BC - 1) / C::BC;
   int tm, tn;
   tile_coords(MT, NT, tm, tn);
@@ -142,6 +144,40 @@ __global__ __launch_bounds__(C::NW * 64, C::NW >= 8 ? 2 : 1) void gemm_bf16_kern
       const uint4 val = *reinterpret_cast<const uint4*>(st + r * 64 + ((ck ^ (((r >> 2) & 1) << 2)) * 8));
       if (m < p.M && n < p.N) *reinterpret_cast<uint4*>(dst0 + size_t(m) * p.ldc + n) = val;
     }
+  } else if (MODE == kModeGeglu) {
+    // The workgroup's 256 x 128 bf16 output tile is assembled in LDS (the idle operand
+    // ring), then written as whole 256-byte rows, 16 bytes per lane.  A tile row is 16
+    // chunks of 16 bytes; rows r and r + 4 (the two lane halves of one accumulator write)
+    // sit 64 bytes apart in the bank space (chunk XOR 4) so their 2-byte writes use
+    // disjoint banks.
+    constexpr int HALF = C::NF / 2;
+    constexpr int CPR16 = C::BC / 8;                   // 16-byte chunks per tile row
+    static_assert(C::BM * C::BC * 2 <= C::LDS_BYTES && CPR16 == 16, "staging");
+    __syncthreads();   // every wave is done reading the last operand stage
+    bf16_t* st = reinterpret_cast<bf16_t*>(lds);
+#pragma unroll
+    for (int jc = 0; jc < HALF; ++jc) {
+      const int cl = wn * (C::BC / C::WN) + jc * 32 + col;   // channel within the tile
+#pragma unroll
+      for (int mf = 0; mf < C::MF; ++mf)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = wm * C::WTM + mf * 32 + acc_row(v, lane);
+          const int chunk = (cl >> 3) ^ (((r >> 2) & 1) << 2);
+          const float val = gelu_f(acc[mf][jc][v]) * acc[mf][jc + HALF][v];
+          st[r * C::BC + chunk * 8 + (cl & 7)] = f2bf(val);
+        }
+    }
+    __syncthreads();
+    constexpr int kIters = C::BM * CPR16 / (C::NW * 64);
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const int idx = it * C::NW * 64 + int(threadIdx.x);
+      const int r = idx / CPR16, ck = idx % CPR16;
+      const int m = m0 + r, n = n0 + ck * 8;
+      const uint4 val = *reinterpret_cast<const uint4*>(st + r * C::BC + ((ck ^ (((r >> 2) & 1) << 2)) * 8));
+      if (m < p.M && n < p.N) *reinterpret_cast<uint4*>(p.C16 + size_t(m) * p.ldc + n) = val;
+    }
   } else {
     constexpr int HALF = C::NF / 2;
 #pragma unroll
@@ -181,7 +217,9 @@ typedef GemmCfg<256, 128, 2, 4, true, 64, 2> CfgPlain;
 template <class C, int MODE, bool DUAL>
 static hipError_t run_bf16(const GemmParams& p, hipStream_t s) {
   const int MT = (p.M + C::BM - 1) / C::BM;
-  const int NT = MODE >= kModePlain ? (p.N + C::BNR - 1) / C::BNR : (p.N + C::BC - 1) / C::BC;
+  const int NT = C::PLAIN ? (p.N + C::BNR - 1) / C::BNR : (p.N + C::BC - 1) / C::BC;
+  static_assert(C::PLAIN == (MODE == kModePlain || MODE == kModeInProj || MODE == kModeOut),
+                "plain-tile modes run on plain configurations");
   gemm_bf16_kernel<C, MODE, DUAL><<<MT * NT, C::NW * 64, 0, s>>>(p);
   return hipGetLastError();
 }
@@ -225,6 +263,17 @@ hipError_t launch_block_gemm_bf16(const BlockGemmArgs& g, hipStream_t s) {
   p.split = g.split;
   if (g.G) return run_bf16<CfgPlain, kModeInProj, false>(p, s);
   return run_bf16<CfgPlain, kModeOut, false>(p, s);
+}
+
+hipError_t launch_geglu_gemm_bf16(const GegluGemmArgs& g, hipStream_t s) {
+  GemmParams p{};
+  p.A = static_cast<const bf16_t*>(g.A);
+  p.B0 = static_cast<const bf16_t*>(g.W1);
+  p.B1 = static_cast<const bf16_t*>(g.W2);
+  p.M = g.M; p.N = g.N; p.K = g.K;
+  p.lda = g.K; p.ldb = g.K; p.ldc = g.N;
+  p.C16 = static_cast<bf16_t*>(g.H);
+  return run_bf16<CfgGate, kModeGeglu, false>(p, s);
 }
 
 // ---------------------------------------------------------------- fp32 VALU GEMM

@@ -94,6 +94,17 @@ struct BlockGemmArgs {
 };
 hipError_t launch_block_gemm_bf16(const BlockGemmArgs& g, hipStream_t s);
 
+// First layer of the gated MLP block, bf16: H[M, N] = RNE(GeLU(A W1^T) * (A W2^T)) with
+// A [M, K], W1, W2 [N, K] (row strides K, N).
+struct GegluGemmArgs {
+  const void* A;
+  const void* W1;
+  const void* W2;
+  int M, N, K;
+  void* H;
+};
+hipError_t launch_geglu_gemm_bf16(const GegluGemmArgs& g, hipStream_t s);
+
 hipError_t launch_gate_gemm_bf16(const GateGemmArgs& g, int epi, hipStream_t s);   // kEpiAB, kEpiRI
 hipError_t launch_plain_gemm_bf16(const PlainGemmArgs& g, hipStream_t s);
 hipError_t launch_plain_gemm_f32(const PlainGemmArgs& g, hipStream_t s);
@@ -106,6 +117,8 @@ hipError_t launch_gate_elementwise_f32(const GateGemmArgs& g, const float* za, c
 // y *= g elementwise.
 hipError_t launch_split_gelu_f32(const float* pq, int M, int R, float* p, float* g, hipStream_t s);
 hipError_t launch_mul_f32(float* y, const float* g, size_t n, hipStream_t s);
+// h[i] = RNE_f32(GeLU(q1[i]) * q2[i]) (GeLU in fp64): the gated MLP's product for fp32 I/O
+hipError_t launch_geglu_f32(const float* q1, const float* q2, float* h, size_t n, hipStream_t s);
 
 // ---------------------------------------------------------------- lru.hip
 // The fused RG-LRU layer (gate GEMM + log-space gates + chunked scan) for bf16 I/O.

@@ -215,6 +215,25 @@ int rglru_block_fwd(int B, int T, int D, int R, rglru_dtype io, float c, const v
                     const void* W_out, void* out, float* h_T, void* conv_state_out, void* ws,
                     size_t ws_bytes, hipStream_t stream);
 
+/* Workspace bytes gated_mlp_fwd needs (0 for invalid arguments). */
+size_t gated_mlp_fwd_workspace_bytes(int B, int T, int D, int MD, rglru_dtype io);
+
+/*
+ * Forward of the gated MLP block (the Griffin model-architecture page, section "MLP block",
+ * Fig. 2(b)): two linear layers D -> MD on the same input (MD = M*D, expansion M = 3 on
+ * the pages), GeLU on the first branch, an elementwise product, and a linear layer MD -> D:
+ *   h = RNE_io( GeLU(x W_1^T) * (x W_2^T) ),  GeLU(q) = q Phi(q) (exact),
+ *   out = RNE_io( h W_3^T ).
+ * No biases.  The two branch outputs are not rounded on their own (for bf16 I/O they stay in
+ * the fp32 accumulators of one matrix-core GEMM whose epilogue forms h).
+ *   x [B,T,D] io; W_1, W_2 [MD,D] io ([out,in]); W_3 [D,MD] io; out [B,T,D] io (output).
+ *   Shapes: D % 64 == 0, MD % 64 == 0, B*T*max(D,MD) < 2^31; otherwise RGLRU_ESHAPE.
+ *   Results are bitwise reproducible run to run.
+ */
+int gated_mlp_fwd(int B, int T, int D, int MD, rglru_dtype io, const void* x, const void* W_1,
+                  const void* W_2, const void* W_3, void* out, void* ws, size_t ws_bytes,
+                  hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -140,3 +140,25 @@ def test_block_rejects_invalid_arguments(lib):
     assert _block(lib, c=-2.0) == -1
     assert _block(lib, ws=None) == -4
     assert _block(lib, wsb=100) == -4
+
+
+def test_mlp_workspace_query(lib):
+    assert lib.gated_mlp_fwd_workspace_bytes(8, 2048, 2560, 7680, 1) >= 8 * 2048 * 7680 * 2
+    assert lib.gated_mlp_fwd_workspace_bytes(8, 2048, 2560, 7680, 0) >= 8 * 2048 * 7680 * 8
+    assert lib.gated_mlp_fwd_workspace_bytes(1, 1, 64, 100, 1) == 0      # MD % 64
+    assert lib.gated_mlp_fwd_workspace_bytes(1, 1, 100, 64, 1) == 0      # D % 64
+    assert lib.gated_mlp_fwd_workspace_bytes(1 << 12, 1 << 10, 64, 1024, 1) == 0   # B*T*MD >= 2^31
+
+
+@no_gpu
+def test_mlp_rejects_invalid_arguments(lib):
+    def call(B=1, T=4, D=64, MD=192, io=1, x=A, W1=A, W2=A, W3=A, out=A, ws=A, wsb=1 << 40):
+        return lib.gated_mlp_fwd(B, T, D, MD, io, x, W1, W2, W3, out, ws, wsb, None)
+    assert call(T=0) == -1
+    assert call(MD=96) == -2
+    assert call(io=4) == -3
+    for k in ("x", "W1", "W2", "W3", "out"):
+        assert call(**{k: None}) == -1, k
+    assert call(W2=BAD) == -1
+    assert call(ws=None) == -4
+    assert call(wsb=5) == -4
