@@ -53,9 +53,21 @@ the GeLU is not fixed by the pages, W_1 (the first argument) is the GeLU branch;
 branch outputs are not rounded on their own, the product h = RNE(GeLU(x W_1^T) (x W_2^T))
 is (one rounding point, where the product is formed), and the output RNE(h W_3^T).
 
+Local (sliding-window) multi-query attention ([ARCH] "Global multi-query attention" and
+"Local sliding-window attention"; window 1024 from [BLOG] "Griffin: Attention for Recent
+Memory"): H query heads of width 128 (H * 128 = D) share one key head and one value head;
+no absolute position embedding, RoPE on queries and keys; each position attends only to a
+fixed number W of the most recent positions.  Readings: RoPE is the original pairwise form
+of Su et al. - pair (2i, 2i+1) of a head vector at position p is rotated by the angle
+p * 10000^(-2i/128) - applied to every dimension of q and k, p the absolute token index;
+the window holds W positions including the current one, keys s with t - W < s <= t; scores
+are scaled by 1/sqrt(128); the projections carry no bias; with bf16 I/O the rotated q and
+k, the values v, the attention output (heads concatenated) and the block output are
+rounded to bf16.
+
 Parity pins: every function here is pinned by a test against closed forms, invariants,
 brute force or library routines (tests/test_oracle_pins.py, tests/test_oracle_grad.py,
-tests/test_oracle_block.py, tests/test_oracle_mlp.py).
+tests/test_oracle_block.py, tests/test_oracle_mlp.py, tests/test_oracle_mqa.py).
 """
 from __future__ import annotations
 
@@ -373,4 +385,86 @@ def gated_mlp_forward(x, W_1, W_2, W_3, io, keep=False):
     out = round_io(h @ np.asarray(W_3, dtype=np.float64).T, io)
     if keep:
         return {"out": out, "h": h}
+    return out
+
+
+# ----------------------------------------------------------------------------------
+# Local multi-query attention (the second temporal-mixing block)
+# ----------------------------------------------------------------------------------
+HEAD_DIM = 128          # [ARCH] "Global multi-query attention": fixed head width
+ROPE_BASE = 10000.0     # RoPE frequency base of Su et al.
+
+
+def rope(v, positions, base=ROPE_BASE) -> np.ndarray:
+    """Rotary position embedding: for each head vector v[..., t, (h,) :] at absolute
+    position positions[t], pair (2i, 2i+1) is rotated by the angle positions[t] * theta_i,
+    theta_i = base^(-2i/d), d the last dimension.
+
+    v [B, T, d] or [B, T, H, d]; positions [T] (integers).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    d = v.shape[-1]
+    theta = base ** (-np.arange(0, d, 2, dtype=np.float64) / d)          # [d/2]
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * theta[None, :]   # [T, d/2]
+    if v.ndim == 4:
+        ang = ang[:, None, :]
+    cos, sin = np.cos(ang), np.sin(ang)
+    even, odd = v[..., 0::2], v[..., 1::2]
+    out = np.empty_like(v)
+    out[..., 0::2] = even * cos - odd * sin
+    out[..., 1::2] = even * sin + odd * cos
+    return out
+
+
+def local_mqa_attention(q, k, v, window, q_pos=None, kv_pos=None) -> np.ndarray:
+    """Sliding-window multi-query attention.
+
+    q [B, T, H, d] (H heads); k, v [B, S, d] (the one shared key/value head).  q_pos [T] and
+    kv_pos [S] are absolute positions (default 0..T-1 and 0..S-1).  Query t attends to the
+    keys s with q_pos[t] - window < kv_pos[s] <= q_pos[t], with weights
+    softmax_s(q_t . k_s / sqrt(d)).  Returns [B, T, H, d]; a query with no key in its window
+    gets zeros.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, T, H, d = q.shape
+    S = k.shape[1]
+    qp = np.arange(T) if q_pos is None else np.asarray(q_pos)
+    kp = np.arange(S) if kv_pos is None else np.asarray(kv_pos)
+    allowed = (kp[None, :] <= qp[:, None]) & (kp[None, :] > qp[:, None] - window)   # [T, S]
+    out = np.zeros((B, T, H, d))
+    for b in range(B):
+        scores = np.einsum("thd,sd->ths", q[b], k[b]) / np.sqrt(d)        # [T, H, S]
+        scores = np.where(allowed[:, None, :], scores, -np.inf)
+        mx = scores.max(axis=-1, keepdims=True)
+        mx = np.where(np.isfinite(mx), mx, 0.0)
+        w = np.exp(scores - mx)
+        den = w.sum(axis=-1, keepdims=True)
+        w = np.divide(w, den, out=np.zeros_like(w), where=den > 0)
+        out[b] = np.einsum("ths,sd->thd", w, v[b])
+    return out
+
+
+def local_mqa_forward(x, W_q, W_k, W_v, W_o, window, io, pos0=0, keep=False):
+    """The local-MQA temporal-mixing block on x [B, T, D] at absolute positions
+    pos0 .. pos0+T-1: q = x W_q^T split into H = D/128 heads, k = x W_k^T, v = x W_v^T
+    (one head each), RoPE on q and k, sliding-window attention, heads concatenated, then
+    x_out = attn W_o^T.  W_q [D, D], W_k, W_v [128, D], W_o [D, D], all [out, in].
+    Returns out [B, T, D]; with keep=True a dict with q, k (rotated), v and attn too.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    B, T, D = x.shape
+    H = D // HEAD_DIM
+    pos = pos0 + np.arange(T)
+    q = (x @ np.asarray(W_q, dtype=np.float64).T).reshape(B, T, H, HEAD_DIM)
+    k = x @ np.asarray(W_k, dtype=np.float64).T
+    v = x @ np.asarray(W_v, dtype=np.float64).T
+    qr = round_io(rope(q, pos), io)
+    kr = round_io(rope(k, pos), io)
+    vr = round_io(v, io)
+    attn = round_io(local_mqa_attention(qr, kr, vr, window, pos, pos).reshape(B, T, D), io)
+    out = round_io(attn @ np.asarray(W_o, dtype=np.float64).T, io)
+    if keep:
+        return {"out": out, "q": qr, "k": kr, "v": vr, "attn": attn}
     return out

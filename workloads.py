@@ -163,3 +163,18 @@ def make_mlp_inputs(w: Workload, expansion: int = 3) -> dict:
             "W_1": _normal(rng, (MD, D), 1.0 / np.sqrt(D), w.io),
             "W_2": _normal(rng, (MD, D), 1.0 / np.sqrt(D), w.io),
             "W_3": _normal(rng, (D, MD), 1.0 / np.sqrt(MD), w.io)}
+
+
+def make_mqa_inputs(w: Workload, window: int = 1024) -> dict:
+    """Inputs of the local-MQA block at model width D = w.D (H = D / 128 heads) from
+    default_rng(w.seed + 15485863) in this order: x [B,T,D] ~ N(0,1), W_q [D, D],
+    W_k, W_v [128, D] ~ N(0, 1/D) (LeCun, fan_in = D), W_o [D, D] ~ N(0, 1/D).  All io-exact
+    fp32; ``window`` is the attention window (1024 on the pages)."""
+    D = w.D
+    rng = np.random.default_rng(w.seed + 15485863)
+    return {"workload": w, "window": int(window),
+            "x": _normal(rng, (w.B, w.T, D), 1.0, w.io),
+            "W_q": _normal(rng, (D, D), 1.0 / np.sqrt(D), w.io),
+            "W_k": _normal(rng, (128, D), 1.0 / np.sqrt(D), w.io),
+            "W_v": _normal(rng, (128, D), 1.0 / np.sqrt(D), w.io),
+            "W_o": _normal(rng, (D, D), 1.0 / np.sqrt(D), w.io)}
