@@ -204,6 +204,7 @@ def main():
         out["recurrent_block_fwd"] = bench_block(g, torch, np, workloads)
         out["prefill_decode_latency"] = bench_latency(g, torch, np, workloads)
         out["gated_mlp_fwd"] = bench_mlp(g, torch, np, workloads)
+        out["local_mqa_fwd"] = bench_mqa(g, torch, np, workloads)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, np)
     print(json.dumps(out))
@@ -367,6 +368,40 @@ def bench_mlp(g, torch, np, workloads, steps=30):
     return {"workload": f"mlp_fwd_bf16_B{B}_T{T}_D{D}_MD{MD}", "ms_per_step": ms,
             "tokens_per_s": M / (ms * 1e-3), "TFLOPs": flop / (ms * 1e-3) / 1e12,
             "flop_per_step": flop, "steps": steps}
+
+
+def bench_mqa(g, torch, np, workloads, steps=30, window=1024):
+    """local_mqa_fwd (q/k/v projections with RoPE, sliding-window attention, output
+    projection) at B=8, T=2048, D=2560 (20 heads of 128), window 1024, bf16."""
+    w = workloads.TRAIN_FWD
+    p = workloads.make_mqa_inputs(w, window)
+    bf = torch.bfloat16
+    dev = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dt)
+    B, T, D = w.B, w.T, w.D
+    x = dev(p["x"], bf)
+    Wqkv = dev(np.concatenate([p["W_q"], p["W_k"], p["W_v"]]), bf)
+    Wo = dev(p["W_o"], bf)
+    out = torch.empty_like(x)
+    ws = g.workspace(g.mqa_fwd_workspace_bytes(B, T, D, bf))
+    _log("local MQA")
+    run = lambda: g.local_mqa_fwd(x, Wqkv, Wo, out, None, None, ws, window, 0)
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    M, H = B * T, D // 128
+    pairs = B * H * sum(min(t + 1, window) for t in range(T))     # (query, key) pairs
+    attn_flop = 4.0 * 128 * pairs
+    flop = 2.0 * M * D * (D + 256) + attn_flop + 2.0 * M * D * D
+    return {"workload": f"mqa_fwd_bf16_B{B}_T{T}_D{D}_H{H}_W{window}", "ms_per_step": ms,
+            "tokens_per_s": M / (ms * 1e-3), "TFLOPs": flop / (ms * 1e-3) / 1e12,
+            "flop_per_step": flop, "attention_flop": attn_flop, "steps": steps}
 
 
 def bench_latency(g, torch, np, workloads):

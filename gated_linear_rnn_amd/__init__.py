@@ -1,5 +1,6 @@
 """MI355X (gfx950) RG-LRU temporal branch: causal Conv1D (width 4) -> RG-LRU, and the
-recurrent block around it (input linears, GeLU branch, output linear) and the gated MLP block.
+recurrent block around it (input linears, GeLU branch, output linear), the gated MLP block and
+the local (sliding-window) multi-query attention block.
 
 The compute path is librglru.so (hand-written HIP kernels behind a C ABI, declared in
 include/rglru.h); this package is its thin ctypes binding.  Importing the package does not
@@ -9,6 +10,7 @@ from ._binding import (EXPORTS, LIB_PATH, RGLRU_BF16, RGLRU_F32, RgluError,  # n
                        backward, block_forward, block_fwd_workspace_bytes, bwd_workspace_bytes,
                        conv1d_causal4, decode_workspace_bytes,
                        forward, fwd_workspace_bytes, gated_mlp_fwd, io_code, load,
-                       mlp_forward, mlp_fwd_workspace_bytes, rglru_block_fwd, rglru_bwd,
+                       local_mqa_fwd, mlp_forward, mlp_fwd_workspace_bytes, mqa_forward,
+                       mqa_fwd_workspace_bytes, rglru_block_fwd, rglru_bwd,
                        rglru_decode_step, rglru_fwd, rglru_gates, rglru_lru, rglru_scan,
                        lru_workspace_bytes, scan_workspace_bytes, status_string, workspace)

@@ -23,7 +23,8 @@ EXPORTS = ("rglru_status_string", "conv1d_causal4", "rglru_fwd_workspace_bytes",
            "rglru_scan",
            "rglru_decode_workspace_bytes", "rglru_decode_step", "rglru_bwd_workspace_bytes",
            "rglru_bwd", "rglru_block_fwd_workspace_bytes", "rglru_block_fwd",
-           "gated_mlp_fwd_workspace_bytes", "gated_mlp_fwd")
+           "gated_mlp_fwd_workspace_bytes", "gated_mlp_fwd", "local_mqa_fwd_workspace_bytes",
+           "local_mqa_fwd")
 
 _lib = None
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -75,6 +76,10 @@ def load(path: str = LIB_PATH):
     lib.gated_mlp_fwd_workspace_bytes.restype = _Z
     lib.gated_mlp_fwd.argtypes = [_I, _I, _I, _I, _I] + [_P] * 5 + [_P, _Z, _P]
     lib.gated_mlp_fwd.restype = _I
+    lib.local_mqa_fwd_workspace_bytes.argtypes = [_I, _I, _I, _I]
+    lib.local_mqa_fwd_workspace_bytes.restype = _Z
+    lib.local_mqa_fwd.argtypes = [_I, _I, _I, _I, _I, _I] + [_P] * 6 + [_P, _Z, _P]
+    lib.local_mqa_fwd.restype = _I
     _lib = lib
     return lib
 
@@ -131,6 +136,10 @@ def block_fwd_workspace_bytes(B, T, D, R, dtype) -> int:
 
 def mlp_fwd_workspace_bytes(B, T, D, MD, dtype) -> int:
     return int(load().gated_mlp_fwd_workspace_bytes(B, T, D, MD, io_code(dtype)))
+
+
+def mqa_fwd_workspace_bytes(B, T, D, dtype) -> int:
+    return int(load().local_mqa_fwd_workspace_bytes(B, T, D, io_code(dtype)))
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
@@ -221,6 +230,14 @@ def gated_mlp_fwd(x, W_1, W_2, W_3, out, ws, stream=None):
            "gated_mlp_fwd")
 
 
+def local_mqa_fwd(x, W_qkv, W_o, out, k_out, v_out, ws, window=1024, pos0=0, stream=None):
+    B, T, D = x.shape
+    _check(load().local_mqa_fwd(B, T, D, io_code(x.dtype), int(window), int(pos0), _ptr(x),
+                                _ptr(W_qkv), _ptr(W_o), _ptr(out), _ptr(k_out), _ptr(v_out),
+                                _ptr(ws), ws.numel(), _stream(stream)),
+           "local_mqa_fwd")
+
+
 # ------------------------------------------------------------------ allocating helpers
 def forward(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0=None, c=8.0,
             ws=None, stream=None):
@@ -279,3 +296,15 @@ def mlp_forward(x, W_1, W_2, W_3, ws=None, stream=None):
         ws = workspace(mlp_fwd_workspace_bytes(B, T, D, W_1.shape[0], x.dtype), x.device)
     gated_mlp_fwd(x, W_1, W_2, W_3, out, ws, stream)
     return out
+
+
+def mqa_forward(x, W_qkv, W_o, window=1024, pos0=0, with_kv=False, ws=None, stream=None):
+    """Allocate out (and k, v when with_kv; the workspace unless given), run local_mqa_fwd."""
+    B, T, D = x.shape
+    out = torch.empty_like(x)
+    k = torch.empty((B, T, 128), dtype=x.dtype, device=x.device) if with_kv else None
+    v = torch.empty((B, T, 128), dtype=x.dtype, device=x.device) if with_kv else None
+    if ws is None:
+        ws = workspace(mqa_fwd_workspace_bytes(B, T, D, x.dtype), x.device)
+    local_mqa_fwd(x, W_qkv, W_o, out, k, v, ws, window, pos0, stream)
+    return (out, k, v) if with_kv else out

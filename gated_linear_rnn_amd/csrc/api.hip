@@ -252,6 +252,34 @@ MlpWs carve_mlp(Carver& cv, int B, int T, int MD, rglru_dtype io) {
   return w;
 }
 
+// ------------------------------------------------------------------ local MQA block
+constexpr int kHeadDim = 128;
+
+int mqa_shape_status(int B, int T, int D, int window, int pos0) {
+  if (B <= 0 || T <= 0 || D <= 0 || window <= 0 || pos0 < 0) return RGLRU_EINVAL;
+  if (D % kHeadDim != 0) return RGLRU_ESHAPE;
+  const int64_t M = int64_t(B) * T;
+  if (M * (D + 2 * kHeadDim) >= (int64_t(1) << 31)) return RGLRU_ESHAPE;
+  if (int64_t(pos0) + T >= (int64_t(1) << 30)) return RGLRU_ESHAPE;
+  return RGLRU_OK;
+}
+
+struct MqaWs {
+  void* q;
+  void* k;
+  void* v;
+  void* attn;
+};
+MqaWs carve_mqa(Carver& cv, int B, int T, int D, rglru_dtype io) {
+  const size_t M = size_t(B) * T, eb = io_bytes(io);
+  MqaWs w;
+  w.q = cv.take<unsigned char>(M * D * eb);
+  w.k = cv.take<unsigned char>(M * kHeadDim * eb);
+  w.v = cv.take<unsigned char>(M * kHeadDim * eb);
+  w.attn = cv.take<unsigned char>(M * D * eb);
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -710,6 +738,68 @@ int gated_mlp_fwd(int B, int T, int D, int MD, rglru_dtype io, const void* x, co
   po.A = q1; po.Bm = W_3; po.M = M; po.N = D; po.K = MD; po.lda = MD; po.ldb = MD; po.ldc = D;
   po.C = static_cast<float*>(out);
   RG_CHECK(launch_plain_gemm_f32(po, stream));
+  return RGLRU_OK;
+}
+
+size_t local_mqa_fwd_workspace_bytes(int B, int T, int D, rglru_dtype io) {
+  if (mqa_shape_status(B, T, D, 1, 0) != RGLRU_OK || !io_ok(io)) return 0;
+  Carver cv(nullptr);
+  carve_mqa(cv, B, T, D, io);
+  return cv.used;
+}
+
+int local_mqa_fwd(int B, int T, int D, rglru_dtype io, int window, int pos0, const void* x,
+                  const void* W_qkv, const void* W_o, void* out, void* k_out, void* v_out,
+                  void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = mqa_shape_status(B, T, D, window, pos0);
+  if (st != RGLRU_OK) return st;
+  if (!io_ok(io)) return RGLRU_EDTYPE;
+  if (!x || !W_qkv || !W_o || !out) return RGLRU_EINVAL;
+  for (const void* p : {x, W_qkv, W_o, (const void*)out, (const void*)k_out, (const void*)v_out,
+                        (const void*)ws})
+    if (p && !aligned16(p)) return RGLRU_EINVAL;
+  if (!ws || ws_bytes < local_mqa_fwd_workspace_bytes(B, T, D, io)) return RGLRU_EWORKSPACE;
+  Carver cv(ws);
+  MqaWs w = carve_mqa(cv, B, T, D, io);
+  if (k_out) w.k = k_out;
+  if (v_out) w.v = v_out;
+  const int M = B * T;
+  const bool bf = io == RGLRU_BF16;
+  if (bf) {
+    QkvGemmArgs g{};
+    g.A = x; g.W = W_qkv; g.M = M; g.D = D; g.T = T; g.pos0 = pos0;
+    g.q = w.q; g.k = w.k; g.v = w.v;
+    RG_CHECK(launch_qkv_gemm_bf16(g, stream));
+  } else {
+    const float* W = static_cast<const float*>(W_qkv);
+    PlainGemmArgs pa{};
+    pa.A = x; pa.M = M; pa.K = D; pa.lda = D; pa.ldb = D;
+    pa.Bm = W; pa.N = D; pa.ldc = D; pa.C = static_cast<float*>(w.q);
+    RG_CHECK(launch_plain_gemm_f32(pa, stream));
+    pa.Bm = W + size_t(D) * D; pa.N = kHeadDim; pa.ldc = kHeadDim; pa.C = static_cast<float*>(w.k);
+    RG_CHECK(launch_plain_gemm_f32(pa, stream));
+    pa.Bm = W + size_t(D + kHeadDim) * D; pa.C = static_cast<float*>(w.v);
+    RG_CHECK(launch_plain_gemm_f32(pa, stream));
+    RG_CHECK(launch_rope_f32(static_cast<float*>(w.q), M, D, T, pos0, stream));
+    RG_CHECK(launch_rope_f32(static_cast<float*>(w.k), M, kHeadDim, T, pos0, stream));
+  }
+  MqaArgs a{};
+  a.q = w.q; a.k = w.k; a.v = w.v; a.o = w.attn;
+  a.B = B; a.T = T; a.S = T; a.H = D / kHeadDim;
+  a.window = window; a.q_pos0 = pos0; a.kv_pos0 = pos0;
+  a.scale_log2 = float(1.4426950408889634 / sqrt(double(kHeadDim)));
+  RG_CHECK(launch_mqa_fwd(a, bf, stream));
+  if (bf) {
+    BlockGemmArgs go{};
+    go.A = w.attn; go.Bm = W_o; go.M = M; go.N = D; go.K = D; go.ldc = D;
+    go.C = out; go.G = nullptr; go.split = 0;
+    RG_CHECK(launch_block_gemm_bf16(go, stream));
+  } else {
+    PlainGemmArgs po{};
+    po.A = w.attn; po.Bm = W_o; po.M = M; po.N = D; po.K = D; po.lda = D; po.ldb = D; po.ldc = D;
+    po.C = static_cast<float*>(out);
+    RG_CHECK(launch_plain_gemm_f32(po, stream));
+  }
   return RGLRU_OK;
 }
 

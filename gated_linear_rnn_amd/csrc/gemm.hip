@@ -22,8 +22,10 @@ namespace rglru {
 // block, N = 2R columns; columns [0, R) are written to C16 as bf16 (the branch input p),
 // columns [R, 2R) go through GeLU and to G16 as bf16.  kModeOut: bf16 C16.
 // kModeGeglu (gate tile: B0 rows and the same B1 rows paired): the first layer of the
-// gated MLP block, C16 = RNE(GeLU(A B0^T) * (A B1^T)).
-enum : int { kModePlain = 3, kModeInProj = 4, kModeOut = 5, kModeGeglu = 6 };
+// gated MLP block, C16 = RNE(GeLU(A B0^T) * (A B1^T)).  kModeQkv: the projections of the
+// local-MQA block, N = D + 256 columns: q = columns [0, D) to C16 (ldc D), k = the next 128
+// to G16, v = the last 128 to V16 (ldc 128); q and k are rotated (RoPE) before rounding.
+enum : int { kModePlain = 3, kModeInProj = 4, kModeOut = 5, kModeGeglu = 6, kModeQkv = 7 };
 
 struct GemmParams {
   const bf16_t* A;
@@ -45,10 +47,20 @@ struct GemmParams {
   // plain epilogue
   float* C;
   const float* addend;
-  bf16_t* C16;        // kModeInProj (p), kModeOut
-  bf16_t* G16;        // kModeInProj (GeLU branch)
-  int split;          // kModeInProj: R
+  bf16_t* C16;        // kModeInProj (p), kModeOut, kModeQkv (q)
+  bf16_t* G16;        // kModeInProj (GeLU branch), kModeQkv (k)
+  bf16_t* V16;        // kModeQkv (v)
+  int split;          // kModeInProj: R; kModeQkv: D
+  int T, pos0;        // kModeQkv: row m is at position pos0 + m % T
 };
+
+// RoPE angle of position pos and frequency theta (radians per position), in turns reduced
+// to [-1/2, 1/2]: the product and the reduction in fp64, so that large positions keep full
+// fp32 accuracy; the hardware sine and cosine (v_sin_f32 / v_cos_f32) take turns.
+__device__ __forceinline__ float rope_turns(int pos, double theta_turns) {
+  const double a = double(pos) * theta_turns;
+  return float(a - rint(a));
+}
 
 // Map the linear workgroup id to a (tile_m, tile_n) pair.  Consecutive workgroup ids are
 // dispatched round-robin over the 8 XCDs; the remap gives every XCD a contiguous range of
@@ -108,7 +120,7 @@ __global__ __launch_bounds__(C::NW * 64, C::NW >= 8 ? 2 : 1) void gemm_bf16_kern
           }
         }
     }
-  } else if (MODE == kModeInProj || MODE == kModeOut) {
+  } else if (MODE == kModeInProj || MODE == kModeOut || MODE == kModeQkv) {
     // bf16 output through LDS: each wave rounds its 128 x 64 block into its own 16 KB of
     // the (now idle) operand ring, then writes whole 128-byte row segments, 16 bytes per
     // lane.  In LDS a block row is 8 chunks of 16 bytes; rows r and r + 4 (the two lane
@@ -120,6 +132,13 @@ __global__ __launch_bounds__(C::NW * 64, C::NW >= 8 ? 2 : 1) void gemm_bf16_kern
     const int nb = n0 + wn * C::WTNR;   // first column of the wave's block
     // the split is a multiple of 64 and so is nb: a block lies on one side of it
     const bool gelu_side = MODE == kModeInProj && nb >= p.split;
+    // kModeQkv: q and k columns are rotated; column pairs (2i, 2i+1) sit in lanes l, l^1
+    const bool rot = MODE == kModeQkv && nb < p.split + 128;
+    double theta[C::NF];   // 10000^(-2i/128) / (2 pi) turns per position, i = pair index
+#pragma unroll
+    for (int f = 0; f < C::NF; ++f)
+      theta[f] = exp2(-double(((nb + f * 32 + col) & 127) >> 1) * (13.287712379549449 / 64.0)) *
+                 0.15915494309189533577;
 #pragma unroll
     for (int mf = 0; mf < C::MF; ++mf)
 #pragma unroll
@@ -128,7 +147,17 @@ __global__ __launch_bounds__(C::NW * 64, C::NW >= 8 ? 2 : 1) void gemm_bf16_kern
         for (int v = 0; v < 16; ++v) {
           const int r = mf * 32 + acc_row(v, lane);
           const int chunk = (f * 4 + (col >> 3)) ^ (((r >> 2) & 1) << 2);
-          const float val = acc[mf][f][v];
+          float val = acc[mf][f][v];
+          if (MODE == kModeQkv) {
+            const float other = __int_as_float(
+                __builtin_amdgcn_mov_dpp(__float_as_int(val), 0xB1, 0xF, 0xF, false));   // lane ^ 1
+            if (rot) {
+              const int m = m0 + wm * C::WTM + r;
+              const float turns = rope_turns(p.pos0 + m % p.T, theta[f]);
+              const float sn = __builtin_amdgcn_sinf(turns), cs = __builtin_amdgcn_cosf(turns);
+              val = (col & 1) ? fmaf(other, sn, val * cs) : fmaf(val, cs, -other * sn);
+            }
+          }
           st[r * 64 + chunk * 8 + (col & 7)] = f2bf(gelu_side ? gelu_f(val) : val);
         }
     // LDS operations of a wave complete in order; the fence keeps the compiler from
@@ -136,13 +165,19 @@ __global__ __launch_bounds__(C::NW * 64, C::NW >= 8 ? 2 : 1) void gemm_bf16_kern
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    bf16_t* const dst0 = gelu_side ? p.G16 - p.split : p.C16;
+    // destination of the block: base pointer (indexed by the global column) and row stride
+    bf16_t* dst0 = gelu_side ? p.G16 - p.split : p.C16;
+    int ldc = p.ldc;
+    if (MODE == kModeQkv && nb >= p.split) {
+      dst0 = nb < p.split + 128 ? p.G16 - p.split : p.V16 - (p.split + 128);
+      ldc = 128;
+    }
 #pragma unroll
     for (int it = 0; it < C::WTM / 8; ++it) {
       const int r = it * 8 + (lane >> 3), ck = lane & 7;
       const int m = m0 + wm * C::WTM + r, n = nb + ck * 8;
       const uint4 val = *reinterpret_cast<const uint4*>(st + r * 64 + ((ck ^ (((r >> 2) & 1) << 2)) * 8));
-      if (m < p.M && n < p.N) *reinterpret_cast<uint4*>(dst0 + size_t(m) * p.ldc + n) = val;
+      if (m < p.M && n < p.N) *reinterpret_cast<uint4*>(dst0 + size_t(m) * ldc + n) = val;
     }
   } else if (MODE == kModeGeglu) {
     // The workgroup's 256 x 128 bf16 output tile is assembled in LDS (the idle operand
@@ -218,7 +253,8 @@ template <class C, int MODE, bool DUAL>
 static hipError_t run_bf16(const GemmParams& p, hipStream_t s) {
   const int MT = (p.M + C::BM - 1) / C::BM;
   const int NT = C::PLAIN ? (p.N + C::BNR - 1) / C::BNR : (p.N + C::BC - 1) / C::BC;
-  static_assert(C::PLAIN == (MODE == kModePlain || MODE == kModeInProj || MODE == kModeOut),
+  static_assert(C::PLAIN == (MODE == kModePlain || MODE == kModeInProj || MODE == kModeOut ||
+                             MODE == kModeQkv),
                 "plain-tile modes run on plain configurations");
   gemm_bf16_kernel<C, MODE, DUAL><<<MT * NT, C::NW * 64, 0, s>>>(p);
   return hipGetLastError();
@@ -263,6 +299,19 @@ hipError_t launch_block_gemm_bf16(const BlockGemmArgs& g, hipStream_t s) {
   p.split = g.split;
   if (g.G) return run_bf16<CfgPlain, kModeInProj, false>(p, s);
   return run_bf16<CfgPlain, kModeOut, false>(p, s);
+}
+
+hipError_t launch_qkv_gemm_bf16(const QkvGemmArgs& g, hipStream_t s) {
+  GemmParams p{};
+  p.A = static_cast<const bf16_t*>(g.A);
+  p.B0 = static_cast<const bf16_t*>(g.W);
+  p.M = g.M; p.N = g.D + 256; p.K = g.D;
+  p.lda = g.D; p.ldb = g.D; p.ldc = g.D;
+  p.C16 = static_cast<bf16_t*>(g.q);
+  p.G16 = static_cast<bf16_t*>(g.k);
+  p.V16 = static_cast<bf16_t*>(g.v);
+  p.split = g.D; p.T = g.T; p.pos0 = g.pos0;
+  return run_bf16<CfgPlain, kModeQkv, false>(p, s);
 }
 
 hipError_t launch_geglu_gemm_bf16(const GegluGemmArgs& g, hipStream_t s) {

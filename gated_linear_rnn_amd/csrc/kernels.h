@@ -105,6 +105,18 @@ struct GegluGemmArgs {
 };
 hipError_t launch_geglu_gemm_bf16(const GegluGemmArgs& g, hipStream_t s);
 
+// Projections of the local-MQA block, bf16: [q k v] = A [W_q; W_k; W_v]^T with W [D + 256, D],
+// q [M, D] and k [M, 128] rotated by RoPE at position pos0 + m % T, v [M, 128].
+struct QkvGemmArgs {
+  const void* A;
+  const void* W;
+  int M, D, T, pos0;
+  void* q;
+  void* k;
+  void* v;
+};
+hipError_t launch_qkv_gemm_bf16(const QkvGemmArgs& g, hipStream_t s);
+
 hipError_t launch_gate_gemm_bf16(const GateGemmArgs& g, int epi, hipStream_t s);   // kEpiAB, kEpiRI
 hipError_t launch_plain_gemm_bf16(const PlainGemmArgs& g, hipStream_t s);
 hipError_t launch_plain_gemm_f32(const PlainGemmArgs& g, hipStream_t s);
@@ -119,6 +131,24 @@ hipError_t launch_split_gelu_f32(const float* pq, int M, int R, float* p, float*
 hipError_t launch_mul_f32(float* y, const float* g, size_t n, hipStream_t s);
 // h[i] = RNE_f32(GeLU(q1[i]) * q2[i]) (GeLU in fp64): the gated MLP's product for fp32 I/O
 hipError_t launch_geglu_f32(const float* q1, const float* q2, float* h, size_t n, hipStream_t s);
+
+// ---------------------------------------------------------------- mqa.hip
+// Sliding-window multi-query attention over rotated q [B,T,H,128], k, v [B,S,128] (io
+// dtype); query t is at absolute position q_pos0 + t, key s at kv_pos0 + s.
+struct MqaArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;                // [B,T,H,128]
+  int B, T, S, H;
+  int window;
+  int q_pos0, kv_pos0;
+  float scale_log2;       // log2(e) / sqrt(128)
+};
+hipError_t launch_mqa_fwd(const MqaArgs& a, bool bf16, hipStream_t s);
+// x [M, ncols] fp32 in place: RoPE on every 128-wide head vector, row m at position
+// pos0 + m % T (fp64 angles)
+hipError_t launch_rope_f32(float* x, int M, int ncols, int T, int pos0, hipStream_t s);
 
 // ---------------------------------------------------------------- lru.hip
 // The fused RG-LRU layer (gate GEMM + log-space gates + chunked scan) for bf16 I/O.

@@ -234,6 +234,36 @@ int gated_mlp_fwd(int B, int T, int D, int MD, rglru_dtype io, const void* x, co
                   const void* W_2, const void* W_3, void* out, void* ws, size_t ws_bytes,
                   hipStream_t stream);
 
+/* Workspace bytes local_mqa_fwd needs (0 for invalid arguments). */
+size_t local_mqa_fwd_workspace_bytes(int B, int T, int D, rglru_dtype io);
+
+/*
+ * Forward of the local (sliding-window) multi-query attention block (the Griffin
+ * model-architecture page, sections "Global multi-query attention" and "Local sliding-window
+ * attention"; window 1024 on the blog page "Griffin's Compromise", section "Griffin:
+ * Attention for Recent Memory"): H = D / 128 query heads of width 128 share one key head
+ * and one value head; RoPE (no absolute position embedding); query t attends to the keys at
+ * the `window` most recent positions up to and including its own:
+ *   [q k v] = x [W_q; W_k; W_v]^T,  q [.., H, 128] and k rotated by RoPE at the absolute
+ *   position pos0 + t (pair (2i, 2i+1) by the angle pos * 10000^(-2i/128)), rounded to io;
+ *   a_t = sum_{s in (t - window, t]} softmax_s(q_t . k_s / sqrt(128)) v_s, per head,
+ *   rounded to io;  out = RNE_io(a W_o^T).
+ * No biases.  For bf16 I/O the projections and both attention products run on the matrix
+ * cores with fp32 accumulation and an online softmax in fp32; for fp32 I/O the projections
+ * accumulate in fp64 and the attention is evaluated in fp64.
+ *   x [B,T,D] io; W_qkv [D + 256, D] io ([out,in]: the D rows of W_q, then the 128 rows of
+ *   W_k, then the 128 rows of W_v); W_o [D,D] io; out [B,T,D] io (output);
+ *   k_out, v_out [B,T,128] io (outputs, nullable): the rotated keys and the values, i.e.
+ *   the key/value cache content of these positions.
+ *   window >= 1; pos0 >= 0 is the absolute position of the first token (RoPE only: the
+ *   attention sees the T tokens of this call).
+ *   Shapes: D % 128 == 0, B*T*(D+256) < 2^31; otherwise RGLRU_ESHAPE.
+ *   Results are bitwise reproducible run to run.
+ */
+int local_mqa_fwd(int B, int T, int D, rglru_dtype io, int window, int pos0, const void* x,
+                  const void* W_qkv, const void* W_o, void* out, void* k_out, void* v_out,
+                  void* ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

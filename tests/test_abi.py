@@ -162,3 +162,25 @@ def test_mlp_rejects_invalid_arguments(lib):
     assert call(W2=BAD) == -1
     assert call(ws=None) == -4
     assert call(wsb=5) == -4
+
+
+def test_mqa_workspace_query(lib):
+    assert lib.local_mqa_fwd_workspace_bytes(8, 2048, 2560, 1) >= 8 * 2048 * (2 * 2560 + 256) * 2
+    assert lib.local_mqa_fwd_workspace_bytes(1, 1, 192, 1) == 0         # D % 128
+    assert lib.local_mqa_fwd_workspace_bytes(1, 1, 128, 9) == 0         # dtype
+
+
+@no_gpu
+def test_mqa_rejects_invalid_arguments(lib):
+    def call(B=1, T=4, D=128, io=1, window=16, pos0=0, x=A, Wqkv=A, Wo=A, out=A, k=None, v=None,
+             ws=A, wsb=1 << 40):
+        return lib.local_mqa_fwd(B, T, D, io, window, pos0, x, Wqkv, Wo, out, k, v, ws, wsb, None)
+    assert call(window=0) == -1
+    assert call(pos0=-1) == -1
+    assert call(D=64) == -2
+    assert call(io=3) == -3
+    for kw in ("x", "Wqkv", "Wo", "out"):
+        assert call(**{kw: None}) == -1, kw
+    assert call(k=BAD) == -1
+    assert call(ws=None) == -4
+    assert call(wsb=7) == -4

@@ -1,0 +1,115 @@
+"""Parity of the local multi-query attention block (local_mqa_fwd: the q/k/v projections with
+RoPE in the GEMM epilogue, the sliding-window attention kernel, the output projection) with
+the oracle's local_mqa_forward (the Griffin model-architecture page, sections "Global
+multi-query attention" and "Local sliding-window attention").
+
+With the recipe's LeCun weights the attention is close to an average over the window, so
+most cases also run with W_q and W_k scaled by 3 (scores 9x larger: sharply peaked weights
+that depend on exactly which keys are in the window) and W_o = I, which makes the block
+output the attention output itself.  The values keep unit scale: the bf16 rounding of the
+weights inside the attention moves the output by about 2^-9 times the spread of the values
+it mixes, which must stay inside the bf16 bar.  The rotated keys and the values the entry point exposes are
+compared too.  Element by element at sizes the oracle finishes in seconds (ragged position
+blocks, head counts that do not fill a head group, windows of 1, 64, 100 and beyond T,
+RoPE offsets), and every output of one full-size sequence.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import TOL, TORCH_IO, dev, err, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(w, window, sharp, gain=3.0):
+    """sharp: W_q and W_k scaled by `gain` (scores gain^2 larger), v left at unit scale, and
+    W_o = I so that the block output is the attention output."""
+    p = workloads.make_mqa_inputs(w, window)
+    if sharp:
+        for name in ("W_q", "W_k"):
+            p[name] = oracle.round_io(p[name] * gain, w.io).astype(np.float32)
+        p["W_o"] = np.eye(w.D, dtype=np.float32)
+    return p
+
+
+def _run(g, p, pos0=0):
+    w = p["workload"]
+    io = TORCH_IO[w.io]
+    Wqkv = np.concatenate([p["W_q"], p["W_k"], p["W_v"]])
+    out, k, v = g.mqa_forward(dev(p["x"], io), dev(Wqkv, io), dev(p["W_o"], io), p["window"], pos0,
+                              with_kv=True)
+    torch.cuda.synchronize()
+    return host(out), host(k), host(v)
+
+
+def _check(g, p, pos0=0, what=""):
+    w = p["workload"]
+    out, k, v = _run(g, p, pos0)
+    o = oracle.local_mqa_forward(p["x"], p["W_q"], p["W_k"], p["W_v"], p["W_o"], p["window"], w.io,
+                                 pos0=pos0, keep=True)
+    eo, ek, ev = err(out, o["out"]), err(k, o["k"]), err(v, o["v"])
+    print(f"{what} io={w.io} B={w.B} T={w.T} D={w.D} W={p['window']} pos0={pos0} "
+          f"err(out)={eo:.3e} err(k)={ek:.3e} err(v)={ev:.3e}", flush=True)
+    assert eo <= TOL[w.io] and ek <= TOL[w.io] and ev <= TOL[w.io]
+
+
+SMALL = [
+    # (workload recipe, B, T, D, window, sharp)
+    (workloads.TINY_F32, 1, 256, 256, 64, True),
+    (workloads.TINY_F32, 2, 100, 128, 1024, True),
+    (workloads.TINY_F32, 1, 70, 256, 1, False),
+    (workloads.TRAIN_FWD, 2, 300, 512, 100, True),
+    (workloads.TRAIN_FWD, 2, 300, 512, 100, False),
+    (workloads.TRAIN_FWD, 1, 1, 128, 1024, True),
+    (workloads.TRAIN_FWD, 1, 700, 256, 1024, True),
+    (workloads.TRAIN_FWD, 3, 200, 640, 64, True),
+    (workloads.TRAIN_FWD, 1, 1500, 384, 1024, True),
+    (workloads.TRAIN_FWD, 1, 130, 128, 1, True),
+]
+
+
+@pytest.mark.parametrize("w,B,T,D,W,sharp", SMALL,
+                         ids=[f"{w.io}-{B}x{T}-D{D}-W{W}-{'sharp' if s else 'init'}"
+                              for w, B, T, D, W, s in SMALL])
+def test_mqa_small_elementwise(lib, w, B, T, D, W, sharp):
+    _check(lib, _inputs(w.with_shape(B=B, T=T, D=D), W, sharp), what=w.name)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_mqa_rope_position_offset(lib, io):
+    """pos0 shifts every RoPE angle (absolute positions of a later chunk); 30000 also checks
+    the angle reduction at large positions."""
+    w = workloads.TRAIN_FWD.with_shape(B=1, T=200, D=256, io=io)
+    _check(lib, _inputs(w, 64, True), pos0=30000, what="pos0")
+
+
+def test_mqa_repeat_is_bitwise_identical(lib):
+    p = _inputs(workloads.TRAIN_FWD.with_shape(B=2, T=500, D=512), 128, True)
+    first = _run(lib, p)
+    for _ in range(2):
+        for a, b in zip(_run(lib, p), first):
+            np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("sharp", [False, True])
+def test_mqa_full_training_shape_one_sequence(lib, sharp):
+    """B=8, T=2048, D=2560 (20 heads), window 1024 in the launch configuration the benchmark
+    times; every output of the last sequence against the oracle on that sequence.  The
+    sharpened case uses gain 2 (scores of standard deviation 4): with gain 3 the logits
+    spread so far (standard deviation 9) that one-ulp differences in the bf16 rounding of q
+    and k (fp32 versus fp64 projection sums over K = 2560) swing near-tied weights by more
+    than the bf16 bar."""
+    w = workloads.TRAIN_FWD
+    p = _inputs(w, 1024, sharp, gain=2.0)
+    out, k, v = _run(lib, p)
+    b = w.B - 1
+    o = oracle.local_mqa_forward(p["x"][b:b + 1], p["W_q"], p["W_k"], p["W_v"], p["W_o"], 1024, "bf16",
+                                 keep=True)
+    eo, ek = err(out[b:b + 1], o["out"]), err(k[b:b + 1], o["k"])
+    print(f"full MQA sharp={sharp} err(out)={eo:.3e} err(k)={ek:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and ek <= TOL["bf16"]
+    assert np.all(np.isfinite(out))
