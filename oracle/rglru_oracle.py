@@ -468,3 +468,39 @@ def local_mqa_forward(x, W_q, W_k, W_v, W_o, window, io, pos0=0, keep=False):
     if keep:
         return {"out": out, "q": qr, "k": kr, "v": vr, "attn": attn}
     return out
+
+
+def local_mqa_decode_step(x_t, W_q, W_k, W_v, W_o, k_cache, v_cache, pos, window, io):
+    """One generation step of the local-MQA block with a bounded key/value cache ([ARCH]
+    "Local sliding-window attention": the cache never holds more than the window).
+
+    x_t [B, D] (the token of each sequence at absolute position pos[b]); k_cache, v_cache
+    [B, window, 128]: slot j holds the rotated key and the value of the most recent
+    position p <= pos[b] with p % window == j (slots of positions below 0 are never read).
+    The step writes the new key and value into slot pos[b] % window, then attends over the
+    cached positions (pos[b] - window, pos[b]].  Returns (out [B, D], new k_cache, new
+    v_cache); the inputs are not modified.
+    """
+    x = np.asarray(x_t, dtype=np.float64)
+    B, D = x.shape
+    H = D // HEAD_DIM
+    pos = np.asarray(pos, dtype=np.int64)
+    kc = np.array(k_cache, dtype=np.float64, copy=True)
+    vc = np.array(v_cache, dtype=np.float64, copy=True)
+    attn = np.zeros((B, D))
+    for b in range(B):
+        p = int(pos[b])
+        q = (x[b] @ np.asarray(W_q, dtype=np.float64).T).reshape(1, 1, H, HEAD_DIM)
+        k = (x[b] @ np.asarray(W_k, dtype=np.float64).T).reshape(1, 1, HEAD_DIM)
+        v = (x[b] @ np.asarray(W_v, dtype=np.float64).T).reshape(1, 1, HEAD_DIM)
+        qr = round_io(rope(q, [p]), io)
+        kc[b, p % window] = round_io(rope(k, [p]), io)[0, 0]
+        vc[b, p % window] = round_io(v, io)[0, 0]
+        slots = np.arange(window)
+        slot_pos = p - ((p - slots) % window)          # the position each slot holds
+        live = slot_pos >= 0
+        a = local_mqa_attention(qr, kc[b:b + 1, live], vc[b:b + 1, live], window,
+                                q_pos=[p], kv_pos=slot_pos[live])
+        attn[b] = round_io(a.reshape(D), io)
+    out = round_io(attn @ np.asarray(W_o, dtype=np.float64).T, io)
+    return out, kc, vc

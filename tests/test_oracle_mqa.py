@@ -148,3 +148,41 @@ def test_block_rounding_points_bf16():
     r = oracle.local_mqa_forward(p["x"], p["W_q"], p["W_k"], p["W_v"], p["W_o"], 16, "bf16", keep=True)
     for name in ("q", "k", "v", "attn", "out"):
         np.testing.assert_array_equal(oracle.round_io(r[name], "bf16"), r[name])
+
+
+@pytest.mark.parametrize("window", [4, 16])
+def test_decode_steps_equal_forward_and_cache_stays_bounded(window):
+    """T decode steps from an empty cache (T longer than the window, so slots are reused)
+    give the forward's outputs for every position; the cache holds exactly the last
+    `window` rotated keys and values, each in slot position % window."""
+    w = workloads.TRAIN_FWD.with_shape(B=2, T=3 * window + 5, D=256, io="f32")
+    p = workloads.make_mqa_inputs(w, window)
+    f = oracle.local_mqa_forward(p["x"], p["W_q"], p["W_k"], p["W_v"], p["W_o"], window, "f32", keep=True)
+    kc = np.zeros((2, window, 128))
+    vc = np.zeros((2, window, 128))
+    for t in range(w.T):
+        out, kc, vc = oracle.local_mqa_decode_step(p["x"][:, t], p["W_q"], p["W_k"], p["W_v"], p["W_o"],
+                                                   kc, vc, [t, t], window, "f32")
+        np.testing.assert_allclose(out, f["out"][:, t], rtol=1e-9, atol=1e-12)
+    for s in range(w.T - window, w.T):
+        np.testing.assert_allclose(kc[:, s % window], f["k"][:, s], rtol=1e-12)
+        np.testing.assert_allclose(vc[:, s % window], f["v"][:, s], rtol=1e-12)
+
+
+def test_decode_ignores_slots_outside_the_window_and_before_zero():
+    """Garbage in slots that hold no live position (before position 0, or evicted) does not
+    change the step; distinct positions per sequence are honoured."""
+    w = workloads.TRAIN_FWD.with_shape(B=2, T=3, D=128, io="f32")
+    p = workloads.make_mqa_inputs(w, 8)
+    rng = np.random.default_rng(9)
+    kc = rng.standard_normal((2, 8, 128))
+    vc = rng.standard_normal((2, 8, 128))
+    pos = [2, 11]
+    a, _, _ = oracle.local_mqa_decode_step(p["x"][:, 0], p["W_q"], p["W_k"], p["W_v"], p["W_o"], kc, vc,
+                                           pos, 8, "f32")
+    kc2, vc2 = kc.copy(), vc.copy()
+    kc2[0, 3:] = 1e3          # sequence 0 at position 2: slots 3..7 hold no position yet
+    vc2[0, 3:] = -1e3
+    b, _, _ = oracle.local_mqa_decode_step(p["x"][:, 0], p["W_q"], p["W_k"], p["W_v"], p["W_o"], kc2, vc2,
+                                           pos, 8, "f32")
+    np.testing.assert_array_equal(a, b)
