@@ -395,13 +395,38 @@ def bench_mqa(g, torch, np, workloads, steps=30, window=1024):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    # decode steps with a full window of cached keys (position 2047), one per batch size
+    dec = []
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for Bd in (1, 64, 256):
+        kc = torch.randn((Bd, window, 128), generator=gen, device="cuda").to(bf)
+        vc = torch.randn((Bd, window, 128), generator=gen, device="cuda").to(bf)
+        xt = torch.randn((Bd, D), generator=gen, device="cuda").to(bf)
+        pos = torch.full((Bd,), 2047, dtype=torch.int32, device="cuda")
+        o = torch.empty((Bd, D), dtype=bf, device="cuda")
+        wsd = g.workspace(g.mqa_decode_workspace_bytes(Bd, D, bf))
+        step = lambda: g.local_mqa_decode_step(pos, xt, Wqkv, Wo, kc, vc, o, wsd)
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+        e2.record()
+        for _ in range(100):
+            step()
+        e3.record()
+        torch.cuda.synchronize()
+        us = e2.elapsed_time(e3) * 10.0
+        dec.append({"B": Bd, "us_per_step": us, "tokens_per_s": Bd / (us * 1e-6),
+                    "cache_bytes_per_sequence": 2 * window * 128 * 2})
+        del kc, vc, wsd
     M, H = B * T, D // 128
     pairs = B * H * sum(min(t + 1, window) for t in range(T))     # (query, key) pairs
     attn_flop = 4.0 * 128 * pairs
     flop = 2.0 * M * D * (D + 256) + attn_flop + 2.0 * M * D * D
     return {"workload": f"mqa_fwd_bf16_B{B}_T{T}_D{D}_H{H}_W{window}", "ms_per_step": ms,
             "tokens_per_s": M / (ms * 1e-3), "TFLOPs": flop / (ms * 1e-3) / 1e12,
-            "flop_per_step": flop, "attention_flop": attn_flop, "steps": steps}
+            "flop_per_step": flop, "attention_flop": attn_flop, "steps": steps,
+            "decode_full_window": dec}
 
 
 def bench_latency(g, torch, np, workloads):

@@ -10,7 +10,8 @@ from ._binding import (EXPORTS, LIB_PATH, RGLRU_BF16, RGLRU_F32, RgluError,  # n
                        backward, block_forward, block_fwd_workspace_bytes, bwd_workspace_bytes,
                        conv1d_causal4, decode_workspace_bytes,
                        forward, fwd_workspace_bytes, gated_mlp_fwd, io_code, load,
-                       local_mqa_fwd, mlp_forward, mlp_fwd_workspace_bytes, mqa_forward,
+                       local_mqa_decode_step, local_mqa_fwd, mlp_forward,
+                       mqa_decode_workspace_bytes, mlp_fwd_workspace_bytes, mqa_forward,
                        mqa_fwd_workspace_bytes, rglru_block_fwd, rglru_bwd,
                        rglru_decode_step, rglru_fwd, rglru_gates, rglru_lru, rglru_scan,
                        lru_workspace_bytes, scan_workspace_bytes, status_string, workspace)

@@ -24,7 +24,7 @@ EXPORTS = ("rglru_status_string", "conv1d_causal4", "rglru_fwd_workspace_bytes",
            "rglru_decode_workspace_bytes", "rglru_decode_step", "rglru_bwd_workspace_bytes",
            "rglru_bwd", "rglru_block_fwd_workspace_bytes", "rglru_block_fwd",
            "gated_mlp_fwd_workspace_bytes", "gated_mlp_fwd", "local_mqa_fwd_workspace_bytes",
-           "local_mqa_fwd")
+           "local_mqa_fwd", "local_mqa_decode_workspace_bytes", "local_mqa_decode_step")
 
 _lib = None
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -80,6 +80,10 @@ def load(path: str = LIB_PATH):
     lib.local_mqa_fwd_workspace_bytes.restype = _Z
     lib.local_mqa_fwd.argtypes = [_I, _I, _I, _I, _I, _I] + [_P] * 6 + [_P, _Z, _P]
     lib.local_mqa_fwd.restype = _I
+    lib.local_mqa_decode_workspace_bytes.argtypes = [_I, _I, _I]
+    lib.local_mqa_decode_workspace_bytes.restype = _Z
+    lib.local_mqa_decode_step.argtypes = [_I, _I, _I, _I] + [_P] * 7 + [_P, _Z, _P]
+    lib.local_mqa_decode_step.restype = _I
     _lib = lib
     return lib
 
@@ -140,6 +144,10 @@ def mlp_fwd_workspace_bytes(B, T, D, MD, dtype) -> int:
 
 def mqa_fwd_workspace_bytes(B, T, D, dtype) -> int:
     return int(load().local_mqa_fwd_workspace_bytes(B, T, D, io_code(dtype)))
+
+
+def mqa_decode_workspace_bytes(B, D, dtype) -> int:
+    return int(load().local_mqa_decode_workspace_bytes(B, D, io_code(dtype)))
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
@@ -236,6 +244,16 @@ def local_mqa_fwd(x, W_qkv, W_o, out, k_out, v_out, ws, window=1024, pos0=0, str
                                 _ptr(W_qkv), _ptr(W_o), _ptr(out), _ptr(k_out), _ptr(v_out),
                                 _ptr(ws), ws.numel(), _stream(stream)),
            "local_mqa_fwd")
+
+
+def local_mqa_decode_step(pos, x_t, W_qkv, W_o, k_cache, v_cache, out, ws, stream=None):
+    """pos: int32 device tensor [B]; k_cache, v_cache [B, window, 128] (updated in place)."""
+    B, D = x_t.shape
+    window = k_cache.shape[1]
+    _check(load().local_mqa_decode_step(B, D, io_code(x_t.dtype), int(window), _ptr(pos), _ptr(x_t),
+                                        _ptr(W_qkv), _ptr(W_o), _ptr(k_cache), _ptr(v_cache),
+                                        _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
+           "local_mqa_decode_step")
 
 
 # ------------------------------------------------------------------ allocating helpers

@@ -18,7 +18,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "conv.hip", "gemm.hip", "lru.hip", "decode.hip", "scan.hip", "bwd.hip", "block.hip",
-           "mqa.hip"]
+           "mqa.hip", "mqa_decode.hip"]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off",                                   # only the explicit fmaf calls fuse

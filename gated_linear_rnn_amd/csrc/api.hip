@@ -803,4 +803,41 @@ int local_mqa_fwd(int B, int T, int D, rglru_dtype io, int window, int pos0, con
   return RGLRU_OK;
 }
 
+size_t local_mqa_decode_workspace_bytes(int B, int D, rglru_dtype io) {
+  if (mqa_shape_status(B, 1, D, 1, 0) != RGLRU_OK || !io_ok(io)) return 0;
+  Carver cv(nullptr);
+  const size_t n = size_t(B) * D * io_bytes(io);
+  cv.take<unsigned char>(io == RGLRU_BF16 ? mqa_decode_partial_bytes(B, D)
+                                          : size_t(B) * (D + 2 * kHeadDim) * sizeof(float));
+  cv.take<unsigned char>(n);
+  cv.take<unsigned char>(n);
+  return cv.used;
+}
+
+int local_mqa_decode_step(int B, int D, rglru_dtype io, int window, const int* pos, const void* x_t,
+                          const void* W_qkv, const void* W_o, void* k_cache, void* v_cache,
+                          void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = mqa_shape_status(B, 1, D, window, 0);
+  if (st != RGLRU_OK) return st;
+  if (int64_t(B) * window * kHeadDim >= (int64_t(1) << 31)) return RGLRU_ESHAPE;
+  if (!io_ok(io)) return RGLRU_EDTYPE;
+  if (!pos || !x_t || !W_qkv || !W_o || !k_cache || !v_cache || !out) return RGLRU_EINVAL;
+  for (const void* p : {(const void*)pos, x_t, W_qkv, W_o, (const void*)k_cache, (const void*)v_cache,
+                        (const void*)out, (const void*)ws})
+    if (p && !aligned16(p)) return RGLRU_EINVAL;
+  if (!ws || ws_bytes < local_mqa_decode_workspace_bytes(B, D, io)) return RGLRU_EWORKSPACE;
+  Carver cv(ws);
+  const size_t n = size_t(B) * D * io_bytes(io);
+  MqaDecodeArgs a{};
+  a.bf16 = io == RGLRU_BF16;
+  a.B = B; a.D = D; a.window = window; a.pos = pos;
+  a.x = x_t; a.Wqkv = W_qkv; a.Wo = W_o; a.kcache = k_cache; a.vcache = v_cache; a.out = out;
+  a.partial = reinterpret_cast<float*>(cv.take<unsigned char>(
+      a.bf16 ? mqa_decode_partial_bytes(B, D) : size_t(B) * (D + 2 * kHeadDim) * sizeof(float)));
+  a.qbuf = cv.take<unsigned char>(n);
+  a.attn = cv.take<unsigned char>(n);
+  RG_CHECK(launch_mqa_decode(a, stream));
+  return RGLRU_OK;
+}
+
 }  // extern "C"

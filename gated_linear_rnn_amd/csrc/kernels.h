@@ -150,6 +150,26 @@ hipError_t launch_mqa_fwd(const MqaArgs& a, bool bf16, hipStream_t s);
 // pos0 + m % T (fp64 angles)
 hipError_t launch_rope_f32(float* x, int M, int ncols, int T, int pos0, hipStream_t s);
 
+// ---------------------------------------------------------------- mqa_decode.hip
+// One local-MQA generation step with a bounded cache (k, v caches [B, W, 128], slot
+// pos % W); x [B, D], W_qkv [D + 256, D], W_o [D, D]; pos [B] int32 on the device.
+struct MqaDecodeArgs {
+  bool bf16;
+  int B, D, window;
+  const int* pos;
+  const void* x;
+  const void* Wqkv;
+  const void* Wo;
+  void* kcache;
+  void* vcache;
+  void* out;             // [B, D]
+  float* partial;        // mqa_decode_partial_bytes(B, D)
+  void* qbuf;            // [B, D] io
+  void* attn;            // [B, D] io
+};
+size_t mqa_decode_partial_bytes(int B, int D);
+hipError_t launch_mqa_decode(const MqaDecodeArgs& a, hipStream_t s);
+
 // ---------------------------------------------------------------- lru.hip
 // The fused RG-LRU layer (gate GEMM + log-space gates + chunked scan) for bf16 I/O.
 struct LruArgs {

@@ -264,6 +264,30 @@ int local_mqa_fwd(int B, int T, int D, rglru_dtype io, int window, int pos0, con
                   const void* W_qkv, const void* W_o, void* out, void* k_out, void* v_out,
                   void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Workspace bytes local_mqa_decode_step needs (0 for invalid arguments). */
+size_t local_mqa_decode_workspace_bytes(int B, int D, rglru_dtype io);
+
+/*
+ * One generation step of the local-MQA block with a bounded key/value cache (the Griffin
+ * model-architecture page, section "Local sliding-window attention": the cache is limited
+ * to the window).  Each sequence b has a cache of `window` slots; slot j holds the rotated
+ * key and the value of the most recent position p <= pos[b] with p % window == j.  The step
+ * computes q, k, v of the token x_t[b] at absolute position pos[b] exactly as local_mqa_fwd
+ * does, writes k and v into slot pos[b] % window, attends over the cached positions
+ * (pos[b] - window, pos[b]] (slots 0 .. min(pos[b], window - 1)) and applies W_o.  Run over
+ * positions 0, 1, 2, ... from an empty cache it reproduces local_mqa_fwd (to fp32
+ * summation order); a prefill hands over by writing local_mqa_fwd's k_out/v_out rows of the
+ * last `window` positions into their slots.
+ *   pos [B] int32, device memory, read by the kernels (a negative position is taken as 0);
+ *   x_t [B,D] io; W_qkv [D + 256, D] and W_o [D,D] io as in local_mqa_fwd;
+ *   k_cache, v_cache [B, window, 128] io, in/out (one slot written per sequence);
+ *   out [B,D] io (output).
+ *   Shapes: D % 128 == 0, B*window*128 < 2^31.  Repeated calls give identical bits.
+ */
+int local_mqa_decode_step(int B, int D, rglru_dtype io, int window, const int* pos, const void* x_t,
+                          const void* W_qkv, const void* W_o, void* k_cache, void* v_cache,
+                          void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -184,3 +184,23 @@ def test_mqa_rejects_invalid_arguments(lib):
     assert call(k=BAD) == -1
     assert call(ws=None) == -4
     assert call(wsb=7) == -4
+
+
+def test_mqa_decode_workspace_query_and_validation(lib):
+    assert lib.local_mqa_decode_workspace_bytes(256, 2560, 1) >= 2 * 256 * 2560 * 2
+    assert lib.local_mqa_decode_workspace_bytes(4, 200, 1) == 0          # D % 128
+
+
+@no_gpu
+def test_mqa_decode_rejects_invalid_arguments(lib):
+    def call(B=2, D=128, io=1, window=16, pos=A, x=A, Wqkv=A, Wo=A, kc=A, vc=A, out=A, ws=A,
+             wsb=1 << 40):
+        return lib.local_mqa_decode_step(B, D, io, window, pos, x, Wqkv, Wo, kc, vc, out, ws, wsb, None)
+    assert call(window=0) == -1
+    assert call(B=0) == -1
+    assert call(D=96) == -2
+    assert call(io=5) == -3
+    for kw in ("pos", "x", "Wqkv", "Wo", "kc", "vc", "out"):
+        assert call(**{kw: None}) == -1, kw
+    assert call(vc=BAD) == -1
+    assert call(ws=None) == -4
