@@ -158,7 +158,7 @@ __global__ __launch_bounds__(C::NW * 64, C::NW >= 8 ? 2 : 1) void gemm_bf16_kern
               val = (col & 1) ? fmaf(other, sn, val * cs) : fmaf(val, cs, -other * sn);
             }
           }
-          st[r * 64 + chunk * 8 + (col & 7)] = f2bf(gelu_side ? gelu_f(val) : val);
+          st[r * 64 + chunk * 8 + (col & 7)] = f2bf(gelu_side ? gelu_fast(val) : val);
         }
     // LDS operations of a wave complete in order; the fence keeps the compiler from
     // moving the reads below above the writes
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(C::NW * 64, C::NW >= 8 ? 2 : 1) void gemm_bf16_kern
         for (int v = 0; v < 16; ++v) {
           const int r = wm * C::WTM + mf * 32 + acc_row(v, lane);
           const int chunk = (cl >> 3) ^ (((r >> 2) & 1) << 2);
-          const float val = gelu_f(acc[mf][jc][v]) * acc[mf][jc + HALF][v];
+          const float val = gelu_fast(acc[mf][jc][v]) * acc[mf][jc + HALF][v];
           st[r * C::BC + chunk * 8 + (cl & 7)] = f2bf(val);
         }
     }
