@@ -205,13 +205,15 @@ struct BlockWs {
   void* p;
   void* g;
   void* y;
+  float* tail;   // bf16: the output linear's split-tail partials
   FwdWs lru;
 };
 
-BlockWs carve_block(Carver& cv, int B, int T, int R, rglru_dtype io) {
+BlockWs carve_block(Carver& cv, int B, int T, int D, int R, rglru_dtype io) {
   const size_t n = size_t(B) * T * R;
   BlockWs w;
   w.pq = io == RGLRU_F32 ? cv.take<float>(2 * n) : nullptr;
+  w.tail = io == RGLRU_BF16 ? cv.take<float>(out_gemm_tail_bytes(B * T, D, R) / sizeof(float)) : nullptr;
   w.p = cv.take<unsigned char>(n * io_bytes(io));
   w.g = cv.take<unsigned char>(n * io_bytes(io));
   w.y = io == RGLRU_F32 ? cv.take<unsigned char>(n * io_bytes(io)) : nullptr;
@@ -239,16 +241,19 @@ int mlp_shape_status(int B, int T, int D, int MD) {
   return RGLRU_OK;
 }
 
-// bf16: h [M, MD] bf16.  fp32: q1 (then h in place) and q2, [M, MD] fp32 each.
+// bf16: h [M, MD] bf16 and the last linear's split-tail partials.  fp32: q1 (then h in
+// place) and q2, [M, MD] fp32 each.
 struct MlpWs {
   void* h;
   float* q2;
+  float* tail;
 };
-MlpWs carve_mlp(Carver& cv, int B, int T, int MD, rglru_dtype io) {
+MlpWs carve_mlp(Carver& cv, int B, int T, int D, int MD, rglru_dtype io) {
   const size_t n = size_t(B) * T * MD;
   MlpWs w;
   w.h = cv.take<unsigned char>(n * io_bytes(io));
   w.q2 = io == RGLRU_F32 ? cv.take<float>(n) : nullptr;
+  w.tail = io == RGLRU_BF16 ? cv.take<float>(out_gemm_tail_bytes(B * T, D, MD) / sizeof(float)) : nullptr;
   return w;
 }
 
@@ -269,6 +274,7 @@ struct MqaWs {
   void* k;
   void* v;
   void* attn;
+  float* tail;   // bf16: the output projection's split-tail partials
 };
 MqaWs carve_mqa(Carver& cv, int B, int T, int D, rglru_dtype io) {
   const size_t M = size_t(B) * T, eb = io_bytes(io);
@@ -277,6 +283,7 @@ MqaWs carve_mqa(Carver& cv, int B, int T, int D, rglru_dtype io) {
   w.k = cv.take<unsigned char>(M * kHeadDim * eb);
   w.v = cv.take<unsigned char>(M * kHeadDim * eb);
   w.attn = cv.take<unsigned char>(M * D * eb);
+  w.tail = io == RGLRU_BF16 ? cv.take<float>(out_gemm_tail_bytes(B * T, D, D) / sizeof(float)) : nullptr;
   return w;
 }
 
@@ -609,7 +616,7 @@ int rglru_bwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const
 size_t rglru_block_fwd_workspace_bytes(int B, int T, int D, int R, rglru_dtype io) {
   if (block_shape_status(B, T, D, R) != RGLRU_OK || !io_ok(io)) return 0;
   Carver cv(nullptr);
-  carve_block(cv, B, T, R, io);
+  carve_block(cv, B, T, D, R, io);
   return cv.used;
 }
 
@@ -632,7 +639,7 @@ int rglru_block_fwd(int B, int T, int D, int R, rglru_dtype io, float c, const v
   if (!ws || ws_bytes < rglru_block_fwd_workspace_bytes(B, T, D, R, io)) return RGLRU_EWORKSPACE;
 
   Carver cv(ws);
-  BlockWs w = carve_block(cv, B, T, R, io);
+  BlockWs w = carve_block(cv, B, T, D, R, io);
   const int M = B * T;
   const bool bf = io == RGLRU_BF16;
 
@@ -685,7 +692,7 @@ int rglru_block_fwd(int B, int T, int D, int R, rglru_dtype io, float c, const v
   if (bf) {
     BlockGemmArgs go{};
     go.A = w.y; go.Bm = W_out; go.M = M; go.N = D; go.K = R; go.ldc = D;
-    go.C = out; go.G = nullptr; go.split = 0;
+    go.C = out; go.G = nullptr; go.split = 0; go.tail_ws = w.tail;
     RG_CHECK(launch_block_gemm_bf16(go, stream));
   } else {
     PlainGemmArgs po{};
@@ -699,7 +706,7 @@ int rglru_block_fwd(int B, int T, int D, int R, rglru_dtype io, float c, const v
 size_t gated_mlp_fwd_workspace_bytes(int B, int T, int D, int MD, rglru_dtype io) {
   if (mlp_shape_status(B, T, D, MD) != RGLRU_OK || !io_ok(io)) return 0;
   Carver cv(nullptr);
-  carve_mlp(cv, B, T, MD, io);
+  carve_mlp(cv, B, T, D, MD, io);
   return cv.used;
 }
 
@@ -714,7 +721,7 @@ int gated_mlp_fwd(int B, int T, int D, int MD, rglru_dtype io, const void* x, co
     if (p && !aligned16(p)) return RGLRU_EINVAL;
   if (!ws || ws_bytes < gated_mlp_fwd_workspace_bytes(B, T, D, MD, io)) return RGLRU_EWORKSPACE;
   Carver cv(ws);
-  MlpWs w = carve_mlp(cv, B, T, MD, io);
+  MlpWs w = carve_mlp(cv, B, T, D, MD, io);
   const int M = B * T;
   if (io == RGLRU_BF16) {
     GegluGemmArgs g1{};
@@ -722,7 +729,7 @@ int gated_mlp_fwd(int B, int T, int D, int MD, rglru_dtype io, const void* x, co
     RG_CHECK(launch_geglu_gemm_bf16(g1, stream));
     BlockGemmArgs g3{};
     g3.A = w.h; g3.Bm = W_3; g3.M = M; g3.N = D; g3.K = MD; g3.ldc = D;
-    g3.C = out; g3.G = nullptr; g3.split = 0;
+    g3.C = out; g3.G = nullptr; g3.split = 0; g3.tail_ws = w.tail;
     RG_CHECK(launch_block_gemm_bf16(g3, stream));
     return RGLRU_OK;
   }
@@ -792,7 +799,7 @@ int local_mqa_fwd(int B, int T, int D, rglru_dtype io, int window, int pos0, con
   if (bf) {
     BlockGemmArgs go{};
     go.A = w.attn; go.Bm = W_o; go.M = M; go.N = D; go.K = D; go.ldc = D;
-    go.C = out; go.G = nullptr; go.split = 0;
+    go.C = out; go.G = nullptr; go.split = 0; go.tail_ws = w.tail;
     RG_CHECK(launch_block_gemm_bf16(go, stream));
   } else {
     PlainGemmArgs po{};

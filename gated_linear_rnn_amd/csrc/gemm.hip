@@ -52,7 +52,28 @@ struct GemmParams {
   bf16_t* V16;        // kModeQkv (v)
   int split;          // kModeInProj: R; kModeQkv: D
   int T, pos0;        // kModeQkv: row m is at position pos0 + m % T
+  // kModeOut tail split: workgroups [0, tail_first) compute whole tiles (the tiles
+  // [0, tail_first) of the grouped order); the remaining tiles are each computed by
+  // tail_split workgroups over equal K ranges into fp32 partials at tail_ws, which
+  // tail_fixup_kernel adds and rounds.  Without a split tail_first = MT * NT.
+  int tail_first, tail_split;
+  float* tail_ws;
 };
+
+// Tile (tm, tn) of position L in the grouped order: groups of GM = 8 row tiles, and within a
+// group all column tiles, so consecutive tiles share row and column panels.
+__device__ __forceinline__ void grouped_tile(int L, int MT, int NT, int& tm, int& tn) {
+  constexpr int GM = 8;
+  const int group = L / (GM * NT);
+  const int first = group * GM;
+  const int gsize = min(GM, MT - first);
+  const int in = L - group * GM * NT;
+  tm = first + in % gsize;
+  tn = in / gsize;
+}
+
+// Number of CUs the tail split plans for (MI355X); another count only makes it less exact.
+constexpr int kPlanCUs = 256;
 
 // RoPE angle of position pos and frequency theta (radians per position), in turns reduced
 // to [-1/2, 1/2]: the product and the reduction in fp64, so that large positions keep full
@@ -62,20 +83,24 @@ __device__ __forceinline__ float rope_turns(int pos, double theta_turns) {
   return float(a - rint(a));
 }
 
-// Map the linear workgroup id to a (tile_m, tile_n) pair.  Consecutive workgroup ids are
-// dispatched round-robin over the 8 XCDs; the remap gives every XCD a contiguous range of
-// the grouped tile order, so the tiles one XCD runs together share U and W panels in its L2.
-__device__ __forceinline__ void tile_coords(int MT, int NT, int& tm, int& tn) {
-  const int nb = gridDim.x;
-  int bid = blockIdx.x;
-  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
-  constexpr int GM = 8;
-  const int group = bid / (GM * NT);
-  const int first = group * GM;
-  const int gsize = min(GM, MT - first);
-  const int in = bid - group * GM * NT;
-  tm = first + in % gsize;
-  tn = in / gsize;
+// Map the workgroup id to a tile (tm, tn) and, for tail-split workgroups, a K part.
+// Consecutive workgroup ids are dispatched round-robin over the 8 XCDs; the remap gives
+// every XCD a contiguous range of the grouped tile order, so the tiles one XCD runs together
+// share panels in its L2 (in the split tail, the parts of a tile stay on one XCD too).
+__device__ __forceinline__ void tile_coords(int MT, int NT, int first, int split, int& tm, int& tn,
+                                            int& part, int& L) {
+  part = 0;
+  if (int(blockIdx.x) < first) {
+    L = blockIdx.x;
+    if ((first & 7) == 0) L = (L & 7) * (first >> 3) + (L >> 3);
+  } else {
+    const int nt = int(gridDim.x) - first;
+    int q = int(blockIdx.x) - first;
+    if ((nt & 7) == 0) q = (q & 7) * (nt >> 3) + (q >> 3);
+    L = first + q / split;
+    part = q % split;
+  }
+  grouped_tile(L, MT, NT, tm, tn);
 }
 
 template <class C, int MODE, bool DUAL>
@@ -87,14 +112,17 @@ __global__ __launch_bounds__(C::NW * 64, C::NW >= 8 ? 2 : 1) void gemm_bf16_kern
   const int MT = (p.M + C::BM - 1) / C::BM;
   constexpr bool kPlainTile = C::PLAIN;   // plain tiles span BNR columns, gate tiles BC channels
   const int NT = kPlainTile ? (p.N + C::BNR - 1) / C::BNR : (p.N + C::BC - 1) / C::BC;
-  int tm, tn;
-  tile_coords(MT, NT, tm, tn);
+  int tm, tn, part, L;
+  tile_coords(MT, NT, p.tail_first, p.tail_split, tm, tn, part, L);
+  const bool tail = MODE == kModeOut && int(blockIdx.x) >= p.tail_first;
   const int m0 = tm * C::BM;
   const int n0 = tn * (kPlainTile ? C::BNR : C::BC);
+  const int kc = tail ? p.K / p.tail_split : p.K;
 
   TileOperands op;
-  op.A = p.A; op.A2 = p.A2; op.B0 = p.B0; op.B1 = p.B1;
-  op.lda = p.lda; op.ldb = p.ldb; op.K = p.K;
+  op.A = p.A + size_t(part) * kc; op.A2 = p.A2;
+  op.B0 = p.B0 + size_t(part) * kc; op.B1 = p.B1;
+  op.lda = p.lda; op.ldb = p.ldb; op.K = kc;
   op.a_row0 = m0; op.a_rows = p.M - m0;
   op.b_row0 = n0; op.b_rows = p.N - n0;
   f32x16_t acc[C::MF][C::NF];
@@ -102,7 +130,19 @@ __global__ __launch_bounds__(C::NW * 64, C::NW >= 8 ? 2 : 1) void gemm_bf16_kern
 
   // ---------------------------------------------------------------- epilogue
   const int col = lane & 31;
-  if (MODE == kModePlain) {
+  if (tail) {
+    // fp32 partial of this K part: the whole tile, row-major [BM][BNR]
+    float* dst = p.tail_ws + (size_t(L - p.tail_first) * p.tail_split + part) * (C::BM * C::BNR);
+#pragma unroll
+    for (int f = 0; f < C::NF; ++f)
+#pragma unroll
+      for (int mf = 0; mf < C::MF; ++mf)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = wm * C::WTM + mf * 32 + acc_row(v, lane);
+          dst[r * C::BNR + wn * C::WTNR + f * 32 + col] = acc[mf][f][v];
+        }
+  } else if (MODE == kModePlain) {
 #pragma unroll
     for (int f = 0; f < C::NF; ++f) {
       const int n = n0 + wn * C::WTNR + f * 32 + col;
@@ -249,14 +289,78 @@ __global__ __launch_bounds__(C::NW * 64, C::NW >= 8 ? 2 : 1) void gemm_bf16_kern
 typedef GemmCfg<256, 128, 2, 4, false, 64, 2> CfgGate;
 typedef GemmCfg<256, 128, 2, 4, true, 64, 2> CfgPlain;
 
+// Tail split of a kModeOut GEMM: the tiles of the last, partly filled round (R of them,
+// R <= half the CUs) are each computed by S workgroups over K / S, so that round takes
+// about 1/S of a full tile's time.  S = 4 or 2, the largest with S R <= CUs and
+// (K / BK) % S == 0; 1 when there is no such round or no split.
+static void plan_tail(int tiles, int ksteps, int& first, int& split) {
+  const int R = tiles % kPlanCUs;
+  first = tiles;
+  split = 1;
+  if (R == 0 || 2 * R > kPlanCUs) return;
+  for (int sp = 4; sp >= 2; sp /= 2)
+    if (sp * R <= kPlanCUs && ksteps % sp == 0) {
+      first = tiles - R;
+      split = sp;
+      return;
+    }
+}
+
+size_t out_gemm_tail_bytes(int M, int N, int K) {
+  typedef GemmCfg<256, 128, 2, 4, true, 64, 2> C;
+  const int tiles = ((M + C::BM - 1) / C::BM) * ((N + C::BNR - 1) / C::BNR);
+  int first, split;
+  plan_tail(tiles, K / C::BK, first, split);
+  return split > 1 ? size_t(tiles - first) * split * C::BM * C::BNR * sizeof(float) : 0;
+}
+
+// The split tail's fixup: sum the S partials of each element in order, round to bf16,
+// store inside the matrix.  One thread per 8 consecutive columns of a tile row.
+template <class C>
+__global__ __launch_bounds__(256) void tail_fixup_kernel(GemmParams p, int MT, int NT) {
+  constexpr int CH = C::BNR / 8;
+  const size_t per_tile = size_t(C::BM) * CH;
+  const size_t idx = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int ntail = MT * NT - p.tail_first;
+  if (idx >= per_tile * ntail) return;
+  const int i = int(idx / per_tile);
+  const int r = int(idx % per_tile) / CH, ck = int(idx % per_tile) % CH;
+  int tm, tn;
+  grouped_tile(p.tail_first + i, MT, NT, tm, tn);
+  const int m = tm * C::BM + r, n = tn * C::BNR + ck * 8;
+  if (m >= p.M || n >= p.N) return;
+  const float* src = p.tail_ws + size_t(i) * p.tail_split * (C::BM * C::BNR) + r * C::BNR + ck * 8;
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = src[e];
+  for (int sp = 1; sp < p.tail_split; ++sp)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] += src[size_t(sp) * (C::BM * C::BNR) + e];
+  uint4 w;
+  w.x = uint32_t(f2bf(v[0])) | (uint32_t(f2bf(v[1])) << 16);
+  w.y = uint32_t(f2bf(v[2])) | (uint32_t(f2bf(v[3])) << 16);
+  w.z = uint32_t(f2bf(v[4])) | (uint32_t(f2bf(v[5])) << 16);
+  w.w = uint32_t(f2bf(v[6])) | (uint32_t(f2bf(v[7])) << 16);
+  *reinterpret_cast<uint4*>(p.C16 + size_t(m) * p.ldc + n) = w;
+}
+
 template <class C, int MODE, bool DUAL>
-static hipError_t run_bf16(const GemmParams& p, hipStream_t s) {
+static hipError_t run_bf16(GemmParams p, hipStream_t s) {
   const int MT = (p.M + C::BM - 1) / C::BM;
   const int NT = C::PLAIN ? (p.N + C::BNR - 1) / C::BNR : (p.N + C::BC - 1) / C::BC;
   static_assert(C::PLAIN == (MODE == kModePlain || MODE == kModeInProj || MODE == kModeOut ||
                              MODE == kModeQkv),
                 "plain-tile modes run on plain configurations");
-  gemm_bf16_kernel<C, MODE, DUAL><<<MT * NT, C::NW * 64, 0, s>>>(p);
+  const int tiles = MT * NT;
+  p.tail_first = tiles;
+  p.tail_split = 1;
+  if (MODE == kModeOut && p.tail_ws) plan_tail(tiles, p.K / C::BK, p.tail_first, p.tail_split);
+  const int grid = p.tail_first + (tiles - p.tail_first) * p.tail_split;
+  gemm_bf16_kernel<C, MODE, DUAL><<<grid, C::NW * 64, 0, s>>>(p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.tail_split == 1) return e;
+  const size_t threads = size_t(tiles - p.tail_first) * C::BM * (C::BNR / 8);
+  tail_fixup_kernel<C><<<int((threads + 255) / 256), 256, 0, s>>>(p, MT, NT);
   return hipGetLastError();
 }
 
@@ -298,6 +402,7 @@ hipError_t launch_block_gemm_bf16(const BlockGemmArgs& g, hipStream_t s) {
   p.G16 = static_cast<bf16_t*>(g.G);
   p.split = g.split;
   if (g.G) return run_bf16<CfgPlain, kModeInProj, false>(p, s);
+  p.tail_ws = g.tail_ws;
   return run_bf16<CfgPlain, kModeOut, false>(p, s);
 }
 

@@ -83,6 +83,8 @@ struct PlainGemmArgs {
 // The linears of the recurrent block, bf16 in and out, C = A Bm^T with row strides K.
 // With G: N = 2 split columns, C[M, split] = the first split columns, G[M, split] = GeLU of
 // the rest (ldc = split); without G: C[M, N] (ldc = N).
+// Without G, tail_ws (out_gemm_tail_bytes(M, N, K) bytes, or NULL) lets the tiles of a last,
+// partly filled round split their K loop (fp32 partials, then a fixed-order fixup).
 struct BlockGemmArgs {
   const void* A;
   const void* Bm;
@@ -91,8 +93,10 @@ struct BlockGemmArgs {
   void* C;
   void* G;
   int split;
+  float* tail_ws;
 };
 hipError_t launch_block_gemm_bf16(const BlockGemmArgs& g, hipStream_t s);
+size_t out_gemm_tail_bytes(int M, int N, int K);
 
 // First layer of the gated MLP block, bf16: H[M, N] = RNE(GeLU(A W1^T) * (A W2^T)) with
 // A [M, K], W1, W2 [N, K] (row strides K, N).
