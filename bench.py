@@ -197,6 +197,9 @@ def main():
     }
     del xs, u, y, ws
     torch.cuda.empty_cache()
+    copy_gbps = measured_copy_gbps(torch)
+    out["hbm"]["measured_copy_GBps"] = copy_gbps
+    out["hbm"]["block_frac_of_measured_copy"] = block_gbps / copy_gbps
 
     if not args.no_extras:
         out["decode"] = bench_decode(g, torch, np, workloads)
@@ -208,6 +211,26 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, np)
     print(json.dumps(out))
+
+
+def measured_copy_gbps(torch, nbytes=1 << 30, reps=20):
+    """Device-to-device copy of a 1 GiB buffer (read + write bytes over the copy time):
+    the achievable HBM bandwidth the block's algorithmic GB/s is also compared with."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 2.0 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return gbps
 
 
 def bench_decode(g, torch, np, workloads):
