@@ -358,9 +358,30 @@ def bench_block(g, torch, np, workloads, steps=50):
     ms = e0.elapsed_time(e1) / steps
     M = B * T
     flop = 2.0 * M * (2 * R * D + 2 * R * R + D * R)
+    # decode steps of the whole block (rglru_block_decode_step), state carried in place
+    dec = []
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    for Bd in (1, 64, 256):
+        xt = torch.randn((Bd, D), generator=gen, device="cuda").to(bf)
+        cs = torch.randn((Bd, 3, R), generator=gen, device="cuda").to(bf)
+        h = torch.randn((Bd, R), generator=gen, device="cuda")
+        o = torch.empty((Bd, D), dtype=bf, device="cuda")
+        wsd = g.workspace(g.block_decode_workspace_bytes(Bd, D, R, bf))
+        step = lambda: g.rglru_block_decode_step(xt, W_in, cw, cb, cs, Wa, Wx, ba, bx, lam, h, W_out, o,
+                                                 wsd, p["c"])
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(100):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 10.0
+        dec.append({"B": Bd, "us_per_step": us, "tokens_per_s": Bd / (us * 1e-6)})
     return {"workload": f"block_fwd_bf16_B{B}_T{T}_D{D}_R{R}", "ms_per_step": ms,
             "tokens_per_s": M / (ms * 1e-3), "TFLOPs": flop / (ms * 1e-3) / 1e12,
-            "flop_per_step": flop, "steps": steps}
+            "flop_per_step": flop, "steps": steps, "decode_step": dec}
 
 
 def bench_mlp(g, torch, np, workloads, steps=30):

@@ -13,5 +13,6 @@ from ._binding import (EXPORTS, LIB_PATH, RGLRU_BF16, RGLRU_F32, RgluError,  # n
                        local_mqa_decode_step, local_mqa_fwd, mlp_forward,
                        mqa_decode_workspace_bytes, mlp_fwd_workspace_bytes, mqa_forward,
                        mqa_fwd_workspace_bytes, rglru_block_fwd, rglru_bwd,
+                       rglru_block_decode_step, block_decode_workspace_bytes,
                        rglru_decode_step, rglru_fwd, rglru_gates, rglru_lru, rglru_scan,
                        lru_workspace_bytes, scan_workspace_bytes, status_string, workspace)

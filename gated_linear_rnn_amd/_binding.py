@@ -24,7 +24,8 @@ EXPORTS = ("rglru_status_string", "conv1d_causal4", "rglru_fwd_workspace_bytes",
            "rglru_decode_workspace_bytes", "rglru_decode_step", "rglru_bwd_workspace_bytes",
            "rglru_bwd", "rglru_block_fwd_workspace_bytes", "rglru_block_fwd",
            "gated_mlp_fwd_workspace_bytes", "gated_mlp_fwd", "local_mqa_fwd_workspace_bytes",
-           "local_mqa_fwd", "local_mqa_decode_workspace_bytes", "local_mqa_decode_step")
+           "local_mqa_fwd", "local_mqa_decode_workspace_bytes", "local_mqa_decode_step",
+           "rglru_block_decode_workspace_bytes", "rglru_block_decode_step")
 
 _lib = None
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -84,6 +85,10 @@ def load(path: str = LIB_PATH):
     lib.local_mqa_decode_workspace_bytes.restype = _Z
     lib.local_mqa_decode_step.argtypes = [_I, _I, _I, _I] + [_P] * 7 + [_P, _Z, _P]
     lib.local_mqa_decode_step.restype = _I
+    lib.rglru_block_decode_workspace_bytes.argtypes = [_I, _I, _I, _I]
+    lib.rglru_block_decode_workspace_bytes.restype = _Z
+    lib.rglru_block_decode_step.argtypes = [_I, _I, _I, _I, _F] + [_P] * 13 + [_P, _Z, _P]
+    lib.rglru_block_decode_step.restype = _I
     _lib = lib
     return lib
 
@@ -148,6 +153,10 @@ def mqa_fwd_workspace_bytes(B, T, D, dtype) -> int:
 
 def mqa_decode_workspace_bytes(B, D, dtype) -> int:
     return int(load().local_mqa_decode_workspace_bytes(B, D, io_code(dtype)))
+
+
+def block_decode_workspace_bytes(B, D, R, dtype) -> int:
+    return int(load().rglru_block_decode_workspace_bytes(B, D, R, io_code(dtype)))
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
@@ -254,6 +263,18 @@ def local_mqa_decode_step(pos, x_t, W_qkv, W_o, k_cache, v_cache, out, ws, strea
                                         _ptr(W_qkv), _ptr(W_o), _ptr(k_cache), _ptr(v_cache),
                                         _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
            "local_mqa_decode_step")
+
+
+def rglru_block_decode_step(x_t, W_in, conv_w, conv_b, conv_state, W_a, W_x, b_a, b_x, lam, h, W_out,
+                            out_t, ws, c=8.0, stream=None):
+    B, D = x_t.shape
+    R = W_in.shape[0] // 2
+    _check(load().rglru_block_decode_step(B, D, R, io_code(x_t.dtype), float(c), _ptr(x_t), _ptr(W_in),
+                                          _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(W_a),
+                                          _ptr(W_x), _ptr(b_a), _ptr(b_x), _ptr(lam), _ptr(h),
+                                          _ptr(W_out), _ptr(out_t), _ptr(ws), ws.numel(),
+                                          _stream(stream)),
+           "rglru_block_decode_step")
 
 
 # ------------------------------------------------------------------ allocating helpers

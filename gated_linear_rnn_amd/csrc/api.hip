@@ -847,4 +847,100 @@ int local_mqa_decode_step(int B, int D, rglru_dtype io, int window, const int* p
   return RGLRU_OK;
 }
 
+size_t rglru_block_decode_workspace_bytes(int B, int D, int R, rglru_dtype io) {
+  if (block_shape_status(B, 1, D, R) != RGLRU_OK || !io_ok(io)) return 0;
+  Carver cv(nullptr);
+  const size_t n = size_t(B) * R;
+  if (io == RGLRU_BF16) {
+    const size_t a = splitk_partial_bytes(B, 2 * R, D), b = splitk_partial_bytes(B, D, R);
+    cv.take<unsigned char>(a > b ? a : b);          // split-K partials of both linears
+    cv.take<unsigned char>(decode_partial_bytes(B, R));
+  } else {
+    cv.take<float>(2 * n);                          // the input linears' product
+  }
+  for (int i = 0; i < 4; ++i) cv.take<unsigned char>(n * io_bytes(io));   // p, g, u, z
+  return cv.used;
+}
+
+int rglru_block_decode_step(int B, int D, int R, rglru_dtype io, float c, const void* x_t,
+                            const void* W_in, const void* conv_w, const float* conv_b,
+                            void* conv_state, const void* W_a, const void* W_x, const float* b_a,
+                            const float* b_x, const float* lambda, float* h, const void* W_out,
+                            void* out_t, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = block_shape_status(B, 1, D, R);
+  if (st != RGLRU_OK) return st;
+  if (!io_ok(io)) return RGLRU_EDTYPE;
+  if (!x_t || !W_in || !W_a || !W_x || !b_a || !b_x || !lambda || !h || !W_out || !out_t || !c_ok(c))
+    return RGLRU_EINVAL;
+  if (conv_w && !conv_state) return RGLRU_EINVAL;
+  for (const void* p : {x_t, W_in, conv_w, (const void*)conv_b, (const void*)conv_state, W_a, W_x,
+                        (const void*)b_a, (const void*)b_x, (const void*)lambda, (const void*)h, W_out,
+                        (const void*)out_t, (const void*)ws})
+    if (p && !aligned16(p)) return RGLRU_EINVAL;
+  if (!ws || ws_bytes < rglru_block_decode_workspace_bytes(B, D, R, io)) return RGLRU_EWORKSPACE;
+  Carver cv(ws);
+  const size_t n = size_t(B) * R;
+  const bool bf = io == RGLRU_BF16;
+  float* part = nullptr;
+  float* dpart = nullptr;
+  float* pq = nullptr;
+  if (bf) {
+    const size_t a = splitk_partial_bytes(B, 2 * R, D), b = splitk_partial_bytes(B, D, R);
+    part = reinterpret_cast<float*>(cv.take<unsigned char>(a > b ? a : b));
+    dpart = reinterpret_cast<float*>(cv.take<unsigned char>(decode_partial_bytes(B, R)));
+  } else {
+    pq = cv.take<float>(2 * n);
+  }
+  void* p = cv.take<unsigned char>(n * io_bytes(io));
+  void* g = cv.take<unsigned char>(n * io_bytes(io));
+  void* u = cv.take<unsigned char>(n * io_bytes(io));
+  void* z = cv.take<unsigned char>(n * io_bytes(io));
+
+  // 1. the input linears: p and g = GeLU(.)
+  if (bf) {
+    const int S = splitk_splits(B, 2 * R, D);
+    RG_CHECK(launch_splitk_bf16(x_t, W_in, B, 2 * R, D, S, part, stream));
+    RG_CHECK(launch_splitk_inproj_bf16(part, S, B, R, p, g, stream));
+  } else {
+    PlainGemmArgs pa{};
+    pa.A = x_t; pa.Bm = W_in; pa.M = B; pa.N = 2 * R; pa.K = D; pa.lda = D; pa.ldb = D; pa.ldc = 2 * R;
+    pa.C = pq;
+    RG_CHECK(launch_plain_gemm_f32(pa, stream));
+    RG_CHECK(launch_split_gelu_f32(pq, B, R, static_cast<float*>(p), static_cast<float*>(g), stream));
+  }
+  // 2. the branch's decode step on p, the state (h, conv history) updated in place
+  const void* uin = p;
+  if (conv_w) {
+    if (bf) RG_CHECK(launch_conv_decode<bf16_t>(B, R, p, conv_w, conv_b, conv_state, u, stream));
+    else RG_CHECK(launch_conv_decode<float>(B, R, p, conv_w, conv_b, conv_state, u, stream));
+    uin = u;
+  }
+  if (bf) {
+    DecodeArgs d{};
+    d.u = uin; d.Wa = W_a; d.Wx = W_x; d.ba = b_a; d.bx = b_x; d.lam = lambda; d.c = c;
+    d.h = h; d.y = z; d.partial = dpart; d.B = B; d.D = R; d.gate = g;
+    RG_CHECK(launch_decode_bf16(d, stream));
+  } else {
+    GateGemmArgs ga{};
+    ga.U = uin; ga.Wa = W_a; ga.Wx = W_x; ga.M = B; ga.N = R; ga.K = R;
+    ga.ba = b_a; ga.bx = b_x; ga.lam = lambda; ga.c = c;
+    ga.u = uin; ga.h = h; ga.y = z;
+    st = gate_projection(io, ga, kEpiDecode, pq, pq + n, stream);
+    if (st != RGLRU_OK) return st;
+    RG_CHECK(launch_mul_f32(static_cast<float*>(z), static_cast<const float*>(g), n, stream));
+  }
+  // 3. the output linear on z
+  if (bf) {
+    const int S = splitk_splits(B, D, R);
+    RG_CHECK(launch_splitk_bf16(z, W_out, B, D, R, S, part, stream));
+    RG_CHECK(launch_splitk_out_bf16(part, S, B, D, out_t, stream));
+  } else {
+    PlainGemmArgs po{};
+    po.A = z; po.Bm = W_out; po.M = B; po.N = D; po.K = R; po.lda = R; po.ldb = R; po.ldc = D;
+    po.C = static_cast<float*>(out_t);
+    RG_CHECK(launch_plain_gemm_f32(po, stream));
+  }
+  return RGLRU_OK;
+}
+
 }  // extern "C"

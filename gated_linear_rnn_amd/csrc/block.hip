@@ -41,6 +41,29 @@ __global__ __launch_bounds__(256) void geglu_f32_kernel(const float* __restrict_
     h[o] = float(gelu_d(double(q1[o])) * double(q2[o]));
 }
 
+// Decode step of the recurrent block (bf16): the input linears' split-K partials [S][M][2R]
+// added in split order; the first R columns rounded to p, GeLU of the rest (the same fp32
+// approximation as the forward GEMM epilogue) rounded to g.  8 columns per thread.
+__global__ __launch_bounds__(256) void inproj_finish_kernel(const float* __restrict__ partial, int S,
+                                                            int M, int R, bf16_t* __restrict__ p,
+                                                            bf16_t* __restrict__ g) {
+  const int N = 2 * R;
+  const size_t idx = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= size_t(M) * (N / 8)) return;
+  const int m = int(idx / (N / 8)), n = int(idx % (N / 8)) * 8;
+  const float* src = partial + size_t(m) * N + n;
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = src[e];
+  for (int s = 1; s < S; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] += src[size_t(s) * M * N + e];
+  const bool gelu = n >= R;
+  bf16_t* dst = gelu ? g + size_t(m) * R + (n - R) : p + size_t(m) * R + n;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dst[e] = f2bf(gelu ? gelu_fast(v[e]) : v[e]);
+}
+
 static int grid_for(size_t n) {
   const size_t blocks = (n + 255) / 256;
   return int(blocks > 8192 ? 8192 : blocks);
@@ -58,6 +81,14 @@ hipError_t launch_mul_f32(float* y, const float* g, size_t n, hipStream_t s) {
 
 hipError_t launch_geglu_f32(const float* q1, const float* q2, float* h, size_t n, hipStream_t s) {
   geglu_f32_kernel<<<grid_for(n), 256, 0, s>>>(q1, q2, h, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_inproj_bf16(const float* partial, int S, int M, int R, void* p, void* g,
+                                     hipStream_t s) {
+  const size_t n = size_t(M) * (2 * R / 8);
+  inproj_finish_kernel<<<int((n + 255) / 256), 256, 0, s>>>(partial, S, M, R, static_cast<bf16_t*>(p),
+                                                         static_cast<bf16_t*>(g));
   return hipGetLastError();
 }
 

@@ -138,6 +138,10 @@ __global__ __launch_bounds__(256) void decode_update_kernel(DecodeArgs p) {
     f4set(hn, j, fmaf(a, f4get(h, j), beta * f4get(u, j)));
   }
   *reinterpret_cast<float4*>(p.h + o) = hn;
+  if (p.gate) {   // the recurrent block's GeLU branch multiplies the state before rounding
+    const float4 g = Io<bf16_t>::load4(static_cast<const bf16_t*>(p.gate) + o);
+    hn.x *= g.x; hn.y *= g.y; hn.z *= g.z; hn.w *= g.w;
+  }
   Io<bf16_t>::store4(static_cast<bf16_t*>(p.y) + o, hn);
 }
 

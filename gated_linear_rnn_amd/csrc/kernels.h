@@ -63,6 +63,7 @@ struct DecodeArgs {
   int B, D;
   int splits;         // set by the launcher
   float* chan;        // set by the launcher: [3, D] per-channel gate constants
+  const void* gate;   // [B, D] bf16 or NULL: y = RNE(h * gate) instead of RNE(h)
 };
 int decode_splits(int B, int D);
 size_t decode_partial_bytes(int B, int D);
@@ -173,6 +174,17 @@ struct MqaDecodeArgs {
 };
 size_t mqa_decode_partial_bytes(int B, int D);
 hipError_t launch_mqa_decode(const MqaDecodeArgs& a, hipStream_t s);
+// Small-M bf16 products for decode steps: partial[S][M][N] = the S K-range partial sums of
+// A [M,K] Bm [N,K]^T (S = splitk_splits(M, N, K)), then RNE_bf16 of their fixed-order sum.
+int splitk_splits(int M, int N, int K);
+size_t splitk_partial_bytes(int M, int N, int K);
+hipError_t launch_splitk_bf16(const void* A, const void* Bm, int M, int N, int K, int S, float* partial,
+                             hipStream_t s);
+hipError_t launch_splitk_out_bf16(const float* partial, int S, int M, int N, void* out, hipStream_t s);
+// The recurrent block's input linears in a decode step: p = RNE(sum), g = RNE(GeLU(sum)) of
+// the partial sums [S][M][2R] (columns [0, R) and [R, 2R)).
+hipError_t launch_splitk_inproj_bf16(const float* partial, int S, int M, int R, void* p, void* g,
+                                     hipStream_t s);
 
 // ---------------------------------------------------------------- lru.hip
 // The fused RG-LRU layer (gate GEMM + log-space gates + chunked scan) for bf16 I/O.

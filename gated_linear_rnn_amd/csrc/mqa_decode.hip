@@ -88,12 +88,17 @@ __global__ __launch_bounds__(CfgSplitK::NW * 64, 2) void splitk_partial_kernel(
   }
 }
 
-static hipError_t launch_splitk(const bf16_t* A, const bf16_t* Bm, int M, int N, int K, int S,
-                                float* partial, hipStream_t st) {
+hipError_t launch_splitk_bf16(const void* A, const void* Bm, int M, int N, int K, int S, float* partial,
+                             hipStream_t st) {
   const int MT = (M + CfgSplitK::BM - 1) / CfgSplitK::BM;
   const int NT = (N + CfgSplitK::BNR - 1) / CfgSplitK::BNR;
-  splitk_partial_kernel<<<MT * NT * S, CfgSplitK::NW * 64, 0, st>>>(A, Bm, M, N, K, S, partial);
+  splitk_partial_kernel<<<MT * NT * S, CfgSplitK::NW * 64, 0, st>>>(
+      static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(Bm), M, N, K, S, partial);
   return hipGetLastError();
+}
+
+size_t splitk_partial_bytes(int M, int N, int K) {
+  return size_t(splitk_splits(M, N, K)) * M * N * sizeof(float);
 }
 
 // position of sequence b (negative positions are taken as 0)
@@ -149,6 +154,12 @@ __global__ __launch_bounds__(256) void out_finish_kernel(const float* partial, i
   float acc = partial[idx];
   for (int s = 1; s < S; ++s) acc += partial[size_t(s) * n + idx];
   Io<IO>::store1(out + idx, acc);
+}
+
+hipError_t launch_splitk_out_bf16(const float* partial, int S, int M, int N, void* out, hipStream_t st) {
+  const size_t n = size_t(M) * N;
+  out_finish_kernel<bf16_t><<<int((n + 255) / 256), 256, 0, st>>>(partial, S, M, N, static_cast<bf16_t*>(out));
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- attention (bf16)
@@ -364,9 +375,9 @@ __global__ __launch_bounds__(128) void decode_attn_f32_kernel(const float* qbuf,
 // ---------------------------------------------------------------- the step
 size_t mqa_decode_partial_bytes(int B, int D) {
   const int N1 = D + 2 * kDhD;
-  const size_t a = size_t(splitk_splits(B, N1, D)) * B * N1;
-  const size_t c = size_t(splitk_splits(B, D, D)) * B * D;
-  return (a > c ? a : c) * sizeof(float);
+  const size_t a = splitk_partial_bytes(B, N1, D);
+  const size_t c = splitk_partial_bytes(B, D, D);
+  return a > c ? a : c;
 }
 
 hipError_t launch_mqa_decode(const MqaDecodeArgs& a, hipStream_t st) {
@@ -376,8 +387,7 @@ hipError_t launch_mqa_decode(const MqaDecodeArgs& a, hipStream_t st) {
   hipError_t e;
   if (a.bf16) {
     const int S1 = splitk_splits(B, N1, D);
-    e = launch_splitk(static_cast<const bf16_t*>(a.x), static_cast<const bf16_t*>(a.Wqkv), B, N1, D, S1,
-                      a.partial, st);
+    e = launch_splitk_bf16(a.x, a.Wqkv, B, N1, D, S1, a.partial, st);
     if (e != hipSuccess) return e;
     qkv_finish_kernel<bf16_t><<<int((pairs + 255) / 256), 256, 0, st>>>(
         a.partial, S1, B, D, a.pos, a.window, static_cast<bf16_t*>(a.qbuf),
@@ -390,13 +400,9 @@ hipError_t launch_mqa_decode(const MqaDecodeArgs& a, hipStream_t st) {
         float(1.4426950408889634 / sqrt(double(kDhD))), static_cast<bf16_t*>(a.attn));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int S2 = splitk_splits(B, D, D);
-    e = launch_splitk(static_cast<const bf16_t*>(a.attn), static_cast<const bf16_t*>(a.Wo), B, D, D, S2,
-                      a.partial, st);
+    e = launch_splitk_bf16(a.attn, a.Wo, B, D, D, S2, a.partial, st);
     if (e != hipSuccess) return e;
-    const size_t n = size_t(B) * D;
-    out_finish_kernel<bf16_t><<<int((n + 255) / 256), 256, 0, st>>>(a.partial, S2, B, D,
-                                                                    static_cast<bf16_t*>(a.out));
-    return hipGetLastError();
+    return launch_splitk_out_bf16(a.partial, S2, B, D, a.out, st);
   }
   PlainGemmArgs pa{};
   pa.A = a.x; pa.Bm = a.Wqkv; pa.M = B; pa.N = N1; pa.K = D; pa.lda = D; pa.ldb = D; pa.ldc = N1;

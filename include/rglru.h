@@ -215,6 +215,27 @@ int rglru_block_fwd(int B, int T, int D, int R, rglru_dtype io, float c, const v
                     const void* W_out, void* out, float* h_T, void* conv_state_out, void* ws,
                     size_t ws_bytes, hipStream_t stream);
 
+/* Workspace bytes rglru_block_decode_step needs (0 for invalid arguments). */
+size_t rglru_block_decode_workspace_bytes(int B, int D, int R, rglru_dtype io);
+
+/*
+ * One generation step of the whole recurrent block (rglru_block_fwd on a length-1 sequence
+ * with the carried state; the blog page "Griffin's Compromise", section "Hawk": generation
+ * reads and writes only the current token and a fixed-size state): the input linears on
+ * x_t, the branch's decode step (rglru_decode_step) on p with the state updated in place,
+ * z = RNE_io(h g), out_t = RNE_io(z W_out^T).  Run over the tokens after an
+ * rglru_block_fwd prefill whose h_T and conv_state_out seed (h, conv_state), it continues
+ * that forward (to fp32 summation order).
+ *   x_t [B,D] io; conv_state [B,3,R] io in/out (ignored when conv_w is NULL); h [B,R] fp32
+ *   in/out; out_t [B,D] io (output); the weights as in rglru_block_fwd.
+ *   Repeated calls give identical bits.
+ */
+int rglru_block_decode_step(int B, int D, int R, rglru_dtype io, float c, const void* x_t,
+                            const void* W_in, const void* conv_w, const float* conv_b,
+                            void* conv_state, const void* W_a, const void* W_x, const float* b_a,
+                            const float* b_x, const float* lambda, float* h, const void* W_out,
+                            void* out_t, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Workspace bytes gated_mlp_fwd needs (0 for invalid arguments). */
 size_t gated_mlp_fwd_workspace_bytes(int B, int T, int D, int MD, rglru_dtype io);
 

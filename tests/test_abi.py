@@ -204,3 +204,28 @@ def test_mqa_decode_rejects_invalid_arguments(lib):
         assert call(**{kw: None}) == -1, kw
     assert call(vc=BAD) == -1
     assert call(ws=None) == -4
+
+
+def test_block_decode_workspace_query(lib):
+    assert lib.rglru_block_decode_workspace_bytes(256, 2560, 2560, 1) >= 4 * 256 * 2560 * 2
+    assert lib.rglru_block_decode_workspace_bytes(1, 64, 96, 1) == 0
+
+
+@no_gpu
+def test_block_decode_rejects_invalid_arguments(lib):
+    def call(B=2, D=64, R=128, io=1, c=8.0, **over):
+        names = ("x", "W_in", "conv_w", "conv_b", "cs", "Wa", "Wx", "ba", "bx", "lam", "h", "W_out", "out", "ws")
+        args = dict.fromkeys(names, A)
+        args.update(conv_w=None, conv_b=None, cs=None)
+        wsb = over.pop("wsb", 1 << 40)
+        args.update(over)
+        return lib.rglru_block_decode_step(B, D, R, io, c, *[args[k] for k in names[:-1]], args["ws"], wsb, None)
+    assert call(B=0) == -1
+    assert call(R=100) == -2
+    assert call(io=2) == -3
+    for k in ("x", "W_in", "Wa", "Wx", "ba", "bx", "lam", "h", "W_out", "out"):
+        assert call(**{k: None}) == -1, k
+    assert call(conv_w=A) == -1                                          # conv_w without state
+    assert call(h=BAD) == -1
+    assert call(ws=None) == -4
+    assert call(wsb=3) == -4

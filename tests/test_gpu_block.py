@@ -117,3 +117,62 @@ def test_block_full_training_shape_one_sequence(lib):
     print(f"full block b={b} err(out)={eo:.3e} err(h_T)={eh:.3e}", flush=True)
     assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
     assert np.all(np.isfinite(out))
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_block_prefill_then_decode(lib, io):
+    """rglru_block_fwd over the first 300 tokens (its h_T and conv_state_out seed the
+    state), then 24 rglru_block_decode_step calls: every output against one oracle block
+    forward over the 324 tokens."""
+    T0, steps = 300, 24
+    w = workloads.TRAIN_FWD.with_shape(B=2, T=T0 + steps, D=192, io=io, h0="normal", history="normal")
+    p = workloads.make_block_inputs(w, d_model=320)
+    d = _device(p)
+    x = d["x_block"]
+    out0, hT, cso = lib.block_forward(x[:, :T0].contiguous(), d["W_in"], d["conv_w"], d["conv_b"],
+                                      d["conv_state"], d["W_a"], d["W_x"], d["b_a"], d["b_x"], d["lam"],
+                                      d["h0"], d["W_out"], p["c"])
+    ws = lib.workspace(lib.block_decode_workspace_bytes(2, 320, 192, TORCH_IO[io]))
+    outs = []
+    for t in range(T0, T0 + steps):
+        o = torch.empty((2, 320), dtype=TORCH_IO[io], device="cuda")
+        lib.rglru_block_decode_step(x[:, t].contiguous(), d["W_in"], d["conv_w"], d["conv_b"], cso,
+                                    d["W_a"], d["W_x"], d["b_a"], d["b_x"], d["lam"], hT, d["W_out"], o,
+                                    ws, p["c"])
+        outs.append(o)
+    torch.cuda.synchronize()
+    want = _oracle(p)
+    e0 = err(host(out0), want["out"][:, :T0])
+    e1 = err(host(torch.stack(outs, 1)), want["out"][:, T0:])
+    eh = err(host(hT), want["h_T"])
+    print(f"block prefill->decode io={io} err(prefill)={e0:.3e} err(decode)={e1:.3e} err(h)={eh:.3e}",
+          flush=True)
+    assert e0 <= TOL[io] and e1 <= TOL[io] and eh <= TOL[io]
+    np.testing.assert_array_equal(host(cso), want["conv_state_out"])
+
+
+def test_block_decode_full_shape_sampled_sequences(lib):
+    """B=256, D = R = 2560 (the decode workload's batch): 8 steps from its seeded state, the
+    outputs of 4 sequences against the oracle block forward over those sequences' 8 tokens."""
+    w = workloads.DECODE.with_shape(T=8, decode=False)
+    p = workloads.make_block_inputs(w)
+    d = _device(p)
+    cs, h = d["conv_state"].clone(), d["h0"].clone()
+    ws = lib.workspace(lib.block_decode_workspace_bytes(w.B, w.D, w.D, torch.bfloat16))
+    outs = []
+    for t in range(8):
+        o = torch.empty((w.B, w.D), dtype=torch.bfloat16, device="cuda")
+        lib.rglru_block_decode_step(d["x_block"][:, t].contiguous(), d["W_in"], d["conv_w"], d["conv_b"],
+                                    cs, d["W_a"], d["W_x"], d["b_a"], d["b_x"], d["lam"], h, d["W_out"], o,
+                                    ws, p["c"])
+        outs.append(o)
+    torch.cuda.synchronize()
+    sel = np.array([0, 1, 128, 255])
+    got = host(torch.stack(outs, 1))[sel]
+    want = oracle.block_forward(x=p["x_block"][sel], W_in=p["W_in"], conv_w=p["conv_w"], conv_b=p["conv_b"],
+                                conv_state_in=p["conv_state"][sel], W_a=p["W_a"], W_x=p["W_x"], b_a=p["b_a"],
+                                b_x=p["b_x"], lam=p["lam"], h0=p["h0"][sel], W_out=p["W_out"], c=p["c"],
+                                io="bf16")
+    e = err(got, want["out"])
+    print(f"block decode B=256 err(out)={e:.3e}", flush=True)
+    assert e <= TOL["bf16"]

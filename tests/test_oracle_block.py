@@ -161,3 +161,20 @@ def test_block_explicit_elementwise_evaluation():
             for dd in range(D):
                 want = f32(sum(W_out[dd, r] * z[r] for r in range(R)))
                 assert abs(o["out"][b, t, dd] - want) <= 2e-6 * max(1.0, abs(want)), (b, t, dd)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_block_decode_steps_equal_forward(io):
+    """The block on a length-1 sequence with the carried (conv history, h) - a decode step -
+    repeated over the tokens equals one block forward over them (the recurrence carries all
+    of the past in the fixed-size state)."""
+    rng = np.random.default_rng(13)
+    p = _block_params(rng, 2, 9, 64, 128, io)
+    full = _block(p)
+    cs, h = p["conv_state"], p["h0"]
+    for t in range(9):
+        step = _block(p, x=p["x_block"][:, t:t + 1], conv_state_in=cs, h0=h)
+        np.testing.assert_allclose(step["out"][:, 0], full["out"][:, t], rtol=1e-12, atol=1e-12)
+        cs, h = step["conv_state_out"], step["h_T"]
+    np.testing.assert_allclose(h, full["h_T"], rtol=1e-12)
+    np.testing.assert_array_equal(cs, full["conv_state_out"])
