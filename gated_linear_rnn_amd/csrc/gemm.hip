@@ -175,30 +175,57 @@ __global__ __launch_bounds__(C::NW * 64, C::NW >= 8 ? 2 : 1) void gemm_bf16_kern
     // kModeQkv: q and k columns are rotated; column pairs (2i, 2i+1) sit in lanes l, l^1
     const bool rot = MODE == kModeQkv && nb < p.split + 128;
     double theta[C::NF];   // 10000^(-2i/128) / (2 pi) turns per position, i = pair index
+    float c1[C::NF], s1[C::NF];   // the rotation by one position
 #pragma unroll
-    for (int f = 0; f < C::NF; ++f)
+    for (int f = 0; f < C::NF; ++f) {
       theta[f] = exp2(-double(((nb + f * 32 + col) & 127) >> 1) * (13.287712379549449 / 64.0)) *
                  0.15915494309189533577;
+      const float t1 = float(theta[f]);
+      c1[f] = __builtin_amdgcn_cosf(t1);
+      s1[f] = __builtin_amdgcn_sinf(t1);
+    }
+    // Accumulator slots 4g .. 4g+3 are four consecutive rows (positions): the angle of the
+    // first is evaluated exactly (fp64 reduction), the next three by rotating it one
+    // position at a time, unless the group straddles the end of a sequence.
 #pragma unroll
     for (int mf = 0; mf < C::MF; ++mf)
 #pragma unroll
       for (int f = 0; f < C::NF; ++f)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = mf * 32 + acc_row(v, lane);
-          const int chunk = (f * 4 + (col >> 3)) ^ (((r >> 2) & 1) << 2);
-          float val = acc[mf][f][v];
-          if (MODE == kModeQkv) {
-            const float other = __int_as_float(
-                __builtin_amdgcn_mov_dpp(__float_as_int(val), 0xB1, 0xF, 0xF, false));   // lane ^ 1
-            if (rot) {
-              const int m = m0 + wm * C::WTM + r;
-              const float turns = rope_turns(p.pos0 + m % p.T, theta[f]);
-              const float sn = __builtin_amdgcn_sinf(turns), cs = __builtin_amdgcn_cosf(turns);
-              val = (col & 1) ? fmaf(other, sn, val * cs) : fmaf(val, cs, -other * sn);
-            }
+        for (int g = 0; g < 4; ++g) {
+          const int rbase = mf * 32 + 8 * g + 4 * (lane >> 5);
+          const int pm = (m0 + wm * C::WTM + rbase) % (MODE == kModeQkv ? p.T : 1);
+          float cs = 1.f, sn = 0.f;
+          if (rot) {
+            const float turns = rope_turns(p.pos0 + pm, theta[f]);
+            sn = __builtin_amdgcn_sinf(turns);
+            cs = __builtin_amdgcn_cosf(turns);
           }
-          st[r * 64 + chunk * 8 + (col & 7)] = f2bf(gelu_side ? gelu_fast(val) : val);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int v = 4 * g + j, r = rbase + j;
+            const int chunk = (f * 4 + (col >> 3)) ^ (((r >> 2) & 1) << 2);
+            float val = acc[mf][f][v];
+            if (MODE == kModeQkv) {
+              const float other = __int_as_float(
+                  __builtin_amdgcn_mov_dpp(__float_as_int(val), 0xB1, 0xF, 0xF, false));   // lane ^ 1
+              if (rot) {
+                if (j > 0) {
+                  if (pm + j < p.T) {
+                    const float cn = fmaf(cs, c1[f], -sn * s1[f]);
+                    sn = fmaf(sn, c1[f], cs * s1[f]);
+                    cs = cn;
+                  } else {     // the group runs into the next sequence(s)
+                    const float turns = rope_turns(p.pos0 + (pm + j) % p.T, theta[f]);
+                    sn = __builtin_amdgcn_sinf(turns);
+                    cs = __builtin_amdgcn_cosf(turns);
+                  }
+                }
+                val = (col & 1) ? fmaf(other, sn, val * cs) : fmaf(val, cs, -other * sn);
+              }
+            }
+            st[r * 64 + chunk * 8 + (col & 7)] = f2bf(gelu_side ? gelu_fast(val) : val);
+          }
         }
     // LDS operations of a wave complete in order; the fence keeps the compiler from
     // moving the reads below above the writes

@@ -165,15 +165,13 @@ __global__ __launch_bounds__(512) void mqa_fwd_bf16_kernel(MqaArgs p) {
     const long kfirst = long(p.kv_pos0) + sbase, klast = kfirst + kKeys - 1;
     const bool whole = sbase + kKeys - 1 <= s_hi && klast <= long(p.q_pos0) + t0 &&
                        kfirst > long(p.q_pos0) + t0 + kQPos - 1 - p.window;
-    float mx = -1e30f;
+    // (raw scores: the 1/sqrt(128) log2(e) scale is folded into the exponent below)
+    float mx = -INFINITY;
     if (whole) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          acc_s[kb][v] *= p.scale_log2;
-          mx = fmaxf(mx, acc_s[kb][v]);
-        }
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, acc_s[kb][v]);
     } else {
       const int rel = int(qpos - p.kv_pos0 - sbase);       // the query's own key index
       const int j_hi = min(rel, s_hi - sbase) - 4 * half;
@@ -184,12 +182,13 @@ __global__ __launch_bounds__(512) void mqa_fwd_bf16_kernel(MqaArgs p) {
         for (int v = 0; v < 16; ++v) {
           const int j = kb * 32 + 8 * (v >> 2) + (v & 3);  // key index minus 4 half
           const bool ok = j <= j_hi && j > j_lo;
-          const float sc = ok ? acc_s[kb][v] * p.scale_log2 : -INFINITY;
+          const float sc = ok ? acc_s[kb][v] : -INFINITY;
           acc_s[kb][v] = sc;
           mx = fmaxf(mx, sc);
         }
     }
     mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(mx))));
+    mx = fmaxf(mx * p.scale_log2, -1e30f);                 // log2 domain; -1e30: nothing valid
     // The reference max m_run only moves when the tile max exceeds it by more than 8 (in
     // log2 units): the weights exp2(s - m_run) then stay below 2^8, exact enough in fp32,
     // and the rescaling of O and l, which needs a new m_run, is mostly skipped.  The final
@@ -211,7 +210,7 @@ __global__ __launch_bounds__(512) void mqa_fwd_bf16_kernel(MqaArgs p) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float e = __builtin_amdgcn_exp2f(acc_s[kb][v] - m_run);
+        const float e = __builtin_amdgcn_exp2f(fmaf(acc_s[kb][v], p.scale_log2, -m_run));
         lsum += e;
         pf[kb * 2 + (v >> 3)][v & 7] = (__bf16)e;
       }

@@ -68,6 +68,8 @@ SMALL = [
     (workloads.TRAIN_FWD, 3, 200, 640, 64, True),
     (workloads.TRAIN_FWD, 1, 1500, 384, 1024, True),
     (workloads.TRAIN_FWD, 1, 130, 128, 1, True),
+    (workloads.TRAIN_FWD, 5, 3, 128, 4, True),      # sequences shorter than a RoPE row group
+    (workloads.TRAIN_FWD, 3, 7, 256, 16, True),     # T % 4 != 0: groups straddle sequences
 ]
 
 
