@@ -26,12 +26,14 @@
 namespace rglru {
 
 constexpr int kDh = 128;                   // head width
-constexpr int kQPos = 64;                  // query positions per workgroup
 constexpr int kHB = 4;                     // heads per workgroup
+constexpr int kMqaWaves = 8;               // waves per workgroup (4 measured ~5% slower)
 constexpr int kKeys = 64;                  // keys per tile
 constexpr int kKBytes = kKeys * kDh * 2;   // K tile: 64 rows x 256 B
 constexpr int kVBytes = kDh * kKeys * 2;   // V^T tile: 128 rows x 128 B
 constexpr int kBuf = kKBytes + kVBytes;
+
+template <int V> struct BufTag { static constexpr int value = V; };
 
 // position of key j (0..63) in a V^T row: bits 2 and 3 swapped (an involution)
 __device__ __forceinline__ int vt_pos(int j) {
@@ -43,8 +45,15 @@ __device__ __forceinline__ int vt_off(int d, int pos) {
   return d * 128 + (((pos >> 3) ^ ((d >> 1) ^ (d >> 4))) & 7) * 16 + (pos & 7) * 2;
 }
 
-__global__ __launch_bounds__(512) void mqa_fwd_bf16_kernel(MqaArgs p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kBuf];
+// NW waves: NW / 4 blocks of 32 positions x 4 heads.
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void mqa_fwd_bf16_kernel(MqaArgs p) {
+  constexpr int kQPos = 32 * (NW / 4);       // query positions per workgroup
+  // Two tile buffers: tile kt is read from one while tile kt + 1 is written into the other.
+  // The loop below is unrolled by two so that each copy of the tile step names its buffers
+  // at compile time (the LDS addresses become constant offsets).
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[kBuf];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[kBuf];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = p.H, T = p.T, S = p.S;
@@ -85,37 +94,46 @@ __global__ __launch_bounds__(512) void mqa_fwd_bf16_kernel(MqaArgs p) {
   }
 
   // ---- tile loads
-  auto load_k = [&](int kt, int buf) {   // DMA: 2 wave instructions of 1 KB (4 rows) each
-    unsigned char* dst = lds + buf * kBuf;
+  auto load_k = [&](int kt, unsigned char* dst) {   // DMA: 16 wave instructions of 1 KB each
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int blk = i * 8 + wave;
+    for (int i = 0; i < 16 / NW; ++i) {
+      const int blk = i * NW + wave;
       const int row = blk * 4 + (lane >> 4), pc = lane & 15;
       const int s = min(s_lo + kt * kKeys + row, s_hi);
       const bf16_t* src = kg + size_t(s) * kDh + ((pc ^ (row & 15)) * 8);
       __builtin_amdgcn_global_load_lds((void*)src, (void*)(dst + blk * 1024), 16, 0, 0);
     }
   };
-  // V: thread -> keys 2 kp and 2 kp + 1 (adjacent positions of V^T), dims 8 dc .. +8
-  uint4 vreg[2];
-  const int vkp = tid >> 4, vdc = tid & 15;
+  // V: thread -> key pairs (2 kp, 2 kp + 1) (adjacent positions of V^T), dims 8 dc .. +8;
+  // 512 pair-chunks per tile, 512 / (64 NW) per thread
+  constexpr int VIT = 8 / NW;
+  uint4 vreg[VIT][2];
+  const int vdc = tid & 15;
   auto fetch_v = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int s = min(s_lo + kt * kKeys + 2 * vkp + i, s_hi);
-      vreg[i] = *reinterpret_cast<const uint4*>(vg + size_t(s) * kDh + vdc * 8);
+    for (int it = 0; it < VIT; ++it) {
+      const int vkp = it * (NW * 4) + (tid >> 4);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int s = min(s_lo + kt * kKeys + 2 * vkp + i, s_hi);
+        vreg[it][i] = *reinterpret_cast<const uint4*>(vg + size_t(s) * kDh + vdc * 8);
+      }
     }
   };
-  auto store_v = [&](int buf) {          // transpose into V^T, keys in the permuted order
-    unsigned char* vt = lds + buf * kBuf + kKBytes;
-    const int pos = vt_pos(2 * vkp);     // even; key 2 kp + 1 sits at pos + 1
-    const uint32_t a[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-    const uint32_t c[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
+  auto store_v = [&](unsigned char* buf) {   // transpose into V^T, keys in the permuted order
+    unsigned char* vt = buf + kKBytes;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t lo = (a[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-      const uint32_t hi = (c[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-      *reinterpret_cast<uint32_t*>(vt + vt_off(vdc * 8 + e, pos)) = lo | (hi << 16);
+    for (int it = 0; it < VIT; ++it) {
+      const int vkp = it * (NW * 4) + (tid >> 4);
+      const int pos = vt_pos(2 * vkp);   // even; key 2 kp + 1 sits at pos + 1
+      const uint32_t a[4] = {vreg[it][0].x, vreg[it][0].y, vreg[it][0].z, vreg[it][0].w};
+      const uint32_t c[4] = {vreg[it][1].x, vreg[it][1].y, vreg[it][1].z, vreg[it][1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t lo = (a[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        const uint32_t hi = (c[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        *reinterpret_cast<uint32_t*>(vt + vt_off(vdc * 8 + e, pos)) = lo | (hi << 16);
+      }
     }
   };
 
@@ -128,20 +146,29 @@ __global__ __launch_bounds__(512) void mqa_fwd_bf16_kernel(MqaArgs p) {
   const int partner = (lane ^ 32) << 2;
 
   if (ntiles > 0) {
-    load_k(0, 0);
+    load_k(0, lds0);
     fetch_v(0);
-    store_v(0);
+    store_v(lds0);
   }
   __syncthreads();
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
+  // one key tile: compute from buffer CUR while the next tile is loaded into the other one
+  // (the buffer is a compile-time choice, so each of the two copies addresses one array)
+  auto tile = [&](int kt, auto cur_tag) {
+    constexpr int CUR = decltype(cur_tag)::value;
+    const unsigned char* cur = CUR == 0 ? lds0 : lds1;
+    unsigned char* nxt = CUR == 0 ? lds1 : lds0;
     const bool more = kt + 1 < ntiles;
+    // Nothing is in flight here after the first tile (each tile ends waiting for its DMA),
+    // but on the first one the Q fragment loads may be: settle them before the next tile's
+    // loads are issued, so that the compiler's wait before the first K fragment read does
+    // not also cover those loads.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     if (more) {
-      load_k(kt + 1, buf ^ 1);
+      load_k(kt + 1, nxt);
       fetch_v(kt + 1);
     }
-    const unsigned char* ks_lds = lds + buf * kBuf;
-    const unsigned char* vt_lds = ks_lds + kKBytes;
+    const unsigned char* ks_lds = cur;
+    const unsigned char* vt_lds = cur + kKBytes;
 
     // ---- S^T = K Q^T: two 32-key blocks
     f32x16_t acc_s[2];
@@ -226,8 +253,12 @@ __global__ __launch_bounds__(512) void mqa_fwd_bf16_kernel(MqaArgs p) {
         acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[j], acc_o[db], 0, 0, 0);
       }
     }
-    if (more) store_v(buf ^ 1);
+    if (more) store_v(nxt);
     __syncthreads();   // the next tile is in LDS; every wave is done with this one
+  };
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    tile(kt, BufTag<0>{});
+    if (kt + 1 < ntiles) tile(kt + 1, BufTag<1>{});
   }
 
   // ---- normalise and store: lane = query, dims 32 db + 8 g + 4 half + 0..3
@@ -288,8 +319,9 @@ __global__ __launch_bounds__(128) void mqa_fwd_f32_kernel(MqaArgs p) {
 
 hipError_t launch_mqa_fwd(const MqaArgs& a, bool bf16, hipStream_t s) {
   if (bf16) {
-    const int HG = (a.H + kHB - 1) / kHB, TB = (a.T + kQPos - 1) / kQPos;
-    mqa_fwd_bf16_kernel<<<a.B * TB * HG, 512, 0, s>>>(a);
+    constexpr int NW = kMqaWaves;
+    const int HG = (a.H + kHB - 1) / kHB, TB = (a.T + 32 * (NW / 4) - 1) / (32 * (NW / 4));
+    mqa_fwd_bf16_kernel<NW><<<a.B * TB * HG, NW * 64, 0, s>>>(a);
   } else {
     const size_t n = size_t(a.B) * a.T * a.H;
     mqa_fwd_f32_kernel<<<int((n + 127) / 128), 128, 0, s>>>(a);
