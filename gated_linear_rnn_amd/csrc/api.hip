@@ -304,6 +304,8 @@ const char* rglru_status_string(int status) {
   }
 }
 
+void rglru_test_set_scan_direct_polls(int polls) { set_scan_direct_polls(polls); }
+
 int conv1d_causal4(int B, int T, int D, rglru_dtype io, const void* x, const void* w,
                    const float* b, const void* state_in, void* u, void* state_out,
                    hipStream_t stream) {

@@ -226,9 +226,14 @@ struct ScanFwdArgs {
   void* h_all;            // [B,T,D] of the scan state type (Acc), or NULL: every h_t
   float* h_T;             // [B,D] or NULL
   void* status;           // look-back words, scan_status_bytes(B,T,D,sizeof(Acc)) bytes
-  uint32_t* counter;      // one ticket counter (zeroed with the status words)
-  bool prefilled;         // status and counter already initialised on this stream
+  uint32_t* counter;      // 64 ticket counters (zeroed with the status words)
+  bool prefilled;         // status and counters already initialised on this stream
+  int groups;             // tile groups, set by the launcher
+  int direct_polls;       // look-back polls before a summary is computed directly; set by the launcher
 };
+// Test hook: polls of an unpublished look-back predecessor before the forward scan computes
+// its summary itself (negative: always, ignoring published values).
+void set_scan_direct_polls(int polls);
 // Look-back status bytes of a scan whose state type has acc_bytes bytes (4 or 8).
 size_t scan_status_bytes(int B, int T, int D, int acc_bytes);
 // Acc = float for bf16 I/O, double for fp32 I/O.

@@ -309,6 +309,18 @@ int local_mqa_decode_step(int B, int D, rglru_dtype io, int window, const int* p
                           const void* W_qkv, const void* W_o, void* k_cache, void* v_cache,
                           void* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Test hook of the forward scan's look-back (rglru_scan, rglru_bwd's state recompute and
+ * the fp32-I/O forward).  A chunk of the chained scan normally takes the summary its
+ * predecessor chunks publish; one that finds a predecessor unpublished after `polls` polls
+ * computes that summary itself from memory (the same bits), so the scan never depends on
+ * the order in which the GPU starts workgroups.  polls < 0 ignores every published value
+ * and always computes them (slow; for tests that this path gives the same bits).  The
+ * setting is process-wide host state read at each launch; the default is 2048.  Not
+ * thread-safe against concurrent launches.
+ */
+void rglru_test_set_scan_direct_polls(int polls);
+
 #ifdef __cplusplus
 }
 #endif
