@@ -208,6 +208,7 @@ def main():
         out["prefill_decode_latency"] = bench_latency(g, torch, np, workloads)
         out["gated_mlp_fwd"] = bench_mlp(g, torch, np, workloads)
         out["local_mqa_fwd"] = bench_mqa(g, torch, np, workloads)
+        out["split_gates_scan"] = bench_split(g, torch, np, workloads, copy_gbps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, np)
     print(json.dumps(out))
@@ -471,6 +472,62 @@ def bench_mqa(g, torch, np, workloads, steps=30, window=1024):
             "tokens_per_s": M / (ms * 1e-3), "TFLOPs": flop / (ms * 1e-3) / 1e12,
             "flop_per_step": flop, "attention_flop": attn_flop, "steps": steps,
             "decode_full_window": dec}
+
+
+def bench_split(g, torch, np, workloads, copy_gbps, steps=50):
+    """The unfused form of the same forward at the headline shape: rglru_gates (the gate GEMM
+    writing a and beta, fp32) then rglru_scan (the conv recomputed from x, the chunked scan,
+    y), timed per kernel with events.  The scan moves 12 bytes per element (x 2, a 4, beta 4,
+    y 2); its interval includes the look-back status fill it launches first."""
+    w = workloads.TRAIN_FWD
+    B, T, D = w.B, w.T, w.D
+    bf = torch.bfloat16
+    p = workloads.make_inputs(w)
+    dev = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dt)
+    x, cw, cb = dev(p["x"], bf), dev(p["conv_w"], bf), dev(p["conv_b"])
+    Wa, Wx, ba, bx, lam = dev(p["W_a"], bf), dev(p["W_x"], bf), dev(p["b_a"]), dev(p["b_x"]), dev(p["lam"])
+    u = torch.empty_like(x)
+    y = torch.empty_like(x)
+    hT = torch.empty((B, D), dtype=torch.float32, device="cuda")
+    a = torch.empty((B, T, D), dtype=torch.float32, device="cuda")
+    beta = torch.empty_like(a)
+    ws = g.workspace(g.scan_workspace_bytes(B, T, D, bf))
+    g.conv1d_causal4(x, cw, cb, None, u, None)
+
+    def once(ev=None):
+        if ev is not None:
+            ev[0].record()
+        g.rglru_gates(u, Wa, Wx, ba, bx, lam, a, beta, p["c"])
+        if ev is not None:
+            ev[1].record()
+        g.rglru_scan(x, cw, cb, None, a, beta, None, y, hT, ws)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(steps):
+        once()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for k in range(steps):
+        once(evs[k])
+    torch.cuda.synchronize()
+    gates_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    scan_bytes = B * T * D * 12
+    scan_gbps = scan_bytes / (scan_ms * 1e-3) / 1e9
+    gflop = 2.0 * B * T * 2 * D * D
+    return {
+        "workload": w.name,
+        "gates_ms": gates_ms,
+        "gates_TFLOPs": gflop / (gates_ms * 1e-3) / 1e12,
+        "scan_ms": scan_ms,
+        "scan_bytes": scan_bytes,
+        "scan_GBps": scan_gbps,
+        "scan_frac_of_peak": scan_gbps / PEAK_HBM_GBPS,
+        "scan_frac_of_measured_copy": scan_gbps / copy_gbps,
+        "tokens_per_s_gates_plus_scan": B * T / ((gates_ms + scan_ms) * 1e-3),
+        "steps": steps,
+    }
 
 
 def bench_latency(g, torch, np, workloads):

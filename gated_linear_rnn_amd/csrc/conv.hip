@@ -161,19 +161,24 @@ template hipError_t launch_conv_decode<bf16_t>(int, int, const void*, const void
 
 // Look-back status words to all ones (empty) and ncounters ticket counters to zero, in one
 // launch.
+// 16-byte stores over the first n4 * 4 words (status is 16-byte aligned), then the tail.
 __global__ __launch_bounds__(256) void fill_status_kernel(uint32_t* __restrict__ status, size_t n,
                                                           uint32_t* __restrict__ counters,
                                                           int ncounters) {
   size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < size_t(ncounters)) counters[i] = 0u;
   const size_t stride = size_t(gridDim.x) * blockDim.x;
-  for (; i < n; i += stride) status[i] = 0xffffffffu;
+  const size_t n4 = n / 4;
+  uint4* s4 = reinterpret_cast<uint4*>(status);
+  const uint4 ones = make_uint4(0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu);
+  for (size_t k = i; k < n4; k += stride) s4[k] = ones;
+  if (i < n - n4 * 4) status[n4 * 4 + i] = 0xffffffffu;
 }
 
 hipError_t launch_fill_status(uint32_t* status, size_t words, uint32_t* counters, int ncounters,
                               hipStream_t s) {
-  size_t blocks = (words + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
+  size_t blocks = (words / 4 + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
   if (blocks == 0) blocks = 1;
   fill_status_kernel<<<int(blocks), 256, 0, s>>>(status, words, counters, ncounters);
   return hipGetLastError();
