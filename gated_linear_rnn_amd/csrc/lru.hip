@@ -107,7 +107,6 @@ __device__ __forceinline__ void lru_epilogue(const LruArgs& p, unsigned char* ld
   // rows of this lane's groups are lrow0 + 32 mf + 8 gq + rr; those >= lim are past the end
   const int lrow0 = wm * C::WTM + 4 * half;
   const int lim = rows - lrow0;
-  const int partner = (lane ^ 32) << 2;               // ds_bpermute byte address
   // Per group: the summary (A = prod a, H) and the running composition over the 32 groups
   // of the wave's 128 rows in time order (for each gq the lower-half lane's group comes
   // first, then the upper-half lane's).  pre[q] is the map in front of this lane's group q.
@@ -131,10 +130,9 @@ __device__ __forceinline__ void lru_epilogue(const LruArgs& p, unsigned char* ld
       Hq = fmaf(a, Hq, bu);
       Aq = Aq * a;
     }
-    const float Ap = __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(Aq)));
-    const float Hp = __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(Hq)));
-    const float A0 = half ? Ap : Aq, H0 = half ? Hp : Hq;   // rows 8gq .. 8gq+3
-    const float A1 = half ? Aq : Ap, H1 = half ? Hq : Hp;   // rows 8gq+4 .. 8gq+7
+    const WaveHalves sa = wave_halves(Aq), sh = wave_halves(Hq);
+    const float A0 = sa.lo, H0 = sh.lo;   // rows 8gq .. 8gq+3 (the lower-half lane's group)
+    const float A1 = sa.hi, H1 = sh.hi;   // rows 8gq+4 .. 8gq+7
     const float R0A = RA, R0H = RH;
     RH = fmaf(A0, RH, H0);
     RA = A0 * RA;

@@ -143,7 +143,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void mqa_fwd_bf16_kernel(MqaArgs p
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc_o[db][v] = 0.f;
   float m_run = -1e30f, l_run = 0.f;          // running max (log2 domain) and partial sum
-  const int partner = (lane ^ 32) << 2;
 
   if (ntiles > 0) {
     load_k(0, lds0);
@@ -214,7 +213,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void mqa_fwd_bf16_kernel(MqaArgs p
           mx = fmaxf(mx, sc);
         }
     }
-    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(mx))));
+    {
+      const WaveHalves mh = wave_halves(mx);       // this lane's and the partner lane's max
+      mx = fmaxf(mh.lo, mh.hi);
+    }
     mx = fmaxf(mx * p.scale_log2, -1e30f);                 // log2 domain; -1e30: nothing valid
     // The reference max m_run only moves when the tile max exceeds it by more than 8 (in
     // log2 units): the weights exp2(s - m_run) then stay below 2^8, exact enough in fp32,
@@ -262,7 +264,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void mqa_fwd_bf16_kernel(MqaArgs p
   }
 
   // ---- normalise and store: lane = query, dims 32 db + 8 g + 4 half + 0..3
-  const float l_tot = l_run + __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(l_run)));
+  const WaveHalves lh = wave_halves(l_run);
+  const float l_tot = lh.lo + lh.hi;   // this lane's and the partner lane's sum
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qok) {
     bf16_t* orow = static_cast<bf16_t*>(p.o) + (size_t(b) * T + t) * size_t(H) * kDh + size_t(head) * kDh;

@@ -209,7 +209,6 @@ __global__ __launch_bounds__(512) void decode_attn_bf16_kernel(const bf16_t* qbu
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc_o[db][v] = 0.f;
   float m_run = -1e30f, l_run = 0.f;
-  const int partner = (lane ^ 32) << 2;
   unsigned char* vt = lds + wave * kWaveVt;
 
   for (int kt = wave; kt < ntiles; kt += 8) {
@@ -254,7 +253,10 @@ __global__ __launch_bounds__(512) void decode_attn_bf16_kernel(const bf16_t* qbu
         acc_s[kb][v] = sc;
         mx = fmaxf(mx, sc);
       }
-    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(mx))));
+    {
+      const WaveHalves mh = wave_halves(mx);       // this lane's and the partner lane's max
+      mx = fmaxf(mh.lo, mh.hi);
+    }
     const bool bump = mx > m_run + 8.f;
     if (__any(bump)) {
       const float m_new = bump ? mx : m_run;

@@ -61,6 +61,18 @@ __device__ __forceinline__ void f4set(float4& v, int j, float s) {
   if (j == 0) v.x = s; else if (j == 1) v.y = s; else if (j == 2) v.z = s; else v.w = s;
 }
 
+// ------------------------------------------------------------------ wave halves
+// The value of x in lanes 0-31 and in lanes 32-63, side by side in every lane:
+// lo[i] = x[i mod 32], hi[i] = x[32 + (i mod 32)].  One gfx950 v_permlane32_swap_b32 with x
+// as both operands (a VALU instruction, no LDS round trip as with ds_bpermute).
+struct WaveHalves {
+  float lo, hi;
+};
+__device__ __forceinline__ WaveHalves wave_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
 // ------------------------------------------------------------------ conv (R1)
 // u = RNE_io(b + w0 x_t + w1 x_{t-1} + w2 x_{t-2} + w3 x_{t-3}), one fixed fma order so
 // every kernel that evaluates u produces the same bits.

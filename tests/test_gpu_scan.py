@@ -93,3 +93,22 @@ def test_full_size_scan_sampled_channels(lib):
     ey, eh = err(y[:, :, ch], o["y"]), err(hT[:, ch], o["h_T"])
     print(f"full-size split scan err(y)={ey:.2e} err(h_T)={eh:.2e}", flush=True)
     assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+EDGES = [
+    # (io, B, T, D): one step, two steps, exactly one 64-step chunk, one chunk and one step,
+    # two full chunks, the largest tile count along T among the small cases
+    ("bf16", 1, 1, 64), ("bf16", 2, 2, 64), ("bf16", 1, 64, 128), ("bf16", 2, 65, 64),
+    ("bf16", 1, 128, 192), ("f32", 1, 3, 64), ("f32", 2, 129, 64), ("bf16", 3, 1000, 64),
+]
+
+
+@pytest.mark.parametrize("io,B,T,D", EDGES, ids=[f"{io}-{B}x{T}x{D}" for io, B, T, D in EDGES])
+def test_split_scan_edge_lengths(lib, io, B, T, D):
+    p = make(workloads.TRAIN_FWD, B=B, T=T, D=D, io=io, h0="normal", history="normal")
+    d = device_inputs(p)
+    y, hT = _split_scan(lib, p, d)
+    o = oracle_forward(p)
+    ey, eh = err(y, o["y"]), err(hT, o["h_T"])
+    print(f"split scan io={io} {B}x{T}x{D} err(y)={ey:.2e} err(h_T)={eh:.2e}", flush=True)
+    assert ey <= TOL[io] and eh <= TOL[io]
