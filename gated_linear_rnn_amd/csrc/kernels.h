@@ -226,7 +226,7 @@ struct ScanFwdArgs {
   void* h_all;            // [B,T,D] of the scan state type (Acc), or NULL: every h_t
   float* h_T;             // [B,D] or NULL
   void* status;           // look-back words, scan_status_bytes(B,T,D,sizeof(Acc)) bytes
-  uint32_t* counter;      // 64 ticket counters (zeroed with the status words)
+  uint32_t* counter;      // 64 words zeroed with the status words (the forward scan takes no tickets)
   bool prefilled;         // status and counters already initialised on this stream
   int groups;             // tile groups, set by the launcher
   int direct_polls;       // look-back polls before a summary is computed directly; set by the launcher
