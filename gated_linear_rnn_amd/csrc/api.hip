@@ -3,6 +3,8 @@
 // HIP call and never allocates device memory.  Declarations and the contract of each
 // entry point are in include/rglru.h.
 #include <math.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 #include "../../include/rglru.h"
@@ -172,6 +174,7 @@ struct BwdWs {
   double* conv_part;
   void* status;
   uint32_t* counter;
+  float* tail;   // bf16: split-tail partials of the input- and weight-gradient products
 };
 
 BwdWs carve_bwd(Carver& cv, int B, int T, int D, rglru_dtype io) {
@@ -194,6 +197,12 @@ BwdWs carve_bwd(Carver& cv, int B, int T, int D, rglru_dtype io) {
   w.conv_part = cv.take<double>(P * 5 * D);
   w.status = cv.take<unsigned char>(scan_status_bytes(B, T, D, acc_bytes(io)));
   w.counter = cv.take<uint32_t>(64);
+  w.tail = nullptr;
+  if (io == RGLRU_BF16) {
+    const size_t tb = std::max(plain_gemm_tail_bytes(int(M), D, 2 * D),
+                               plain_gemm_tail_bytes(2 * D, D, int(Mp)));
+    if (tb) w.tail = cv.take<float>(tb / sizeof(float));
+  }
   return w;
 }
 
@@ -567,6 +576,7 @@ int rglru_bwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const
   pg.A = w.dz_hi; pg.A2 = bf ? w.dz_lo : nullptr; pg.Bm = w.WT;
   pg.M = M; pg.N = D; pg.K = 2 * D; pg.lda = 2 * D; pg.ldb = 2 * D; pg.ldc = D;
   pg.C = du; pg.addend = du;
+  pg.tail_ws = w.tail;
   if (bf) RG_CHECK(launch_plain_gemm_bf16(pg, stream));
   else RG_CHECK(launch_plain_gemm_f32(pg, stream));
 
@@ -585,16 +595,26 @@ int rglru_bwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const
                                      static_cast<float*>(w.uT), Mp, Mp, stream));
   }
   const size_t eb = io_bytes(io);
-  for (int gi = 0; gi < 2; ++gi) {
+  if (bf) {
+    // dW_a and dW_x in one product over the 2D rows of dz^T (rows past D land in dW_x), so
+    // the two share their rounds on the CUs and a last, partly filled round splits its K
     PlainGemmArgs q{};
-    q.A = static_cast<const unsigned char*>(w.dzT_hi) + size_t(gi) * D * Mp * eb;
-    q.A2 = bf ? static_cast<const unsigned char*>(w.dzT_lo) + size_t(gi) * D * Mp * eb : nullptr;
-    q.Bm = w.uT;
-    q.M = D; q.N = D; q.K = Mp; q.lda = Mp; q.ldb = Mp; q.ldc = D;
-    q.C = gi == 0 ? dW_a : dW_x;
-    q.addend = nullptr;
-    if (bf) RG_CHECK(launch_plain_gemm_bf16(q, stream));
-    else RG_CHECK(launch_plain_gemm_f32(q, stream));
+    q.A = w.dzT_hi; q.A2 = w.dzT_lo; q.Bm = w.uT;
+    q.M = 2 * D; q.N = D; q.K = Mp; q.lda = Mp; q.ldb = Mp; q.ldc = D;
+    q.C = dW_a; q.C2 = dW_x; q.m_split = D; q.addend = nullptr;
+    q.tail_ws = w.tail;
+    RG_CHECK(launch_plain_gemm_bf16(q, stream));
+  } else {
+    for (int gi = 0; gi < 2; ++gi) {
+      PlainGemmArgs q{};
+      q.A = static_cast<const unsigned char*>(w.dzT_hi) + size_t(gi) * D * Mp * eb;
+      q.A2 = nullptr;
+      q.Bm = w.uT;
+      q.M = D; q.N = D; q.K = Mp; q.lda = Mp; q.ldb = Mp; q.ldc = D;
+      q.C = gi == 0 ? dW_a : dW_x;
+      q.addend = nullptr;
+      RG_CHECK(launch_plain_gemm_f32(q, stream));
+    }
   }
 
   // 5. conv backward and the fixed-order reductions

@@ -47,12 +47,14 @@ struct GemmParams {
   // plain epilogue
   float* C;
   const float* addend;
+  float* C2;          // kModePlain: rows m >= m_split go to C2 (row m - m_split)
+  int m_split;
   bf16_t* C16;        // kModeInProj (p), kModeOut, kModeQkv (q)
   bf16_t* G16;        // kModeInProj (GeLU branch), kModeQkv (k)
   bf16_t* V16;        // kModeQkv (v)
   int split;          // kModeInProj: R; kModeQkv: D
   int T, pos0;        // kModeQkv: row m is at position pos0 + m % T
-  // kModeOut tail split: workgroups [0, tail_first) compute whole tiles (the tiles
+  // kModeOut / kModePlain tail split: workgroups [0, tail_first) compute whole tiles (the tiles
   // [0, tail_first) of the grouped order); the remaining tiles are each computed by
   // tail_split workgroups over equal K ranges into fp32 partials at tail_ws, which
   // tail_fixup_kernel adds and rounds.  Without a split tail_first = MT * NT.
@@ -114,13 +116,13 @@ __global__ __launch_bounds__(C::NW * 64, C::NW >= 8 ? 2 : 1) void gemm_bf16_kern
   const int NT = kPlainTile ? (p.N + C::BNR - 1) / C::BNR : (p.N + C::BC - 1) / C::BC;
   int tm, tn, part, L;
   tile_coords(MT, NT, p.tail_first, p.tail_split, tm, tn, part, L);
-  const bool tail = MODE == kModeOut && int(blockIdx.x) >= p.tail_first;
+  const bool tail = (MODE == kModeOut || MODE == kModePlain) && int(blockIdx.x) >= p.tail_first;
   const int m0 = tm * C::BM;
   const int n0 = tn * (kPlainTile ? C::BNR : C::BC);
   const int kc = tail ? p.K / p.tail_split : p.K;
 
   TileOperands op;
-  op.A = p.A + size_t(part) * kc; op.A2 = p.A2;
+  op.A = p.A + size_t(part) * kc; op.A2 = p.A2 ? p.A2 + size_t(part) * kc : nullptr;
   op.B0 = p.B0 + size_t(part) * kc; op.B1 = p.B1;
   op.lda = p.lda; op.ldb = p.ldb; op.K = kc;
   op.a_row0 = m0; op.a_rows = p.M - m0;
@@ -156,7 +158,8 @@ __global__ __launch_bounds__(C::NW * 64, C::NW >= 8 ? 2 : 1) void gemm_bf16_kern
             const size_t o = size_t(m) * p.ldc + n;
             float val = acc[mf][f][v];
             if (p.addend) val += p.addend[o];
-            p.C[o] = val;
+            if (m < p.m_split) p.C[o] = val;
+            else p.C2[size_t(m - p.m_split) * p.ldc + n] = val;
           }
         }
     }
@@ -340,6 +343,7 @@ size_t out_gemm_tail_bytes(int M, int N, int K) {
   plan_tail(tiles, K / C::BK, first, split);
   return split > 1 ? size_t(tiles - first) * split * C::BM * C::BNR * sizeof(float) : 0;
 }
+size_t plain_gemm_tail_bytes(int M, int N, int K) { return out_gemm_tail_bytes(M, N, K); }
 
 // The split tail's fixup: sum the S partials of each element in order, round to bf16,
 // store inside the matrix.  One thread per 8 consecutive columns of a tile row.
@@ -371,6 +375,34 @@ __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmParams p, int MT, i
   *reinterpret_cast<uint4*>(p.C16 + size_t(m) * p.ldc + n) = w;
 }
 
+// The same fixup for the fp32 plain mode: partials summed in order, the addend added last
+// (as the untiled epilogue does), rows past m_split written to C2.
+template <class C>
+__global__ __launch_bounds__(256) void tail_fixup_f32_kernel(GemmParams p, int MT, int NT) {
+  constexpr int CH = C::BNR / 8;
+  const size_t per_tile = size_t(C::BM) * CH;
+  const size_t idx = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int ntail = MT * NT - p.tail_first;
+  if (idx >= per_tile * ntail) return;
+  const int i = int(idx / per_tile);
+  const int r = int(idx % per_tile) / CH, ck = int(idx % per_tile) % CH;
+  int tm, tn;
+  grouped_tile(p.tail_first + i, MT, NT, tm, tn);
+  const int m = tm * C::BM + r, n0 = tn * C::BNR + ck * 8;
+  if (m >= p.M) return;
+  const float* src = p.tail_ws + size_t(i) * p.tail_split * (C::BM * C::BNR) + r * C::BNR + ck * 8;
+  float* dst = m < p.m_split ? p.C + size_t(m) * p.ldc : p.C2 + size_t(m - p.m_split) * p.ldc;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int n = n0 + e;
+    if (n >= p.N) break;
+    float v = src[e];
+    for (int sp = 1; sp < p.tail_split; ++sp) v += src[size_t(sp) * (C::BM * C::BNR) + e];
+    if (p.addend) v += p.addend[size_t(m) * p.ldc + n];
+    dst[n] = v;
+  }
+}
+
 template <class C, int MODE, bool DUAL>
 static hipError_t run_bf16(GemmParams p, hipStream_t s) {
   const int MT = (p.M + C::BM - 1) / C::BM;
@@ -381,13 +413,15 @@ static hipError_t run_bf16(GemmParams p, hipStream_t s) {
   const int tiles = MT * NT;
   p.tail_first = tiles;
   p.tail_split = 1;
-  if (MODE == kModeOut && p.tail_ws) plan_tail(tiles, p.K / C::BK, p.tail_first, p.tail_split);
+  if ((MODE == kModeOut || MODE == kModePlain) && p.tail_ws)
+    plan_tail(tiles, p.K / C::BK, p.tail_first, p.tail_split);
   const int grid = p.tail_first + (tiles - p.tail_first) * p.tail_split;
   gemm_bf16_kernel<C, MODE, DUAL><<<grid, C::NW * 64, 0, s>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.tail_split == 1) return e;
   const size_t threads = size_t(tiles - p.tail_first) * C::BM * (C::BNR / 8);
-  tail_fixup_kernel<C><<<int((threads + 255) / 256), 256, 0, s>>>(p, MT, NT);
+  if (MODE == kModePlain) tail_fixup_f32_kernel<C><<<int((threads + 255) / 256), 256, 0, s>>>(p, MT, NT);
+  else tail_fixup_kernel<C><<<int((threads + 255) / 256), 256, 0, s>>>(p, MT, NT);
   return hipGetLastError();
 }
 
@@ -415,6 +449,9 @@ hipError_t launch_plain_gemm_bf16(const PlainGemmArgs& g, hipStream_t s) {
   p.M = g.M; p.N = g.N; p.K = g.K;
   p.lda = g.lda; p.ldb = g.ldb; p.ldc = g.ldc;
   p.C = g.C; p.addend = g.addend;
+  p.C2 = g.C2;
+  p.m_split = g.m_split > 0 ? g.m_split : g.M;
+  p.tail_ws = g.tail_ws;
   if (g.A2) return run_bf16<CfgPlain, kModePlain, true>(p, s);
   return run_bf16<CfgPlain, kModePlain, false>(p, s);
 }

@@ -79,7 +79,15 @@ struct PlainGemmArgs {
   int lda, ldb, ldc;
   float* C;
   const float* addend;   // may equal C (read before write by the same thread) or NULL
+  // bf16 operands only: rows m >= m_split go to C2 (row m - m_split, same ldc; addend must
+  // be NULL then); m_split = 0 means M (everything in C).  tail_ws (plain_gemm_tail_bytes
+  // bytes, or NULL) lets the tiles of a last, partly filled round split their K loop.
+  float* C2;
+  int m_split;
+  float* tail_ws;
 };
+// fp32 partials a plain bf16 GEMM of this shape needs for its split tail (0: no split).
+size_t plain_gemm_tail_bytes(int M, int N, int K);
 
 // The linears of the recurrent block, bf16 in and out, C = A Bm^T with row strides K.
 // With G: N = 2 split columns, C[M, split] = the first split columns, G[M, split] = GeLU of

@@ -112,3 +112,22 @@ def test_split_scan_edge_lengths(lib, io, B, T, D):
     ey, eh = err(y, o["y"]), err(hT, o["h_T"])
     print(f"split scan io={io} {B}x{T}x{D} err(y)={ey:.2e} err(h_T)={eh:.2e}", flush=True)
     assert ey <= TOL[io] and eh <= TOL[io]
+
+
+def test_direct_summaries_over_a_long_chain(lib):
+    """T = 2500: 40 chunks, so a look-back can collect more summaries than its 16-entry
+    window (the rest are read again, or computed again, on the way forward)."""
+    p = make(workloads.TRAIN_FWD, B=1, T=2500, D=64, h0="normal", history="normal")
+    d = device_inputs(p)
+    try:
+        y0, h0 = _split_scan(lib, p, d)
+        lib.rglru_test_set_scan_direct_polls(-1)
+        y1, h1 = _split_scan(lib, p, d)
+    finally:
+        lib.rglru_test_set_scan_direct_polls(DEFAULT_POLLS)
+    np.testing.assert_array_equal(y0, y1)
+    np.testing.assert_array_equal(h0, h1)
+    o = oracle_forward(p)
+    ey, eh = err(y0, o["y"]), err(h0, o["h_T"])
+    print(f"long chain err(y)={ey:.2e} err(h_T)={eh:.2e}", flush=True)
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
