@@ -89,13 +89,34 @@ template hipError_t launch_transpose<float>(const float*, int, int, int, float*,
 
 constexpr int kBSteps = 8, kBTG = 16, kBChunk = 128, kBCh = 64;
 
+// 4 consecutive elements moved in their storage format (global -> LDS), widened on read.
+template <typename IO> struct Raw4x;
+template <> struct Raw4x<bf16_t> {
+  uint2 v;
+  __device__ __forceinline__ void zero() { v = make_uint2(0u, 0u); }
+  __device__ __forceinline__ void load(const bf16_t* g) { v = *reinterpret_cast<const uint2*>(g); }
+  __device__ __forceinline__ void store(bf16_t* l) const { *reinterpret_cast<uint2*>(l) = v; }
+  __device__ __forceinline__ static float4 read(const bf16_t* l) { return Io<bf16_t>::load4(l); }
+};
+template <> struct Raw4x<float> {
+  float4 v;
+  __device__ __forceinline__ void zero() { v = make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ __forceinline__ void load(const float* g) { v = *reinterpret_cast<const float4*>(g); }
+  __device__ __forceinline__ void store(float* l) const { *reinterpret_cast<float4*>(l) = v; }
+  __device__ __forceinline__ static float4 read(const float* l) { return *reinterpret_cast<const float4*>(l); }
+};
+
 template <typename IO>
 __global__ __launch_bounds__(256) void conv_bwd_kernel(ConvBwdArgs p) {
-  // du and x staging; after the time loop the same LDS holds the fp64 tile reduction
-  __shared__ __attribute__((aligned(16))) float smem[2 * (kBChunk + 3) * kBCh];
-  static_assert(sizeof(double) * kBTG * 5 * kBCh <= sizeof(float) * 2 * (kBChunk + 3) * kBCh, "");
-  float* dus = smem;
-  float* xs = smem + (kBChunk + 3) * kBCh;
+  // du (fp32) and x (in its I/O type: 2 bytes at bf16, so three workgroups fit on a CU)
+  // staging; after the time loop the same LDS holds the fp64 tile reduction
+  constexpr int kDuBytes = (kBChunk + 3) * kBCh * 4;
+  constexpr int kXBytes = (kBChunk + 3) * kBCh * int(sizeof(IO));
+  constexpr int kRedBytes = int(sizeof(double)) * kBTG * 5 * kBCh;
+  constexpr int kSmem = kDuBytes + kXBytes > kRedBytes ? kDuBytes + kXBytes : kRedBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmem];
+  float* dus = reinterpret_cast<float*>(smem);
+  IO* xs = reinterpret_cast<IO*>(smem + kDuBytes);
   double (*sRed)[5][kBCh] = reinterpret_cast<double (*)[5][kBCh]>(smem);
   const int B = p.B, T = p.T, D = p.D;
   const int nchunks = (T + kBChunk - 1) / kBChunk;
@@ -116,10 +137,11 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(ConvBwdArgs p) {
     if (tdu < T) v = *reinterpret_cast<const float4*>(p.du + (size_t(b) * T + tdu) * D + d0 + 4 * q);
     *reinterpret_cast<float4*>(&dus[rr * kBCh + 4 * q]) = v;
     const int tx = t0 - 3 + rr;
-    float4 xv = make_float4(0, 0, 0, 0);
-    if (tx >= 0 && tx < T) xv = Io<IO>::load4(x + (size_t(b) * T + tx) * D + d0 + 4 * q);
-    else if (tx < 0 && cs) xv = Io<IO>::load4(cs + (size_t(b) * 3 + 3 + tx) * D + d0 + 4 * q);
-    *reinterpret_cast<float4*>(&xs[rr * kBCh + 4 * q]) = xv;
+    Raw4x<IO> xv;
+    xv.zero();
+    if (tx >= 0 && tx < T) xv.load(x + (size_t(b) * T + tx) * D + d0 + 4 * q);
+    else if (tx < 0 && cs) xv.load(cs + (size_t(b) * 3 + 3 + tx) * D + d0 + 4 * q);
+    xv.store(&xs[rr * kBCh + 4 * q]);
   }
   const IO* w = static_cast<const IO*>(p.conv_w);
   const float4 w0 = Io<IO>::load4(w + d), w1 = Io<IO>::load4(w + D + d),
@@ -134,10 +156,10 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(ConvBwdArgs p) {
     const float4 du1 = *reinterpret_cast<const float4*>(&dus[(lt + 1) * kBCh + 4 * cg]);
     const float4 du2 = *reinterpret_cast<const float4*>(&dus[(lt + 2) * kBCh + 4 * cg]);
     const float4 du3 = *reinterpret_cast<const float4*>(&dus[(lt + 3) * kBCh + 4 * cg]);
-    const float4 x0 = *reinterpret_cast<const float4*>(&xs[(lt + 3) * kBCh + 4 * cg]);
-    const float4 x1 = *reinterpret_cast<const float4*>(&xs[(lt + 2) * kBCh + 4 * cg]);
-    const float4 x2 = *reinterpret_cast<const float4*>(&xs[(lt + 1) * kBCh + 4 * cg]);
-    const float4 x3 = *reinterpret_cast<const float4*>(&xs[lt * kBCh + 4 * cg]);
+    const float4 x0 = Raw4x<IO>::read(&xs[(lt + 3) * kBCh + 4 * cg]);
+    const float4 x1 = Raw4x<IO>::read(&xs[(lt + 2) * kBCh + 4 * cg]);
+    const float4 x2 = Raw4x<IO>::read(&xs[(lt + 1) * kBCh + 4 * cg]);
+    const float4 x3 = Raw4x<IO>::read(&xs[lt * kBCh + 4 * cg]);
     float4 dxv;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -181,35 +203,31 @@ template hipError_t launch_conv_bwd<float>(const ConvBwdArgs&, hipStream_t);
 template hipError_t launch_conv_bwd<bf16_t>(const ConvBwdArgs&, hipStream_t);
 
 // Sums of per-tile partials in a fixed order (tile index ascending), in fp64.
+// One thread per (quantity, channel): q < 3 the scan partials (db_a, db_x, the dLambda sum),
+// q = 3 .. 7 the conv partials (dconv_w rows 0..3, dconv_b).  Each sums its P partial rows
+// in order, so the result does not depend on how threads are scheduled.
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs p) {
-  const int d = blockIdx.x * blockDim.x + threadIdx.x;
-  if (d >= p.D) return;
   const size_t D = p.D;
-  double sa = 0, sx = 0, sl = 0;
-  for (int q = 0; q < p.P; ++q) {
-    const double* r = p.scan_part + size_t(q) * 3 * D;
-    sa += r[d];
-    sx += r[D + d];
-    sl += r[2 * D + d];
-  }
-  p.db_a[d] = float(sa);
-  p.db_x[d] = float(sx);
-  p.dlambda[d] = float(sl * double(sigmoid_negf(p.lam[d])));
-  if (p.conv_part) {
-    double sw[4] = {0, 0, 0, 0}, sb = 0;
-    for (int q = 0; q < p.P; ++q) {
-      const double* r = p.conv_part + size_t(q) * 5 * D;
-      for (int k = 0; k < 4; ++k) sw[k] += r[k * D + d];
-      sb += r[4 * D + d];
-    }
-    if (p.dconv_w)
-      for (int k = 0; k < 4; ++k) p.dconv_w[k * D + d] = float(sw[k]);
-    if (p.dconv_b) p.dconv_b[d] = float(sb);
+  const size_t idx = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int nq = p.conv_part ? 8 : 3;
+  if (idx >= size_t(nq) * D) return;
+  const int q = int(idx / D), d = int(idx % D);
+  const double* src = q < 3 ? p.scan_part + size_t(q) * D + d : p.conv_part + size_t(q - 3) * D + d;
+  const size_t stride = (q < 3 ? 3 : 5) * D;
+  double acc = 0.0;
+  for (int r = 0; r < p.P; ++r) acc += src[size_t(r) * stride];
+  switch (q) {
+    case 0: p.db_a[d] = float(acc); break;
+    case 1: p.db_x[d] = float(acc); break;
+    case 2: p.dlambda[d] = float(acc * double(sigmoid_negf(p.lam[d]))); break;
+    case 7: if (p.dconv_b) p.dconv_b[d] = float(acc); break;
+    default: if (p.dconv_w) p.dconv_w[size_t(q - 3) * D + d] = float(acc); break;
   }
 }
 
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
-  reduce_kernel<<<(a.D + 255) / 256, 256, 0, s>>>(a);
+  const size_t threads = size_t(a.conv_part ? 8 : 3) * a.D;
+  reduce_kernel<<<int((threads + 255) / 256), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
