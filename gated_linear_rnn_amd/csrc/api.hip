@@ -174,7 +174,7 @@ struct BwdWs {
   double* conv_part;
   void* status;
   uint32_t* counter;
-  float* tail;   // bf16: split-tail partials of the input- and weight-gradient products
+  float* tail;   // bf16: split-tail partials of the recompute, input- and weight-gradient products
 };
 
 BwdWs carve_bwd(Carver& cv, int B, int T, int D, rglru_dtype io) {
@@ -199,8 +199,9 @@ BwdWs carve_bwd(Carver& cv, int B, int T, int D, rglru_dtype io) {
   w.counter = cv.take<uint32_t>(64);
   w.tail = nullptr;
   if (io == RGLRU_BF16) {
-    const size_t tb = std::max(plain_gemm_tail_bytes(int(M), D, 2 * D),
-                               plain_gemm_tail_bytes(2 * D, D, int(Mp)));
+    const size_t tb = std::max({plain_gemm_tail_bytes(int(M), D, 2 * D),
+                                plain_gemm_tail_bytes(2 * D, D, int(Mp)),
+                                gate_gemm_tail_bytes(int(M), D, D)});
     if (tb) w.tail = cv.take<float>(tb / sizeof(float));
   }
   return w;
@@ -538,6 +539,7 @@ int rglru_bwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const
   g.U = u; g.Wa = W_a; g.Wx = W_x; g.M = M; g.N = D; g.K = D;
   g.ba = b_a; g.bx = b_x; g.lam = lambda; g.c = c;
   g.out0 = w.r; g.out1 = w.i;
+  g.tail_ws = w.tail;
   st = gate_projection(io, g, kEpiRI, w.r, w.i, stream);
   if (st != RGLRU_OK) return st;
   ScanFwdArgs sf{};

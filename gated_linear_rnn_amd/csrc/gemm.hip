@@ -116,14 +116,15 @@ __global__ __launch_bounds__(C::NW * 64, C::NW >= 8 ? 2 : 1) void gemm_bf16_kern
   const int NT = kPlainTile ? (p.N + C::BNR - 1) / C::BNR : (p.N + C::BC - 1) / C::BC;
   int tm, tn, part, L;
   tile_coords(MT, NT, p.tail_first, p.tail_split, tm, tn, part, L);
-  const bool tail = (MODE == kModeOut || MODE == kModePlain) && int(blockIdx.x) >= p.tail_first;
+  const bool tail = (MODE == kModeOut || MODE == kModePlain || MODE == kEpiAB || MODE == kEpiRI) &&
+                    int(blockIdx.x) >= p.tail_first;
   const int m0 = tm * C::BM;
   const int n0 = tn * (kPlainTile ? C::BNR : C::BC);
   const int kc = tail ? p.K / p.tail_split : p.K;
 
   TileOperands op;
   op.A = p.A + size_t(part) * kc; op.A2 = p.A2 ? p.A2 + size_t(part) * kc : nullptr;
-  op.B0 = p.B0 + size_t(part) * kc; op.B1 = p.B1;
+  op.B0 = p.B0 + size_t(part) * kc; op.B1 = p.B1 ? p.B1 + size_t(part) * kc : nullptr;
   op.lda = p.lda; op.ldb = p.ldb; op.K = kc;
   op.a_row0 = m0; op.a_rows = p.M - m0;
   op.b_row0 = n0; op.b_rows = p.N - n0;
@@ -133,17 +134,22 @@ __global__ __launch_bounds__(C::NW * 64, C::NW >= 8 ? 2 : 1) void gemm_bf16_kern
   // ---------------------------------------------------------------- epilogue
   const int col = lane & 31;
   if (tail) {
-    // fp32 partial of this K part: the whole tile, row-major [BM][BNR]
+    // fp32 partial of this K part: the whole tile, row-major [BM][BNR], columns in B-tile
+    // row order (gate tiles: the BC z^a channels, then the BC z^x channels)
     float* dst = p.tail_ws + (size_t(L - p.tail_first) * p.tail_split + part) * (C::BM * C::BNR);
 #pragma unroll
-    for (int f = 0; f < C::NF; ++f)
+    for (int f = 0; f < C::NF; ++f) {
+      constexpr int HF = C::NF / 2;
+      const int bcol = C::PLAIN ? wn * C::WTNR + f * 32 + col
+                                : (f / HF) * C::BC + wn * (C::BC / C::WN) + (f % HF) * 32 + col;
 #pragma unroll
       for (int mf = 0; mf < C::MF; ++mf)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = wm * C::WTM + mf * 32 + acc_row(v, lane);
-          dst[r * C::BNR + wn * C::WTNR + f * 32 + col] = acc[mf][f][v];
+          dst[r * C::BNR + bcol] = acc[mf][f][v];
         }
+    }
   } else if (MODE == kModePlain) {
 #pragma unroll
     for (int f = 0; f < C::NF; ++f) {
@@ -344,6 +350,13 @@ size_t out_gemm_tail_bytes(int M, int N, int K) {
   return split > 1 ? size_t(tiles - first) * split * C::BM * C::BNR * sizeof(float) : 0;
 }
 size_t plain_gemm_tail_bytes(int M, int N, int K) { return out_gemm_tail_bytes(M, N, K); }
+size_t gate_gemm_tail_bytes(int M, int N, int K) {
+  typedef GemmCfg<256, 128, 2, 4, false, 64, 2> C;
+  const int tiles = ((M + C::BM - 1) / C::BM) * ((N + C::BC - 1) / C::BC);
+  int first, split;
+  plan_tail(tiles, K / C::BK, first, split);
+  return split > 1 ? size_t(tiles - first) * split * C::BM * C::BNR * sizeof(float) : 0;
+}
 
 // The split tail's fixup: sum the S partials of each element in order, round to bf16,
 // store inside the matrix.  One thread per 8 consecutive columns of a tile row.
@@ -403,6 +416,41 @@ __global__ __launch_bounds__(256) void tail_fixup_f32_kernel(GemmParams p, int M
   }
 }
 
+// The same fixup for the gate modes: z^a and z^x of each (row, channel) summed over the
+// parts in order, then the gate epilogue of the whole tiles.
+template <class C, int MODE>
+__global__ __launch_bounds__(256) void tail_fixup_gate_kernel(GemmParams p, int MT, int NT) {
+  const size_t per_tile = size_t(C::BM) * C::BC;
+  const size_t idx = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int ntail = MT * NT - p.tail_first;
+  if (idx >= per_tile * ntail) return;
+  const int i = int(idx / per_tile);
+  const int r = int(idx % per_tile) / C::BC, c = int(idx % per_tile) % C::BC;
+  int tm, tn;
+  grouped_tile(p.tail_first + i, MT, NT, tm, tn);
+  const int m = tm * C::BM + r, ch = tn * C::BC + c;
+  if (m >= p.M || ch >= p.N) return;
+  const float* src = p.tail_ws + size_t(i) * p.tail_split * (C::BM * C::BNR) + r * C::BNR + c;
+  float za = src[0], zx = src[C::BC];
+  for (int sp = 1; sp < p.tail_split; ++sp) {
+    za += src[size_t(sp) * (C::BM * C::BNR)];
+    zx += src[size_t(sp) * (C::BM * C::BNR) + C::BC];
+  }
+  const GateChan k = gate_chan(p.ba[ch], p.bx[ch], p.lam[ch], p.c);
+  const size_t o = size_t(m) * p.N + ch;
+  if (MODE == kEpiRI) {
+    float rr, ii;
+    gate_fast_ri(za, zx, k, rr, ii);
+    p.out0[o] = rr;
+    p.out1[o] = ii;
+  } else {
+    float a, beta;
+    gate_fast(za, zx, k, a, beta);
+    p.out0[o] = a;
+    p.out1[o] = beta;
+  }
+}
+
 template <class C, int MODE, bool DUAL>
 static hipError_t run_bf16(GemmParams p, hipStream_t s) {
   const int MT = (p.M + C::BM - 1) / C::BM;
@@ -413,12 +461,17 @@ static hipError_t run_bf16(GemmParams p, hipStream_t s) {
   const int tiles = MT * NT;
   p.tail_first = tiles;
   p.tail_split = 1;
-  if ((MODE == kModeOut || MODE == kModePlain) && p.tail_ws)
+  if ((MODE == kModeOut || MODE == kModePlain || MODE == kEpiAB || MODE == kEpiRI) && p.tail_ws)
     plan_tail(tiles, p.K / C::BK, p.tail_first, p.tail_split);
   const int grid = p.tail_first + (tiles - p.tail_first) * p.tail_split;
   gemm_bf16_kernel<C, MODE, DUAL><<<grid, C::NW * 64, 0, s>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.tail_split == 1) return e;
+  if (MODE == kEpiAB || MODE == kEpiRI) {
+    const size_t gthreads = size_t(tiles - p.tail_first) * C::BM * C::BC;
+    tail_fixup_gate_kernel<C, MODE><<<int((gthreads + 255) / 256), 256, 0, s>>>(p, MT, NT);
+    return hipGetLastError();
+  }
   const size_t threads = size_t(tiles - p.tail_first) * C::BM * (C::BNR / 8);
   if (MODE == kModePlain) tail_fixup_f32_kernel<C><<<int((threads + 255) / 256), 256, 0, s>>>(p, MT, NT);
   else tail_fixup_kernel<C><<<int((threads + 255) / 256), 256, 0, s>>>(p, MT, NT);
@@ -434,6 +487,7 @@ hipError_t launch_gate_gemm_bf16(const GateGemmArgs& g, int epi, hipStream_t s) 
   p.lda = g.K; p.ldb = g.K; p.ldc = g.N;
   p.ba = g.ba; p.bx = g.bx; p.lam = g.lam; p.c = g.c;
   p.out0 = g.out0; p.out1 = g.out1;
+  p.tail_ws = g.tail_ws;
   switch (epi) {
     case kEpiAB: return run_bf16<CfgGate, kEpiAB, false>(p, s);
     case kEpiRI: return run_bf16<CfgGate, kEpiRI, false>(p, s);

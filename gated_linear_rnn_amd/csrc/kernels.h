@@ -45,7 +45,11 @@ struct GateGemmArgs {
   const void* u;      // kEpiDecode: u [M, N] io
   float* h;           // kEpiDecode: state [M, N] in/out
   void* y;            // kEpiDecode: y [M, N] io
+  // bf16 kEpiAB / kEpiRI: fp32 partials (gate_gemm_tail_bytes bytes) or NULL; with them the
+  // tiles of a last, partly filled round split their K loop and a fixup applies the gates
+  float* tail_ws;
 };
+size_t gate_gemm_tail_bytes(int M, int N, int K);
 
 // One bf16 decode step after the conv: split-K gate projection into `partial`, then the
 // fixed-order sum, the gates and the state update (decode.hip).
