@@ -215,7 +215,8 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs p) {
   const double* src = q < 3 ? p.scan_part + size_t(q) * D + d : p.conv_part + size_t(q - 3) * D + d;
   const size_t stride = (q < 3 ? 3 : 5) * D;
   double acc = 0.0;
-  for (int r = 0; r < p.P; ++r) acc += src[size_t(r) * stride];
+#pragma unroll 8
+  for (int r = 0; r < p.P; ++r) acc += src[size_t(r) * stride];   // loads ahead, adds in order
   switch (q) {
     case 0: p.db_a[d] = float(acc); break;
     case 1: p.db_x[d] = float(acc); break;

@@ -402,17 +402,22 @@ __global__ __launch_bounds__(256) void tail_fixup_f32_kernel(GemmParams p, int M
   int tm, tn;
   grouped_tile(p.tail_first + i, MT, NT, tm, tn);
   const int m = tm * C::BM + r, n0 = tn * C::BNR + ck * 8;
-  if (m >= p.M) return;
+  if (m >= p.M || n0 >= p.N) return;
   const float* src = p.tail_ws + size_t(i) * p.tail_split * (C::BM * C::BNR) + r * C::BNR + ck * 8;
+  float4 v0 = *reinterpret_cast<const float4*>(src), v1 = *reinterpret_cast<const float4*>(src + 4);
+  for (int sp = 1; sp < p.tail_split; ++sp) {
+    const float4 a0 = *reinterpret_cast<const float4*>(src + size_t(sp) * (C::BM * C::BNR));
+    const float4 a1 = *reinterpret_cast<const float4*>(src + size_t(sp) * (C::BM * C::BNR) + 4);
+    v0.x += a0.x; v0.y += a0.y; v0.z += a0.z; v0.w += a0.w;
+    v1.x += a1.x; v1.y += a1.y; v1.z += a1.z; v1.w += a1.w;
+  }
+  const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
   float* dst = m < p.m_split ? p.C + size_t(m) * p.ldc : p.C2 + size_t(m - p.m_split) * p.ldc;
+  const float* add = p.addend ? p.addend + size_t(m) * p.ldc : nullptr;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int n = n0 + e;
-    if (n >= p.N) break;
-    float v = src[e];
-    for (int sp = 1; sp < p.tail_split; ++sp) v += src[size_t(sp) * (C::BM * C::BNR) + e];
-    if (p.addend) v += p.addend[size_t(m) * p.ldc + n];
-    dst[n] = v;
+    if (n < p.N) dst[n] = add ? v[e] + add[n] : v[e];
   }
 }
 
