@@ -325,21 +325,26 @@ __global__ __launch_bounds__(C::NW * 64, C::NW >= 8 ? 2 : 1) void gemm_bf16_kern
 typedef GemmCfg<256, 128, 2, 4, false, 64, 2> CfgGate;
 typedef GemmCfg<256, 128, 2, 4, true, 64, 2> CfgPlain;
 
-// Tail split of a kModeOut GEMM: the tiles of the last, partly filled round (R of them,
-// R <= half the CUs) are each computed by S workgroups over K / S, so that round takes
-// about 1/S of a full tile's time.  S = 4 or 2, the largest with S R <= CUs and
-// (K / BK) % S == 0; 1 when there is no such round or no split.
+// Tail split: the tiles of the last, partly filled round (R of them) are each computed by
+// S workgroups over K / S, so that they take about ceil(S R / CUs) / S of a full tile's
+// time instead of one.  S in {2, 3, 4} with (K / BK) % S == 0 minimising that (the
+// smaller S on a tie, fewer partials); 1 when nothing is gained (no partial round, or a
+// last round so full that no split fits it in fewer tile times).
 static void plan_tail(int tiles, int ksteps, int& first, int& split) {
   const int R = tiles % kPlanCUs;
   first = tiles;
   split = 1;
-  if (R == 0 || 2 * R > kPlanCUs) return;
-  for (int sp = 4; sp >= 2; sp /= 2)
-    if (sp * R <= kPlanCUs && ksteps % sp == 0) {
-      first = tiles - R;
+  if (R == 0) return;
+  double best = 1.0;
+  for (int sp = 2; sp <= 4; ++sp) {
+    if (ksteps % sp) continue;
+    const double cost = double((sp * R + kPlanCUs - 1) / kPlanCUs) / sp;
+    if (cost < best - 1e-9) {
+      best = cost;
       split = sp;
-      return;
+      first = tiles - R;
     }
+  }
 }
 
 size_t out_gemm_tail_bytes(int M, int N, int K) {
