@@ -229,6 +229,9 @@ __global__ __launch_bounds__(512) void decode_attn_bf16_kernel(const bf16_t* qbu
         *reinterpret_cast<uint32_t*>(vt + dvt_off(dc * 8 + e, ps)) = lo | (hi << 16);
       }
     }
+    // the V loads stay ahead of the K loads: with both in flight at once the wave needs more
+    // than its 256 registers and spills
+    __builtin_amdgcn_sched_barrier(0);
     // S^T = K Q^T, K rows straight from the cache
     f32x16_t acc_s[2];
 #pragma unroll
