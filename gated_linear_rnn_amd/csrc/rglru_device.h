@@ -19,6 +19,15 @@ __device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float(uint32_
 // fp32 -> bf16, round to nearest even (gfx950 v_cvt_pk_bf16_f32); NaN stays NaN.
 __device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
+// 16 bytes that this kernel reads exactly once, loaded with the non-temporal hint: a stream
+// of such loads keeps more of HBM's read bandwidth than ordinary ones (measured on a plain
+// 1 GiB read: ~6.1-6.6 TB/s against ~5.2-5.9 TB/s).  Not for data that is read again soon.
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_once4(const void* p) {
+  const f32x4v_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4v_t*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 // I/O element traits: load/store 4 consecutive channels as fp32.
 template <typename IO> struct Io;
 
@@ -29,6 +38,10 @@ template <> struct Io<float> {
   }
   __device__ __forceinline__ static void store4(float* p, float4 v) {
     *reinterpret_cast<float4*>(p) = v;
+  }
+  // a store of output that nothing in the kernel reads back, with the non-temporal hint
+  __device__ __forceinline__ static void store4_once(float* p, float4 v) {
+    __builtin_nontemporal_store(f32x4v_t{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4v_t*>(p));
   }
   __device__ __forceinline__ static float round(float v) { return v; }
   __device__ __forceinline__ static float load1(const float* p) { return *p; }
@@ -47,6 +60,12 @@ template <> struct Io<bf16_t> {
     r.x = uint32_t(f2bf(v.x)) | (uint32_t(f2bf(v.y)) << 16);
     r.y = uint32_t(f2bf(v.z)) | (uint32_t(f2bf(v.w)) << 16);
     *reinterpret_cast<uint2*>(p) = r;
+  }
+  __device__ __forceinline__ static void store4_once(bf16_t* p, float4 v) {
+    typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
+    const u32x2v_t r = {uint32_t(f2bf(v.x)) | (uint32_t(f2bf(v.y)) << 16),
+                        uint32_t(f2bf(v.z)) | (uint32_t(f2bf(v.w)) << 16)};
+    __builtin_nontemporal_store(r, reinterpret_cast<u32x2v_t*>(p));
   }
   // value after rounding to bf16 (nearest even), as fp32
   __device__ __forceinline__ static float round(float v) { return bf2f(f2bf(v)); }

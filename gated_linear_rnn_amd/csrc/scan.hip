@@ -264,8 +264,8 @@ __global__ __launch_bounds__(256, sizeof(Acc) == 4 ? 4 : 2) void scan_fwd_kernel
   for (int s = 0; s < kFSteps; ++s) {
     if (tf + s < T) {
       const uint32_t o = lane_g + uint32_t(s) * uint32_t(D) * 4u;
-      ga[s] = *reinterpret_cast<const float4*>(ta + o);
-      gb[s] = *reinterpret_cast<const float4*>(tbeta + o);
+      ga[s] = load_once4(ta + o);
+      gb[s] = load_once4(tbeta + o);
     }
   }
   // x rows from a base at row max(t0 - 3, 0) of the sequence, so every row t >= 0 the tile
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(256, sizeof(Acc) == 4 ? 4 : 2) void scan_fwd_kernel
     if (t < T) {
       const size_t o = (size_t(b) * T + t) * D + d;
       const float4 hf = make_float4(float(h[0]), float(h[1]), float(h[2]), float(h[3]));
-      if (y) Io<IO>::store4(y + o, hf);
+      if (y) Io<IO>::store4_once(y + o, hf);
       if (h_all) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) h_all[o + j] = h[j];
