@@ -44,6 +44,9 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-extras", action="store_true", help="skip the decode and fwd+bwd timings")
+    ap.add_argument("--split-only", action="store_true",
+                    help="only time the unfused path (rglru_gates, then rglru_scan) and print "
+                         "its figures (for kernel profiles of the scan)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -110,6 +113,9 @@ def main():
 
     g.load()
     torch.cuda.set_device(0)
+    if args.split_only:
+        print(json.dumps(bench_split(g, torch, np, workloads, measured_copy_gbps(torch))))
+        return
     w = workloads.TRAIN_FWD
     B, T, D = w.B, w.T, w.D
     M = B * T
@@ -477,8 +483,9 @@ def bench_mqa(g, torch, np, workloads, steps=30, window=1024):
 def bench_split(g, torch, np, workloads, copy_gbps, steps=50):
     """The unfused form of the same forward at the headline shape: rglru_gates (the gate GEMM
     writing a and beta, fp32) then rglru_scan (the conv recomputed from x, the chunked scan,
-    y), timed per kernel with events.  The scan moves 12 bytes per element (x 2, a 4, beta 4,
-    y 2); its interval includes the look-back status fill it launches first."""
+    y), timed per kernel with events, then the scan alone, back to back.  The scan moves 12
+    bytes per element (x 2, a 4, beta 4, y 2); its interval includes the look-back status
+    fill it launches first."""
     w = workloads.TRAIN_FWD
     B, T, D = w.B, w.T, w.D
     bf = torch.bfloat16
@@ -515,6 +522,15 @@ def bench_split(g, torch, np, workloads, copy_gbps, steps=50):
     scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     scan_bytes = B * T * D * 12
     scan_gbps = scan_bytes / (scan_ms * 1e-3) / 1e9
+    # the scan alone, back to back (no gates kernel writing a and beta just before)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.rglru_scan(x, cw, cb, None, a, beta, None, y, hT, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    alone_ms = e0.elapsed_time(e1) / steps
+    alone_gbps = scan_bytes / (alone_ms * 1e-3) / 1e9
     gflop = 2.0 * B * T * 2 * D * D
     return {
         "workload": w.name,
@@ -525,6 +541,9 @@ def bench_split(g, torch, np, workloads, copy_gbps, steps=50):
         "scan_GBps": scan_gbps,
         "scan_frac_of_peak": scan_gbps / PEAK_HBM_GBPS,
         "scan_frac_of_measured_copy": scan_gbps / copy_gbps,
+        "scan_alone_ms": alone_ms,
+        "scan_alone_GBps": alone_gbps,
+        "scan_alone_frac_of_peak": alone_gbps / PEAK_HBM_GBPS,
         "tokens_per_s_gates_plus_scan": B * T / ((gates_ms + scan_ms) * 1e-3),
         "steps": steps,
     }
