@@ -47,6 +47,9 @@ def _parse():
     ap.add_argument("--split-only", action="store_true",
                     help="only time the unfused path (rglru_gates, then rglru_scan) and print "
                          "its figures (for kernel profiles of the scan)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only time the decode extra (1024 steps at B=256, eager and one graph) "
+                         "and print its figures (for kernel profiles of the decode step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -113,6 +116,9 @@ def main():
 
     g.load()
     torch.cuda.set_device(0)
+    if args.decode_only:
+        print(json.dumps(bench_decode(g, torch, np, workloads)))
+        return
     if args.split_only:
         print(json.dumps(bench_split(g, torch, np, workloads, measured_copy_gbps(torch))))
         return
