@@ -23,6 +23,10 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off",                                   # only the explicit fmaf calls fuse
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",  # no packed fp32 VALU ops
+    # the only read-modify-write atomics are single-lane ticket counters: without the wave
+    # reduction this pass adds, the wait for the returned value sits at its first use, so
+    # loads issued in between stay in flight
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wno-unused-command-line-argument",
 ]
 

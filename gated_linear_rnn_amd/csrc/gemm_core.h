@@ -113,30 +113,30 @@ __device__ __forceinline__ void sched_reads_spread() {
   }
 }
 
-// Accumulate the tile into acc.  lds must hold C::LDS_BYTES; wave = wave index in the WG.
+// The operand DMA of one wave: per-lane source offsets (elements) of its global_load_lds
+// instructions, and the issue of one k-step into its ring stage.
 template <class C, bool DUAL>
-__device__ __forceinline__ void gemm_mainloop(const TileOperands& op, unsigned char* lds, int lane,
-                                              int wave, f32x16_t (&acc)[C::MF][C::NF]) {
-  const int wm = wave / C::WN, wn = wave % C::WN;
-  // per-lane source offsets (elements) of this wave's DMA loads
+struct GemmDma {
   uint32_t off[C::QPW];
+  int KT1;   // k-steps per pass
+  __device__ __forceinline__ GemmDma(const TileOperands& op, int lane, int wave) {
 #pragma unroll
-  for (int q = 0; q < C::QPW; ++q) {
-    const int r = (q * C::NW + wave) * C::RPI + lane / C::CPR;
-    const int pchunk = lane % C::CPR;
-    if (q < C::QA) {
-      const int gm = op.a_row0 + min(r, op.a_rows - 1);
-      off[q] = uint32_t(gm) * uint32_t(op.lda) + uint32_t((pchunk ^ ((r / C::RP) % C::CPR)) * 8);
-    } else {
-      const int rb = r - C::BM;
-      const int gn = op.b_row0 + min(C::PLAIN ? rb : rb % C::BC, op.b_rows - 1);
-      off[q] = uint32_t(gn) * uint32_t(op.ldb) + uint32_t((pchunk ^ ((rb / C::RP) % C::CPR)) * 8);
+    for (int q = 0; q < C::QPW; ++q) {
+      const int r = (q * C::NW + wave) * C::RPI + lane / C::CPR;
+      const int pchunk = lane % C::CPR;
+      if (q < C::QA) {
+        const int gm = op.a_row0 + min(r, op.a_rows - 1);
+        off[q] = uint32_t(gm) * uint32_t(op.lda) + uint32_t((pchunk ^ ((r / C::RP) % C::CPR)) * 8);
+      } else {
+        const int rb = r - C::BM;
+        const int gn = op.b_row0 + min(C::PLAIN ? rb : rb % C::BC, op.b_rows - 1);
+        off[q] = uint32_t(gn) * uint32_t(op.ldb) + uint32_t((pchunk ^ ((rb / C::RP) % C::CPR)) * 8);
+      }
     }
+    KT1 = op.K / C::BK;
   }
-  const int KT1 = op.K / C::BK;                // k-steps per pass
-  const int KT = DUAL ? 2 * KT1 : KT1;
-
-  auto issue = [&](int kt) {
+  __device__ __forceinline__ void issue(const TileOperands& op, unsigned char* lds, int wave,
+                                        int kt) const {
     const bf16_t* abase = (DUAL && kt >= KT1) ? op.A2 : op.A;
     const int kofs = (DUAL && kt >= KT1 ? kt - KT1 : kt) * C::BK;
     unsigned char* sbase = lds + (kt % C::STAGES) * C::STAGE;
@@ -146,7 +146,20 @@ __device__ __forceinline__ void gemm_mainloop(const TileOperands& op, unsigned c
       const bf16_t* gp = base + off[q] + kofs;
       __builtin_amdgcn_global_load_lds((void*)gp, (void*)(sbase + (q * C::NW + wave) * 1024), 16, 0, 0);
     }
-  };
+  }
+};
+
+// Accumulate the tile into acc.  lds must hold C::LDS_BYTES; wave = wave index in the WG.
+// first_issued: the caller has already issued k-step 0 (GemmDma::issue with the same op)
+// and nothing else on the vector-memory counter since, apart from operations it waits for.
+template <class C, bool DUAL>
+__device__ __forceinline__ void gemm_mainloop(const TileOperands& op, unsigned char* lds, int lane,
+                                              int wave, f32x16_t (&acc)[C::MF][C::NF],
+                                              bool first_issued = false) {
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const GemmDma<C, DUAL> dma(op, lane, wave);
+  const int KT = DUAL ? 2 * dma.KT1 : dma.KT1;
+  auto issue = [&](int kt) { dma.issue(op, lds, wave, kt); };
 
   // LDS byte offsets of this lane's operand fragment rows
   int arow[C::MF], brow[C::NF];
@@ -194,7 +207,7 @@ __device__ __forceinline__ void gemm_mainloop(const TileOperands& op, unsigned c
   constexpr int NM = C::MF * C::NF, NR = C::MF + C::NF, NM1 = NM / 2;
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
-    if (s < KT) issue(s);
+    if (s < KT && (s > 0 || !first_issued)) issue(s);
   if (S - 2 < KT) wait_dma_barrier<(S - 2) * C::QPW>();
   else wait_dma_barrier<0>();
   if (S - 1 < KT) issue(S - 1);

@@ -212,28 +212,50 @@ __global__ __launch_bounds__(CfgLru::NW * 64, 2) void lru_fused_kernel(LruArgs p
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   __shared__ uint32_t s_ticket;
   const int G = p.groups, g = blockIdx.x % G;
-  if (tid == 0) s_ticket = atomicAdd(p.counters + g, 1u);
-  __syncthreads();
-  const int k = __builtin_amdgcn_readfirstlane(int(s_ticket));
   const int B = p.B, T = p.T, D = p.D;
   const int NT = (D + kLruCh - 1) / kLruCh;
   const int per_level = B * NT / G;
-  const int tt = k / per_level;
-  const int chain = g + G * (k % per_level);
-  const int b = chain / NT, tn = chain % NT;
+  auto tile_of = [&](int k, int& b, int& tn, int& tt) {
+    tt = k / per_level;
+    const int chain = g + G * (k % per_level);
+    b = chain / NT;
+    tn = chain % NT;
+  };
+  auto operands = [&](int b, int tn, int tt) {
+    TileOperands op;
+    op.A = static_cast<const bf16_t*>(p.u); op.A2 = nullptr;
+    op.B0 = static_cast<const bf16_t*>(p.Wa);
+    op.B1 = static_cast<const bf16_t*>(p.Wx);
+    op.lda = D; op.ldb = D; op.K = D;
+    op.a_row0 = b * T + tt * kLruRows; op.a_rows = min(kLruRows, T - tt * kLruRows);
+    op.b_row0 = tn * kLruCh; op.b_rows = min(kLruCh, D - tn * kLruCh);
+    return op;
+  };
+  // The ticket's atomic round trip overlaps the first k-step's operand loads: those are
+  // issued for the tile this workgroup gets when the tickets of its group go in launch
+  // order (ticket blockIdx / G); if the ticket says otherwise, the loads are waited for and
+  // the tile's own are issued instead.
+  uint32_t ticket = 0;
+  if (tid == 0) ticket = atomicAdd(p.counters + g, 1u);
+  int b, tn, tt;
+  const int kp = int(blockIdx.x) / G;
+  tile_of(kp, b, tn, tt);
+  TileOperands op = operands(b, tn, tt);
+  GemmDma<C, false>(op, lane, wave).issue(op, lds, wave, 0);
+  if (tid == 0) s_ticket = ticket;  // after the loads are issued: the wait for the atomic
+                                    // (vmcnt in issue order) leaves them in flight
+  wait_dma_barrier<C::QPW>();       // the ticket is in LDS; the first k-step may still land
+  const int k = __builtin_amdgcn_readfirstlane(int(s_ticket));
+  const bool hit = k == kp;
+  if (!hit) {
+    wait_dma_barrier<0>();          // every wave's loads into stage 0 have landed
+    tile_of(k, b, tn, tt);
+    op = operands(b, tn, tt);
+  }
   const int t0 = tt * kLruRows;
   const int rows = min(kLruRows, T - t0);
-  const bf16_t* u = static_cast<const bf16_t*>(p.u);
-
-  TileOperands op;
-  op.A = u; op.A2 = nullptr;
-  op.B0 = static_cast<const bf16_t*>(p.Wa);
-  op.B1 = static_cast<const bf16_t*>(p.Wx);
-  op.lda = D; op.ldb = D; op.K = D;
-  op.a_row0 = b * T + t0; op.a_rows = rows;
-  op.b_row0 = tn * kLruCh; op.b_rows = min(kLruCh, D - tn * kLruCh);
   f32x16_t acc[C::MF][C::NF];
-  gemm_mainloop<C, false>(op, lds, lane, wave, acc);
+  gemm_mainloop<C, false>(op, lds, lane, wave, acc, hit);
 
   // ---------------------------------------------------------------- scan epilogue
   lru_epilogue<true, GATED>(p, lds, acc, lane, wave, b, tn, tt, t0, rows);
