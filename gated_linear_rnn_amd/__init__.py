@@ -15,5 +15,5 @@ from ._binding import (EXPORTS, LIB_PATH, RGLRU_BF16, RGLRU_F32, RgluError,  # n
                        mqa_fwd_workspace_bytes, rglru_block_fwd, rglru_bwd,
                        rglru_block_decode_step, block_decode_workspace_bytes,
                        rglru_decode_step, rglru_fwd, rglru_gates, rglru_lru, rglru_scan,
-                       rglru_test_set_scan_direct_polls,
+                       rglru_test_set_scan_direct_polls, rglru_test_set_lru_ticket_guess,
                        lru_workspace_bytes, scan_workspace_bytes, status_string, workspace)

@@ -26,7 +26,7 @@ EXPORTS = ("rglru_status_string", "conv1d_causal4", "rglru_fwd_workspace_bytes",
            "gated_mlp_fwd_workspace_bytes", "gated_mlp_fwd", "local_mqa_fwd_workspace_bytes",
            "local_mqa_fwd", "local_mqa_decode_workspace_bytes", "local_mqa_decode_step",
            "rglru_block_decode_workspace_bytes", "rglru_block_decode_step",
-           "rglru_test_set_scan_direct_polls")
+           "rglru_test_set_scan_direct_polls", "rglru_test_set_lru_ticket_guess")
 
 _lib = None
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -64,6 +64,8 @@ def load(path: str = LIB_PATH):
     lib.rglru_scan.restype = _I
     lib.rglru_test_set_scan_direct_polls.argtypes = [_I]
     lib.rglru_test_set_scan_direct_polls.restype = None
+    lib.rglru_test_set_lru_ticket_guess.argtypes = [_I]
+    lib.rglru_test_set_lru_ticket_guess.restype = None
     lib.rglru_decode_workspace_bytes.argtypes = [_I, _I, _I]
     lib.rglru_decode_workspace_bytes.restype = _Z
     lib.rglru_decode_step.argtypes = [_I, _I, _I, _F] + [_P] * 11 + [_P, _Z, _P]
@@ -212,6 +214,12 @@ def rglru_test_set_scan_direct_polls(polls: int) -> None:
     """Test hook: look-back polls before the forward scan computes a predecessor's summary
     itself (negative: always).  Process-wide; the library default is 2048."""
     load().rglru_test_set_scan_direct_polls(int(polls))
+
+
+def rglru_test_set_lru_ticket_guess(offset: int) -> None:
+    """Test hook: shift the fused kernel's guess of each workgroup's ticket by `offset`
+    (> 0 makes the guesses miss, so the reload path runs; <= 0 restores the default)."""
+    load().rglru_test_set_lru_ticket_guess(int(offset))
 
 
 def rglru_decode_step(x_t, conv_w, conv_b, conv_state, W_a, W_x, b_a, b_x, lam, h, y_t, ws,

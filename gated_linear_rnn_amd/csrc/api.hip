@@ -315,6 +315,7 @@ const char* rglru_status_string(int status) {
 }
 
 void rglru_test_set_scan_direct_polls(int polls) { set_scan_direct_polls(polls); }
+void rglru_test_set_lru_ticket_guess(int offset) { set_lru_ticket_guess(offset); }
 
 int conv1d_causal4(int B, int T, int D, rglru_dtype io, const void* x, const void* w,
                    const float* b, const void* state_in, void* u, void* state_out,

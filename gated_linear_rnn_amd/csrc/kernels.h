@@ -216,8 +216,10 @@ struct LruArgs {
   uint32_t* counters;     // 64 ticket counters (zeroed with the status words)
   int groups;             // set by the launcher
   const void* gate;       // [B,T,D] bf16 multiplier of the output (the block's GeLU branch) or NULL
+  int ticket_guess;       // set by the launcher: added to the launch-order ticket guess (0)
 };
 int lru_chunks(int T);
+void set_lru_ticket_guess(int offset);
 size_t lru_status_bytes(int B, int T, int D);
 hipError_t launch_lru_fused(const LruArgs& a, bool prefilled, hipStream_t s);
 

@@ -238,7 +238,7 @@ __global__ __launch_bounds__(CfgLru::NW * 64, 2) void lru_fused_kernel(LruArgs p
   uint32_t ticket = 0;
   if (tid == 0) ticket = atomicAdd(p.counters + g, 1u);
   int b, tn, tt;
-  const int kp = int(blockIdx.x) / G;
+  const int kp = (int(blockIdx.x) / G + p.ticket_guess) % (int(gridDim.x) / G);
   tile_of(kp, b, tn, tt);
   TileOperands op = operands(b, tn, tt);
   GemmDma<C, false>(op, lane, wave).issue(op, lds, wave, 0);
@@ -261,8 +261,12 @@ __global__ __launch_bounds__(CfgLru::NW * 64, 2) void lru_fused_kernel(LruArgs p
   lru_epilogue<true, GATED>(p, lds, acc, lane, wave, b, tn, tt, t0, rows);
 }
 
+static int g_lru_ticket_guess = 0;
+void set_lru_ticket_guess(int offset) { g_lru_ticket_guess = offset > 0 ? offset : 0; }
+
 hipError_t launch_lru_fused(const LruArgs& a_in, bool prefilled, hipStream_t s) {
   LruArgs a = a_in;
+  a.ticket_guess = g_lru_ticket_guess;
   const int NT = (a.D + kLruCh - 1) / kLruCh;
   const int chains = a.B * NT;
   a.groups = lru_groups(chains);

@@ -321,6 +321,18 @@ int local_mqa_decode_step(int B, int D, rglru_dtype io, int window, const int* p
  */
 void rglru_test_set_scan_direct_polls(int polls);
 
+/*
+ * Test hook of the fused RG-LRU kernel (rglru_fwd, rglru_lru, rglru_block_fwd).  Each of its
+ * workgroups takes a ticket (which tile it computes) from an atomic counter and, while the
+ * atomic is in flight, already loads the first operand block of the tile it would get if
+ * tickets went in launch order; when the ticket differs it waits for those loads and loads
+ * its own tile.  offset > 0 shifts that guess by `offset` tickets, so (nearly) every
+ * workgroup takes the second path; results must not change.  Values <= 0 restore the
+ * default (0).  Process-wide host state read at each launch; not thread-safe against
+ * concurrent launches.
+ */
+void rglru_test_set_lru_ticket_guess(int offset);
+
 #ifdef __cplusplus
 }
 #endif
