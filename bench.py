@@ -50,6 +50,9 @@ def _parse():
     ap.add_argument("--decode-only", action="store_true",
                     help="only time the decode extra (1024 steps at B=256, eager and one graph) "
                          "and print its figures (for kernel profiles of the decode step)")
+    ap.add_argument("--bwd-only", action="store_true",
+                    help="only time the fwd+bwd extra (rglru_fwd + rglru_bwd at B=4, T=2048, "
+                         "D=5376) and print its figures (for kernel profiles of the backward)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -116,6 +119,9 @@ def main():
 
     g.load()
     torch.cuda.set_device(0)
+    if args.bwd_only:
+        print(json.dumps(bench_fwd_bwd(g, torch, np, workloads)))
+        return
     if args.decode_only:
         print(json.dumps(bench_decode(g, torch, np, workloads)))
         return
