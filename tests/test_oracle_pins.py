@@ -302,9 +302,10 @@ def test_output_rounding_points():
     np.testing.assert_array_equal(o["u"], oracle.round_io(o["u"], "bf16"))
 
 
-# ---------------------------------------------------------------- fp32 fma emulation (R1 input)
-def _round_f32_exact(fr):
-    """Nearest fp32 (ties to even) of an exact rational, by integer arithmetic."""
+# ---------------------------------------------------------------- R1: the conv sum, rounded once
+def _round_exact(fr, bits):
+    """Nearest binary float with `bits` significant bits (ties to even) of an exact
+    rational, by integer arithmetic; normal range only (fp32: 24 bits, bf16: 8 bits)."""
     from fractions import Fraction
     if fr == 0:
         return 0.0
@@ -313,7 +314,7 @@ def _round_f32_exact(fr):
     e = mag.numerator.bit_length() - mag.denominator.bit_length()
     if Fraction(2) ** e > mag:
         e -= 1
-    ulp = Fraction(2) ** (e - 23)
+    ulp = Fraction(2) ** (e - (bits - 1))
     q = mag / ulp
     n = q.numerator // q.denominator
     rem = q - n
@@ -322,24 +323,66 @@ def _round_f32_exact(fr):
     return sign * float(n * ulp)
 
 
-def test_fma_f32_matches_exact_rational_rounding():
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_conv_rounds_the_exact_sum_all_taps_and_bias(io):
+    """R1 on the conv of the "Recurrent block" section: u = RNE_io(b + sum_k w_k x_{t-k}),
+    the exact rational sum of all four taps and a non-zero bias, rounded once to the I/O
+    dtype.  Inputs are I/O-dtype values (bf16 ones for bf16), the bias fp32, the history
+    non-zero, and the magnitudes spread so that the terms do not share an exponent."""
     from fractions import Fraction
-    rng = np.random.default_rng(40)
-    n = 3000
-    a = (rng.standard_normal(n) * 2.0 ** rng.integers(-20, 20, n)).astype(np.float32)
-    b = (rng.standard_normal(n) * 2.0 ** rng.integers(-20, 20, n)).astype(np.float32)
-    c = (rng.standard_normal(n) * 2.0 ** rng.integers(-40, 40, n)).astype(np.float32)
-    # constructed halfway cases: fp64 rounding of a*b + c lands exactly on an fp32 midpoint
-    # while the exact value lies just below (a naive double rounding picks the wrong side)
-    ta = np.array([1 + 2.0 ** -23, -(1 + 2.0 ** -23), 1 + 2.0 ** -23], dtype=np.float32)
-    tb = np.array([2.0 ** -24 * (1 - 2.0 ** -23), 2.0 ** -24 * (1 - 2.0 ** -23),
-                   -(2.0 ** -24) * (1 - 2.0 ** -23)], dtype=np.float32)
-    tc = np.array([1 + 2.0 ** -23, -(1 + 2.0 ** -23), 1 + 2.0 ** -21], dtype=np.float32)
-    a, b, c = np.concatenate([a, ta]), np.concatenate([b, tb]), np.concatenate([c, tc])
-    got = oracle.fma_f32(a, b, c)
-    want = np.array([_round_f32_exact(Fraction(float(x)) * Fraction(float(y)) + Fraction(float(z)))
-                     for x, y, z in zip(a, b, c)])
-    np.testing.assert_array_equal(got, want)
-    assert got[-3] == np.float32(1 + 2.0 ** -23)          # not the even neighbour 1 + 2^-22
-    naive = (a.astype(np.float64) * b + c).astype(np.float32)
-    assert np.any(naive != got)                             # the cases do discriminate
+    rng = np.random.default_rng(41 if io == "f32" else 42)
+    B, T, D = 2, 13, 24
+    q = (lambda v: oracle.round_io(v, io))
+    x = q(rng.standard_normal((B, T, D)) * 2.0 ** rng.integers(-6, 7, (B, T, D)))
+    st = q(rng.standard_normal((B, 3, D)) * 2.0 ** rng.integers(-6, 7, (B, 3, D)))
+    w = q(rng.standard_normal((4, D)) * 2.0 ** rng.integers(-4, 5, (4, D)))
+    assert np.all(w != 0)
+    cb = oracle.round_io(rng.standard_normal(D) * 2.0 ** rng.integers(-10, 3, D), "f32")
+    u, _ = oracle.conv1d_causal4(x, w, cb, st, io)
+    X = np.concatenate([st, x], axis=1)
+    bits = 24 if io == "f32" else 8
+    want = np.empty((B, T, D))
+    for b in range(B):
+        for t in range(T):
+            for d in range(D):
+                s = Fraction(float(cb[d]))
+                for k in range(4):
+                    s += Fraction(float(w[k, d])) * Fraction(float(X[b, t + 3 - k, d]))
+                want[b, t, d] = _round_exact(s, bits)
+    np.testing.assert_array_equal(u, want)
+    # the taps matter one by one: dropping any tap, or the bias, changes u somewhere
+    for k in range(4):
+        w2 = w.copy()
+        w2[k] = 0.0
+        assert np.any(oracle.conv1d_causal4(x, w2, cb, st, io)[0] != u)
+    assert np.any(oracle.conv1d_causal4(x, w, None, st, io)[0] != u)
+
+
+def test_round_exact_helper_on_hand_cases():
+    from fractions import Fraction
+    assert _round_exact(Fraction(1) + Fraction(1, 2 ** 24), 24) == 1.0            # tie -> even
+    assert _round_exact(Fraction(1) + Fraction(3, 2 ** 24), 24) == 1 + 2.0 ** -22
+    assert _round_exact(Fraction(1) + Fraction(1, 2 ** 8), 8) == 1.0
+    assert _round_exact(-(Fraction(1) + Fraction(3, 2 ** 8)), 8) == -(1 + 2.0 ** -6)
+    assert _round_exact(Fraction(1) + Fraction(1, 2 ** 8) + Fraction(1, 2 ** 40), 8) == 1 + 2.0 ** -7
+
+
+def test_conv_rounds_once_not_twice():
+    """Constructed sums where rounding first to fp32 and then to the I/O dtype picks the
+    other neighbour: the bias 1 + 2^-8 is an exact bf16 halfway point and a tiny tap moves
+    the exact sum just above (or below) it, by far less than an fp32 ulp; for fp32 I/O the
+    bias 1 + 2^-24 plays the same part.  R1 rounds the exact sum once."""
+    from fractions import Fraction
+    tiny = 2.0 ** -20 * 2.0 ** -20                      # w = x = 2^-20 (bf16 and fp32 values)
+    for io, half, bits in (("bf16", 1 + 2.0 ** -8, 8), ("f32", 1 + 2.0 ** -24, 24)):
+        cb = np.array([half, half, -half, half], dtype=np.float64)
+        w = np.zeros((4, 4)); w[2] = [2.0 ** -20, -(2.0 ** -20), 2.0 ** -20, 0.0]
+        x = np.zeros((1, 3, 4)); x[0, 0] = 2.0 ** -20    # tap 2 sees x_0 at t = 2
+        u, _ = oracle.conv1d_causal4(x, w, cb, None, io)
+        got = u[0, 2]
+        want = [_round_exact(Fraction(half) + Fraction(tiny), bits),
+                _round_exact(Fraction(half) - Fraction(tiny), bits),
+                _round_exact(-Fraction(half) + Fraction(tiny), bits),
+                _round_exact(Fraction(half), bits)]
+        np.testing.assert_array_equal(got, want)
+        assert got[0] != got[3] and got[0] > got[1]     # the tiny tap decides the neighbour
