@@ -2,16 +2,25 @@
 """Benchmark of the RG-LRU temporal branch (conv width 4 -> RG-LRU) on one MI355X.
 
 Headline workload: the training-shape forward B=8, T=2048, D_RNN=2560, bf16 I/O with
-fp32 scan state.  One step is one pass of the whole forward hot path over one batch:
-    conv1d_causal4 (K0: width-4 causal conv)
-    -> rglru_lru (K1: MFMA gate GEMM with the log-space gates and the chunked scan fused
-       into its epilogue)
-which is what rglru_fwd launches (rglru_fwd folds the look-back status initialisation
-into K0; rglru_lru launches it itself, so the K1 interval includes that small fill).
-Inputs are resident in HBM before the timed region; three input sets rotate so
-consecutive steps do not re-read the same x from the 256 MB Infinity Cache.  HIP events
-on the library's stream (the torch current stream) bracket every launch, giving
-per-kernel durations over the timed region.
+fp32 scan state.  One step is one call of the product entry point rglru_fwd over one batch:
+its conv launch (K0, width-4 causal conv, which also initialises the look-back status) and
+the fused RG-LRU kernel (K1: MFMA gate GEMM with the log-space gates and the chunked scan
+in its epilogue).  Inputs are resident in HBM before the timed region; three input sets
+rotate so consecutive steps do not re-read the same x from the 256 MB Infinity Cache.
+The warm-up runs the requested steps and then continues until the clocks have been under
+load for --warm-seconds (a short warm-up under-reports); the JSON says how long it ran.
+
+The per-kernel split comes from a second pass over the same inputs that launches the two
+halves through their own entry points (conv1d_causal4, then rglru_lru, whose interval also
+holds the look-back status fill it launches first), with HIP events on the library's
+stream (the torch current stream) around each launch; medians are reported, and the
+roofline uses the average launch duration of the fused kernel.
+
+Further legs (--no-extras skips them): the long-sequence forward (B=2, T=32768, D=4096),
+the tiny fp32 forward's latency, 1024 decode steps at B=256, the fwd+bwd training workload
+(B=4, T=2048, D=5376), the next rows (recurrent block, gated MLP, local MQA), the unfused
+gates + scan split, prefill/decode latency tables.  The CPU oracle is timed per workload
+on bounded samples (stated in the output).
 
 Prints ONE JSON line.  With --gpus N > 1 it exits with a message: the build runs on one
 GPU (no cross-GPU path exists).
@@ -42,6 +51,8 @@ def _parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warm-seconds", type=float, default=1.0,
+                    help="keep warming up after --warmup steps until this much time has passed")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-extras", action="store_true", help="skip the decode and fwd+bwd timings")
     ap.add_argument("--split-only", action="store_true",
@@ -53,6 +64,8 @@ def _parse():
     ap.add_argument("--bwd-only", action="store_true",
                     help="only time the fwd+bwd extra (rglru_fwd + rglru_bwd at B=4, T=2048, "
                          "D=5376) and print its figures (for kernel profiles of the backward)")
+    ap.add_argument("--long-only", action="store_true",
+                    help="only time the long-sequence forward (B=2, T=32768, D=4096)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -128,6 +141,9 @@ def main():
     if args.split_only:
         print(json.dumps(bench_split(g, torch, np, workloads, measured_copy_gbps(torch))))
         return
+    if args.long_only:
+        print(json.dumps(bench_long(g, torch, np, workloads)))
+        return
     w = workloads.TRAIN_FWD
     B, T, D = w.B, w.T, w.D
     M = B * T
@@ -143,39 +159,49 @@ def main():
     u = torch.empty((B, T, D), dtype=bf, device="cuda")
     y = torch.empty((B, T, D), dtype=bf, device="cuda")
     hT = torch.empty((B, D), dtype=torch.float32, device="cuda")
-    ws = g.workspace(g.lru_workspace_bytes(B, T, D, bf))
+    ws = g.workspace(g.fwd_workspace_bytes(B, T, D, bf))
     c = p["c"]
 
-    def step(k, ev=None):
-        x = xs[k % len(xs)]
-        if ev is not None:
-            ev[0].record()
-        g.conv1d_causal4(x, conv_w, conv_b, None, u, None)
-        if ev is not None:
-            ev[1].record()
-        g.rglru_lru(u, W_a, W_x, b_a, b_x, lam, None, y, hT, ws, c)
-        if ev is not None:
-            ev[2].record()
+    def step(k):
+        g.rglru_fwd(xs[k % len(xs)], conv_w, conv_b, None, W_a, W_x, b_a, b_x, lam, None, y, hT,
+                    None, ws, c)
 
-    _log(f"warmup {args.warmup} steps")
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    _log(f"timing {args.steps} steps")
+    warm_steps, warm_s = warm_up(torch, step, args.warmup, args.warm_seconds)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    _log(f"timing {args.steps} steps of rglru_fwd")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(k, evs[k])
+        evs[k][0].record()
+        step(k)
+        evs[k][1].record()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall = t1 - t0
-    ms = lambda i, j: float(np.mean([e[i].elapsed_time(e[j]) for e in evs]))
-    conv_ms, lru_ms = ms(0, 1), ms(1, 2)
+    wall = time.perf_counter() - t0
+    step_ms = [e[0].elapsed_time(e[1]) for e in evs]
     tokens_per_s = M * args.steps / wall
 
+    # per-kernel split: the same work through the two halves' entry points
+    _log(f"per-kernel split: {args.steps} steps of conv1d_causal4 + rglru_lru")
+    wsl = g.workspace(g.lru_workspace_bytes(B, T, D, bf))
+    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for k in range(args.steps + 3):
+        e = kev[k - 3] if k >= 3 else None
+        if e is not None:
+            e[0].record()
+        g.conv1d_causal4(xs[k % len(xs)], conv_w, conv_b, None, u, None)
+        if e is not None:
+            e[1].record()
+        g.rglru_lru(u, W_a, W_x, b_a, b_x, lam, None, y, hT, wsl, c)
+        if e is not None:
+            e[2].record()
+    torch.cuda.synchronize()
+    conv_l = [e[0].elapsed_time(e[1]) for e in kev]
+    lru_l = [e[1].elapsed_time(e[2]) for e in kev]
+    conv_ms, lru_ms = float(np.median(conv_l)), float(np.median(lru_l))
+    lru_avg = float(np.mean(lru_l))
+
     gemm_flop = 2.0 * M * (2 * D) * D
-    lru_tflops = gemm_flop / (lru_ms * 1e-3) / 1e12
+    lru_tflops = gemm_flop / (lru_avg * 1e-3) / 1e12
     block_bytes = M * D * (2 + 2) + 2 * D * D * 2      # x in, y out, W_a and W_x once
     block_gbps = block_bytes / (wall / args.steps) / 1e9
     conv_bytes = M * D * (2 + 2)
@@ -187,39 +213,44 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warm_steps,
+        "warmup_s": warm_s,
         "ms_per_step": wall * 1e3 / args.steps,
+        "ms_per_step_median_events": float(np.median(step_ms)),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "T": T, "D_RNN": D, "io": "bf16",
-                   "scan_state": "fp32", "c": c},
+                   "scan_state": "fp32", "c": c, "entry_point": "rglru_fwd"},
         "roofline": {
-            "kernel": "lru_fused_kernel (rglru_lru: gate GEMM + gates + chunked scan)",
+            "kernel": "lru_fused_kernel (gate GEMM + gates + chunked scan)",
             "bound": "mfma", "achieved": lru_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": lru_tflops / PEAK_BF16_TFLOPS, "traffic": _lru_traffic(),
-            "flop_per_launch": gemm_flop, "avg_launch_ms": lru_ms,
-            "note": "interval includes the look-back status initialisation launch",
+            "flop_per_launch": gemm_flop, "avg_launch_ms": lru_avg, "median_launch_ms": lru_ms,
+            "note": "launch interval of rglru_lru, which also holds its look-back status fill",
         },
         "hbm": {
-            "block_achieved_GBps": block_bytes / (wall / args.steps) / 1e9,
+            "block_achieved_GBps": block_gbps,
             "block_bytes_per_step": block_bytes,
             "block_frac_of_peak": block_gbps / PEAK_HBM_GBPS,
             "conv_kernel_GBps": conv_bytes / (conv_ms * 1e-3) / 1e9,
             "lru_kernel_GBps": lru_bytes / (lru_ms * 1e-3) / 1e9,
             "peak_GBps": PEAK_HBM_GBPS,
         },
-        "per_kernel_ms": {"conv": conv_ms, "lru_fused": lru_ms},
+        "per_kernel_ms_median": {"conv": conv_ms, "lru_fused": lru_ms},
         "block_tokens_per_s_kernels": M / ((conv_ms + lru_ms) * 1e-3),
     }
-    del xs, u, y, ws
+    del xs, u, y, ws, wsl
     torch.cuda.empty_cache()
     copy_gbps = measured_copy_gbps(torch)
     out["hbm"]["measured_copy_GBps"] = copy_gbps
     out["hbm"]["block_frac_of_measured_copy"] = block_gbps / copy_gbps
 
     if not args.no_extras:
+        out["long_fwd"] = bench_long(g, torch, np, workloads)
+        out["tiny_fwd_f32"] = bench_tiny(g, torch, np, workloads)
         out["decode"] = bench_decode(g, torch, np, workloads)
         out["train_fwd_bwd"] = bench_fwd_bwd(g, torch, np, workloads)
         out["recurrent_block_fwd"] = bench_block(g, torch, np, workloads)
@@ -229,7 +260,105 @@ def main():
         out["split_gates_scan"] = bench_split(g, torch, np, workloads, copy_gbps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, np)
+        out["cpu_baseline_per_workload"] = cpu_baseline_per_workload(np, workloads)
     print(json.dumps(out))
+
+
+def warm_up(torch, step, steps, seconds):
+    """Run `steps` steps, then keep going until `seconds` have passed (synchronising every
+    25 steps so the clock measures GPU time).  Returns (steps run, seconds)."""
+    _log(f"warmup: {steps} steps, then until {seconds:.1f} s")
+    t0 = time.perf_counter()
+    n = 0
+    while n < steps or time.perf_counter() - t0 < seconds:
+        step(n)
+        n += 1
+        if n % 25 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n, time.perf_counter() - t0
+
+
+def bench_long(g, torch, np, workloads, steps=10):
+    """The long-sequence forward, B=2, T=32768, D=4096 (a^c in [0.999, 0.9999], h0 ~ N(0,1)):
+    rglru_fwd per call (median of `steps` after a timed warm-up), and the per-kernel split
+    through conv1d_causal4 + rglru_lru with events."""
+    w = workloads.LONG_FWD
+    B, T, D = w.B, w.T, w.D
+    M = B * T
+    bf = torch.bfloat16
+    dev = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dt)
+    _log(f"long forward {B}x{T}x{D}: drawing inputs")
+    p = workloads.make_inputs(w)
+    x = dev(p["x"], bf)
+    cw, cb = dev(p["conv_w"], bf), dev(p["conv_b"])
+    Wa, Wx, ba, bx, lam = dev(p["W_a"], bf), dev(p["W_x"], bf), dev(p["b_a"]), dev(p["b_x"]), dev(p["lam"])
+    h0 = dev(p["h0"])
+    del p
+    y = torch.empty_like(x)
+    hT = torch.empty((B, D), dtype=torch.float32, device="cuda")
+    ws = g.workspace(g.fwd_workspace_bytes(B, T, D, bf))
+    fwd = lambda k: g.rglru_fwd(x, cw, cb, None, Wa, Wx, ba, bx, lam, h0, y, hT, None, ws, 8.0)
+    warm_up(torch, fwd, 3, 0.5)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for k in range(steps):
+        evs[k][0].record()
+        fwd(k)
+        evs[k][1].record()
+    torch.cuda.synchronize()
+    fwd_ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    u = torch.empty_like(x)
+    wsl = g.workspace(g.lru_workspace_bytes(B, T, D, bf))
+    for k in range(steps):
+        evs[k][0].record()
+        g.conv1d_causal4(x, cw, cb, None, u, None)
+        evs[k][1].record()
+        g.rglru_lru(u, Wa, Wx, ba, bx, lam, h0, y, hT, wsl, 8.0)
+        evs[k][2].record()
+    torch.cuda.synchronize()
+    conv_ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    lru_ms = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+    flop = 2.0 * M * (2 * D) * D
+    block_bytes = M * D * (2 + 2) + 2 * D * D * 2
+    out = {"workload": w.name, "steps": steps, "ms_per_call_median": fwd_ms,
+           "tokens_per_s": M / (fwd_ms * 1e-3),
+           "per_kernel_ms_median": {"conv": conv_ms, "lru_fused": lru_ms},
+           "lru_TFLOPs": flop / (lru_ms * 1e-3) / 1e12,
+           "lru_frac_of_bf16_peak": flop / (lru_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+           "flop_per_call": flop,
+           "block_GBps": block_bytes / (fwd_ms * 1e-3) / 1e9,
+           "conv_GBps": M * D * 4 / (conv_ms * 1e-3) / 1e9}
+    del x, y, u, ws, wsl
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_tiny(g, torch, np, workloads, steps=200):
+    """The tiny fp32 forward (B=1, T=256, D=256): latency of one rglru_fwd call (median of
+    `steps` calls, each bracketed by events)."""
+    w = workloads.TINY_F32
+    p = workloads.make_inputs(w)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda")
+    x, cw, cb = dev(p["x"]), dev(p["conv_w"]), dev(p["conv_b"])
+    Wa, Wx, ba, bx, lam = dev(p["W_a"]), dev(p["W_x"]), dev(p["b_a"]), dev(p["b_x"]), dev(p["lam"])
+    y = torch.empty_like(x)
+    hT = torch.empty((w.B, w.D), device="cuda")
+    ws = g.workspace(g.fwd_workspace_bytes(w.B, w.T, w.D, torch.float32))
+    fwd = lambda k=0: g.rglru_fwd(x, cw, cb, None, Wa, Wx, ba, bx, lam, None, y, hT, None, ws, 8.0)
+    for _ in range(20):
+        fwd()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    lat = []
+    for _ in range(steps):
+        e0.record()
+        fwd()
+        e1.record()
+        torch.cuda.synchronize()
+        lat.append(e0.elapsed_time(e1))
+    ms = float(np.median(lat))
+    return {"workload": w.name, "calls": steps, "us_per_call_median": ms * 1e3,
+            "tokens_per_s": w.B * w.T / (ms * 1e-3)}
 
 
 def measured_copy_gbps(torch, nbytes=1 << 30, reps=20):
@@ -271,15 +400,18 @@ def bench_decode(g, torch, np, workloads):
         for t in range(steps):
             g.rglru_decode_step(toks[t % w.T], cw, cb, hist, Wa, Wx, ba, bx, lam, h, y, ws, p["c"])
 
+    reps = 3
     _log("decode: eager")
     run()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    run()
-    e1.record()
-    torch.cuda.synchronize()
-    eager_ms = e0.elapsed_time(e1)
+    eager = []
+    for _ in range(reps):
+        e0.record()
+        run()
+        e1.record()
+        torch.cuda.synchronize()
+        eager.append(e0.elapsed_time(e1))
     _log("decode: graph")
     graph = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
@@ -290,11 +422,14 @@ def bench_decode(g, torch, np, workloads):
     torch.cuda.current_stream().wait_stream(s)
     graph.replay()
     torch.cuda.synchronize()
-    e0.record()
-    graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    graph_ms = e0.elapsed_time(e1)
+    graphed = []
+    for _ in range(reps):
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graphed.append(e0.elapsed_time(e1))
+    eager_ms, graph_ms = float(np.median(eager)), float(np.median(graphed))
     state_bytes = B * D * (4 + 4 + 6 + 6 + 2 + 2)   # h r/w, history r/w, x_t, y_t
     w_bytes = 2 * D * D * 2
     best = min(eager_ms, graph_ms)
@@ -305,6 +440,7 @@ def bench_decode(g, torch, np, workloads):
         "us_per_step_eager": eager_ms * 1e3 / steps, "us_per_step_graph": graph_ms * 1e3 / steps,
         "state_update_GBps": state_bytes * steps / (best * 1e-3) / 1e9,
         "state_plus_weights_GBps": (state_bytes + w_bytes) * steps / (best * 1e-3) / 1e9,
+        "runs": reps, "statistic": "median over runs of 1024 dependent steps",
         "note": "W (26 MB) and the state (16 MB) stay resident in the 256 MB Infinity Cache",
     }
 
@@ -329,10 +465,11 @@ def bench_fwd_bwd(g, torch, np, workloads):
         g.backward(x, cw, cb, None, Wa, Wx, ba, bx, lam, None, dy, None, p["c"], ws=wsb)
 
     e0, e_mid, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-    once()
+    for _ in range(5):
+        once()
     torch.cuda.synchronize()
     fwd, bwd = [], []
-    for _ in range(3):
+    for _ in range(20):
         e0.record()
         once()
         e1.record()
@@ -340,7 +477,7 @@ def bench_fwd_bwd(g, torch, np, workloads):
         fwd.append(e0.elapsed_time(e_mid))
         bwd.append(e_mid.elapsed_time(e1))
     f, b = float(np.median(fwd)), float(np.median(bwd))
-    return {"workload": w.name, "fwd_ms": f, "bwd_ms": b,
+    return {"workload": w.name, "fwd_ms": f, "bwd_ms": b, "runs": len(fwd), "statistic": "median",
             "tokens_per_s_fwd_bwd": B * T / ((f + b) * 1e-3)}
 
 
@@ -635,6 +772,78 @@ def cpu_baseline(p, np, min_seconds=10.0):
             "sample": f"oracle forward (fp64 NumPy, BLAS threads = cores) over the whole "
                       f"{Bs}x{T}x{p['x'].shape[2]} workload, {reps} times ({reps * Bs * T} tokens, "
                       f"{dt:.1f} s)"}
+
+
+def _timed(fn, min_seconds):
+    """Run fn until min_seconds have passed; returns (runs, seconds)."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            return reps, dt
+
+
+def cpu_baseline_per_workload(np, workloads, min_seconds=4.0):
+    """The CPU oracle, as it stands, on a bounded sample of each workload, in tokens/s (the
+    sample of each is stated).  Every sample keeps the workload's D, distributions and
+    weights; only batch rows, sequence length or decode steps are cut, which the oracle's
+    cost scales with linearly (its GEMMs are per row, its recurrence per step)."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    out = {"cores": cores, "kind": "oracle", "unit": "tokens/s"}
+
+    w = workloads.TINY_F32
+    p = workloads.make_inputs(w)
+    _log("cpu baseline: tiny forward")
+    reps, dt = _timed(lambda: oracle.forward(p["x"], p["conv_w"], p["conv_b"], None, p["W_a"],
+                                             p["W_x"], p["b_a"], p["b_x"], p["lam"], None, p["c"],
+                                             "f32"), min_seconds)
+    out[w.name] = {"value": reps * w.B * w.T / dt,
+                   "sample": f"the whole workload, {reps} forwards in {dt:.1f} s"}
+
+    w = workloads.DECODE
+    steps = 8
+    p = workloads.make_inputs(w.with_shape(T=steps))
+    _log(f"cpu baseline: {steps} decode steps at B={w.B}")
+
+    def dec():
+        hist, h = p["conv_state"], p["h0"]
+        for t in range(steps):
+            y, hist, h = oracle.decode_step(p["x"][t], p["conv_w"], p["conv_b"], hist, p["W_a"],
+                                            p["W_x"], p["b_a"], p["b_x"], p["lam"], h, p["c"], "bf16")
+    reps, dt = _timed(dec, min_seconds)
+    out[w.name] = {"value": reps * steps * w.B / dt,
+                   "sample": f"{steps} of the 1024 dependent steps at B={w.B}, D={w.D}, "
+                             f"{reps} times in {dt:.1f} s (the cost per step does not change "
+                             f"with the step index)"}
+
+    w = workloads.LONG_FWD
+    Ts = 2048
+    p = workloads.make_inputs(w.with_shape(B=1, T=Ts))
+    _log(f"cpu baseline: long forward, one sequence of {Ts} steps")
+    reps, dt = _timed(lambda: oracle.forward(p["x"], p["conv_w"], p["conv_b"], None, p["W_a"],
+                                             p["W_x"], p["b_a"], p["b_x"], p["lam"], p["h0"],
+                                             p["c"], "bf16"), min_seconds)
+    out[w.name] = {"value": reps * Ts / dt,
+                   "sample": f"one sequence of {Ts} of the {w.T} steps at D={w.D} (the "
+                             f"workload's recipe), {reps} forwards in {dt:.1f} s"}
+
+    w = workloads.TRAIN_BWD
+    p = workloads.make_inputs(w.with_shape(B=1))
+    _log("cpu baseline: fwd+bwd, one sequence")
+
+    def fb():
+        oracle.forward(p["x"], p["conv_w"], p["conv_b"], None, p["W_a"], p["W_x"], p["b_a"],
+                       p["b_x"], p["lam"], None, p["c"], "bf16")
+        oracle.backward(p["x"], p["conv_w"], p["conv_b"], None, p["W_a"], p["W_x"], p["b_a"],
+                        p["b_x"], p["lam"], None, p["c"], "bf16", p["dy"])
+    reps, dt = _timed(fb, min_seconds)
+    out[w.name] = {"value": reps * w.T / dt,
+                   "sample": f"one of the {w.B} sequences ({w.T} steps, D={w.D}), forward then "
+                             f"backward, {reps} times in {dt:.1f} s"}
+    return out
 
 
 if __name__ == "__main__":

@@ -15,6 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librglru.so")
 
 RGLRU_F32, RGLRU_BF16 = 0, 1
+RGLRU_ESTALL = -7
 _IO = {torch.float32: RGLRU_F32, torch.bfloat16: RGLRU_BF16}
 
 # Symbols declared in include/rglru.h.
@@ -26,7 +27,7 @@ EXPORTS = ("rglru_status_string", "conv1d_causal4", "rglru_fwd_workspace_bytes",
            "gated_mlp_fwd_workspace_bytes", "gated_mlp_fwd", "local_mqa_fwd_workspace_bytes",
            "local_mqa_fwd", "local_mqa_decode_workspace_bytes", "local_mqa_decode_step",
            "rglru_block_decode_workspace_bytes", "rglru_block_decode_step",
-           "rglru_test_set_scan_direct_polls", "rglru_test_set_lru_ticket_guess")
+           "rglru_workspace_status")
 
 _lib = None
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -62,10 +63,8 @@ def load(path: str = LIB_PATH):
     lib.rglru_scan_workspace_bytes.restype = _Z
     lib.rglru_scan.argtypes = [_I, _I, _I, _I] + [_P] * 9 + [_P, _Z, _P]
     lib.rglru_scan.restype = _I
-    lib.rglru_test_set_scan_direct_polls.argtypes = [_I]
-    lib.rglru_test_set_scan_direct_polls.restype = None
-    lib.rglru_test_set_lru_ticket_guess.argtypes = [_I]
-    lib.rglru_test_set_lru_ticket_guess.restype = None
+    lib.rglru_workspace_status.argtypes = [_P, _Z, _P]
+    lib.rglru_workspace_status.restype = _I
     lib.rglru_decode_workspace_bytes.argtypes = [_I, _I, _I]
     lib.rglru_decode_workspace_bytes.restype = _Z
     lib.rglru_decode_step.argtypes = [_I, _I, _I, _F] + [_P] * 11 + [_P, _Z, _P]
@@ -210,16 +209,13 @@ def rglru_scan(x, conv_w, conv_b, conv_state_in, a, beta, h0, y, h_T, ws, stream
            "rglru_scan")
 
 
-def rglru_test_set_scan_direct_polls(polls: int) -> None:
-    """Test hook: look-back polls before the forward scan computes a predecessor's summary
-    itself (negative: always).  Process-wide; the library default is 2048."""
-    load().rglru_test_set_scan_direct_polls(int(polls))
-
-
-def rglru_test_set_lru_ticket_guess(offset: int) -> None:
-    """Test hook: shift the fused kernel's guess of each workgroup's ticket by `offset`
-    (> 0 makes the guesses miss, so the reload path runs; <= 0 restores the default)."""
-    load().rglru_test_set_lru_ticket_guess(int(offset))
+def rglru_workspace_status(ws, stream=None) -> int:
+    """RGLRU_OK (0) or RGLRU_ESTALL (-7) for the chained scans of the last call on `ws`
+    (synchronises the stream).  Other negative codes raise."""
+    code = int(load().rglru_workspace_status(_ptr(ws), ws.numel(), _stream(stream)))
+    if code not in (0, RGLRU_ESTALL):
+        _check(code, "rglru_workspace_status")
+    return code
 
 
 def rglru_decode_step(x_t, conv_w, conv_b, conv_state, W_a, W_x, b_a, b_x, lam, h, y_t, ws,

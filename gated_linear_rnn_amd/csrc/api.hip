@@ -10,6 +10,11 @@
 #include "../../include/rglru.h"
 #include "kernels.h"
 #include "rglru_device.h"
+#include "rglru_testing.h"
+
+namespace rglru {
+const Knobs kDefaultKnobs = {0, kDirectPolls, kMaxPolls};
+}
 
 using namespace rglru;
 
@@ -56,36 +61,59 @@ bool c_ok(float c) { return c >= 0.f && isfinite(c); }
 // fp32 I/O: u, a, beta (the unfused gates) and the scan's look-back status and counter.
 struct FwdWs {
   void* u;
-  float* a;      // fp32 io: z^a, then a in place
-  float* beta;   // fp32 io: z^x, then beta in place
+  float* a;      // unfused path: a (fp32 io: z^a, then a in place)
+  float* beta;   // unfused path: beta (fp32 io: z^x, then beta in place)
   void* status;
   uint32_t* counter;
+  float* tail;   // bf16 unfused path: the gate GEMM's split-tail partials
 };
 
-// The RG-LRU layer's scratch (everything after u).
-void carve_lru(Carver& cv, FwdWs& w, int B, int T, int D, rglru_dtype io) {
+// Which form the RG-LRU layer takes.  fp32 I/O: always the unfused gates + scan.  bf16: the
+// fused kernel, except where its tiles (256 steps x 128 channels, lru_tiles of them) leave
+// the last of two or more rounds of 256 CUs at most 60% full; the unfused form then fills
+// its rounds (the gate GEMM splits the K loop of its own partly filled last round; the scan
+// is memory-bound) and is faster.  A pure function of the shape, so the workspace size and
+// the bits of every call follow it.
+bool lru_unfused(int B, int T, int D, rglru_dtype io) {
+  if (io != RGLRU_BF16) return true;
+  const long tiles = lru_tiles(B, T, D), rem = tiles % 256;
+  return tiles > 512 && rem != 0 && rem * 5 <= 256 * 3;
+}
+
+// The counter words every chained-scan workspace starts with (ticket counters, stall flag).
+uint32_t* carve_counters(Carver& cv) { return cv.take<uint32_t>(kCounterWords); }
+
+// The RG-LRU layer's scratch after the counters and u.  `fused`: the caller always runs the
+// fused kernel on bf16 (the recurrent block's gated form).
+void carve_lru(Carver& cv, FwdWs& w, int B, int T, int D, rglru_dtype io, bool fused = false) {
   const size_t n = size_t(B) * T * D;
-  if (io == RGLRU_BF16) {
-    w.a = w.beta = nullptr;
+  w.a = w.beta = w.tail = nullptr;
+  if ((fused && io == RGLRU_BF16) || !lru_unfused(B, T, D, io)) {
     w.status = cv.take<unsigned char>(lru_status_bytes(B, T, D));
   } else {
     w.a = cv.take<float>(n);
     w.beta = cv.take<float>(n);
     w.status = cv.take<unsigned char>(scan_status_bytes(B, T, D, acc_bytes(io)));
+    if (io == RGLRU_BF16) {
+      const size_t tb = gate_gemm_tail_bytes(B * T, D, D);
+      if (tb) w.tail = cv.take<float>(tb / sizeof(float));
+    }
   }
-  w.counter = cv.take<uint32_t>(64);
 }
 
 FwdWs carve_fwd(Carver& cv, int B, int T, int D, rglru_dtype io) {
   const size_t n = size_t(B) * T * D;
   FwdWs w;
+  w.counter = carve_counters(cv);
   w.u = cv.take<unsigned char>(n * io_bytes(io));
   carve_lru(cv, w, B, T, D, io);
   return w;
 }
 
-size_t status_fill_words(int B, int T, int D, rglru_dtype io) {
-  return (io == RGLRU_BF16 ? lru_status_bytes(B, T, D) : scan_status_bytes(B, T, D, acc_bytes(io))) / 4;
+// Look-back status words of the RG-LRU layer's scratch (carve_lru with the same `fused`).
+size_t status_fill_words(int B, int T, int D, rglru_dtype io, bool fused = false) {
+  const bool unfused = !(fused && io == RGLRU_BF16) && lru_unfused(B, T, D, io);
+  return (unfused ? scan_status_bytes(B, T, D, acc_bytes(io)) : lru_status_bytes(B, T, D)) / 4;
 }
 
 // The gate projection for M rows: out0/out1 per the epilogue kind.
@@ -110,40 +138,44 @@ int gate_projection(rglru_dtype io, GateGemmArgs g, int epi, float* zscratch_a,
 int forward_scan(rglru_dtype io, int B, int T, int D, const void* x, const void* conv_w,
                  const float* conv_b, const void* conv_state_in, const float* a, const float* beta,
                  const float* h0, void* y, float* h_T, void* status, uint32_t* counter,
-                 bool prefilled, hipStream_t stream) {
+                 bool prefilled, const Knobs& k, hipStream_t stream) {
   ScanFwdArgs sa{};
   sa.B = B; sa.T = T; sa.D = D;
   sa.x = x; sa.conv_w = conv_w; sa.conv_b = conv_b; sa.conv_state = conv_w ? conv_state_in : nullptr;
   sa.a = a; sa.beta = beta; sa.from_ri = false; sa.lam = nullptr; sa.c = 0.f;
   sa.h0 = h0; sa.y = y; sa.h_all = nullptr; sa.h_T = h_T;
   sa.status = status; sa.counter = counter; sa.prefilled = prefilled;
+  sa.direct_polls = k.scan_direct_polls;
   if (io == RGLRU_BF16) RG_CHECK((launch_scan_fwd<bf16_t, float>(sa, stream)));
   else RG_CHECK((launch_scan_fwd<float, double>(sa, stream)));
   return RGLRU_OK;
 }
 
-// The RG-LRU layer on the conv output u (Eq. (1)-(4)): the fused kernel for bf16 I/O, the
-// gate projection then the scan for fp32 I/O.  `prefilled`: the launch before it on the
-// stream already initialised the look-back status and counters.
+// The RG-LRU layer on the conv output u (Eq. (1)-(4)): the fused kernel, or the gate
+// projection then the scan (lru_unfused).  `prefilled`: the launch before it on the stream
+// already initialised the look-back status and counters.
 int lru_layer(rglru_dtype io, int B, int T, int D, float c, const void* u, const void* W_a,
               const void* W_x, const float* b_a, const float* b_x, const float* lambda,
-              const float* h0, void* y, float* h_T, FwdWs& w, bool prefilled, hipStream_t stream) {
-  if (io == RGLRU_BF16) {
+              const float* h0, void* y, float* h_T, FwdWs& w, bool prefilled, const Knobs& k,
+              hipStream_t stream) {
+  if (!lru_unfused(B, T, D, io)) {
     LruArgs la{};
     la.u = u; la.Wa = W_a; la.Wx = W_x; la.ba = b_a; la.bx = b_x; la.lam = lambda; la.c = c;
     la.h0 = h0; la.y = y; la.hT = h_T; la.B = B; la.T = T; la.D = D;
     la.status = static_cast<uint32_t*>(w.status); la.counters = w.counter;
+    la.ticket_guess = k.lru_ticket_guess; la.max_polls = k.lookback_polls;
+    la.stall = w.counter + kStallWord;
     RG_CHECK(launch_lru_fused(la, prefilled, stream));
     return RGLRU_OK;
   }
   GateGemmArgs g{};
   g.U = u; g.Wa = W_a; g.Wx = W_x; g.M = B * T; g.N = D; g.K = D;
   g.ba = b_a; g.bx = b_x; g.lam = lambda; g.c = c;
-  g.out0 = w.a; g.out1 = w.beta;
+  g.out0 = w.a; g.out1 = w.beta; g.tail_ws = w.tail;
   int st = gate_projection(io, g, kEpiAB, w.a, w.beta, stream);
   if (st != RGLRU_OK) return st;
   return forward_scan(io, B, T, D, u, nullptr, nullptr, nullptr, w.a, w.beta, h0, y, h_T,
-                      w.status, w.counter, prefilled, stream);
+                      w.status, w.counter, prefilled, k, stream);
 }
 
 struct ScanWs {
@@ -152,8 +184,8 @@ struct ScanWs {
 };
 ScanWs carve_scan(Carver& cv, int B, int T, int D, rglru_dtype io) {
   ScanWs w;
+  w.counter = carve_counters(cv);
   w.status = cv.take<unsigned char>(scan_status_bytes(B, T, D, acc_bytes(io)));
-  w.counter = cv.take<uint32_t>(64);
   return w;
 }
 
@@ -182,6 +214,7 @@ BwdWs carve_bwd(Carver& cv, int B, int T, int D, rglru_dtype io) {
   const size_t eb = io_bytes(io);
   const size_t P = size_t(B) * scan_chunks(T);
   BwdWs w;
+  w.counter = carve_counters(cv);
   w.u = cv.take<unsigned char>(n * eb);
   w.r = cv.take<float>(n);
   w.i = cv.take<float>(n);
@@ -196,7 +229,6 @@ BwdWs carve_bwd(Carver& cv, int B, int T, int D, rglru_dtype io) {
   w.scan_part = cv.take<double>(P * 3 * D);
   w.conv_part = cv.take<double>(P * 5 * D);
   w.status = cv.take<unsigned char>(scan_status_bytes(B, T, D, acc_bytes(io)));
-  w.counter = cv.take<uint32_t>(64);
   w.tail = nullptr;
   if (io == RGLRU_BF16) {
     const size_t tb = std::max({plain_gemm_tail_bytes(int(M), D, 2 * D),
@@ -222,13 +254,14 @@ struct BlockWs {
 BlockWs carve_block(Carver& cv, int B, int T, int D, int R, rglru_dtype io) {
   const size_t n = size_t(B) * T * R;
   BlockWs w;
+  w.lru.counter = carve_counters(cv);
   w.pq = io == RGLRU_F32 ? cv.take<float>(2 * n) : nullptr;
   w.tail = io == RGLRU_BF16 ? cv.take<float>(out_gemm_tail_bytes(B * T, D, R) / sizeof(float)) : nullptr;
   w.p = cv.take<unsigned char>(n * io_bytes(io));
   w.g = cv.take<unsigned char>(n * io_bytes(io));
   w.y = io == RGLRU_F32 ? cv.take<unsigned char>(n * io_bytes(io)) : nullptr;
   w.lru.u = cv.take<unsigned char>(n * io_bytes(io));
-  carve_lru(cv, w.lru, B, T, R, io);
+  carve_lru(cv, w.lru, B, T, R, io, /*fused=*/true);
   return w;
 }
 
@@ -310,12 +343,10 @@ const char* rglru_status_string(int status) {
     case RGLRU_EWORKSPACE: return "RGLRU_EWORKSPACE: workspace missing or too small";
     case RGLRU_EHIP: return "RGLRU_EHIP: HIP launch or runtime error";
     case RGLRU_EINTERNAL: return "RGLRU_EINTERNAL: internal error";
+    case RGLRU_ESTALL: return "RGLRU_ESTALL: a chained-scan wait for a predecessor chunk gave up (outputs hold NaN)";
     default: return "unknown rglru status";
   }
 }
-
-void rglru_test_set_scan_direct_polls(int polls) { set_scan_direct_polls(polls); }
-void rglru_test_set_lru_ticket_guess(int offset) { set_lru_ticket_guess(offset); }
 
 int conv1d_causal4(int B, int T, int D, rglru_dtype io, const void* x, const void* w,
                    const float* b, const void* state_in, void* u, void* state_out,
@@ -338,10 +369,11 @@ size_t rglru_fwd_workspace_bytes(int B, int T, int D, rglru_dtype io) {
   return cv.used;
 }
 
-int rglru_fwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const void* conv_w,
-              const float* conv_b, const void* conv_state_in, const void* W_a, const void* W_x,
-              const float* b_a, const float* b_x, const float* lambda, const float* h0, void* y,
-              float* h_T, void* conv_state_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+static int fwd_impl(const Knobs& k, int B, int T, int D, rglru_dtype io, float c, const void* x,
+                    const void* conv_w, const float* conv_b, const void* conv_state_in,
+                    const void* W_a, const void* W_x, const float* b_a, const float* b_x,
+                    const float* lambda, const float* h0, void* y, float* h_T,
+                    void* conv_state_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = shape_status(B, T, D);
   if (st != RGLRU_OK) return st;
   if (!io_ok(io)) return RGLRU_EDTYPE;
@@ -369,13 +401,23 @@ int rglru_fwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const
     u = w.u;
     prefilled = true;
   }
-  return lru_layer(io, B, T, D, c, u, W_a, W_x, b_a, b_x, lambda, h0, y, h_T, w, prefilled, stream);
+  return lru_layer(io, B, T, D, c, u, W_a, W_x, b_a, b_x, lambda, h0, y, h_T, w, prefilled, k,
+                   stream);
+}
+
+int rglru_fwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const void* conv_w,
+              const float* conv_b, const void* conv_state_in, const void* W_a, const void* W_x,
+              const float* b_a, const float* b_x, const float* lambda, const float* h0, void* y,
+              float* h_T, void* conv_state_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return fwd_impl(kDefaultKnobs, B, T, D, io, c, x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a,
+                  b_x, lambda, h0, y, h_T, conv_state_out, ws, ws_bytes, stream);
 }
 
 size_t rglru_lru_workspace_bytes(int B, int T, int D, rglru_dtype io) {
   if (shape_status(B, T, D) != RGLRU_OK || !io_ok(io)) return 0;
   Carver cv(nullptr);
   FwdWs w;
+  w.counter = carve_counters(cv);
   carve_lru(cv, w, B, T, D, io);
   return cv.used;
 }
@@ -394,8 +436,10 @@ int rglru_lru(int B, int T, int D, rglru_dtype io, float c, const void* u, const
   Carver cv(ws);
   FwdWs w;
   w.u = nullptr;
+  w.counter = carve_counters(cv);
   carve_lru(cv, w, B, T, D, io);
-  return lru_layer(io, B, T, D, c, u, W_a, W_x, b_a, b_x, lambda, h0, y, h_T, w, false, stream);
+  return lru_layer(io, B, T, D, c, u, W_a, W_x, b_a, b_x, lambda, h0, y, h_T, w, false,
+                   kDefaultKnobs, stream);
 }
 
 int rglru_gates(int B, int T, int D, rglru_dtype io, float c, const void* u, const void* W_a,
@@ -422,9 +466,10 @@ size_t rglru_scan_workspace_bytes(int B, int T, int D, rglru_dtype io) {
   return cv.used;
 }
 
-int rglru_scan(int B, int T, int D, rglru_dtype io, const void* x, const void* conv_w,
-               const float* conv_b, const void* conv_state_in, const float* a, const float* beta,
-               const float* h0, void* y, float* h_T, void* ws, size_t ws_bytes, hipStream_t stream) {
+static int scan_impl(const Knobs& k, int B, int T, int D, rglru_dtype io, const void* x,
+                     const void* conv_w, const float* conv_b, const void* conv_state_in,
+                     const float* a, const float* beta, const float* h0, void* y, float* h_T,
+                     void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = shape_status(B, T, D);
   if (st != RGLRU_OK) return st;
   if (!io_ok(io)) return RGLRU_EDTYPE;
@@ -437,7 +482,14 @@ int rglru_scan(int B, int T, int D, rglru_dtype io, const void* x, const void* c
   Carver cv(ws);
   ScanWs w = carve_scan(cv, B, T, D, io);
   return forward_scan(io, B, T, D, x, conv_w, conv_b, conv_state_in, a, beta, h0, y, h_T,
-                      w.status, w.counter, false, stream);
+                      w.status, w.counter, false, k, stream);
+}
+
+int rglru_scan(int B, int T, int D, rglru_dtype io, const void* x, const void* conv_w,
+               const float* conv_b, const void* conv_state_in, const float* a, const float* beta,
+               const float* h0, void* y, float* h_T, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return scan_impl(kDefaultKnobs, B, T, D, io, x, conv_w, conv_b, conv_state_in, a, beta, h0, y,
+                   h_T, ws, ws_bytes, stream);
 }
 
 size_t rglru_decode_workspace_bytes(int B, int D, rglru_dtype io) {
@@ -447,8 +499,6 @@ size_t rglru_decode_workspace_bytes(int B, int D, rglru_dtype io) {
   if (io == RGLRU_F32) {
     cv.take<float>(size_t(B) * D);
     cv.take<float>(size_t(B) * D);
-  } else {
-    cv.take<unsigned char>(decode_partial_bytes(B, D));
   }
   return cv.used;
 }
@@ -472,8 +522,6 @@ int rglru_decode_step(int B, int D, rglru_dtype io, float c, const void* x_t, co
   void* ubuf = cv.take<unsigned char>(size_t(B) * D * io_bytes(io));
   float* za = io == RGLRU_F32 ? cv.take<float>(size_t(B) * D) : nullptr;
   float* zx = io == RGLRU_F32 ? cv.take<float>(size_t(B) * D) : nullptr;
-  float* partial = io == RGLRU_BF16 ? reinterpret_cast<float*>(cv.take<unsigned char>(decode_partial_bytes(B, D)))
-                                    : nullptr;
   const void* u = x_t;
   if (conv_w) {
     if (io == RGLRU_BF16) RG_CHECK(launch_conv_decode<bf16_t>(B, D, x_t, conv_w, conv_b, conv_state, ubuf, stream));
@@ -483,7 +531,7 @@ int rglru_decode_step(int B, int D, rglru_dtype io, float c, const void* x_t, co
   if (io == RGLRU_BF16) {
     DecodeArgs d{};
     d.u = u; d.Wa = W_a; d.Wx = W_x; d.ba = b_a; d.bx = b_x; d.lam = lambda; d.c = c;
-    d.h = h; d.y = y_t; d.partial = partial; d.B = B; d.D = D;
+    d.h = h; d.y = y_t; d.B = B; d.D = D;
     RG_CHECK(launch_decode_bf16(d, stream));
     return RGLRU_OK;
   }
@@ -501,12 +549,13 @@ size_t rglru_bwd_workspace_bytes(int B, int T, int D, rglru_dtype io) {
   return cv.used;
 }
 
-int rglru_bwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const void* conv_w,
-              const float* conv_b, const void* conv_state_in, const void* W_a, const void* W_x,
-              const float* b_a, const float* b_x, const float* lambda, const float* h0,
-              const void* dy, const float* dh_T, float* dx, float* dconv_w, float* dconv_b,
-              float* dW_a, float* dW_x, float* db_a, float* db_x, float* dlambda, float* dh0,
-              void* ws, size_t ws_bytes, hipStream_t stream) {
+static int bwd_impl(const Knobs& k, int B, int T, int D, rglru_dtype io, float c, const void* x,
+                    const void* conv_w, const float* conv_b, const void* conv_state_in,
+                    const void* W_a, const void* W_x, const float* b_a, const float* b_x,
+                    const float* lambda, const float* h0, const void* dy, const float* dh_T,
+                    float* dx, float* dconv_w, float* dconv_b, float* dW_a, float* dW_x,
+                    float* db_a, float* db_x, float* dlambda, float* dh0, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
   int st = shape_status(B, T, D);
   if (st != RGLRU_OK) return st;
   if (!io_ok(io)) return RGLRU_EDTYPE;
@@ -548,7 +597,7 @@ int rglru_bwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const
   sf.x = x; sf.conv_w = conv_w; sf.conv_b = conv_b; sf.conv_state = cs;
   sf.a = w.r; sf.beta = w.i; sf.from_ri = true; sf.lam = lambda; sf.c = c;
   sf.h0 = h0; sf.y = nullptr; sf.h_all = w.h_all; sf.h_T = nullptr;
-  sf.status = w.status; sf.counter = w.counter;
+  sf.status = w.status; sf.counter = w.counter; sf.direct_polls = k.scan_direct_polls;
   if (bf) RG_CHECK((launch_scan_fwd<bf16_t, float>(sf, stream)));
   else RG_CHECK((launch_scan_fwd<float, double>(sf, stream)));
 
@@ -560,6 +609,7 @@ int rglru_bwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const
   sb.dy = dy; sb.dh_T = dh_T; sb.lam = lambda; sb.c = c;
   sb.dz_hi = w.dz_hi; sb.dz_lo = w.dz_lo; sb.du = du; sb.dh0 = dh0;
   sb.partial = w.scan_part; sb.status = w.status; sb.counter = w.counter;
+  sb.max_polls = k.lookback_polls; sb.stall = w.counter + kStallWord;
   if (bf) RG_CHECK((launch_scan_bwd<bf16_t, float>(sb, stream)));
   else RG_CHECK((launch_scan_bwd<float, double>(sb, stream)));
 
@@ -638,6 +688,17 @@ int rglru_bwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const
   return RGLRU_OK;
 }
 
+int rglru_bwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const void* conv_w,
+              const float* conv_b, const void* conv_state_in, const void* W_a, const void* W_x,
+              const float* b_a, const float* b_x, const float* lambda, const float* h0,
+              const void* dy, const float* dh_T, float* dx, float* dconv_w, float* dconv_b,
+              float* dW_a, float* dW_x, float* db_a, float* db_x, float* dlambda, float* dh0,
+              void* ws, size_t ws_bytes, hipStream_t stream) {
+  return bwd_impl(kDefaultKnobs, B, T, D, io, c, x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a,
+                  b_x, lambda, h0, dy, dh_T, dx, dconv_w, dconv_b, dW_a, dW_x, db_a, db_x, dlambda,
+                  dh0, ws, ws_bytes, stream);
+}
+
 size_t rglru_block_fwd_workspace_bytes(int B, int T, int D, int R, rglru_dtype io) {
   if (block_shape_status(B, T, D, R) != RGLRU_OK || !io_ok(io)) return 0;
   Carver cv(nullptr);
@@ -645,12 +706,12 @@ size_t rglru_block_fwd_workspace_bytes(int B, int T, int D, int R, rglru_dtype i
   return cv.used;
 }
 
-int rglru_block_fwd(int B, int T, int D, int R, rglru_dtype io, float c, const void* x,
-                    const void* W_in, const void* conv_w, const float* conv_b,
-                    const void* conv_state_in, const void* W_a, const void* W_x,
-                    const float* b_a, const float* b_x, const float* lambda, const float* h0,
-                    const void* W_out, void* out, float* h_T, void* conv_state_out, void* ws,
-                    size_t ws_bytes, hipStream_t stream) {
+static int block_impl(const Knobs& k, int B, int T, int D, int R, rglru_dtype io, float c,
+                      const void* x, const void* W_in, const void* conv_w, const float* conv_b,
+                      const void* conv_state_in, const void* W_a, const void* W_x,
+                      const float* b_a, const float* b_x, const float* lambda, const float* h0,
+                      const void* W_out, void* out, float* h_T, void* conv_state_out, void* ws,
+                      size_t ws_bytes, hipStream_t stream) {
   int st = block_shape_status(B, T, D, R);
   if (st != RGLRU_OK) return st;
   if (!io_ok(io)) return RGLRU_EDTYPE;
@@ -687,7 +748,7 @@ int rglru_block_fwd(int B, int T, int D, int R, rglru_dtype io, float c, const v
   bool prefilled = false;
   if (conv_w) {
     uint32_t* fill = static_cast<uint32_t*>(w.lru.status);
-    const size_t words = status_fill_words(B, T, R, io);
+    const size_t words = status_fill_words(B, T, R, io, /*fused=*/true);
     if (bf)
       RG_CHECK(launch_conv_fwd<bf16_t>(B, T, R, w.p, conv_w, conv_b, conv_state_in, w.lru.u,
                                        conv_state_out, stream, fill, words, w.lru.counter));
@@ -706,11 +767,15 @@ int rglru_block_fwd(int B, int T, int D, int R, rglru_dtype io, float c, const v
     la.u = u; la.Wa = W_a; la.Wx = W_x; la.ba = b_a; la.bx = b_x; la.lam = lambda; la.c = c;
     la.h0 = h0; la.y = w.y; la.hT = h_T; la.gate = w.g; la.B = B; la.T = T; la.D = R;
     la.status = static_cast<uint32_t*>(w.lru.status); la.counters = w.lru.counter;
+    la.ticket_guess = k.lru_ticket_guess; la.max_polls = k.lookback_polls;
+    la.stall = w.lru.counter + kStallWord;
     RG_CHECK(launch_lru_fused(la, prefilled, stream));
   } else {
-    st = lru_layer(io, B, T, R, c, u, W_a, W_x, b_a, b_x, lambda, h0, w.y, h_T, w.lru, prefilled, stream);
+    st = lru_layer(io, B, T, R, c, u, W_a, W_x, b_a, b_x, lambda, h0, w.y, h_T, w.lru, prefilled,
+                   k, stream);
     if (st != RGLRU_OK) return st;
-    RG_CHECK(launch_mul_f32(static_cast<float*>(w.y), static_cast<const float*>(w.g), size_t(M) * R, stream));
+    RG_CHECK(launch_mul_f32(static_cast<float*>(w.y), static_cast<const float*>(w.g), size_t(M) * R,
+                            stream));
   }
 
   // 3. the output linear on z
@@ -726,6 +791,27 @@ int rglru_block_fwd(int B, int T, int D, int R, rglru_dtype io, float c, const v
     RG_CHECK(launch_plain_gemm_f32(po, stream));
   }
   return RGLRU_OK;
+}
+
+int rglru_block_fwd(int B, int T, int D, int R, rglru_dtype io, float c, const void* x,
+                    const void* W_in, const void* conv_w, const float* conv_b,
+                    const void* conv_state_in, const void* W_a, const void* W_x,
+                    const float* b_a, const float* b_x, const float* lambda, const float* h0,
+                    const void* W_out, void* out, float* h_T, void* conv_state_out, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
+  return block_impl(kDefaultKnobs, B, T, D, R, io, c, x, W_in, conv_w, conv_b, conv_state_in, W_a,
+                    W_x, b_a, b_x, lambda, h0, W_out, out, h_T, conv_state_out, ws, ws_bytes,
+                    stream);
+}
+
+int rglru_workspace_status(const void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ws || !aligned16(ws)) return RGLRU_EINVAL;
+  if (ws_bytes < kCounterWords * sizeof(uint32_t)) return RGLRU_EWORKSPACE;
+  uint32_t flag = 0;
+  RG_CHECK(hipMemcpyAsync(&flag, static_cast<const uint32_t*>(ws) + kStallWord, sizeof(flag),
+                          hipMemcpyDeviceToHost, stream));
+  RG_CHECK(hipStreamSynchronize(stream));
+  return flag ? RGLRU_ESTALL : RGLRU_OK;
 }
 
 size_t gated_mlp_fwd_workspace_bytes(int B, int T, int D, int MD, rglru_dtype io) {
@@ -879,7 +965,6 @@ size_t rglru_block_decode_workspace_bytes(int B, int D, int R, rglru_dtype io) {
   if (io == RGLRU_BF16) {
     const size_t a = splitk_partial_bytes(B, 2 * R, D), b = splitk_partial_bytes(B, D, R);
     cv.take<unsigned char>(a > b ? a : b);          // split-K partials of both linears
-    cv.take<unsigned char>(decode_partial_bytes(B, R));
   } else {
     cv.take<float>(2 * n);                          // the input linears' product
   }
@@ -907,12 +992,10 @@ int rglru_block_decode_step(int B, int D, int R, rglru_dtype io, float c, const 
   const size_t n = size_t(B) * R;
   const bool bf = io == RGLRU_BF16;
   float* part = nullptr;
-  float* dpart = nullptr;
   float* pq = nullptr;
   if (bf) {
     const size_t a = splitk_partial_bytes(B, 2 * R, D), b = splitk_partial_bytes(B, D, R);
     part = reinterpret_cast<float*>(cv.take<unsigned char>(a > b ? a : b));
-    dpart = reinterpret_cast<float*>(cv.take<unsigned char>(decode_partial_bytes(B, R)));
   } else {
     pq = cv.take<float>(2 * n);
   }
@@ -943,7 +1026,7 @@ int rglru_block_decode_step(int B, int D, int R, rglru_dtype io, float c, const 
   if (bf) {
     DecodeArgs d{};
     d.u = uin; d.Wa = W_a; d.Wx = W_x; d.ba = b_a; d.bx = b_x; d.lam = lambda; d.c = c;
-    d.h = h; d.y = z; d.partial = dpart; d.B = B; d.D = R; d.gate = g;
+    d.h = h; d.y = z; d.B = B; d.D = R; d.gate = g;
     RG_CHECK(launch_decode_bf16(d, stream));
   } else {
     GateGemmArgs ga{};
@@ -966,6 +1049,64 @@ int rglru_block_decode_step(int B, int D, int R, rglru_dtype io, float c, const 
     RG_CHECK(launch_plain_gemm_f32(po, stream));
   }
   return RGLRU_OK;
+}
+
+// ------------------------------------------------------------------ test entry points
+// Declared in rglru_testing.h (not part of the public header): the public calls with the
+// chained-scan settings passed explicitly instead of kDefaultKnobs.
+
+static Knobs knobs_of(const rglru_testing_knobs* t) {
+  return t ? Knobs{t->lru_ticket_guess, t->scan_direct_polls, t->lookback_polls} : kDefaultKnobs;
+}
+
+void rglru_testing_default_knobs(rglru_testing_knobs* t) {
+  if (!t) return;
+  t->lru_ticket_guess = kDefaultKnobs.lru_ticket_guess;
+  t->scan_direct_polls = kDefaultKnobs.scan_direct_polls;
+  t->lookback_polls = kDefaultKnobs.lookback_polls;
+}
+
+int rglru_testing_fwd(const rglru_testing_knobs* t, int B, int T, int D, rglru_dtype io, float c,
+                      const void* x, const void* conv_w, const float* conv_b,
+                      const void* conv_state_in, const void* W_a, const void* W_x,
+                      const float* b_a, const float* b_x, const float* lambda, const float* h0,
+                      void* y, float* h_T, void* conv_state_out, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  return fwd_impl(knobs_of(t), B, T, D, io, c, x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a,
+                  b_x, lambda, h0, y, h_T, conv_state_out, ws, ws_bytes, stream);
+}
+
+int rglru_testing_scan(const rglru_testing_knobs* t, int B, int T, int D, rglru_dtype io,
+                       const void* x, const void* conv_w, const float* conv_b,
+                       const void* conv_state_in, const float* a, const float* beta,
+                       const float* h0, void* y, float* h_T, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  return scan_impl(knobs_of(t), B, T, D, io, x, conv_w, conv_b, conv_state_in, a, beta, h0, y,
+                   h_T, ws, ws_bytes, stream);
+}
+
+int rglru_testing_bwd(const rglru_testing_knobs* t, int B, int T, int D, rglru_dtype io, float c,
+                      const void* x, const void* conv_w, const float* conv_b,
+                      const void* conv_state_in, const void* W_a, const void* W_x,
+                      const float* b_a, const float* b_x, const float* lambda, const float* h0,
+                      const void* dy, const float* dh_T, float* dx, float* dconv_w,
+                      float* dconv_b, float* dW_a, float* dW_x, float* db_a, float* db_x,
+                      float* dlambda, float* dh0, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return bwd_impl(knobs_of(t), B, T, D, io, c, x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a,
+                  b_x, lambda, h0, dy, dh_T, dx, dconv_w, dconv_b, dW_a, dW_x, db_a, db_x, dlambda,
+                  dh0, ws, ws_bytes, stream);
+}
+
+int rglru_testing_block_fwd(const rglru_testing_knobs* t, int B, int T, int D, int R,
+                            rglru_dtype io, float c, const void* x, const void* W_in,
+                            const void* conv_w, const float* conv_b, const void* conv_state_in,
+                            const void* W_a, const void* W_x, const float* b_a, const float* b_x,
+                            const float* lambda, const float* h0, const void* W_out, void* out,
+                            float* h_T, void* conv_state_out, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  return block_impl(knobs_of(t), B, T, D, R, io, c, x, W_in, conv_w, conv_b, conv_state_in, W_a,
+                    W_x, b_a, b_x, lambda, h0, W_out, out, h_T, conv_state_out, ws, ws_bytes,
+                    stream);
 }
 
 }  // extern "C"

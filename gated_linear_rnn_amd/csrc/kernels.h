@@ -7,6 +7,23 @@
 
 namespace rglru {
 
+// ---------------------------------------------------------------- chained-scan settings
+// Every workspace of a call that runs a chained scan starts with 64 counter words, zeroed
+// by the call: ticket counters, and at kStallWord the flag a look-back sets when it gives up
+// waiting for a predecessor chunk (rglru_workspace_status reads it).
+constexpr int kCounterWords = 64;
+constexpr int kStallWord = 63;
+// Polls of an unpublished predecessor before the forward scan computes its summary itself.
+constexpr int kDirectPolls = 2048;
+// Settings of the chained scans that only the test entry points change; every public entry
+// point runs with kDefaultKnobs.
+struct Knobs {
+  int lru_ticket_guess;   // fused RG-LRU kernel: shift of the launch-order ticket guess
+  int scan_direct_polls;  // forward scan: see ScanFwdArgs::direct_polls
+  int lookback_polls;     // fused kernel and reverse scan: polls before a look-back gives up
+};
+extern const Knobs kDefaultKnobs;
+
 // ---------------------------------------------------------------- conv.hip
 // With fill/counter, the same launch also prepares the look-back status of a following
 // scan (fill_words words set to all ones, counter[0..63] = 0).
@@ -51,8 +68,8 @@ struct GateGemmArgs {
 };
 size_t gate_gemm_tail_bytes(int M, int N, int K);
 
-// One bf16 decode step after the conv: split-K gate projection into `partial`, then the
-// fixed-order sum, the gates and the state update (decode.hip).
+// One bf16 decode step after the conv: the gate projection, the gates and the state update
+// in one kernel (decode.hip); no workspace.
 struct DecodeArgs {
   const void* u;      // [B, D] bf16, the conv output of the step
   const void* Wa;     // [D, D] bf16
@@ -63,14 +80,9 @@ struct DecodeArgs {
   float c;
   float* h;           // [B, D] state, in/out
   void* y;            // [B, D] bf16
-  float* partial;     // decode_partial_bytes(B, D): the split sums, then 3 D gate constants
   int B, D;
-  int splits;         // set by the launcher
-  float* chan;        // set by the launcher: [3, D] per-channel gate constants
   const void* gate;   // [B, D] bf16 or NULL: y = RNE(h * gate) instead of RNE(h)
 };
-int decode_splits(int B, int D);
-size_t decode_partial_bytes(int B, int D);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 
 // C[M,N] = A[M,K] B[N,K]^T (+ addend), fp32 output.  With A2 (bf16 only) the product
@@ -216,10 +228,12 @@ struct LruArgs {
   uint32_t* counters;     // 64 ticket counters (zeroed with the status words)
   int groups;             // set by the launcher
   const void* gate;       // [B,T,D] bf16 multiplier of the output (the block's GeLU branch) or NULL
-  int ticket_guess;       // set by the launcher: added to the launch-order ticket guess (0)
+  int ticket_guess;       // added to the launch-order ticket guess (0; tests shift it)
+  int max_polls;          // look-back polls before giving up (kMaxPolls; < 0: at once)
+  uint32_t* stall;        // set to 1 when a look-back gives up (counters + kStallWord)
 };
 int lru_chunks(int T);
-void set_lru_ticket_guess(int offset);
+long lru_tiles(int B, int T, int D);   // workgroups of one fused launch
 size_t lru_status_bytes(int B, int T, int D);
 hipError_t launch_lru_fused(const LruArgs& a, bool prefilled, hipStream_t s);
 
@@ -243,11 +257,10 @@ struct ScanFwdArgs {
   uint32_t* counter;      // 64 words zeroed with the status words (the forward scan takes no tickets)
   bool prefilled;         // status and counters already initialised on this stream
   int groups;             // tile groups, set by the launcher
-  int direct_polls;       // look-back polls before a summary is computed directly; set by the launcher
+  int direct_polls;       // look-back polls of an unpublished predecessor before its summary
+                          // is computed from memory (kDirectPolls; < 0: always, ignoring
+                          // published values)
 };
-// Test hook: polls of an unpublished look-back predecessor before the forward scan computes
-// its summary itself (negative: always, ignoring published values).
-void set_scan_direct_polls(int polls);
 // Look-back status bytes of a scan whose state type has acc_bytes bytes (4 or 8).
 size_t scan_status_bytes(int B, int T, int D, int acc_bytes);
 // Acc = float for bf16 I/O, double for fp32 I/O.
@@ -271,7 +284,9 @@ struct ScanBwdArgs {
   float* dh0;             // [B,D] or NULL
   double* partial;        // [B * nchunks, 3, D]: db_a, db_x, dL partial sums
   void* status;
-  uint32_t* counter;
+  uint32_t* counter;      // 64 words: the ticket counter, ..., the stall flag (kStallWord)
+  int max_polls;          // look-back polls before giving up (kMaxPolls; < 0: at once)
+  uint32_t* stall;        // set to 1 when a look-back gives up
 };
 int scan_chunks(int T);
 template <typename IO, typename Acc> hipError_t launch_scan_bwd(const ScanBwdArgs& a, hipStream_t s);

@@ -43,6 +43,7 @@ static_assert(kTileBytes + kEpiScratch <= CfgLru::LDS_BYTES, "epilogue LDS");
 static_assert(2 * kTileBytes + kEpiScratch + 1024 <= 160 * 1024, "gated epilogue LDS");
 
 int lru_chunks(int T) { return (T + kLruRows - 1) / kLruRows; }
+long lru_tiles(int B, int T, int D) { return long(B) * ((D + kLruCh - 1) / kLruCh) * lru_chunks(T); }
 size_t lru_status_bytes(int B, int T, int D) { return 3ull * lru_chunks(T) * size_t(B) * D * 4; }
 
 static int lru_groups(int chains) {
@@ -160,7 +161,8 @@ __device__ __forceinline__ void lru_epilogue(const LruArgs& p, unsigned char* ld
         publish<float>(aggA + size_t(tt) * BD + base, At);
         publish<float>(aggH + size_t(tt) * BD + base, Ht);
         carry = lookback_carry<float>(incl + base, aggA + base, aggH + base, tt, BD,
-                                      eLb + chl * 2 * kWindow, eLb + chl * 2 * kWindow + kWindow);
+                                      eLb + chl * 2 * kWindow, eLb + chl * 2 * kWindow + kWindow,
+                                      p.max_polls, p.stall);
       } else {
         carry = p.h0 ? p.h0[base] : 0.f;
       }
@@ -261,17 +263,15 @@ __global__ __launch_bounds__(CfgLru::NW * 64, 2) void lru_fused_kernel(LruArgs p
   lru_epilogue<true, GATED>(p, lds, acc, lane, wave, b, tn, tt, t0, rows);
 }
 
-static int g_lru_ticket_guess = 0;
-void set_lru_ticket_guess(int offset) { g_lru_ticket_guess = offset > 0 ? offset : 0; }
-
 hipError_t launch_lru_fused(const LruArgs& a_in, bool prefilled, hipStream_t s) {
   LruArgs a = a_in;
-  a.ticket_guess = g_lru_ticket_guess;
+  if (a.ticket_guess < 0) a.ticket_guess = 0;
   const int NT = (a.D + kLruCh - 1) / kLruCh;
   const int chains = a.B * NT;
   a.groups = lru_groups(chains);
   if (!prefilled) {
-    const hipError_t e = launch_fill_status(a.status, lru_status_bytes(a.B, a.T, a.D) / 4, a.counters, 64, s);
+    const hipError_t e = launch_fill_status(a.status, lru_status_bytes(a.B, a.T, a.D) / 4,
+                                            a.counters, kCounterWords, s);
     if (e != hipSuccess) return e;
   }
   const int tiles = chains * lru_chunks(a.T);

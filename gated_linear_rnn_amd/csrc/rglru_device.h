@@ -93,17 +93,71 @@ __device__ __forceinline__ WaveHalves wave_halves(float x) {
 }
 
 // ------------------------------------------------------------------ conv (R1)
-// u = RNE_io(b + w0 x_t + w1 x_{t-1} + w2 x_{t-2} + w3 x_{t-3}), one fixed fma order so
-// every kernel that evaluates u produces the same bits.
+// fp64 -> bf16, round to nearest even in one step (no intermediate fp32 rounding), returned
+// as the fp32 value it represents.  Normal range: the 45 dropped significand bits are
+// rounded away on the bit pattern (adding half an ulp minus one plus the lowest kept bit
+// carries exactly when the dropped part exceeds half, or equals half with an odd kept part),
+// and the result, 8 significant bits, converts to fp32 exactly.  Below 2^-126 bf16 is
+// subnormal with a fixed ulp of 2^-133: rounded with rint at that scale.
+__device__ __forceinline__ float f64_to_bf16_value(double v) {
+  if (!(fabs(v) >= 0x1p-126)) {                     // subnormal range, zero, or NaN
+    if (v != v) return __builtin_nanf("");
+    return float(rint(v * 0x1p133) * 0x1p-133);
+  }
+  uint64_t bits = uint64_t(__double_as_longlong(v));
+  bits += ((uint64_t(1) << 44) - 1) + ((bits >> 45) & 1);
+  bits &= ~((uint64_t(1) << 45) - 1);
+  return float(__longlong_as_double((long long)bits));
+}
+
+// u = RNE_io(b + w0 x_t + w1 x_{t-1} + w2 x_{t-2} + w3 x_{t-3}), rounded once: the exact sum
+// (taken in fp64 in one fixed order, bias then taps 0..3; every product of two fp32 or bf16
+// values is exact in fp64, so fma(w, x, acc) is the add of the exact product), rounded once
+// to the I/O dtype.  Every kernel that evaluates u uses this, so all of them produce the
+// same bits.
+__device__ __forceinline__ double conv_sum_f64(float b, float w0, float w1, float w2, float w3,
+                                               float x0, float x1, float x2, float x3) {
+  double acc = double(b);
+  acc = fma(double(w0), double(x0), acc);
+  acc = fma(double(w1), double(x1), acc);
+  acc = fma(double(w2), double(x2), acc);
+  acc = fma(double(w3), double(x3), acc);
+  return acc;
+}
+
 template <typename IO>
 __device__ __forceinline__ float conv_u(float b, float w0, float w1, float w2, float w3,
-                                        float x0, float x1, float x2, float x3) {
-  float acc = b;
-  acc = fmaf(w0, x0, acc);
-  acc = fmaf(w1, x1, acc);
-  acc = fmaf(w2, x2, acc);
-  acc = fmaf(w3, x3, acc);
-  return Io<IO>::round(acc);
+                                        float x0, float x1, float x2, float x3);
+
+template <>
+__device__ __forceinline__ float conv_u<float>(float b, float w0, float w1, float w2, float w3,
+                                               float x0, float x1, float x2, float x3) {
+  return float(conv_sum_f64(b, w0, w1, w2, w3, x0, x1, x2, x3));
+}
+
+// bf16 I/O, mostly in fp32: the fp32 fma chain s (each bf16 product is exact in fp32, so the
+// chain only rounds its 4 partial sums) is within 4.01 * 2^-24 * m of the exact sum S, where
+// m = |b| + sum |w_k x_k|.  bf16 rounding changes value only at the halfway points between
+// bf16 neighbours; the one inside s's bf16 interval has s's top 16 bits and 0x8000 below.
+// When s is more than 8 * 2^-24 * m from it, S lies strictly on the same side of it (and no
+// other halfway point is nearer than half a bf16 ulp), so RNE_bf16(s) = RNE_bf16(S).  The
+// rare sums closer than that (about 2^-12 of them for sums without cancellation) take the
+// fp64 sum and its one rounding instead.
+template <>
+__device__ __forceinline__ float conv_u<bf16_t>(float b, float w0, float w1, float w2, float w3,
+                                                float x0, float x1, float x2, float x3) {
+  float s = fmaf(w0, x0, b);
+  s = fmaf(w1, x1, s);
+  s = fmaf(w2, x2, s);
+  s = fmaf(w3, x3, s);
+  float m = fmaf(fabsf(w0), fabsf(x0), fabsf(b));
+  m = fmaf(fabsf(w1), fabsf(x1), m);
+  m = fmaf(fabsf(w2), fabsf(x2), m);
+  m = fmaf(fabsf(w3), fabsf(x3), m);
+  const float mid = __uint_as_float((__float_as_uint(s) & 0xffff0000u) | 0x8000u);
+  if (__builtin_expect(fabsf(s - mid) > m * 0x1p-21f, 1))   // s - mid is exact (one binade)
+    return Io<bf16_t>::round(s);
+  return f64_to_bf16_value(conv_sum_f64(b, w0, w1, w2, w3, x0, x1, x2, x3));
 }
 
 // ------------------------------------------------------------------ GeLU
@@ -248,8 +302,9 @@ __device__ __forceinline__ typename Words<Acc>::W peek(const typename Words<Acc>
                            __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Upper bound on polls of one predecessor word; beyond it the carry becomes NaN (the
-// output is then visibly wrong) instead of the kernel waiting forever.
+// Default bound on polls of one predecessor word; beyond it the look-back gives up: the
+// carry becomes NaN (the output is then visibly wrong), the stall flag is set for the host,
+// and the kernel goes on instead of waiting forever.
 constexpr int kMaxPolls = 1 << 20;
 
 // Decoupled look-back for one channel, with a canonical result.  `incl`, `aggA`, `aggH`
@@ -261,14 +316,22 @@ constexpr int kMaxPolls = 1 << 20;
 // would compute, whatever the timing: results are reproducible run to run.  At most
 // kWindow aggregates are collected; past that the walk waits for an inclusive state.
 // `bufA`, `bufH` are kWindow values of scratch (LDS) owned by the calling thread.
+// A wait that exceeds max_polls polls of one word (max_polls < 0: any look-back at all)
+// gives up: it stores 1 to *stall and returns NaN.
 constexpr int kWindow = 16;
 
 template <typename Acc>
 __device__ __forceinline__ Acc lookback_carry(const typename Words<Acc>::W* incl,
                                               const typename Words<Acc>::W* aggA,
                                               const typename Words<Acc>::W* aggH, int pos,
-                                              size_t stride, Acc* bufA, Acc* bufH) {
+                                              size_t stride, Acc* bufA, Acc* bufH, int max_polls,
+                                              uint32_t* stall) {
   typedef Words<Acc> Wd;
+  auto give_up = [&]() {
+    __hip_atomic_store(stall, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return Wd::val(Wd::kNaN);
+  };
+  if (max_polls < 0) return give_up();
   int j = pos - 1;
   int n = 0;
   int polls = 0;
@@ -291,7 +354,7 @@ __device__ __forceinline__ Acc lookback_carry(const typename Words<Acc>::W* incl
         continue;
       }
     }
-    if (++polls > kMaxPolls) return Wd::val(Wd::kNaN);
+    if (++polls > max_polls) return give_up();
     __builtin_amdgcn_s_sleep(1);
   }
   for (int k = n - 1; k >= 0; --k) h = fmaA(bufA[k], h, bufH[k]);

@@ -400,18 +400,13 @@ __global__ __launch_bounds__(256, sizeof(Acc) == 4 ? 4 : 2) void scan_fwd_kernel
 
 }
 
-// Polls of an unpublished predecessor before its summary is computed directly (see
-// scan_lookback); about a millisecond, far longer than a running workgroup takes to publish.
-static int g_scan_direct_polls = 2048;
-void set_scan_direct_polls(int polls) { g_scan_direct_polls = polls; }
-
 template <typename IO, typename Acc>
 hipError_t launch_scan_fwd(const ScanFwdArgs& a_in, hipStream_t s) {
   ScanFwdArgs a = a_in;
-  a.direct_polls = g_scan_direct_polls;
   if (!a.prefilled) {
     const size_t words = 3ull * scan_fwd_chunks(a.T) * size_t(a.B) * a.D * sizeof(Acc) / 4;
-    const hipError_t e = launch_fill_status(static_cast<uint32_t*>(a.status), words, a.counter, 64, s);
+    const hipError_t e =
+        launch_fill_status(static_cast<uint32_t*>(a.status), words, a.counter, kCounterWords, s);
     if (e != hipSuccess) return e;
   }
   const int chains = a.B * (a.D / kCh);
@@ -522,7 +517,7 @@ __global__ __launch_bounds__(256) void scan_bwd_kernel(ScanBwdArgs p) {
       Acc carry;
       if (pos == 0) carry = p.dh_T ? Acc(p.dh_T[base + j]) : Acc(0);
       else carry = lookback_carry<Acc>(incl + base + j, aggA + base + j, aggH + base + j, pos, BD,
-                                       sLb[cg][0], sLb[cg][1]);
+                                       sLb[cg][0], sLb[cg][1], p.max_polls, p.stall);
       publish<Acc>(incl + size_t(pos) * BD + base + j, fmaA(Ag[j], carry, Hg[j]));
       sCarry[4 * cg + j] = carry;
     }
@@ -638,7 +633,8 @@ __global__ __launch_bounds__(256) void scan_bwd_kernel(ScanBwdArgs p) {
 template <typename IO, typename Acc>
 hipError_t launch_scan_bwd(const ScanBwdArgs& a, hipStream_t s) {
   const hipError_t e = launch_fill_status(static_cast<uint32_t*>(a.status),
-                                          scan_status_bytes(a.B, a.T, a.D, sizeof(Acc)) / 4, a.counter, 1, s);
+                                          scan_status_bytes(a.B, a.T, a.D, sizeof(Acc)) / 4,
+                                          a.counter, kCounterWords, s);
   if (e != hipSuccess) return e;
   const int tiles = scan_chunks(a.T) * a.B * (a.D / kCh);
   scan_bwd_kernel<IO, Acc><<<tiles, 256, 0, s>>>(a);

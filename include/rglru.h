@@ -32,6 +32,8 @@
  *     launch nothing.  A launch failure returns RGLRU_EHIP.  Device faults surface at
  *     the caller's next synchronisation.  No C++ exception crosses this interface.
  *   - Calls that share a workspace must not overlap in time.
+ *   - Every call runs with the same fixed settings: nothing set by an earlier call changes
+ *     a later one.
  */
 #ifndef RGLRU_H
 #define RGLRU_H
@@ -50,7 +52,8 @@ typedef enum {
   RGLRU_EDTYPE = -3,     /* unknown I/O dtype */
   RGLRU_EWORKSPACE = -4, /* ws null or smaller than the query returns */
   RGLRU_EHIP = -5,       /* a kernel launch or HIP runtime call failed */
-  RGLRU_EINTERNAL = -6
+  RGLRU_EINTERNAL = -6,
+  RGLRU_ESTALL = -7      /* rglru_workspace_status: a chained-scan wait gave up */
 } rglru_status;
 
 typedef enum { RGLRU_F32 = 0, RGLRU_BF16 = 1 } rglru_dtype;
@@ -62,8 +65,10 @@ const char* rglru_status_string(int status);
  * Causal depthwise Conv1D, temporal width 4 (the "Recurrent block" section of the
  * Griffin model-architecture page: a small separable Conv1D with 4*D parameters).
  *   u[b,t,d] = RNE_io( b[d] + w[0,d] x[b,t,d] + w[1,d] x[b,t-1,d] + w[2,d] x[b,t-2,d]
- *                      + w[3,d] x[b,t-3,d] ), evaluated in fp32,
+ *                      + w[3,d] x[b,t-3,d] ),
  * with x[b,t,d] for t < 0 taken from state_in[b,3+t,d] (zeros when state_in is NULL).
+ * The sum is taken in fp64 (bias, then taps 0..3; every product is exact there) and
+ * rounded once to the I/O dtype.
  *   x [B,T,D] io; w [4,D] io; b [D] fp32 or NULL (zero); state_in [B,3,D] io or NULL;
  *   u [B,T,D] io (output); state_out [B,3,D] io or NULL: the last three time rows of
  *   [state_in || x].
@@ -310,28 +315,15 @@ int local_mqa_decode_step(int B, int D, rglru_dtype io, int window, const int* p
                           void* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * Test hook of the forward scan's look-back (rglru_scan, rglru_bwd's state recompute and
- * the fp32-I/O forward).  A chunk of the chained scan normally takes the summary its
- * predecessor chunks publish; one that finds a predecessor unpublished after `polls` polls
- * computes that summary itself from memory (the same bits), so the scan never depends on
- * the order in which the GPU starts workgroups.  polls < 0 ignores every published value
- * and always computes them (slow; for tests that this path gives the same bits).  The
- * setting is process-wide host state read at each launch; the default is 2048.  Not
- * thread-safe against concurrent launches.
+ * Status of the chained scans of the last call that ran on the workspace `ws` (a workspace
+ * of rglru_fwd, rglru_lru, rglru_scan, rglru_bwd or rglru_block_fwd, which all start with
+ * the same counter words).  Chunks of a chained scan (the blog page "Griffin's Compromise",
+ * "Term explanation: Parallel scan") wait for the summary of their predecessor chunk; that
+ * wait is bounded, and one that gives up writes NaN where the carry was needed instead of
+ * hanging.  Returns RGLRU_ESTALL if any wait of that call gave up, RGLRU_OK otherwise.
+ * Synchronous: copies one word to the host on `stream` and waits for the stream.
  */
-void rglru_test_set_scan_direct_polls(int polls);
-
-/*
- * Test hook of the fused RG-LRU kernel (rglru_fwd, rglru_lru, rglru_block_fwd).  Each of its
- * workgroups takes a ticket (which tile it computes) from an atomic counter and, while the
- * atomic is in flight, already loads the first operand block of the tile it would get if
- * tickets went in launch order; when the ticket differs it waits for those loads and loads
- * its own tile.  offset > 0 shifts that guess by `offset` tickets, so (nearly) every
- * workgroup takes the second path; results must not change.  Values <= 0 restore the
- * default (0).  Process-wide host state read at each launch; not thread-safe against
- * concurrent launches.
- */
-void rglru_test_set_lru_ticket_guess(int offset);
+int rglru_workspace_status(const void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

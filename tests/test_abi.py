@@ -10,10 +10,11 @@ import gated_linear_rnn_amd as g
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rglru.h")
+TEST_HEADER = os.path.join(ROOT, "gated_linear_rnn_amd", "csrc", "rglru_testing.h")
 
 
-def _declared_functions():
-    src = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    src = open(header).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w ]*?[\s\*]+([a-z_][a-z0-9_]*)\s*\(", src, re.M)
     return sorted(set(names))
@@ -33,9 +34,31 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name), name
 
 
+def test_public_header_has_no_test_hooks():
+    """The public interface takes no process-wide settings: test-only entry points live in
+    their own header, take their settings as an argument, and the public names are disjoint
+    from them."""
+    public = _declared_functions()
+    assert not [n for n in public if "test" in n], public
+    src = open(HEADER).read()
+    assert "rglru_testing" not in src and "test hook" not in src.lower()
+    from gated_linear_rnn_amd import testing
+    assert _declared_functions(TEST_HEADER) == sorted(testing.EXPORTS)
+
+
+def test_test_only_symbols_are_exported_and_take_their_settings_per_call(lib):
+    from gated_linear_rnn_amd import testing
+    for name in testing.EXPORTS:
+        assert hasattr(lib, name), name
+    k = testing.knobs()
+    assert (k.lru_ticket_guess, k.scan_direct_polls, k.lookback_polls) == (0, 2048, 1 << 20)
+    assert testing.knobs(lookback_polls=-1).lookback_polls == -1
+    assert testing.knobs().lookback_polls == 1 << 20          # nothing persists between calls
+
+
 def test_status_strings_cover_every_code(lib):
     codes = {0: "RGLRU_OK", -1: "RGLRU_EINVAL", -2: "RGLRU_ESHAPE", -3: "RGLRU_EDTYPE",
-             -4: "RGLRU_EWORKSPACE", -5: "RGLRU_EHIP", -6: "RGLRU_EINTERNAL"}
+             -4: "RGLRU_EWORKSPACE", -5: "RGLRU_EHIP", -6: "RGLRU_EINTERNAL", -7: "RGLRU_ESTALL"}
     for c, name in codes.items():
         assert g.status_string(c).startswith(name)
     assert "unknown" in g.status_string(7)
@@ -229,3 +252,10 @@ def test_block_decode_rejects_invalid_arguments(lib):
     assert call(h=BAD) == -1
     assert call(ws=None) == -4
     assert call(wsb=3) == -4
+
+
+@no_gpu
+def test_workspace_status_rejects_invalid_arguments(lib):
+    assert lib.rglru_workspace_status(None, 1 << 20, None) == -1
+    assert lib.rglru_workspace_status(BAD, 1 << 20, None) == -1
+    assert lib.rglru_workspace_status(A, 255, None) == -4

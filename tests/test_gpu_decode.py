@@ -12,14 +12,17 @@ from gpu_util import TOL, TORCH_IO, dev, err, host, sample_channels
 pytestmark = pytest.mark.gpu
 
 
-def _run(g, p, steps, channels=None, conv=True):
+def _run(g, p, steps, channels=None, conv=True, rows=None):
     """Run `steps` decode steps on the GPU; compare every y_t (and the final state) with the
-    oracle, restricted to `channels` when given."""
+    oracle, restricted to `channels` when given.  `rows`: sequences that are also compared
+    on every channel (sequences are independent, so the oracle runs on those rows alone)."""
     w = p["workload"]
     io = TORCH_IO[w.io]
     B, D = w.B, w.D
     S = np.arange(D) if channels is None else channels
     St = torch.from_numpy(S).cuda()
+    R = np.arange(0) if rows is None else np.asarray(rows)
+    Rt = torch.from_numpy(R).cuda()
     x = dev(p["x"][:steps], io)                        # [steps, B, D]
     cw = dev(p["conv_w"], io) if conv else None
     cb = dev(p["conv_b"]) if conv else None
@@ -29,10 +32,13 @@ def _run(g, p, steps, channels=None, conv=True):
     h = dev(p["h0"])
     ws = g.workspace(g.decode_workspace_bytes(B, D, io))
     ys = torch.empty((steps, B, len(S)), dtype=torch.float32, device="cuda")
+    yr = torch.empty((steps, len(R), D), dtype=torch.float32, device="cuda")
     y_t = torch.empty((B, D), dtype=io, device="cuda")
     for t in range(steps):
         g.rglru_decode_step(x[t], cw, cb, hist, Wa, Wx, ba, bx, lam, h, y_t, ws, p["c"])
         ys[t] = y_t.float().index_select(1, St)
+        if len(R):
+            yr[t] = y_t.float().index_select(0, Rt)
     torch.cuda.synchronize()
     # oracle, channel subset: the conv history is kept for every channel (the gates read all
     # of u), the state only matters on S
@@ -52,6 +58,22 @@ def _run(g, p, steps, channels=None, conv=True):
     assert worst <= TOL[w.io] and eh <= TOL[w.io]
     if conv:
         np.testing.assert_array_equal(host(hist), hist_o)
+    if len(R):
+        hist_r = p["conv_state"][R].astype(np.float64)
+        h_r = p["h0"][R].astype(np.float64).copy()
+        worst_r = 0.0
+        for t in range(steps):
+            o = oracle.forward(p["x"][t][R][:, None, :], p["conv_w"] if conv else None,
+                               p["conv_b"] if conv else None, hist_r if conv else None, p["W_a"],
+                               p["W_x"], p["b_a"], p["b_x"], p["lam"], h_r, p["c"], w.io)
+            worst_r = max(worst_r, err(host(yr[t]), o["y"][:, 0, :]))
+            h_r = o["h_T"]
+            if conv:
+                hist_r = o["conv_state_out"]
+        eh_r = err(host(h)[R], h_r)
+        print(f"decode rows {R.tolist()}, all {D} channels: err(y)={worst_r:.3e} err(h)={eh_r:.3e}",
+              flush=True)
+        assert worst_r <= TOL[w.io] and eh_r <= TOL[w.io]
 
 
 @pytest.mark.parametrize("io,B,D", [("f32", 3, 128), ("bf16", 16, 256), ("bf16", 5, 192),
@@ -94,10 +116,12 @@ def test_decode_continues_forward(lib):
 
 
 @pytest.mark.timeout(900)
-def test_decode_full_workload_channel_subset(lib):
+def test_decode_full_workload(lib):
+    """All 1024 steps at B = 256, D = 2560: a channel subset of every sequence, and every
+    channel of four sequences (first, last and two inside)."""
     p = workloads.make_inputs(workloads.DECODE)
     S = sample_channels(workloads.DECODE.D, 24, seed=5)
-    _run(lib, p, workloads.DECODE.T, channels=S)
+    _run(lib, p, workloads.DECODE.T, channels=S, rows=[0, 77, 128, workloads.DECODE.B - 1])
 
 
 def test_decode_graph_replays_match_eager(lib):

@@ -66,13 +66,53 @@ def test_tiny_f32_workload_full(lib):
     _check(lib, p, what="tiny")
 
 
-@pytest.mark.timeout(600)
+def _one_sequence(p, b):
+    """The inputs of sequence b alone (sequences are independent: the recurrence is per
+    (sequence, channel) and the gate projection per (sequence, step))."""
+    q = dict(p)
+    for k in ("x", "conv_state", "h0"):
+        if q.get(k) is not None:
+            q[k] = q[k][b:b + 1]
+    return q
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("w", [workloads.TRAIN_FWD, workloads.LONG_FWD, workloads.TRAIN_BWD],
                          ids=lambda w: w.name)
-def test_forward_full_size_channel_subset(lib, w):
+def test_forward_full_size(lib, w):
+    """The full workload in one call: a seeded channel subset of every sequence, and every
+    channel of one whole sequence (all channel tiles and time tiles of the fused kernel)."""
     p = workloads.make_inputs(w)
+    d = device_inputs(p)
+    y, hT, _ = gpu_forward(lib, d, p["c"])
     S = sample_channels(w.D, 40, seed=w.seed)
-    _check(lib, p, channels=S, what=w.name)
+    o = oracle_forward(p, channels=S)
+    ey, eh = err(y[:, :, S], o["y"]), err(hT[:, S], o["h_T"])
+    print(f"{w.name} channel subset ({len(S)} of {w.D}) err(y)={ey:.3e} err(h_T)={eh:.3e}", flush=True)
+    assert ey <= TOL[w.io] and eh <= TOL[w.io]
+    b = w.B - 1
+    del o
+    o = oracle_forward(_one_sequence(p, b))
+    ey, eh = err(y[b:b + 1], o["y"]), err(hT[b:b + 1], o["h_T"])
+    print(f"{w.name} sequence {b}, all {w.D} channels err(y)={ey:.3e} err(h_T)={eh:.3e}", flush=True)
+    assert ey <= TOL[w.io] and eh <= TOL[w.io]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("B,T,D", [(2, 2048, 4608), (3, 1700, 2752)])
+def test_forward_where_fused_rounds_fill_poorly(lib, B, T, D):
+    """Shapes whose fused tiles (256 steps x 128 channels) leave the last of their rounds of
+    256 CUs at most 60% full (2 x 8 x 36 = 576 tiles, a quarter-full third round; 3 x 7 x 22 =
+    462 tiles stay fused below 512): the first runs as the gate GEMM with its split-K tail,
+    then the scan.  Every channel of every sequence against the oracle, and bitwise
+    repeatable."""
+    import torch
+    p = make(workloads.TRAIN_BWD, B=B, T=T, D=D, h0="normal", history="normal")
+    _check(lib, p, what=f"rounds {B}x{T}x{D}")
+    d = device_inputs(p)
+    y1, h1, _ = gpu_forward(lib, d, p["c"])
+    y2, h2, _ = gpu_forward(lib, d, p["c"])
+    assert np.array_equal(y1, y2) and np.array_equal(h1, h2)
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])

@@ -86,13 +86,43 @@ def test_conv_entry_point_matches_oracle(lib, io):
     lib.conv1d_causal4(d["x"], d["conv_w"], d["conv_b"], d["conv_state"], u, so)
     torch.cuda.synchronize()
     uo, soo = oracle.conv1d_causal4(p["x"], p["conv_w"], p["conv_b"], p["conv_state"], io)
-    # fp32 evaluation of four fmas: error <= 4 * 2^-24 * sum |terms|, then one rounding to
-    # the I/O dtype (half an ulp of each side)
-    mag, _ = oracle.conv1d_causal4(np.abs(p["x"]), np.abs(p["conv_w"]), np.abs(p["conv_b"]),
-                                   np.abs(p["conv_state"]), "f64")
-    ulp = 2.0 ** -23 if io == "f32" else 2.0 ** -7
-    assert np.all(np.abs(host(u) - uo) <= 4 * 2.0 ** -24 * mag + ulp * np.abs(uo))
+    # the kernel takes the sum in fp64 in the definition's order and rounds it once
+    np.testing.assert_array_equal(host(u), uo)
     np.testing.assert_array_equal(host(so), soo)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_conv_rounds_once_on_constructed_sums(lib, io):
+    """Sums where rounding first to fp32 and then to the I/O dtype would pick the other
+    neighbour, and sums in bf16's subnormal range; the kernel's u must equal the oracle's
+    once-rounded sum bit for bit.  Channels 0..31, step 3: u = s (1 + 2^-p) + s' 2^-40 with
+    p = 8 (bf16) or 24 (fp32), i.e. an exact halfway point of the I/O dtype moved by a tap
+    product far below an fp32 ulp.  Channels 32..63, step 5: u = k 2^-140."""
+    D, p = 64, (8 if io == "bf16" else 24)
+    rng = np.random.default_rng(8)
+    ch = np.arange(D)
+    lo = ch < 32
+    s1 = np.where(ch % 2 == 0, 1.0, -1.0)
+    s2 = np.where(ch % 4 < 2, 1.0, -1.0)
+    w = np.zeros((4, D))
+    x = np.zeros((1, 6, D))
+    w[3] = np.where(lo, s1, 0.0)                 # step 3, tap 3: x_0 = 1
+    w[2] = np.where(lo, s1 * 2.0 ** -p, 0.0)     # tap 2: x_1 = 1
+    w[1] = np.where(lo, s2 * 2.0 ** -20, 0.0)    # tap 1: x_2 = 2^-20
+    x[0, 0] = x[0, 1] = np.where(lo, 1.0, 0.0)
+    x[0, 2] = np.where(lo, 2.0 ** -20, 0.0)
+    w[0] = np.where(lo, 0.0, 2.0 ** -70)         # step 5, tap 0: x_5 = k 2^-70
+    x[0, 5] = np.where(lo, 0.0, rng.integers(1, 256, D) * 2.0 ** -70)
+    d = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(dt)
+    dt = TORCH_IO[io]
+    xd, wd = d(x, dt), d(w, dt)
+    assert np.array_equal(host(xd), x) and np.array_equal(host(wd), w)
+    u = torch.empty_like(xd)
+    lib.conv1d_causal4(xd, wd, None, None, u, None)
+    torch.cuda.synchronize()
+    uo, _ = oracle.conv1d_causal4(x, w, None, None, io)
+    np.testing.assert_array_equal(host(u), uo)
+    assert len(np.unique(uo[0, 3, :32])) == 4         # the tiny taps decide the neighbour
 
 
 def test_forward_is_bitwise_reproducible(lib):

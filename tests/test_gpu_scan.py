@@ -1,9 +1,9 @@
 """The forward scan's look-back computed both ways: from the summaries other workgroups
 publish, and from memory when a predecessor chunk's summary is missing (the path that keeps
 the chained scan (the blog page "Griffin's Compromise", "Term explanation: Parallel scan")
-independent of the order in which the GPU starts workgroups).  The test hook forces the
-second path for every chunk; the results must be bitwise the same as the normal ones (the
-carry is canonical), and both must match the oracle.
+independent of the order in which the GPU starts workgroups).  The test-only entry points
+(rglru_testing.h) force the second path for every chunk; the results must be bitwise the
+same as the normal ones (the carry is canonical), and both must match the oracle.
 """
 import numpy as np
 import pytest
@@ -14,11 +14,10 @@ from gpu_util import TOL, device_inputs, err, host, make, oracle_forward
 
 pytestmark = pytest.mark.gpu
 
-DEFAULT_POLLS = 2048
 
-
-def _split_scan(g, p, d, conv=True):
-    """conv -> rglru_gates -> rglru_scan; returns (y, h_T) on the host."""
+def _split_scan(g, p, d, conv=True, knobs=None):
+    """conv -> rglru_gates -> rglru_scan (rglru_testing_scan with `knobs`); returns (y, h_T)
+    on the host."""
     u = torch.empty_like(d["x"])
     a = torch.empty(d["x"].shape, dtype=torch.float32, device="cuda")
     beta = torch.empty_like(a)
@@ -31,8 +30,13 @@ def _split_scan(g, p, d, conv=True):
     else:
         u = d["x"]
     g.rglru_gates(u, d["W_a"], d["W_x"], d["b_a"], d["b_x"], d["lam"], a, beta, p["c"])
-    g.rglru_scan(d["x"], d["conv_w"] if conv else None, d["conv_b"] if conv else None,
-                 d["conv_state"] if conv else None, a, beta, d["h0"], y, hT, ws)
+    args = (d["x"], d["conv_w"] if conv else None, d["conv_b"] if conv else None,
+            d["conv_state"] if conv else None, a, beta, d["h0"], y, hT, ws)
+    if knobs is None:
+        g.rglru_scan(*args)
+    else:
+        from gated_linear_rnn_amd import testing
+        testing.rglru_scan(knobs, *args)
     torch.cuda.synchronize()
     return host(y), host(hT)
 
@@ -43,14 +47,11 @@ def test_direct_summaries_give_the_same_bits(lib, io, conv):
     # T = 333: six 64-step chunks, the last one partial
     p = make(workloads.TRAIN_FWD, B=2, T=333, D=128, io=io, h0="normal", history="normal")
     d = device_inputs(p)
-    try:
-        y0, h0 = _split_scan(lib, p, d, conv)
-        lib.rglru_test_set_scan_direct_polls(-1)     # every summary computed from memory
-        y1, h1 = _split_scan(lib, p, d, conv)
-        lib.rglru_test_set_scan_direct_polls(0)      # computed whenever not yet published
-        y2, h2 = _split_scan(lib, p, d, conv)
-    finally:
-        lib.rglru_test_set_scan_direct_polls(DEFAULT_POLLS)
+    from gated_linear_rnn_amd import testing
+    y0, h0 = _split_scan(lib, p, d, conv)
+    # every summary computed from memory; computed whenever not yet published
+    y1, h1 = _split_scan(lib, p, d, conv, testing.knobs(scan_direct_polls=-1))
+    y2, h2 = _split_scan(lib, p, d, conv, testing.knobs(scan_direct_polls=0))
     np.testing.assert_array_equal(y0, y1)
     np.testing.assert_array_equal(h0, h1)
     np.testing.assert_array_equal(y0, y2)
@@ -69,13 +70,10 @@ def test_backward_with_direct_summaries_gives_the_same_bits(lib):
     args = (d["x"], d["conv_w"], d["conv_b"], None, d["W_a"], d["W_x"], d["b_a"], d["b_x"],
             d["lam"], None, d["dy"])
     names = ["dx", "dconv_w", "dconv_b", "dW_a", "dW_x", "db_a", "db_x", "dlambda", "dh0"]
-    try:
-        g0 = lib.backward(*args, c=p["c"])
-        lib.rglru_test_set_scan_direct_polls(-1)
-        g1 = lib.backward(*args, c=p["c"])
-        torch.cuda.synchronize()
-    finally:
-        lib.rglru_test_set_scan_direct_polls(DEFAULT_POLLS)
+    from gated_linear_rnn_amd import testing
+    g0 = lib.backward(*args, c=p["c"])
+    g1, _ = testing.backward(testing.knobs(scan_direct_polls=-1), *args, c=p["c"])
+    torch.cuda.synchronize()
     for n in names:
         assert torch.equal(g0[n], g1[n]), n
 
@@ -119,12 +117,9 @@ def test_direct_summaries_over_a_long_chain(lib):
     window (the rest are read again, or computed again, on the way forward)."""
     p = make(workloads.TRAIN_FWD, B=1, T=2500, D=64, h0="normal", history="normal")
     d = device_inputs(p)
-    try:
-        y0, h0 = _split_scan(lib, p, d)
-        lib.rglru_test_set_scan_direct_polls(-1)
-        y1, h1 = _split_scan(lib, p, d)
-    finally:
-        lib.rglru_test_set_scan_direct_polls(DEFAULT_POLLS)
+    from gated_linear_rnn_amd import testing
+    y0, h0 = _split_scan(lib, p, d)
+    y1, h1 = _split_scan(lib, p, d, knobs=testing.knobs(scan_direct_polls=-1))
     np.testing.assert_array_equal(y0, y1)
     np.testing.assert_array_equal(h0, h1)
     o = oracle_forward(p)

@@ -2,9 +2,9 @@
 ticket counter (tiles of one chain must start in time order for the chained scan: the
 blog page "Griffin's Compromise", "Term explanation: Parallel scan") and, while that
 atomic is in flight, loads the first operand block of the tile it would get if tickets went
-in launch order.  The test hook shifts the guess so that (nearly) every workgroup finds it
-wrong, waits for those loads and loads its own tile: the results must be bitwise the same
-as with the normal guess, and match the oracle.
+in launch order.  The test-only entry points (rglru_testing.h) shift the guess so that
+(nearly) every workgroup finds it wrong, waits for those loads and loads its own tile: the
+results must be bitwise the same as with the normal guess, and match the oracle.
 """
 import numpy as np
 import pytest
@@ -16,12 +16,13 @@ from gpu_util import TOL, TORCH_IO, dev, device_inputs, err, gpu_forward, host, 
 pytestmark = pytest.mark.gpu
 
 
-def _with_guess(g, offset, fn):
-    try:
-        g.rglru_test_set_lru_ticket_guess(offset)
-        return fn()
-    finally:
-        g.rglru_test_set_lru_ticket_guess(0)
+def _fwd_with_guess(d, c, offset):
+    from gated_linear_rnn_amd import testing
+    y, hT, _, _ = testing.forward(testing.knobs(lru_ticket_guess=offset), d["x"], d["conv_w"],
+                                  d["conv_b"], d["conv_state"], d["W_a"], d["W_x"], d["b_a"],
+                                  d["b_x"], d["lam"], d["h0"], c)
+    torch.cuda.synchronize()
+    return host(y), host(hT)
 
 
 @pytest.mark.parametrize("offset", [1, 5])
@@ -30,7 +31,7 @@ def test_forward_with_wrong_guesses_gives_the_same_bits(lib, offset):
     p = make(workloads.TRAIN_FWD, B=2, T=600, D=384, h0="normal", history="normal")
     d = device_inputs(p)
     y0, h0, _ = gpu_forward(lib, d, p["c"])
-    y1, h1, _ = _with_guess(lib, offset, lambda: gpu_forward(lib, d, p["c"]))
+    y1, h1 = _fwd_with_guess(d, p["c"], offset)
     np.testing.assert_array_equal(y0, y1)
     np.testing.assert_array_equal(h0, h1)
     o = oracle_forward(p)
@@ -44,7 +45,7 @@ def test_full_size_forward_with_wrong_guesses_gives_the_same_bits(lib):
     p = workloads.make_inputs(workloads.TRAIN_FWD)
     d = device_inputs(p)
     y0, h0, _ = gpu_forward(lib, d, p["c"])
-    y1, h1, _ = _with_guess(lib, 1, lambda: gpu_forward(lib, d, p["c"]))
+    y1, h1 = _fwd_with_guess(d, p["c"], 1)
     assert np.array_equal(y0, y1) and np.array_equal(h0, h1)
 
 
@@ -57,14 +58,46 @@ def test_gated_block_with_wrong_guesses_gives_the_same_bits(lib):
     d = device_inputs(p)
     d.update(x_block=dev(p["x_block"], io), W_in=dev(p["W_in"], io), W_out=dev(p["W_out"], io))
 
-    def run():
-        out, hT, _ = lib.block_forward(d["x_block"], d["W_in"], d["conv_w"], d["conv_b"],
-                                       d["conv_state"], d["W_a"], d["W_x"], d["b_a"], d["b_x"],
-                                       d["lam"], d["h0"], d["W_out"], p["c"])
-        torch.cuda.synchronize()
-        return host(out), host(hT)
-
-    o0, h0 = run()
-    o1, h1 = _with_guess(lib, 3, run)
+    from gated_linear_rnn_amd import testing
+    args = (d["x_block"], d["W_in"], d["conv_w"], d["conv_b"], d["conv_state"], d["W_a"], d["W_x"],
+            d["b_a"], d["b_x"], d["lam"], d["h0"], d["W_out"], p["c"])
+    out, hT, _ = lib.block_forward(*args)
+    torch.cuda.synchronize()
+    o0, h0 = host(out), host(hT)
+    out, hT, _ = testing.block_forward(testing.knobs(lru_ticket_guess=3), *args)
+    torch.cuda.synchronize()
+    o1, h1 = host(out), host(hT)
     np.testing.assert_array_equal(o0, o1)
     np.testing.assert_array_equal(h0, h1)
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_a_lookback_that_gives_up_is_reported(lib, io):
+    """A look-back told to give up at once (lookback_polls < 0: the fused kernel's, and the
+    reverse scan's in the backward) writes NaN where the carry was needed, every kernel still
+    ends, and rglru_workspace_status reports RGLRU_ESTALL; the next ordinary call on the same
+    workspace is clean again.  (fp32 I/O runs the forward scan, which never gives up: it
+    computes a missing summary itself, so only its backward can stall.)"""
+    from gated_linear_rnn_amd import testing
+    p = make(workloads.TRAIN_BWD, B=2, T=600, D=128, io=io, h0="normal", history="normal")
+    d = device_inputs(p)
+    fargs = (d["x"], d["conv_w"], d["conv_b"], d["conv_state"], d["W_a"], d["W_x"], d["b_a"],
+             d["b_x"], d["lam"], d["h0"])
+    stop = testing.knobs(lookback_polls=-1)
+    y, hT, _, ws = testing.forward(stop, *fargs, c=p["c"])
+    st = lib.rglru_workspace_status(ws)
+    if io == "bf16":
+        assert st == lib.RGLRU_ESTALL
+        yh = host(y)
+        assert np.isnan(yh[:, 256:]).all() and np.isfinite(yh[:, :256]).all()
+    else:
+        assert st == 0
+    y2, _, _ = lib.forward(*fargs, c=p["c"], ws=ws)
+    assert lib.rglru_workspace_status(ws) == 0
+    o = oracle_forward(p)
+    assert err(host(y2), o["y"]) <= TOL[io]
+    g, wsb = testing.backward(stop, *fargs, d["dy"], c=p["c"])
+    assert lib.rglru_workspace_status(wsb) == lib.RGLRU_ESTALL
+    assert np.isnan(host(g["dx"])).any()
+    lib.backward(*fargs, d["dy"], c=p["c"], ws=wsb)
+    assert lib.rglru_workspace_status(wsb) == 0

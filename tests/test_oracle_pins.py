@@ -369,20 +369,19 @@ def test_round_exact_helper_on_hand_cases():
 
 def test_conv_rounds_once_not_twice():
     """Constructed sums where rounding first to fp32 and then to the I/O dtype picks the
-    other neighbour: the bias 1 + 2^-8 is an exact bf16 halfway point and a tiny tap moves
-    the exact sum just above (or below) it, by far less than an fp32 ulp; for fp32 I/O the
-    bias 1 + 2^-24 plays the same part.  R1 rounds the exact sum once."""
+    other neighbour: taps give 1 + 2^-p (p = 8 for bf16, 24 for fp32: an exact halfway point
+    of the I/O dtype) and a tap product of +-2^-40 moves the sum just above or below it, by
+    far less than an fp32 ulp.  R1 rounds the exact sum once."""
     from fractions import Fraction
-    tiny = 2.0 ** -20 * 2.0 ** -20                      # w = x = 2^-20 (bf16 and fp32 values)
-    for io, half, bits in (("bf16", 1 + 2.0 ** -8, 8), ("f32", 1 + 2.0 ** -24, 24)):
-        cb = np.array([half, half, -half, half], dtype=np.float64)
-        w = np.zeros((4, 4)); w[2] = [2.0 ** -20, -(2.0 ** -20), 2.0 ** -20, 0.0]
-        x = np.zeros((1, 3, 4)); x[0, 0] = 2.0 ** -20    # tap 2 sees x_0 at t = 2
-        u, _ = oracle.conv1d_causal4(x, w, cb, None, io)
-        got = u[0, 2]
-        want = [_round_exact(Fraction(half) + Fraction(tiny), bits),
-                _round_exact(Fraction(half) - Fraction(tiny), bits),
-                _round_exact(-Fraction(half) + Fraction(tiny), bits),
-                _round_exact(Fraction(half), bits)]
-        np.testing.assert_array_equal(got, want)
-        assert got[0] != got[3] and got[0] > got[1]     # the tiny tap decides the neighbour
+    for io, p in (("bf16", 8), ("f32", 24)):
+        D = 4
+        s1 = np.array([1.0, 1.0, -1.0, -1.0])
+        s2 = np.array([1.0, -1.0, 1.0, -1.0])
+        w = np.zeros((4, D)); w[3] = s1; w[2] = s1 * 2.0 ** -p; w[1] = s2 * 2.0 ** -20
+        x = np.zeros((1, 4, D)); x[0, 0] = x[0, 1] = 1.0; x[0, 2] = 2.0 ** -20
+        assert np.array_equal(oracle.round_io(w, io), w)
+        u, _ = oracle.conv1d_causal4(x, w, None, None, io)
+        want = [_round_exact(Fraction(int(a)) * (1 + Fraction(1, 2 ** p)) + Fraction(int(b), 2 ** 40),
+                             8 if io == "bf16" else 24) for a, b in zip(s1, s2)]
+        np.testing.assert_array_equal(u[0, 3], want)
+        assert len(set(want)) == 4                      # the tiny tap decides the neighbour
