@@ -499,6 +499,8 @@ size_t rglru_decode_workspace_bytes(int B, int D, rglru_dtype io) {
   if (io == RGLRU_F32) {
     cv.take<float>(size_t(B) * D);
     cv.take<float>(size_t(B) * D);
+  } else {
+    cv.take<unsigned char>(decode_partial_bytes(B, D));
   }
   return cv.used;
 }
@@ -522,6 +524,9 @@ int rglru_decode_step(int B, int D, rglru_dtype io, float c, const void* x_t, co
   void* ubuf = cv.take<unsigned char>(size_t(B) * D * io_bytes(io));
   float* za = io == RGLRU_F32 ? cv.take<float>(size_t(B) * D) : nullptr;
   float* zx = io == RGLRU_F32 ? cv.take<float>(size_t(B) * D) : nullptr;
+  float* partial = io == RGLRU_BF16
+                       ? reinterpret_cast<float*>(cv.take<unsigned char>(decode_partial_bytes(B, D)))
+                       : nullptr;
   const void* u = x_t;
   if (conv_w) {
     if (io == RGLRU_BF16) RG_CHECK(launch_conv_decode<bf16_t>(B, D, x_t, conv_w, conv_b, conv_state, ubuf, stream));
@@ -531,7 +536,7 @@ int rglru_decode_step(int B, int D, rglru_dtype io, float c, const void* x_t, co
   if (io == RGLRU_BF16) {
     DecodeArgs d{};
     d.u = u; d.Wa = W_a; d.Wx = W_x; d.ba = b_a; d.bx = b_x; d.lam = lambda; d.c = c;
-    d.h = h; d.y = y_t; d.B = B; d.D = D;
+    d.h = h; d.y = y_t; d.partial = partial; d.B = B; d.D = D;
     RG_CHECK(launch_decode_bf16(d, stream));
     return RGLRU_OK;
   }
@@ -965,6 +970,7 @@ size_t rglru_block_decode_workspace_bytes(int B, int D, int R, rglru_dtype io) {
   if (io == RGLRU_BF16) {
     const size_t a = splitk_partial_bytes(B, 2 * R, D), b = splitk_partial_bytes(B, D, R);
     cv.take<unsigned char>(a > b ? a : b);          // split-K partials of both linears
+    cv.take<unsigned char>(decode_partial_bytes(B, R));
   } else {
     cv.take<float>(2 * n);                          // the input linears' product
   }
@@ -992,10 +998,12 @@ int rglru_block_decode_step(int B, int D, int R, rglru_dtype io, float c, const 
   const size_t n = size_t(B) * R;
   const bool bf = io == RGLRU_BF16;
   float* part = nullptr;
+  float* dpart = nullptr;
   float* pq = nullptr;
   if (bf) {
     const size_t a = splitk_partial_bytes(B, 2 * R, D), b = splitk_partial_bytes(B, D, R);
     part = reinterpret_cast<float*>(cv.take<unsigned char>(a > b ? a : b));
+    dpart = reinterpret_cast<float*>(cv.take<unsigned char>(decode_partial_bytes(B, R)));
   } else {
     pq = cv.take<float>(2 * n);
   }
@@ -1026,7 +1034,7 @@ int rglru_block_decode_step(int B, int D, int R, rglru_dtype io, float c, const 
   if (bf) {
     DecodeArgs d{};
     d.u = uin; d.Wa = W_a; d.Wx = W_x; d.ba = b_a; d.bx = b_x; d.lam = lambda; d.c = c;
-    d.h = h; d.y = z; d.B = B; d.D = R; d.gate = g;
+    d.h = h; d.y = z; d.partial = dpart; d.B = B; d.D = R; d.gate = g;
     RG_CHECK(launch_decode_bf16(d, stream));
   } else {
     GateGemmArgs ga{};

@@ -68,8 +68,8 @@ struct GateGemmArgs {
 };
 size_t gate_gemm_tail_bytes(int M, int N, int K);
 
-// One bf16 decode step after the conv: the gate projection, the gates and the state update
-// in one kernel (decode.hip); no workspace.
+// One bf16 decode step after the conv: split-K gate projection into `partial`, then the
+// fixed-order sum, the gates and the state update (decode.hip).
 struct DecodeArgs {
   const void* u;      // [B, D] bf16, the conv output of the step
   const void* Wa;     // [D, D] bf16
@@ -80,9 +80,14 @@ struct DecodeArgs {
   float c;
   float* h;           // [B, D] state, in/out
   void* y;            // [B, D] bf16
+  float* partial;     // decode_partial_bytes(B, D): the split sums, then 3 D gate constants
   int B, D;
+  int splits;         // set by the launcher
+  float* chan;        // set by the launcher: [3, D] per-channel gate constants
   const void* gate;   // [B, D] bf16 or NULL: y = RNE(h * gate) instead of RNE(h)
 };
+int decode_splits(int B, int D);
+size_t decode_partial_bytes(int B, int D);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 
 // C[M,N] = A[M,K] B[N,K]^T (+ addend), fp32 output.  With A2 (bf16 only) the product
