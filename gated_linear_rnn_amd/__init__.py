@@ -15,5 +15,6 @@ from ._binding import (EXPORTS, LIB_PATH, RGLRU_BF16, RGLRU_F32, RgluError,  # n
                        mqa_fwd_workspace_bytes, rglru_block_fwd, rglru_bwd,
                        rglru_block_decode_step, block_decode_workspace_bytes,
                        rglru_decode_step, rglru_fwd, rglru_gates, rglru_lru, rglru_scan,
-                       rglru_workspace_status, RGLRU_ESTALL,
+                       rglru_workspace_status, RGLRU_ESTALL, rglru_decode_step_noalloc,
+                       NOALLOC_SCRATCH_BYTES,
                        lru_workspace_bytes, scan_workspace_bytes, status_string, workspace)

@@ -27,7 +27,7 @@ EXPORTS = ("rglru_status_string", "conv1d_causal4", "rglru_fwd_workspace_bytes",
            "gated_mlp_fwd_workspace_bytes", "gated_mlp_fwd", "local_mqa_fwd_workspace_bytes",
            "local_mqa_fwd", "local_mqa_decode_workspace_bytes", "local_mqa_decode_step",
            "rglru_block_decode_workspace_bytes", "rglru_block_decode_step",
-           "rglru_workspace_status")
+           "rglru_workspace_status", "rglru_decode_step_noalloc")
 
 _lib = None
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -69,6 +69,8 @@ def load(path: str = LIB_PATH):
     lib.rglru_decode_workspace_bytes.restype = _Z
     lib.rglru_decode_step.argtypes = [_I, _I, _I, _F] + [_P] * 11 + [_P, _Z, _P]
     lib.rglru_decode_step.restype = _I
+    lib.rglru_decode_step_noalloc.argtypes = [_I, _I, _I, _F] + [_P] * 11 + [_P]
+    lib.rglru_decode_step_noalloc.restype = _I
     lib.rglru_bwd_workspace_bytes.argtypes = [_I, _I, _I, _I]
     lib.rglru_bwd_workspace_bytes.restype = _Z
     lib.rglru_bwd.argtypes = [_I, _I, _I, _I, _F] + [_P] * 21 + [_P, _Z, _P]
@@ -226,6 +228,20 @@ def rglru_decode_step(x_t, conv_w, conv_b, conv_state, W_a, W_x, b_a, b_x, lam, 
                                     _ptr(b_a), _ptr(b_x), _ptr(lam), _ptr(h), _ptr(y_t),
                                     _ptr(ws), ws.numel(), _stream(stream)),
            "rglru_decode_step")
+
+
+def rglru_decode_step_noalloc(x_t, conv_w, conv_b, conv_state, W_a, W_x, b_a, b_x, lam, h, y_t,
+                              c=8.0, stream=None):
+    """rglru_decode_step without a workspace (the library's fixed per-GPU scratch)."""
+    B, D = x_t.shape
+    _check(load().rglru_decode_step_noalloc(B, D, io_code(x_t.dtype), float(c), _ptr(x_t),
+                                            _ptr(conv_w), _ptr(conv_b), _ptr(conv_state),
+                                            _ptr(W_a), _ptr(W_x), _ptr(b_a), _ptr(b_x), _ptr(lam),
+                                            _ptr(h), _ptr(y_t), _stream(stream)),
+           "rglru_decode_step_noalloc")
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 def rglru_bwd(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, dy, dh_T, dx,

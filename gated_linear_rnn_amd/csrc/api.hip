@@ -5,6 +5,8 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <stdint.h>
 
 #include "../../include/rglru.h"
@@ -330,6 +332,34 @@ MqaWs carve_mqa(Carver& cv, int B, int T, int D, rglru_dtype io) {
   return w;
 }
 
+// ------------------------------------------------------------------ allocation-free decode
+// The fixed scratch of rglru_decode_step_noalloc: one array per GPU, held by that GPU until
+// the process ends.  Host code never passes `scratch` itself to a kernel (on the host it is
+// only a stand-in for the symbol): it uses the device address hipGetSymbolAddress returns,
+// looked up once per device with that device current and kept in scratch_dev.
+static __device__ __align__(256) unsigned char scratch[RGLRU_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_dev[kMaxDevices];
+std::mutex scratch_mu;
+
+// The current device's scratch address (nullptr if the lookup fails).
+void* scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = scratch_dev[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  p = scratch_dev[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+    scratch_dev[dev].store(q, std::memory_order_release);
+    p = q;
+  }
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -344,6 +374,7 @@ const char* rglru_status_string(int status) {
     case RGLRU_EHIP: return "RGLRU_EHIP: HIP launch or runtime error";
     case RGLRU_EINTERNAL: return "RGLRU_EINTERNAL: internal error";
     case RGLRU_ESTALL: return "RGLRU_ESTALL: a chained-scan wait for a predecessor chunk gave up (outputs hold NaN)";
+    case RGLRU_ESCRATCH: return "RGLRU_ESCRATCH: the shape needs more than the allocation-free entry point's fixed scratch";
     default: return "unknown rglru status";
   }
 }
@@ -545,6 +576,22 @@ int rglru_decode_step(int B, int D, rglru_dtype io, float c, const void* x_t, co
   g.ba = b_a; g.bx = b_x; g.lam = lambda; g.c = c;
   g.u = u; g.h = h; g.y = y_t;
   return gate_projection(io, g, kEpiDecode, za, zx, stream);
+}
+
+int rglru_decode_step_noalloc(int B, int D, rglru_dtype io, float c, const void* x_t,
+                              const void* conv_w, const float* conv_b, void* conv_state,
+                              const void* W_a, const void* W_x, const float* b_a,
+                              const float* b_x, const float* lambda, float* h, void* y_t,
+                              hipStream_t stream) {
+  int st = shape_status(B, 1, D);
+  if (st != RGLRU_OK) return st;
+  if (!io_ok(io)) return RGLRU_EDTYPE;
+  const size_t need = rglru_decode_workspace_bytes(B, D, io);
+  if (need > RGLRU_NOALLOC_SCRATCH_BYTES) return RGLRU_ESCRATCH;
+  void* ws = scratch_of_current_device();
+  if (!ws) return RGLRU_EHIP;
+  return rglru_decode_step(B, D, io, c, x_t, conv_w, conv_b, conv_state, W_a, W_x, b_a, b_x,
+                           lambda, h, y_t, ws, RGLRU_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t rglru_bwd_workspace_bytes(int B, int T, int D, rglru_dtype io) {

@@ -53,7 +53,8 @@ typedef enum {
   RGLRU_EWORKSPACE = -4, /* ws null or smaller than the query returns */
   RGLRU_EHIP = -5,       /* a kernel launch or HIP runtime call failed */
   RGLRU_EINTERNAL = -6,
-  RGLRU_ESTALL = -7      /* rglru_workspace_status: a chained-scan wait gave up */
+  RGLRU_ESTALL = -7,     /* rglru_workspace_status: a chained-scan wait gave up */
+  RGLRU_ESCRATCH = -8    /* allocation-free call: the shape needs more than the fixed scratch */
 } rglru_status;
 
 typedef enum { RGLRU_F32 = 0, RGLRU_BF16 = 1 } rglru_dtype;
@@ -166,6 +167,24 @@ int rglru_decode_step(int B, int D, rglru_dtype io, float c, const void* x_t,
                       const void* W_a, const void* W_x, const float* b_a,
                       const float* b_x, const float* lambda, float* h, void* y_t,
                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * rglru_decode_step for callers that cannot allocate device memory or pass a workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  The same
+ * step and the same results; the scratch the step needs (rglru_decode_workspace_bytes(B, D,
+ * io) bytes: the step's conv output, plus the fp32 gate pre-activations for fp32 I/O) lives in
+ * a fixed device array of RGLRU_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it
+ * runs on until the process ends.  A shape that needs more returns RGLRU_ESCRATCH and
+ * launches nothing.  Nothing in the scratch carries over between calls, but every call on
+ * one GPU uses the same array: calls that overlap in time on one GPU (two streams, two
+ * threads) race and must be serialised by the caller.
+ */
+#define RGLRU_NOALLOC_SCRATCH_BYTES (32u << 20)
+int rglru_decode_step_noalloc(int B, int D, rglru_dtype io, float c, const void* x_t,
+                              const void* conv_w, const float* conv_b, void* conv_state,
+                              const void* W_a, const void* W_x, const float* b_a,
+                              const float* b_x, const float* lambda, float* h, void* y_t,
+                              hipStream_t stream);
 
 /* Workspace bytes rglru_bwd needs for this shape (0 for invalid arguments). */
 size_t rglru_bwd_workspace_bytes(int B, int T, int D, rglru_dtype io);

@@ -259,3 +259,15 @@ def test_workspace_status_rejects_invalid_arguments(lib):
     assert lib.rglru_workspace_status(None, 1 << 20, None) == -1
     assert lib.rglru_workspace_status(BAD, 1 << 20, None) == -1
     assert lib.rglru_workspace_status(A, 255, None) == -4
+
+
+@no_gpu
+def test_noalloc_decode_rejects_before_any_hip_call(lib):
+    """rglru_decode_step_noalloc validates the shape and its fixed scratch size first."""
+    f = lib.rglru_decode_step_noalloc
+    args = lambda B, D, io=1: (B, D, io, 8.0, A, None, None, None, A, A, A, A, A, A, A, None)
+    assert f(*args(0, 64)) == -1
+    assert f(*args(2, 96)) == -2
+    assert f(*args(2, 64, io=5)) == -3
+    assert g.status_string(-8).startswith("RGLRU_ESCRATCH")
+    assert f(*args(1024, 8192)) == -8                      # needs more than the fixed scratch
