@@ -198,6 +198,9 @@ def main():
     conv_l = [e[0].elapsed_time(e[1]) for e in kev]
     lru_l = [e[1].elapsed_time(e[2]) for e in kev]
     conv_ms, lru_ms = float(np.median(conv_l)), float(np.median(lru_l))
+    # the roofline's launch duration: the mean interval of rglru_lru in this pass, where it
+    # alternates with the conv as in the step (launched back to back, the kernel runs ~7%
+    # slower: the clock drops under uninterrupted matrix-core load)
     lru_avg = float(np.mean(lru_l))
 
     gemm_flop = 2.0 * M * (2 * D) * D
@@ -228,8 +231,10 @@ def main():
             "kernel": "lru_fused_kernel (gate GEMM + gates + chunked scan)",
             "bound": "mfma", "achieved": lru_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": lru_tflops / PEAK_BF16_TFLOPS, "traffic": _lru_traffic(),
-            "flop_per_launch": gemm_flop, "avg_launch_ms": lru_avg, "median_launch_ms": lru_ms,
-            "note": "launch interval of rglru_lru, which also holds its look-back status fill",
+            "flop_per_launch": gemm_flop, "avg_launch_ms": lru_avg,
+            "median_launch_ms": lru_ms, "launches_timed": args.steps,
+            "note": "mean event interval of rglru_lru calls alternating with conv1d_causal4; "
+                    "each call also launches the look-back status fill (about 4.5 us) first",
         },
         "hbm": {
             "block_achieved_GBps": block_gbps,
