@@ -482,8 +482,39 @@ def bench_fwd_bwd(g, torch, np, workloads):
         fwd.append(e0.elapsed_time(e_mid))
         bwd.append(e_mid.elapsed_time(e1))
     f, b = float(np.median(fwd)), float(np.median(bwd))
+    del wsf, wsb
+    # the training pair that keeps the forward's activations: rglru_fwd_train writes u, r, i
+    # and every h_t, and rglru_bwd_saved starts from them instead of evaluating the forward
+    wst = g.workspace(g.fwd_train_workspace_bytes(B, T, D, bf))
+    wss = g.workspace(g.bwd_saved_workspace_bytes(B, T, D, bf))
+    saved = g.workspace(g.train_saved_bytes(B, T, D, bf))
+
+    def once_saved():
+        g.forward_train(x, cw, cb, None, Wa, Wx, ba, bx, lam, None, p["c"], ws=wst, saved=saved)
+        e_mid.record()
+        g.backward(x, cw, cb, None, Wa, Wx, None, None, lam, None, dy, None, p["c"], ws=wss,
+                   saved=saved)
+
+    for _ in range(5):
+        once_saved()
+    torch.cuda.synchronize()
+    fwd_s, bwd_s = [], []
+    for _ in range(20):
+        e0.record()
+        once_saved()
+        e1.record()
+        torch.cuda.synchronize()
+        fwd_s.append(e0.elapsed_time(e_mid))
+        bwd_s.append(e_mid.elapsed_time(e1))
+    fs, bs = float(np.median(fwd_s)), float(np.median(bwd_s))
     return {"workload": w.name, "fwd_ms": f, "bwd_ms": b, "runs": len(fwd), "statistic": "median",
-            "tokens_per_s_fwd_bwd": B * T / ((f + b) * 1e-3)}
+            "tokens_per_s_fwd_bwd": B * T / ((f + b) * 1e-3),
+            "saved_activations": {
+                "fwd_train_ms": fs, "bwd_saved_ms": bs,
+                "tokens_per_s_fwd_bwd": B * T / ((fs + bs) * 1e-3),
+                "saved_bytes": g.train_saved_bytes(B, T, D, bf),
+                "note": "rglru_fwd_train keeps u, r, i and every h_t; rglru_bwd_saved reads them "
+                        "instead of evaluating the forward again (same gradients, bit for bit)"}}
 
 
 def bench_block(g, torch, np, workloads, steps=50):

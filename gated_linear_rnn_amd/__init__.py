@@ -16,5 +16,7 @@ from ._binding import (EXPORTS, LIB_PATH, RGLRU_BF16, RGLRU_F32, RgluError,  # n
                        rglru_block_decode_step, block_decode_workspace_bytes,
                        rglru_decode_step, rglru_fwd, rglru_gates, rglru_lru, rglru_scan,
                        rglru_workspace_status, RGLRU_ESTALL, rglru_decode_step_noalloc,
-                       NOALLOC_SCRATCH_BYTES,
+                       NOALLOC_SCRATCH_BYTES, rglru_fwd_train, rglru_bwd_saved,
+                       forward_train, train_saved_bytes, fwd_train_workspace_bytes,
+                       bwd_saved_workspace_bytes,
                        lru_workspace_bytes, scan_workspace_bytes, status_string, workspace)

@@ -27,7 +27,9 @@ EXPORTS = ("rglru_status_string", "conv1d_causal4", "rglru_fwd_workspace_bytes",
            "gated_mlp_fwd_workspace_bytes", "gated_mlp_fwd", "local_mqa_fwd_workspace_bytes",
            "local_mqa_fwd", "local_mqa_decode_workspace_bytes", "local_mqa_decode_step",
            "rglru_block_decode_workspace_bytes", "rglru_block_decode_step",
-           "rglru_workspace_status", "rglru_decode_step_noalloc")
+           "rglru_workspace_status", "rglru_decode_step_noalloc", "rglru_train_saved_bytes",
+           "rglru_fwd_train_workspace_bytes", "rglru_fwd_train", "rglru_bwd_saved_workspace_bytes",
+           "rglru_bwd_saved")
 
 _lib = None
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -75,6 +77,14 @@ def load(path: str = LIB_PATH):
     lib.rglru_bwd_workspace_bytes.restype = _Z
     lib.rglru_bwd.argtypes = [_I, _I, _I, _I, _F] + [_P] * 21 + [_P, _Z, _P]
     lib.rglru_bwd.restype = _I
+    for q in ("rglru_train_saved_bytes", "rglru_fwd_train_workspace_bytes",
+              "rglru_bwd_saved_workspace_bytes"):
+        getattr(lib, q).argtypes = [_I, _I, _I, _I]
+        getattr(lib, q).restype = _Z
+    lib.rglru_fwd_train.argtypes = [_I, _I, _I, _I, _F] + [_P] * 13 + [_P, _Z, _P, _Z, _P]
+    lib.rglru_fwd_train.restype = _I
+    lib.rglru_bwd_saved.argtypes = [_I, _I, _I, _I, _F] + [_P] * 19 + [_P, _Z, _P, _Z, _P]
+    lib.rglru_bwd_saved.restype = _I
     lib.rglru_block_fwd_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
     lib.rglru_block_fwd_workspace_bytes.restype = _Z
     lib.rglru_block_fwd.argtypes = [_I, _I, _I, _I, _I, _F] + [_P] * 15 + [_P, _Z, _P]
@@ -143,6 +153,18 @@ def decode_workspace_bytes(B, D, dtype) -> int:
 
 def bwd_workspace_bytes(B, T, D, dtype) -> int:
     return int(load().rglru_bwd_workspace_bytes(B, T, D, io_code(dtype)))
+
+
+def train_saved_bytes(B, T, D, dtype) -> int:
+    return int(load().rglru_train_saved_bytes(B, T, D, io_code(dtype)))
+
+
+def fwd_train_workspace_bytes(B, T, D, dtype) -> int:
+    return int(load().rglru_fwd_train_workspace_bytes(B, T, D, io_code(dtype)))
+
+
+def bwd_saved_workspace_bytes(B, T, D, dtype) -> int:
+    return int(load().rglru_bwd_saved_workspace_bytes(B, T, D, io_code(dtype)))
 
 
 def block_fwd_workspace_bytes(B, T, D, R, dtype) -> int:
@@ -256,6 +278,29 @@ def rglru_bwd(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, dy,
            "rglru_bwd")
 
 
+def rglru_fwd_train(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, y, h_T,
+                    conv_state_out, saved, ws, c=8.0, stream=None):
+    B, T, D = x.shape
+    _check(load().rglru_fwd_train(B, T, D, io_code(x.dtype), float(c), _ptr(x), _ptr(conv_w),
+                                  _ptr(conv_b), _ptr(conv_state_in), _ptr(W_a), _ptr(W_x),
+                                  _ptr(b_a), _ptr(b_x), _ptr(lam), _ptr(h0), _ptr(y), _ptr(h_T),
+                                  _ptr(conv_state_out), _ptr(saved), saved.numel(), _ptr(ws),
+                                  ws.numel(), _stream(stream)),
+           "rglru_fwd_train")
+
+
+def rglru_bwd_saved(x, conv_w, conv_b, conv_state_in, W_a, W_x, lam, h0, dy, dh_T, dx, dconv_w,
+                    dconv_b, dW_a, dW_x, db_a, db_x, dlam, dh0, saved, ws, c=8.0, stream=None):
+    B, T, D = x.shape
+    _check(load().rglru_bwd_saved(B, T, D, io_code(x.dtype), float(c), _ptr(x), _ptr(conv_w),
+                                  _ptr(conv_b), _ptr(conv_state_in), _ptr(W_a), _ptr(W_x),
+                                  _ptr(lam), _ptr(h0), _ptr(dy), _ptr(dh_T), _ptr(dx),
+                                  _ptr(dconv_w), _ptr(dconv_b), _ptr(dW_a), _ptr(dW_x),
+                                  _ptr(db_a), _ptr(db_x), _ptr(dlam), _ptr(dh0), _ptr(saved),
+                                  saved.numel(), _ptr(ws), ws.numel(), _stream(stream)),
+           "rglru_bwd_saved")
+
+
 def rglru_block_fwd(x, W_in, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, W_out,
                     out, h_T, conv_state_out, ws, c=8.0, stream=None):
     B, T, D = x.shape
@@ -321,9 +366,27 @@ def forward(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0=None, 
     return y, h_T, cs_out
 
 
+def forward_train(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0=None, c=8.0,
+                  ws=None, saved=None, stream=None):
+    """Allocate y, h_T, conv_state_out and the saved activations (and the workspace unless
+    given), run rglru_fwd_train; returns (y, h_T, conv_state_out, saved)."""
+    B, T, D = x.shape
+    y = torch.empty_like(x)
+    h_T = torch.empty((B, D), dtype=torch.float32, device=x.device)
+    cs_out = torch.empty((B, 3, D), dtype=x.dtype, device=x.device) if conv_w is not None else None
+    if ws is None:
+        ws = workspace(fwd_train_workspace_bytes(B, T, D, x.dtype), x.device)
+    if saved is None:
+        saved = workspace(train_saved_bytes(B, T, D, x.dtype), x.device)
+    rglru_fwd_train(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, y, h_T, cs_out,
+                    saved, ws, c, stream)
+    return y, h_T, cs_out, saved
+
+
 def backward(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, dy, dh_T=None,
-             c=8.0, ws=None, stream=None):
-    """Allocate every gradient (fp32) and run rglru_bwd; returns a dict."""
+             c=8.0, ws=None, stream=None, saved=None):
+    """Allocate every gradient (fp32) and run rglru_bwd, or rglru_bwd_saved when `saved`
+    (from forward_train) is given; returns a dict."""
     B, T, D = x.shape
     dev = x.device
     f32 = dict(dtype=torch.float32, device=dev)
@@ -333,6 +396,13 @@ def backward(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, dy, 
          "dW_a": torch.empty((D, D), **f32), "dW_x": torch.empty((D, D), **f32),
          "db_a": torch.empty((D,), **f32), "db_x": torch.empty((D,), **f32),
          "dlambda": torch.empty((D,), **f32), "dh0": torch.empty((B, D), **f32)}
+    if saved is not None:
+        if ws is None:
+            ws = workspace(bwd_saved_workspace_bytes(B, T, D, x.dtype), dev)
+        rglru_bwd_saved(x, conv_w, conv_b, conv_state_in, W_a, W_x, lam, h0, dy, dh_T, g["dx"],
+                        g["dconv_w"], g["dconv_b"], g["dW_a"], g["dW_x"], g["db_a"], g["db_x"],
+                        g["dlambda"], g["dh0"], saved, ws, c, stream)
+        return g
     if ws is None:
         ws = workspace(bwd_workspace_bytes(B, T, D, x.dtype), dev)
     rglru_bwd(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, dy, dh_T, g["dx"],

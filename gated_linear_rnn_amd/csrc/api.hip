@@ -192,11 +192,27 @@ ScanWs carve_scan(Carver& cv, int B, int T, int D, rglru_dtype io) {
 }
 
 // ------------------------------------------------------------------ backward
-struct BwdWs {
+// What the backward reads of the forward (the chain rule needs u_t, r_t, i_t and h_{t-1}):
+// u, the conv output (io), the gates r and i (fp32) and every state h_t (the scan state type).
+struct SavedAct {
   void* u;
   float* r;
   float* i;
-  void* h_all;   // scan state type
+  void* h_all;
+};
+
+SavedAct carve_saved(Carver& cv, int B, int T, int D, rglru_dtype io) {
+  const size_t n = size_t(B) * T * D;
+  SavedAct a;
+  a.u = cv.take<unsigned char>(n * io_bytes(io));
+  a.r = cv.take<float>(n);
+  a.i = cv.take<float>(n);
+  a.h_all = cv.take<unsigned char>(n * acc_bytes(io));
+  return a;
+}
+
+struct BwdWs {
+  SavedAct act;  // recomputed here unless the caller passes the training forward's
   void* dz_hi;   // [M, 2D] (bf16) or fp32 dz
   void* dz_lo;   // [M, 2D] bf16 (bf16 io only)
   void* dzT_hi;  // [2D, Mp]
@@ -211,16 +227,15 @@ struct BwdWs {
   float* tail;   // bf16: split-tail partials of the recompute, input- and weight-gradient products
 };
 
-BwdWs carve_bwd(Carver& cv, int B, int T, int D, rglru_dtype io) {
+// `recompute`: the backward evaluates the forward itself (rglru_bwd) and holds its
+// activations here; without it they come from the caller (rglru_bwd_saved).
+BwdWs carve_bwd(Carver& cv, int B, int T, int D, rglru_dtype io, bool recompute = true) {
   const size_t M = size_t(B) * T, n = M * D, Mp = (M + 63) / 64 * 64;
   const size_t eb = io_bytes(io);
   const size_t P = size_t(B) * scan_chunks(T);
   BwdWs w;
   w.counter = carve_counters(cv);
-  w.u = cv.take<unsigned char>(n * eb);
-  w.r = cv.take<float>(n);
-  w.i = cv.take<float>(n);
-  w.h_all = cv.take<unsigned char>(n * acc_bytes(io));
+  w.act = recompute ? carve_saved(cv, B, T, D, io) : SavedAct{nullptr, nullptr, nullptr, nullptr};
   w.dz_hi = cv.take<unsigned char>(2 * n * eb);
   w.dz_lo = io == RGLRU_BF16 ? cv.take<unsigned char>(2 * n * eb) : nullptr;
   w.dzT_hi = cv.take<unsigned char>(2 * size_t(D) * Mp * eb);
@@ -235,10 +250,75 @@ BwdWs carve_bwd(Carver& cv, int B, int T, int D, rglru_dtype io) {
   if (io == RGLRU_BF16) {
     const size_t tb = std::max({plain_gemm_tail_bytes(int(M), D, 2 * D),
                                 plain_gemm_tail_bytes(2 * D, D, int(Mp)),
-                                gate_gemm_tail_bytes(int(M), D, D)});
+                                recompute ? gate_gemm_tail_bytes(int(M), D, D) : size_t(0)});
     if (tb) w.tail = cv.take<float>(tb / sizeof(float));
   }
   return w;
+}
+
+// Scratch of the training forward: the counters, the forward scan's look-back status and the
+// gate projection's split-tail partials (bf16).
+struct TrainWs {
+  uint32_t* counter;
+  void* status;
+  float* tail;
+};
+
+TrainWs carve_train(Carver& cv, int B, int T, int D, rglru_dtype io) {
+  TrainWs w;
+  w.counter = carve_counters(cv);
+  w.status = cv.take<unsigned char>(scan_status_bytes(B, T, D, acc_bytes(io)));
+  w.tail = nullptr;
+  if (io == RGLRU_BF16) {
+    const size_t tb = gate_gemm_tail_bytes(B * T, D, D);
+    if (tb) w.tail = cv.take<float>(tb / sizeof(float));
+  }
+  return w;
+}
+
+// The forward as the backward evaluates it, keeping its activations in `a`: u = conv(x) (x
+// itself without the conv; the conv launch also initialises the scan's look-back status),
+// r and i from the gate projection (kEpiRI epilogue), then the forward scan from (r, i)
+// writing every h_t and, where given, y, h_T and the conv state.  *u_out = u.
+static int forward_acts(rglru_dtype io, int B, int T, int D, float c, const void* x,
+                        const void* conv_w, const float* conv_b, const void* cs, const void* W_a,
+                        const void* W_x, const float* b_a, const float* b_x, const float* lambda,
+                        const float* h0, const SavedAct& a, float* tail, void* status,
+                        uint32_t* counter, void* y, float* h_T, void* conv_state_out,
+                        const Knobs& k, hipStream_t stream, const void** u_out) {
+  const bool bf = io == RGLRU_BF16;
+  const void* u = x;
+  bool prefilled = false;
+  if (conv_w) {
+    uint32_t* fill = static_cast<uint32_t*>(status);
+    const size_t words = scan_status_bytes(B, T, D, acc_bytes(io)) / 4;
+    if (bf)
+      RG_CHECK(launch_conv_fwd<bf16_t>(B, T, D, x, conv_w, conv_b, cs, a.u, conv_state_out, stream,
+                                       fill, words, counter));
+    else
+      RG_CHECK(launch_conv_fwd<float>(B, T, D, x, conv_w, conv_b, cs, a.u, conv_state_out, stream,
+                                      fill, words, counter));
+    u = a.u;
+    prefilled = true;
+  }
+  GateGemmArgs g{};
+  g.U = u; g.Wa = W_a; g.Wx = W_x; g.M = B * T; g.N = D; g.K = D;
+  g.ba = b_a; g.bx = b_x; g.lam = lambda; g.c = c;
+  g.out0 = a.r; g.out1 = a.i;
+  g.tail_ws = tail;
+  const int st = gate_projection(io, g, kEpiRI, a.r, a.i, stream);
+  if (st != RGLRU_OK) return st;
+  ScanFwdArgs sf{};
+  sf.B = B; sf.T = T; sf.D = D;
+  sf.x = u; sf.conv_w = nullptr; sf.conv_b = nullptr; sf.conv_state = nullptr;   // u is in memory
+  sf.a = a.r; sf.beta = a.i; sf.from_ri = true; sf.lam = lambda; sf.c = c;
+  sf.h0 = h0; sf.y = y; sf.h_all = a.h_all; sf.h_T = h_T;
+  sf.status = status; sf.counter = counter; sf.prefilled = prefilled;
+  sf.direct_polls = k.scan_direct_polls;
+  if (bf) RG_CHECK((launch_scan_fwd<bf16_t, float>(sf, stream)));
+  else RG_CHECK((launch_scan_fwd<float, double>(sf, stream)));
+  *u_out = u;
+  return RGLRU_OK;
 }
 
 // ------------------------------------------------------------------ recurrent block
@@ -607,57 +687,50 @@ static int bwd_impl(const Knobs& k, int B, int T, int D, rglru_dtype io, float c
                     const float* lambda, const float* h0, const void* dy, const float* dh_T,
                     float* dx, float* dconv_w, float* dconv_b, float* dW_a, float* dW_x,
                     float* db_a, float* db_x, float* dlambda, float* dh0, void* ws,
-                    size_t ws_bytes, hipStream_t stream) {
+                    size_t ws_bytes, hipStream_t stream, const void* saved = nullptr,
+                    size_t saved_bytes = 0) {
   int st = shape_status(B, T, D);
   if (st != RGLRU_OK) return st;
   if (!io_ok(io)) return RGLRU_EDTYPE;
-  if (!x || !W_a || !W_x || !b_a || !b_x || !lambda || !dy || !dx || !dW_a || !dW_x || !db_a ||
-      !db_x || !dlambda || !c_ok(c))
+  if (!x || !W_a || !W_x || (!saved && (!b_a || !b_x)) || !lambda || !dy || !dx || !dW_a ||
+      !dW_x || !db_a || !db_x || !dlambda || !c_ok(c))
     return RGLRU_EINVAL;
   if (conv_w && (!dconv_w || !dconv_b)) return RGLRU_EINVAL;
   for (const void* p : {x, conv_w, (const void*)conv_b, conv_state_in, W_a, W_x, (const void*)b_a,
                         (const void*)b_x, (const void*)lambda, (const void*)h0, dy, (const void*)dh_T,
                         (const void*)dx, (const void*)dconv_w, (const void*)dconv_b,
                         (const void*)dW_a, (const void*)dW_x, (const void*)db_a, (const void*)db_x,
-                        (const void*)dlambda, (const void*)dh0, (const void*)ws})
+                        (const void*)dlambda, (const void*)dh0, (const void*)ws, saved})
     if (p && !aligned16(p)) return RGLRU_EINVAL;
-  if (!ws || ws_bytes < rglru_bwd_workspace_bytes(B, T, D, io)) return RGLRU_EWORKSPACE;
+  if (saved && saved_bytes < rglru_train_saved_bytes(B, T, D, io)) return RGLRU_EINVAL;
+  const size_t need = saved ? rglru_bwd_saved_workspace_bytes(B, T, D, io)
+                            : rglru_bwd_workspace_bytes(B, T, D, io);
+  if (!ws || ws_bytes < need) return RGLRU_EWORKSPACE;
 
   Carver cv(ws);
-  BwdWs w = carve_bwd(cv, B, T, D, io);
+  BwdWs w = carve_bwd(cv, B, T, D, io, /*recompute=*/!saved);
+  if (saved) {
+    Carver sv(const_cast<void*>(saved));
+    w.act = carve_saved(sv, B, T, D, io);
+  }
   const int M = B * T;
   const int Mp = (M + 63) / 64 * 64;
   const bool bf = io == RGLRU_BF16;
   const void* cs = conv_w ? conv_state_in : nullptr;
 
-  // 1. recompute u, the gates (r, i) and every state h_t
-  const void* u = x;
-  if (conv_w) {
-    if (bf) RG_CHECK(launch_conv_fwd<bf16_t>(B, T, D, x, conv_w, conv_b, cs, w.u, nullptr, stream));
-    else RG_CHECK(launch_conv_fwd<float>(B, T, D, x, conv_w, conv_b, cs, w.u, nullptr, stream));
-    u = w.u;
+  // 1. u, the gates (r, i) and every state h_t: recomputed, or the training forward's
+  const void* u = conv_w ? w.act.u : x;
+  if (!saved) {
+    st = forward_acts(io, B, T, D, c, x, conv_w, conv_b, cs, W_a, W_x, b_a, b_x, lambda, h0, w.act,
+                      w.tail, w.status, w.counter, nullptr, nullptr, nullptr, k, stream, &u);
+    if (st != RGLRU_OK) return st;
   }
-  GateGemmArgs g{};
-  g.U = u; g.Wa = W_a; g.Wx = W_x; g.M = M; g.N = D; g.K = D;
-  g.ba = b_a; g.bx = b_x; g.lam = lambda; g.c = c;
-  g.out0 = w.r; g.out1 = w.i;
-  g.tail_ws = w.tail;
-  st = gate_projection(io, g, kEpiRI, w.r, w.i, stream);
-  if (st != RGLRU_OK) return st;
-  ScanFwdArgs sf{};
-  sf.B = B; sf.T = T; sf.D = D;
-  sf.x = x; sf.conv_w = conv_w; sf.conv_b = conv_b; sf.conv_state = cs;
-  sf.a = w.r; sf.beta = w.i; sf.from_ri = true; sf.lam = lambda; sf.c = c;
-  sf.h0 = h0; sf.y = nullptr; sf.h_all = w.h_all; sf.h_T = nullptr;
-  sf.status = w.status; sf.counter = w.counter; sf.direct_polls = k.scan_direct_polls;
-  if (bf) RG_CHECK((launch_scan_fwd<bf16_t, float>(sf, stream)));
-  else RG_CHECK((launch_scan_fwd<float, double>(sf, stream)));
 
   // 2. reverse scan: dz^a, dz^x, the direct du term, dh0, partial sums
   float* du = conv_w ? w.du : dx;   // without the conv, du is dx
   ScanBwdArgs sb{};
   sb.B = B; sb.T = T; sb.D = D;
-  sb.u = u; sb.r = w.r; sb.i = w.i; sb.h_all = w.h_all; sb.h0 = h0;
+  sb.u = u; sb.r = w.act.r; sb.i = w.act.i; sb.h_all = w.act.h_all; sb.h0 = h0;
   sb.dy = dy; sb.dh_T = dh_T; sb.lam = lambda; sb.c = c;
   sb.dz_hi = w.dz_hi; sb.dz_lo = w.dz_lo; sb.du = du; sb.dh0 = dh0;
   sb.partial = w.scan_part; sb.status = w.status; sb.counter = w.counter;
@@ -749,6 +822,67 @@ int rglru_bwd(int B, int T, int D, rglru_dtype io, float c, const void* x, const
   return bwd_impl(kDefaultKnobs, B, T, D, io, c, x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a,
                   b_x, lambda, h0, dy, dh_T, dx, dconv_w, dconv_b, dW_a, dW_x, db_a, db_x, dlambda,
                   dh0, ws, ws_bytes, stream);
+}
+
+size_t rglru_train_saved_bytes(int B, int T, int D, rglru_dtype io) {
+  if (shape_status(B, T, D) != RGLRU_OK || !io_ok(io)) return 0;
+  Carver cv(nullptr);
+  carve_saved(cv, B, T, D, io);
+  return cv.used;
+}
+
+size_t rglru_fwd_train_workspace_bytes(int B, int T, int D, rglru_dtype io) {
+  if (shape_status(B, T, D) != RGLRU_OK || !io_ok(io)) return 0;
+  Carver cv(nullptr);
+  carve_train(cv, B, T, D, io);
+  return cv.used;
+}
+
+size_t rglru_bwd_saved_workspace_bytes(int B, int T, int D, rglru_dtype io) {
+  if (shape_status(B, T, D) != RGLRU_OK || !io_ok(io)) return 0;
+  Carver cv(nullptr);
+  carve_bwd(cv, B, T, D, io, /*recompute=*/false);
+  return cv.used;
+}
+
+int rglru_fwd_train(int B, int T, int D, rglru_dtype io, float c, const void* x,
+                    const void* conv_w, const float* conv_b, const void* conv_state_in,
+                    const void* W_a, const void* W_x, const float* b_a, const float* b_x,
+                    const float* lambda, const float* h0, void* y, float* h_T,
+                    void* conv_state_out, void* saved, size_t saved_bytes, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
+  int st = shape_status(B, T, D);
+  if (st != RGLRU_OK) return st;
+  if (!io_ok(io)) return RGLRU_EDTYPE;
+  if (!x || !W_a || !W_x || !b_a || !b_x || !lambda || !y || !saved || !c_ok(c)) return RGLRU_EINVAL;
+  for (const void* p : {x, conv_w, (const void*)conv_b, conv_state_in, W_a, W_x, (const void*)b_a,
+                        (const void*)b_x, (const void*)lambda, (const void*)h0, (const void*)y,
+                        (const void*)h_T, (const void*)conv_state_out, (const void*)saved,
+                        (const void*)ws})
+    if (p && !aligned16(p)) return RGLRU_EINVAL;
+  if (saved_bytes < rglru_train_saved_bytes(B, T, D, io)) return RGLRU_EINVAL;
+  if (!ws || ws_bytes < rglru_fwd_train_workspace_bytes(B, T, D, io)) return RGLRU_EWORKSPACE;
+  Carver cv(ws);
+  const TrainWs w = carve_train(cv, B, T, D, io);
+  Carver sv(saved);
+  const SavedAct a = carve_saved(sv, B, T, D, io);
+  const void* u = nullptr;
+  return forward_acts(io, B, T, D, c, x, conv_w, conv_b, conv_w ? conv_state_in : nullptr, W_a, W_x,
+                      b_a, b_x, lambda, h0, a, w.tail, w.status, w.counter, y, h_T,
+                      conv_state_out, kDefaultKnobs, stream, &u);
+}
+
+int rglru_bwd_saved(int B, int T, int D, rglru_dtype io, float c, const void* x,
+                    const void* conv_w, const float* conv_b, const void* conv_state_in,
+                    const void* W_a, const void* W_x, const float* lambda, const float* h0,
+                    const void* dy, const float* dh_T, float* dx, float* dconv_w,
+                    float* dconv_b, float* dW_a, float* dW_x, float* db_a, float* db_x,
+                    float* dlambda, float* dh0, const void* saved, size_t saved_bytes, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
+  if (!saved) return RGLRU_EINVAL;
+  return bwd_impl(kDefaultKnobs, B, T, D, io, c, x, conv_w, conv_b, conv_state_in, W_a, W_x,
+                  nullptr, nullptr, lambda, h0, dy, dh_T, dx, dconv_w, dconv_b, dW_a, dW_x, db_a,
+                  db_x, dlambda, dh0, ws, ws_bytes, stream, saved, saved_bytes);
 }
 
 size_t rglru_block_fwd_workspace_bytes(int B, int T, int D, int R, rglru_dtype io) {

@@ -210,6 +210,46 @@ int rglru_bwd(int B, int T, int D, rglru_dtype io, float c, const void* x,
               float* db_a, float* db_x, float* dlambda, float* dh0, void* ws,
               size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Training forward: rglru_fwd that also keeps what the backward reads (the chain rule
+ * through Eq. (1)-(4) needs u_t, r_t, i_t and h_{t-1}), so that rglru_bwd_saved does not
+ * evaluate the forward again.  The same launches as the first part of rglru_bwd: u = the
+ * conv output, r and i from the gate projection, then the forward scan from (r, i) writing
+ * y, h_T and every state h_t.  y matches the oracle to the same tolerance as rglru_fwd's;
+ * the two differ in the last bits where rglru_fwd evaluates the gates in another order.
+ *   saved: caller-owned device buffer of rglru_train_saved_bytes(B, T, D, io) bytes,
+ *   16-byte aligned, written in full (its layout is private to the library: pass it only to
+ *   rglru_bwd_saved with the same shape, dtype and inputs).  At 4 x 2048 x 5376 bf16 that
+ *   is 0.62 GB: u (io), r and i (fp32), h_t (fp32; fp64 for fp32 I/O).
+ *   ws: rglru_fwd_train_workspace_bytes(B, T, D, io) bytes of scratch.
+ *   Other arguments as in rglru_fwd; y must not be NULL.
+ */
+size_t rglru_train_saved_bytes(int B, int T, int D, rglru_dtype io);
+size_t rglru_fwd_train_workspace_bytes(int B, int T, int D, rglru_dtype io);
+int rglru_fwd_train(int B, int T, int D, rglru_dtype io, float c, const void* x,
+                    const void* conv_w, const float* conv_b, const void* conv_state_in,
+                    const void* W_a, const void* W_x, const float* b_a, const float* b_x,
+                    const float* lambda, const float* h0, void* y, float* h_T,
+                    void* conv_state_out, void* saved, size_t saved_bytes, void* ws,
+                    size_t ws_bytes, hipStream_t stream);
+
+/*
+ * rglru_bwd from the activations rglru_fwd_train kept in `saved` (same shape, dtype and
+ * inputs x, conv_w, conv_b, conv_state_in, W_a, W_x, lambda, h0 and c): the forward is not
+ * evaluated again, so b_a and b_x are not needed.  The gradients equal rglru_bwd's bit for
+ * bit (rglru_bwd evaluates the forward with the same kernels in the same order).
+ *   ws: rglru_bwd_saved_workspace_bytes(B, T, D, io) bytes.  saved_bytes smaller than
+ *   rglru_train_saved_bytes or saved NULL: RGLRU_EINVAL.  Other arguments as in rglru_bwd.
+ */
+size_t rglru_bwd_saved_workspace_bytes(int B, int T, int D, rglru_dtype io);
+int rglru_bwd_saved(int B, int T, int D, rglru_dtype io, float c, const void* x,
+                    const void* conv_w, const float* conv_b, const void* conv_state_in,
+                    const void* W_a, const void* W_x, const float* lambda, const float* h0,
+                    const void* dy, const float* dh_T, float* dx, float* dconv_w,
+                    float* dconv_b, float* dW_a, float* dW_x, float* db_a, float* db_x,
+                    float* dlambda, float* dh0, const void* saved, size_t saved_bytes, void* ws,
+                    size_t ws_bytes, hipStream_t stream);
+
 /* Workspace bytes rglru_block_fwd needs (0 for invalid arguments). */
 size_t rglru_block_fwd_workspace_bytes(int B, int T, int D, int R, rglru_dtype io);
 

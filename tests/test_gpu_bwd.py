@@ -82,3 +82,84 @@ def test_backward_is_bitwise_reproducible(lib):
 def test_backward_full_training_workload(lib):
     p = workloads.make_inputs(workloads.TRAIN_BWD)
     _check(lib, p, what="full")
+
+
+# ---------------------------------------------------------------- training forward + saved backward
+def _train_pair(g, p, conv=True, dh_T=None):
+    """rglru_fwd_train then rglru_bwd_saved, and rglru_bwd on the same inputs."""
+    d = device_inputs(p)
+    cw, cb, cs = (d["conv_w"], d["conv_b"], d["conv_state"]) if conv else (None, None, None)
+    dhT_d = None if dh_T is None else torch.from_numpy(dh_T.astype(np.float32)).cuda()
+    y, hT, cso, saved = g.forward_train(d["x"], cw, cb, cs, d["W_a"], d["W_x"], d["b_a"],
+                                        d["b_x"], d["lam"], d["h0"], p["c"])
+    got = g.backward(d["x"], cw, cb, cs, d["W_a"], d["W_x"], None, None, d["lam"], d["h0"],
+                     d["dy"], dhT_d, p["c"], saved=saved)
+    ref = g.backward(d["x"], cw, cb, cs, d["W_a"], d["W_x"], d["b_a"], d["b_x"], d["lam"],
+                     d["h0"], d["dy"], dhT_d, p["c"])
+    torch.cuda.synchronize()
+    return (y, hT, cso), got, ref
+
+
+TRAIN = [
+    (workloads.TINY_F32, 2, 200, 128, True),
+    (workloads.TRAIN_BWD, 2, 300, 192, True),
+    (workloads.TRAIN_BWD, 1, 130, 64, False),
+    (workloads.TRAIN_BWD, 3, 1, 64, True),
+]
+
+
+@pytest.mark.parametrize("w,B,T,D,conv", TRAIN,
+                         ids=[f"{w.io}-{B}x{T}x{D}-{'conv' if cv else 'noconv'}" for w, B, T, D, cv in TRAIN])
+def test_train_forward_matches_oracle_and_saved_backward_matches_bwd(lib, w, B, T, D, conv):
+    wl = w.with_shape(B=B, T=T, D=D, with_dy=True, h0="normal", history="normal")
+    p = workloads.make_inputs(wl)
+    dh_T = np.random.default_rng(3).standard_normal((B, D))
+    (y, hT, cso), got, ref = _train_pair(lib, p, conv=conv, dh_T=dh_T)
+    from gpu_util import oracle_forward
+    want = oracle_forward(p, conv=conv)
+    e = {"y": err(host(y), want["y"]), "h_T": err(host(hT), want["h_T"])}
+    if conv:
+        e["conv_state"] = err(host(cso), want["conv_state_out"])
+    print(f"train fwd io={w.io} shape={p['x'].shape} " + " ".join(f"{k}={v:.2e}" for k, v in e.items()),
+          flush=True)
+    for k, v in e.items():
+        assert v <= TOL[w.io], (k, v)
+    if conv:
+        assert e["conv_state"] == 0.0
+    for n in NAMES:
+        if ref[n] is None:
+            assert got[n] is None
+            continue
+        assert torch.equal(got[n], ref[n]), n
+
+
+def test_saved_backward_rejects_short_saved_buffer(lib):
+    p = workloads.make_inputs(workloads.TRAIN_BWD.with_shape(B=1, T=64, D=64, with_dy=True))
+    d = device_inputs(p)
+    _, _, _, saved = lib.forward_train(d["x"], d["conv_w"], d["conv_b"], None, d["W_a"], d["W_x"],
+                                       d["b_a"], d["b_x"], d["lam"], None, p["c"])
+    with pytest.raises(lib.RgluError):
+        lib.backward(d["x"], d["conv_w"], d["conv_b"], None, d["W_a"], d["W_x"], None, None,
+                     d["lam"], None, d["dy"], None, p["c"], saved=saved[:-16])
+
+
+@pytest.mark.timeout(900)
+def test_saved_backward_full_training_workload_equals_bwd(lib):
+    """At 4 x 2048 x 5376: rglru_bwd_saved gives rglru_bwd's gradients bit for bit (those
+    are checked against the oracle element by element above), and rglru_fwd_train's y on
+    every channel of one sequence matches the oracle."""
+    p = workloads.make_inputs(workloads.TRAIN_BWD)
+    (y, hT, _), got, ref = _train_pair(lib, p)
+    for n in NAMES:
+        assert torch.equal(got[n], ref[n]), n
+    from gpu_util import oracle_forward
+    b = 3
+    q = dict(p)
+    q["x"] = p["x"][b:b + 1]
+    q["conv_state"] = None if p["conv_state"] is None else p["conv_state"][b:b + 1]
+    q["h0"] = None if p["h0"] is None else p["h0"][b:b + 1]
+    want = oracle_forward(q)
+    e_y = err(host(y)[b:b + 1], want["y"])
+    e_h = err(host(hT)[b:b + 1], want["h_T"])
+    print(f"train fwd full b={b} err(y)={e_y:.2e} err(h_T)={e_h:.2e}", flush=True)
+    assert e_y <= TOL["bf16"] and e_h <= TOL["bf16"]
