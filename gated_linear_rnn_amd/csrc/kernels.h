@@ -232,6 +232,7 @@ struct LruArgs {
   uint32_t* status;       // lru_status_bytes(B,T,D) bytes of look-back words
   uint32_t* counters;     // 64 ticket counters (zeroed with the status words)
   int groups;             // set by the launcher
+  int chain_bw;           // sequences per block of the chain order (set by the launcher)
   const void* gate;       // [B,T,D] bf16 multiplier of the output (the block's GeLU branch) or NULL
   int ticket_guess;       // added to the launch-order ticket guess (0; tests shift it)
   int max_polls;          // look-back polls before giving up (kMaxPolls; < 0: at once)

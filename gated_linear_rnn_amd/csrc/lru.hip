@@ -20,11 +20,13 @@
 // its g before rounding.
 //
 // Tiles of one chain (sequence b, channel tile) must be started in time order: every
-// workgroup takes a ticket from the counter of its group g = blockIdx % G; group g owns
-// the chains c = g, g + G, ... (so all tiles of a chain share one counter), and tickets
-// enumerate its tiles time-level by time-level.  A tile only waits on tiles with lower
-// tickets of its own counter, which have already started: no deadlock.  G = 8 matches the
-// round-robin dispatch of workgroups over the 8 XCDs, so a chain stays on one XCD's L2.
+// workgroup takes a ticket from the counter of its group g = blockIdx % G; group g owns a
+// contiguous range of the chains in a blocked order (blocks of bw sequences, channel tile
+// by channel tile), so all tiles of a chain share one counter, and tickets enumerate its
+// tiles time-level by time-level.  A tile only waits on tiles with lower tickets of its own
+// counter, which have already started: no deadlock.  G = 8 matches the round-robin
+// dispatch of workgroups over the 8 XCDs, so a chain stays on one XCD's L2, and the blocked
+// order makes the tiles an XCD runs together share their u and W panels there.
 #include "gemm_core.h"
 #include "kernels.h"
 
@@ -217,11 +219,15 @@ __global__ __launch_bounds__(CfgLru::NW * 64, 2) void lru_fused_kernel(LruArgs p
   const int B = p.B, T = p.T, D = p.D;
   const int NT = (D + kLruCh - 1) / kLruCh;
   const int per_level = B * NT / G;
+  const int bw = p.chain_bw;
   auto tile_of = [&](int k, int& b, int& tn, int& tt) {
     tt = k / per_level;
-    const int chain = g + G * (k % per_level);
-    b = chain / NT;
-    tn = chain % NT;
+    // position of the chain in the blocked chain order (blocks of bw sequences, channel
+    // tile by channel tile): group g owns positions g * per_level .. + per_level - 1
+    const int o = g * per_level + k % per_level;
+    const int blk = o / (bw * NT), rem = o % (bw * NT);
+    b = blk * bw + rem % bw;
+    tn = rem / bw;
   };
   auto operands = [&](int b, int tn, int tt) {
     TileOperands op;
@@ -269,6 +275,11 @@ hipError_t launch_lru_fused(const LruArgs& a_in, bool prefilled, hipStream_t s) 
   const int NT = (a.D + kLruCh - 1) / kLruCh;
   const int chains = a.B * NT;
   a.groups = lru_groups(chains);
+  // a group's chains span bw sequences (u panels) and about per_level / bw channel tiles
+  // (W panels) per time level; blocks of up to 4 sequences keep both few: at 8 x 2048 x 2560,
+  // 4 u panels and 5 W panels per level instead of 8 and 3 (the kernel's fetches beyond L2,
+  // FETCH_SIZE, drop from 1.04 to 0.83 GB per launch at the same speed)
+  a.chain_bw = a.B % 4 == 0 ? 4 : (a.B % 2 == 0 ? 2 : 1);
   if (!prefilled) {
     const hipError_t e = launch_fill_status(a.status, lru_status_bytes(a.B, a.T, a.D) / 4,
                                             a.counters, kCounterWords, s);
