@@ -145,8 +145,91 @@ __global__ __launch_bounds__(256) void decode_update_kernel(DecodeArgs p) {
   Io<bf16_t>::store4(static_cast<bf16_t*>(p.y) + o, hn);
 }
 
+// Small batches (B <= kGemvMaxB = 4): the step's gate projection is a matrix-vector product per
+// sequence, bound by streaming W.  One wave per channel reads that channel's W_a and W_x rows
+// once (16-byte loads along K), multiplies them with the B rows of u (staged once per
+// workgroup in LDS), sums its 64 lanes in a fixed butterfly order, and applies the gates and
+// the state update itself: one launch after the conv, no partial sums in memory.  Each lane
+// sums its K chunks in order, so repeated calls give identical bits.
+constexpr int kGemvMaxB = 4;                  // at B = 6 and 8 the split-K pair is as fast
+constexpr int kGemvWaves = 8;                  // channels per workgroup
+constexpr int kGemvMaxD = 4096;                // u staging: BB * kGemvMaxD * 2 bytes of LDS
+
+bool decode_uses_gemv(int B, int D) { return B <= kGemvMaxB && D <= kGemvMaxD; }
+
+__device__ __forceinline__ float bfl(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bfh(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <int BB>
+__global__ __launch_bounds__(kGemvWaves * 64) void decode_gemv_kernel(DecodeArgs p) {
+  __shared__ __attribute__((aligned(16))) bf16_t su[BB * kGemvMaxD];
+  const int B = p.B, D = p.D;
+  const int lane = threadIdx.x & 63;
+  // u [B, D] into LDS, 16 bytes per thread per trip
+  const uint4* ug = static_cast<const uint4*>(p.u);
+  uint4* ul = reinterpret_cast<uint4*>(su);
+  const int n16 = B * D / 8;
+  for (int i = threadIdx.x; i < n16; i += blockDim.x) ul[i] = ug[i];
+  __syncthreads();
+  const int ch = blockIdx.x * kGemvWaves + int(threadIdx.x >> 6);
+  if (ch >= D) return;                         // the whole wave: ch is wave-uniform
+  const uint4* wa = reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(p.Wa) + size_t(ch) * D);
+  const uint4* wx = reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(p.Wx) + size_t(ch) * D);
+  float sa[BB], sx[BB];
+#pragma unroll
+  for (int b = 0; b < BB; ++b) { sa[b] = 0.f; sx[b] = 0.f; }
+  for (int c = lane; c < D / 8; c += 64) {     // 8 consecutive k per 16-byte chunk
+    const uint4 va = wa[c], vx = wx[c];
+    const float a8[8] = {bfl(va.x), bfh(va.x), bfl(va.y), bfh(va.y), bfl(va.z), bfh(va.z), bfl(va.w), bfh(va.w)};
+    const float x8[8] = {bfl(vx.x), bfh(vx.x), bfl(vx.y), bfh(vx.y), bfl(vx.z), bfh(vx.z), bfl(vx.w), bfh(vx.w)};
+#pragma unroll
+    for (int b = 0; b < BB; ++b) {
+      if (b < B) {
+        const uint4 vu = ul[size_t(b) * (D / 8) + c];
+        const float u8[8] = {bfl(vu.x), bfh(vu.x), bfl(vu.y), bfh(vu.y), bfl(vu.z), bfh(vu.z), bfl(vu.w), bfh(vu.w)};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          sa[b] = fmaf(a8[e], u8[e], sa[b]);
+          sx[b] = fmaf(x8[e], u8[e], sx[b]);
+        }
+      }
+    }
+  }
+  // butterfly over the 64 lanes; a + b == b + a, so every lane ends with the same sums
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+    for (int b = 0; b < BB; ++b) {
+      sa[b] += __shfl_xor(sa[b], off);
+      sx[b] += __shfl_xor(sx[b], off);
+    }
+  if (lane >= B) return;
+  float za = 0.f, zx = 0.f;
+#pragma unroll
+  for (int b = 0; b < BB; ++b)
+    if (b == lane) { za = sa[b]; zx = sx[b]; }
+  const int b = lane;
+  const GateChan k = gate_chan(p.ba[ch], p.bx[ch], p.lam[ch], p.c);
+  float a, beta;
+  gate_fast(za, zx, k, a, beta);
+  const size_t o = size_t(b) * D + ch;
+  const float hn = fmaf(a, p.h[o], beta * bf2f(su[o]));
+  p.h[o] = hn;
+  const float yv = p.gate ? hn * bf2f(static_cast<const bf16_t*>(p.gate)[o]) : hn;
+  static_cast<bf16_t*>(p.y)[o] = f2bf(yv);
+}
+
 hipError_t launch_decode_bf16(const DecodeArgs& a_in, hipStream_t s) {
   DecodeArgs a = a_in;
+  if (decode_uses_gemv(a.B, a.D)) {
+    const int blocks = (a.D + kGemvWaves - 1) / kGemvWaves;
+    switch (a.B) {
+      case 1: decode_gemv_kernel<1><<<blocks, kGemvWaves * 64, 0, s>>>(a); break;
+      case 2: decode_gemv_kernel<2><<<blocks, kGemvWaves * 64, 0, s>>>(a); break;
+      default: decode_gemv_kernel<4><<<blocks, kGemvWaves * 64, 0, s>>>(a); break;
+    }
+    return hipGetLastError();
+  }
   a.splits = decode_splits(a.B, a.D);
   a.chan = a.partial + size_t(a.splits) * 2 * size_t(a.B) * a.D;
   const int MT = (a.B + CfgDecode::BM - 1) / CfgDecode::BM;

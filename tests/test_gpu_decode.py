@@ -83,6 +83,33 @@ def test_decode_small_elementwise(lib, io, B, D):
     _run(lib, p, 40)
 
 
+@pytest.mark.parametrize("B,D", [(1, 2560), (2, 192), (3, 320), (4, 256), (4, 4096)])
+def test_decode_small_batch_single_launch(lib, B, D):
+    """B <= 4 takes the one-launch matrix-vector form of the step (per-channel waves,
+    u staged in LDS); every element of every step against the oracle."""
+    p = workloads.make_inputs(workloads.DECODE.with_shape(B=B, D=D, T=12))
+    _run(lib, p, 12)
+
+
+def test_decode_small_batch_is_bitwise_reproducible(lib):
+    p = workloads.make_inputs(workloads.DECODE.with_shape(B=3, D=640, T=4))
+    io = TORCH_IO["bf16"]
+    outs = []
+    for _ in range(2):
+        x = dev(p["x"], io)
+        hist, h = dev(p["conv_state"], io), dev(p["h0"])
+        y = torch.empty((3, 640), dtype=io, device="cuda")
+        ws = lib.workspace(lib.decode_workspace_bytes(3, 640, io))
+        for t in range(4):
+            lib.rglru_decode_step(x[t], dev(p["conv_w"], io), dev(p["conv_b"]), hist,
+                                  dev(p["W_a"], io), dev(p["W_x"], io), dev(p["b_a"]),
+                                  dev(p["b_x"]), dev(p["lam"]), h, y, ws, p["c"])
+        torch.cuda.synchronize()
+        outs.append((y.clone(), h.clone(), hist.clone()))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+
+
 def test_decode_without_conv(lib):
     p = workloads.make_inputs(workloads.DECODE.with_shape(B=4, D=128, T=10))
     _run(lib, p, 10, conv=False)
