@@ -15,7 +15,7 @@
 #include "rglru_testing.h"
 
 namespace rglru {
-const Knobs kDefaultKnobs = {0, kDirectPolls, kMaxPolls};
+const Knobs kDefaultKnobs = {0, kDirectPolls, kMaxPolls, 0};
 }
 
 using namespace rglru;
@@ -79,7 +79,7 @@ struct FwdWs {
 bool lru_unfused(int B, int T, int D, rglru_dtype io) {
   if (io != RGLRU_BF16) return true;
   const long tiles = lru_tiles(B, T, D), rem = tiles % 256;
-  return tiles > 512 && rem != 0 && rem * 5 <= 256 * 3;
+  return rem != 0 && rem * 5 <= 256 * 3;
 }
 
 // The counter words every chained-scan workspace starts with (ticket counters, stall flag).
@@ -103,12 +103,12 @@ void carve_lru(Carver& cv, FwdWs& w, int B, int T, int D, rglru_dtype io, bool f
   }
 }
 
-FwdWs carve_fwd(Carver& cv, int B, int T, int D, rglru_dtype io) {
+FwdWs carve_fwd(Carver& cv, int B, int T, int D, rglru_dtype io, bool fused = false) {
   const size_t n = size_t(B) * T * D;
   FwdWs w;
   w.counter = carve_counters(cv);
   w.u = cv.take<unsigned char>(n * io_bytes(io));
-  carve_lru(cv, w, B, T, D, io);
+  carve_lru(cv, w, B, T, D, io, fused);
   return w;
 }
 
@@ -160,7 +160,7 @@ int lru_layer(rglru_dtype io, int B, int T, int D, float c, const void* u, const
               const void* W_x, const float* b_a, const float* b_x, const float* lambda,
               const float* h0, void* y, float* h_T, FwdWs& w, bool prefilled, const Knobs& k,
               hipStream_t stream) {
-  if (!lru_unfused(B, T, D, io)) {
+  if ((k.lru_force_fused && io == RGLRU_BF16) || !lru_unfused(B, T, D, io)) {
     LruArgs la{};
     la.u = u; la.Wa = W_a; la.Wx = W_x; la.ba = b_a; la.bx = b_x; la.lam = lambda; la.c = c;
     la.h0 = h0; la.y = y; la.hT = h_T; la.B = B; la.T = T; la.D = D;
@@ -495,14 +495,17 @@ static int fwd_impl(const Knobs& k, int B, int T, int D, rglru_dtype io, float c
     if (p && !aligned16(p)) return RGLRU_EINVAL;
   if (!ws || ws_bytes < rglru_fwd_workspace_bytes(B, T, D, io)) return RGLRU_EWORKSPACE;
 
+  // (the fused form's workspace is never larger than the unfused one's, so a forced fused
+  // form fits the workspace sized for the shape's own form)
+  const bool fused = k.lru_force_fused != 0;
   Carver cv(ws);
-  FwdWs w = carve_fwd(cv, B, T, D, io);
+  FwdWs w = carve_fwd(cv, B, T, D, io, fused);
   const void* u = x;
   bool prefilled = false;
   if (conv_w) {
     // the conv launch also initialises the layer's look-back status and counters
     uint32_t* fill = static_cast<uint32_t*>(w.status);
-    const size_t words = status_fill_words(B, T, D, io);
+    const size_t words = status_fill_words(B, T, D, io, fused);
     if (io == RGLRU_BF16)
       RG_CHECK(launch_conv_fwd<bf16_t>(B, T, D, x, conv_w, conv_b, conv_state_in, w.u, conv_state_out,
                                        stream, fill, words, w.counter));
@@ -1245,7 +1248,8 @@ int rglru_block_decode_step(int B, int D, int R, rglru_dtype io, float c, const 
 // chained-scan settings passed explicitly instead of kDefaultKnobs.
 
 static Knobs knobs_of(const rglru_testing_knobs* t) {
-  return t ? Knobs{t->lru_ticket_guess, t->scan_direct_polls, t->lookback_polls} : kDefaultKnobs;
+  return t ? Knobs{t->lru_ticket_guess, t->scan_direct_polls, t->lookback_polls, t->lru_force_fused}
+           : kDefaultKnobs;
 }
 
 void rglru_testing_default_knobs(rglru_testing_knobs* t) {
@@ -1253,6 +1257,7 @@ void rglru_testing_default_knobs(rglru_testing_knobs* t) {
   t->lru_ticket_guess = kDefaultKnobs.lru_ticket_guess;
   t->scan_direct_polls = kDefaultKnobs.scan_direct_polls;
   t->lookback_polls = kDefaultKnobs.lookback_polls;
+  t->lru_force_fused = kDefaultKnobs.lru_force_fused;
 }
 
 int rglru_testing_fwd(const rglru_testing_knobs* t, int B, int T, int D, rglru_dtype io, float c,

@@ -21,6 +21,7 @@ struct Knobs {
   int lru_ticket_guess;   // fused RG-LRU kernel: shift of the launch-order ticket guess
   int scan_direct_polls;  // forward scan: see ScanFwdArgs::direct_polls
   int lookback_polls;     // fused kernel and reverse scan: polls before a look-back gives up
+  int lru_force_fused;    // bf16 RG-LRU layer: the fused kernel whatever the shape (1) or by shape (0)
 };
 extern const Knobs kDefaultKnobs;
 

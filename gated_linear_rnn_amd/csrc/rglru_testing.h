@@ -21,6 +21,11 @@
  *                     predecessor before the look-back gives up (default 2^20); < 0 gives up
  *                     at once.  Giving up writes NaN where the carry was needed and makes
  *                     rglru_workspace_status return RGLRU_ESTALL; every kernel still ends.
+ *   lru_force_fused   bf16 RG-LRU layer of the forward: 1 runs the fused kernel whatever the
+ *                     shape (default 0: the form the shape selects, which for shapes whose
+ *                     fused tiles leave their last round of 256 CUs at most 60% full is the
+ *                     gate projection then the scan).  Lets the tests reach the fused kernel
+ *                     at every shape; the workspace sized for the shape's form suffices.
  */
 #ifndef RGLRU_TESTING_H
 #define RGLRU_TESTING_H
@@ -35,6 +40,7 @@ typedef struct {
   int lru_ticket_guess;
   int scan_direct_polls;
   int lookback_polls;
+  int lru_force_fused;
 } rglru_testing_knobs;
 
 /* Fills *knobs with the settings every public call uses. */

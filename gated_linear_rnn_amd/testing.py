@@ -21,7 +21,7 @@ EXPORTS = ("rglru_testing_default_knobs", "rglru_testing_fwd", "rglru_testing_sc
 
 class Knobs(ctypes.Structure):
     _fields_ = [("lru_ticket_guess", ctypes.c_int), ("scan_direct_polls", ctypes.c_int),
-                ("lookback_polls", ctypes.c_int)]
+                ("lookback_polls", ctypes.c_int), ("lru_force_fused", ctypes.c_int)]
 
 
 _declared = False

@@ -14,10 +14,28 @@ from gpu_util import TOL, device_inputs, err, gpu_forward, make, oracle_forward,
 pytestmark = pytest.mark.gpu
 
 
-def _check(g, p, conv=True, channels=None, what=""):
+def _forced_fused(d, c, conv=True):
+    """The forward with the bf16 RG-LRU layer in the fused kernel whatever the shape (the
+    test-only entry point; the public call picks the form by shape)."""
+    import torch
+    from gated_linear_rnn_amd import testing
+    from gpu_util import host
+    y, hT, cso, _ = testing.forward(testing.knobs(lru_force_fused=1), d["x"],
+                                    d["conv_w"] if conv else None, d["conv_b"] if conv else None,
+                                    d["conv_state"] if conv else None, d["W_a"], d["W_x"],
+                                    d["b_a"], d["b_x"], d["lam"], d["h0"], c)
+    torch.cuda.synchronize()
+    return host(y), host(hT), None if cso is None else host(cso)
+
+
+def _check(g, p, conv=True, channels=None, what="", fused=False):
     io = p["workload"].io
     d = device_inputs(p)
-    y, hT, cso = gpu_forward(g, d, p["c"], conv=conv)
+    if fused:
+        y, hT, cso = _forced_fused(d, p["c"], conv=conv)
+        what = what + " (fused)"
+    else:
+        y, hT, cso = gpu_forward(g, d, p["c"], conv=conv)
     o = oracle_forward(p, channels=channels, conv=conv)
     S = slice(None) if channels is None else channels
     ey, eh = err(y[:, :, S], o["y"]), err(hT[:, S], o["h_T"])
@@ -45,6 +63,8 @@ SMALL = [
 def test_forward_small_elementwise(lib, w, B, T, D):
     p = make(w, B=B, T=T, D=D)
     _check(lib, p, what=w.name)
+    if w.io == "bf16":   # small bf16 shapes take the unfused form: check the fused kernel too
+        _check(lib, p, what=w.name, fused=True)
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
@@ -53,12 +73,16 @@ def test_forward_with_conv_state_and_h0(lib, io):
     p = workloads.make_inputs(w)
     p["conv_b"] = np.random.default_rng(0).standard_normal(128).astype(np.float32) * 0.1
     _check(lib, p, what="state")
+    if io == "bf16":
+        _check(lib, p, what="state", fused=True)
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_forward_without_conv(lib, io):
     p = make(workloads.TRAIN_FWD, B=2, T=200, D=128, io=io)
     _check(lib, p, conv=False, what="noconv")
+    if io == "bf16":
+        _check(lib, p, conv=False, what="noconv", fused=True)
 
 
 def test_tiny_f32_workload_full(lib):
@@ -99,16 +123,19 @@ def test_forward_full_size(lib, w):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("B,T,D", [(2, 2048, 4608), (3, 1700, 2752)])
+@pytest.mark.parametrize("B,T,D", [(2, 2048, 4608), (3, 1700, 2752), (1, 512, 2560),
+                                   (8, 512, 2560)])
 def test_forward_where_fused_rounds_fill_poorly(lib, B, T, D):
-    """Shapes whose fused tiles (256 steps x 128 channels) leave the last of their rounds of
-    256 CUs at most 60% full (2 x 8 x 36 = 576 tiles, a quarter-full third round; 3 x 7 x 22 =
-    462 tiles stay fused below 512): the first runs as the gate GEMM with its split-K tail,
-    then the scan.  Every channel of every sequence against the oracle, and bitwise
-    repeatable."""
+    """The forward's form by shape: shapes whose fused tiles (256 steps x 128 channels)
+    leave the last of their rounds of 256 CUs at most 60% full run as the gate GEMM with its
+    split-K tail, then the scan (2 x 8 x 36 = 576 tiles: a quarter-full third round; 1 x 2 x 20
+    = 40 tiles; 8 x 2 x 20 = 320 tiles: a quarter-full second round); 3 x 7 x 22 = 462 tiles
+    fill their second round to 80% and stay fused.  Every channel of every sequence against
+    the oracle in both forms, and bitwise repeatable."""
     import torch
     p = make(workloads.TRAIN_BWD, B=B, T=T, D=D, h0="normal", history="normal")
     _check(lib, p, what=f"rounds {B}x{T}x{D}")
+    _check(lib, p, what=f"rounds {B}x{T}x{D}", fused=True)
     d = device_inputs(p)
     y1, h1, _ = gpu_forward(lib, d, p["c"])
     y2, h2, _ = gpu_forward(lib, d, p["c"])

@@ -17,8 +17,10 @@ pytestmark = pytest.mark.gpu
 
 
 def _fwd_with_guess(d, c, offset):
+    """The forward with the fused kernel (forced: small shapes take the unfused form) and its
+    ticket guess shifted by `offset`."""
     from gated_linear_rnn_amd import testing
-    y, hT, _, _ = testing.forward(testing.knobs(lru_ticket_guess=offset), d["x"], d["conv_w"],
+    y, hT, _, _ = testing.forward(testing.knobs(lru_ticket_guess=offset, lru_force_fused=1), d["x"], d["conv_w"],
                                   d["conv_b"], d["conv_state"], d["W_a"], d["W_x"], d["b_a"],
                                   d["b_x"], d["lam"], d["h0"], c)
     torch.cuda.synchronize()
@@ -30,7 +32,7 @@ def test_forward_with_wrong_guesses_gives_the_same_bits(lib, offset):
     # 2 sequences x 3 channel tiles x 3 time tiles (the last one ragged)
     p = make(workloads.TRAIN_FWD, B=2, T=600, D=384, h0="normal", history="normal")
     d = device_inputs(p)
-    y0, h0, _ = gpu_forward(lib, d, p["c"])
+    y0, h0 = _fwd_with_guess(d, p["c"], 0)
     y1, h1 = _fwd_with_guess(d, p["c"], offset)
     np.testing.assert_array_equal(y0, y1)
     np.testing.assert_array_equal(h0, h1)
@@ -83,7 +85,7 @@ def test_a_lookback_that_gives_up_is_reported(lib, io):
     d = device_inputs(p)
     fargs = (d["x"], d["conv_w"], d["conv_b"], d["conv_state"], d["W_a"], d["W_x"], d["b_a"],
              d["b_x"], d["lam"], d["h0"])
-    stop = testing.knobs(lookback_polls=-1)
+    stop = testing.knobs(lookback_polls=-1, lru_force_fused=1)
     y, hT, _, ws = testing.forward(stop, *fargs, c=p["c"])
     st = lib.rglru_workspace_status(ws)
     if io == "bf16":
