@@ -125,12 +125,9 @@ int gate_projection(rglru_dtype io, GateGemmArgs g, int epi, float* zscratch_a,
     RG_CHECK(launch_gate_gemm_bf16(g, epi, s));
     return RGLRU_OK;
   }
-  PlainGemmArgs pa{};
-  pa.A = g.U; pa.Bm = g.Wa; pa.M = g.M; pa.N = g.N; pa.K = g.K;
-  pa.lda = g.K; pa.ldb = g.K; pa.ldc = g.N; pa.C = zscratch_a;
-  RG_CHECK(launch_plain_gemm_f32(pa, s));
-  pa.Bm = g.Wx; pa.C = zscratch_x;
-  RG_CHECK(launch_plain_gemm_f32(pa, s));
+  RG_CHECK(launch_gemm_f32_pair(static_cast<const float*>(g.U), static_cast<const float*>(g.Wa),
+                                static_cast<const float*>(g.Wx), g.M, g.N, g.K, zscratch_a,
+                                zscratch_x, s));
   RG_CHECK(launch_gate_elementwise_f32(g, zscratch_a, zscratch_x, epi, s));
   return RGLRU_OK;
 }

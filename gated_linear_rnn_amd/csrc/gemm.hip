@@ -559,30 +559,55 @@ hipError_t launch_geglu_gemm_bf16(const GegluGemmArgs& g, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------- fp32 VALU GEMM
-// For fp32 I/O (the tiny fp32 workload): C = A B^T (+ addend), 64x64 tiles, 4x4 per
-// thread, K-slices of 16 staged transposed in LDS.  Products of fp32 values are exact in
-// fp64, so the fp64 accumulation leaves one rounding per output (the weight-gradient
-// reductions run over B*T rows).  Latency-bound at these sizes.
-__global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A,
-                                                       const float* __restrict__ Bm, int M, int N,
-                                                       int K, int lda, int ldb, int ldc,
-                                                       float* C, const float* addend) {
-  __shared__ float As[16][68];
-  __shared__ float Bs[16][68];
+// For fp32 I/O (the tiny fp32 workload): C = A B^T (+ addend), TM x TM tiles, 4x4 per thread,
+// K-slices of 16 staged transposed in LDS.  Products of fp32 values are exact in fp64, so the
+// fp64 accumulation leaves one rounding per output (the weight-gradient reductions run over
+// B*T rows); each output is summed over k in order by one thread, so the tile size does not
+// change any bit.  Latency-bound at these sizes: 64 x 64 tiles (256 threads) when they give
+// the GPU at least one workgroup per CU, else 32 x 32 tiles (64 threads, four times the
+// workgroups).  With B1 (grid.y = 2) the same launch also computes C1 = A B1^T: the two gate
+// projections of the fp32 forward in one launch.
+template <int TM>
+__global__ __launch_bounds__(TM * TM / 16) void gemm_f32_kernel(
+    const float* __restrict__ A, const float* __restrict__ B0, const float* __restrict__ B1,
+    int M, int N, int K, int lda, int ldb, int ldc, float* C0, float* C1,
+    const float* addend) {
+  constexpr int NTH = TM * TM / 16, TX = TM / 4, LPT = TM * 4 / NTH;
+  __shared__ float As[16][TM + 4];
+  __shared__ float Bs[16][TM + 4];
+  const float* Bm = blockIdx.y ? B1 : B0;
+  float* C = blockIdx.y ? C1 : C0;
   const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;
-  const int NT = (N + 63) / 64;
-  const int m0 = (blockIdx.x / NT) * 64, n0 = (blockIdx.x % NT) * 64;
-  const int lr = tid >> 2, lk = (tid & 3) * 4;
-  const float* ap = A + size_t(min(m0 + lr, M - 1)) * lda + lk;
-  const float* bp = Bm + size_t(min(n0 + lr, N - 1)) * ldb + lk;
+  const int tx = tid % TX, ty = tid / TX;
+  const int NT = (N + TM - 1) / TM;
+  const int m0 = (blockIdx.x / NT) * TM, n0 = (blockIdx.x % NT) * TM;
+  const float* ap[LPT];
+  const float* bp[LPT];
+  int lr[LPT], lk[LPT];
+#pragma unroll
+  for (int q = 0; q < LPT; ++q) {
+    const int idx = tid + q * NTH;
+    lr[q] = idx >> 2;
+    lk[q] = (idx & 3) * 4;
+    ap[q] = A + size_t(min(m0 + lr[q], M - 1)) * lda + lk[q];
+    bp[q] = Bm + size_t(min(n0 + lr[q], N - 1)) * ldb + lk[q];
+  }
   double acc[4][4] = {};
   for (int k0 = 0; k0 < K; k0 += 16) {
-    const float4 av = *reinterpret_cast<const float4*>(ap + k0);
-    const float4 bv = *reinterpret_cast<const float4*>(bp + k0);
+    float4 av[LPT], bv[LPT];
+#pragma unroll
+    for (int q = 0; q < LPT; ++q) {
+      av[q] = *reinterpret_cast<const float4*>(ap[q] + k0);
+      bv[q] = *reinterpret_cast<const float4*>(bp[q] + k0);
+    }
     __syncthreads();
-    As[lk + 0][lr] = av.x; As[lk + 1][lr] = av.y; As[lk + 2][lr] = av.z; As[lk + 3][lr] = av.w;
-    Bs[lk + 0][lr] = bv.x; Bs[lk + 1][lr] = bv.y; Bs[lk + 2][lr] = bv.z; Bs[lk + 3][lr] = bv.w;
+#pragma unroll
+    for (int q = 0; q < LPT; ++q) {
+      As[lk[q] + 0][lr[q]] = av[q].x; As[lk[q] + 1][lr[q]] = av[q].y;
+      As[lk[q] + 2][lr[q]] = av[q].z; As[lk[q] + 3][lr[q]] = av[q].w;
+      Bs[lk[q] + 0][lr[q]] = bv[q].x; Bs[lk[q] + 1][lr[q]] = bv[q].y;
+      Bs[lk[q] + 2][lr[q]] = bv[q].z; Bs[lk[q] + 3][lr[q]] = bv[q].w;
+    }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
@@ -613,12 +638,29 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
   }
 }
 
-hipError_t launch_plain_gemm_f32(const PlainGemmArgs& g, hipStream_t s) {
-  const int blocks = ((g.M + 63) / 64) * ((g.N + 63) / 64);
-  gemm_f32_kernel<<<blocks, 256, 0, s>>>(static_cast<const float*>(g.A),
-                                         static_cast<const float*>(g.Bm), g.M, g.N, g.K, g.lda,
-                                         g.ldb, g.ldc, g.C, g.addend);
+static hipError_t launch_gemm_f32(const float* A, const float* B0, const float* B1, int M, int N,
+                                  int K, int lda, int ldb, int ldc, float* C0, float* C1,
+                                  const float* addend, hipStream_t s) {
+  const int pairs = B1 ? 2 : 1;
+  const long tiles64 = long((M + 63) / 64) * ((N + 63) / 64) * pairs;
+  if (tiles64 >= 256) {
+    const dim3 grid(((M + 63) / 64) * ((N + 63) / 64), pairs);
+    gemm_f32_kernel<64><<<grid, 256, 0, s>>>(A, B0, B1, M, N, K, lda, ldb, ldc, C0, C1, addend);
+  } else {
+    const dim3 grid(((M + 31) / 32) * ((N + 31) / 32), pairs);
+    gemm_f32_kernel<32><<<grid, 64, 0, s>>>(A, B0, B1, M, N, K, lda, ldb, ldc, C0, C1, addend);
+  }
   return hipGetLastError();
+}
+
+hipError_t launch_plain_gemm_f32(const PlainGemmArgs& g, hipStream_t s) {
+  return launch_gemm_f32(static_cast<const float*>(g.A), static_cast<const float*>(g.Bm), nullptr,
+                         g.M, g.N, g.K, g.lda, g.ldb, g.ldc, g.C, nullptr, g.addend, s);
+}
+
+hipError_t launch_gemm_f32_pair(const float* A, const float* B0, const float* B1, int M, int N,
+                                int K, float* C0, float* C1, hipStream_t s) {
+  return launch_gemm_f32(A, B0, B1, M, N, K, K, K, N, C0, C1, nullptr, s);
 }
 
 template <int EPI>

@@ -155,6 +155,9 @@ hipError_t launch_qkv_gemm_bf16(const QkvGemmArgs& g, hipStream_t s);
 hipError_t launch_gate_gemm_bf16(const GateGemmArgs& g, int epi, hipStream_t s);   // kEpiAB, kEpiRI
 hipError_t launch_plain_gemm_bf16(const PlainGemmArgs& g, hipStream_t s);
 hipError_t launch_plain_gemm_f32(const PlainGemmArgs& g, hipStream_t s);
+// C0 = A B0^T and C1 = A B1^T (fp32, [M,N], K-contiguous operands) in one launch
+hipError_t launch_gemm_f32_pair(const float* A, const float* B0, const float* B1, int M, int N,
+                                int K, float* C0, float* C1, hipStream_t s);
 // fp32 I/O: gate math from pre-activations za, zx [M, N] (already W u, bias not added).
 hipError_t launch_gate_elementwise_f32(const GateGemmArgs& g, const float* za, const float* zx,
                                        int epi, hipStream_t s);
