@@ -44,7 +44,8 @@ def test_noalloc_decode_equals_workspace_decode(lib, io):
     big = workloads.DECODE.with_shape(B=256, D=2560, T=3, io=io) if io == "bf16" else \
         workloads.DECODE.with_shape(B=64, D=1024, T=3, io=io)
     small = workloads.DECODE.with_shape(B=8, D=512, T=3, io=io)
-    for w in (big, small):                      # the second call is smaller than the first
+    tiny = workloads.DECODE.with_shape(B=2, D=256, T=3, io=io)   # bf16: the one-launch step
+    for w in (big, small, tiny):                # each call smaller than the one before
         p = workloads.make_inputs(w)
         a, b, outs = _both(lib, p, tio)
         for ya, yb in outs:
