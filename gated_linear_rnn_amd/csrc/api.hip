@@ -134,14 +134,26 @@ int gate_projection(rglru_dtype io, GateGemmArgs g, int epi, float* zscratch_a,
 
 // The forward scan over (a, beta): K2.  `prefilled` when the conv launch before it on the
 // stream already initialised the look-back status.
+// `gz`, when given, makes a and beta the raw projections z^a = u W_a and z^x = u W_x: the
+// scan then forms the gates itself (Eq. (2)-(4)) from them, the biases and Lambda.
+struct GateZ {
+  const float* b_a;
+  const float* b_x;
+  const float* lam;
+  float c;
+};
 int forward_scan(rglru_dtype io, int B, int T, int D, const void* x, const void* conv_w,
                  const float* conv_b, const void* conv_state_in, const float* a, const float* beta,
                  const float* h0, void* y, float* h_T, void* status, uint32_t* counter,
-                 bool prefilled, const Knobs& k, hipStream_t stream) {
+                 bool prefilled, const Knobs& k, hipStream_t stream, const GateZ* gz = nullptr) {
   ScanFwdArgs sa{};
   sa.B = B; sa.T = T; sa.D = D;
   sa.x = x; sa.conv_w = conv_w; sa.conv_b = conv_b; sa.conv_state = conv_w ? conv_state_in : nullptr;
   sa.a = a; sa.beta = beta; sa.from_ri = false; sa.lam = nullptr; sa.c = 0.f;
+  sa.from_z = gz != nullptr;
+  if (gz) {
+    sa.zb_a = gz->b_a; sa.zb_x = gz->b_x; sa.lam = gz->lam; sa.c = gz->c;
+  }
   sa.h0 = h0; sa.y = y; sa.h_all = nullptr; sa.h_T = h_T;
   sa.status = status; sa.counter = counter; sa.prefilled = prefilled;
   sa.direct_polls = k.scan_direct_polls;
@@ -166,6 +178,18 @@ int lru_layer(rglru_dtype io, int B, int T, int D, float c, const void* u, const
     la.stall = w.counter + kStallWord;
     RG_CHECK(launch_lru_fused(la, prefilled, stream));
     return RGLRU_OK;
+  }
+  if (io == RGLRU_F32 && scan_fwd_tiles(B, T, D) >= 256) {
+    // fp32 with a scan that fills the CUs: the two projections in one GEMM launch, the
+    // gates formed inside the scan (one launch and one pass over a and beta fewer).  On
+    // fewer tiles the scan's per-thread chain is the critical path and the gate math runs
+    // faster in the wide elementwise launch below.
+    RG_CHECK(launch_gemm_f32_pair(static_cast<const float*>(u), static_cast<const float*>(W_a),
+                                  static_cast<const float*>(W_x), B * T, D, D, w.a, w.beta,
+                                  stream));
+    const GateZ gz{b_a, b_x, lambda, c};
+    return forward_scan(io, B, T, D, u, nullptr, nullptr, nullptr, w.a, w.beta, h0, y, h_T,
+                        w.status, w.counter, prefilled, k, stream, &gz);
   }
   GateGemmArgs g{};
   g.U = u; g.Wa = W_a; g.Wx = W_x; g.M = B * T; g.N = D; g.K = D;

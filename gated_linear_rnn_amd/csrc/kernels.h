@@ -257,6 +257,10 @@ struct ScanFwdArgs {
   const float* a;         // [B,T,D] fp32   (kEpiAB layout) -- or r when from_ri
   const float* beta;      // [B,T,D] fp32                   -- or i when from_ri
   bool from_ri;           // gates given as (r, i): a, beta recomputed with lam, c
+  bool from_z;            // gates given as the projections (z^a, z^x): r = sigma(z^a + zb_a),
+                          // i = sigma(z^x + zb_x), then as from_ri
+  const float* zb_a;      // [D] biases of the from_z mode
+  const float* zb_x;
   const float* lam;
   float c;
   const float* h0;        // [B,D] or NULL
@@ -273,6 +277,7 @@ struct ScanFwdArgs {
 };
 // Look-back status bytes of a scan whose state type has acc_bytes bytes (4 or 8).
 size_t scan_status_bytes(int B, int T, int D, int acc_bytes);
+long scan_fwd_tiles(int B, int T, int D);   // workgroups of one forward scan launch
 // Acc = float for bf16 I/O, double for fp32 I/O.
 template <typename IO, typename Acc> hipError_t launch_scan_fwd(const ScanFwdArgs& a, hipStream_t s);
 

@@ -47,6 +47,8 @@ constexpr int kFChunk = kFSteps * kTG;    // forward: 64 time steps per tile
 
 int scan_chunks(int T) { return (T + kChunk - 1) / kChunk; }
 __host__ __device__ inline int scan_fwd_chunks(int T) { return (T + kFChunk - 1) / kFChunk; }
+long scan_fwd_tiles(int B, int T, int D) { return long(B) * (D / kCh) * scan_fwd_chunks(T); }
+
 // Sized for the finer forward chunking (the backward runs both scans on one buffer).
 size_t scan_status_bytes(int B, int T, int D, int acc_bytes) {
   const int ch = scan_fwd_chunks(T) > scan_chunks(T) ? scan_fwd_chunks(T) : scan_chunks(T);
@@ -99,12 +101,17 @@ static int scan_groups(int chains) {
 // chunk summary below, so both produce the same bits.
 template <typename Acc>
 __device__ __forceinline__ void scan_elem(bool valid, float ga, float gb, float u, float L,
-                                          bool from_ri, float c, Acc& av, Acc& bu) {
+                                          bool from_ri, bool from_z, float zba, float zbx,
+                                          float c, Acc& av, Acc& bu) {
   float a = 1.f, beta = 0.f;
   if (valid) {
     a = ga;
     beta = gb;
-    if (from_ri) {
+    if (from_z) {   // the projections: r and i as gate_from_z forms them
+      a = sigmoidf_stable(ga + zba);
+      beta = sigmoidf_stable(gb + zbx);
+    }
+    if (from_ri || from_z) {
       const Gate g = gate_from_ri(a, beta, L, c);
       a = g.a;
       beta = g.m * g.i;
@@ -142,8 +149,9 @@ __device__ void scan_chunk_summary(const ScanFwdArgs& p, int b, int ch, int chun
       if (conv) u = conv_u<IO>(w[4], w[0], w[1], w[2], w[3], x0, xat(t - 1), xat(t - 2), xat(t - 3));
       const size_t o = (size_t(b) * T + (valid ? t : 0)) * D + ch;
       const float ga = valid ? p.a[o] : 1.f, gb = valid ? p.beta[o] : 0.f;
+      const float zba = p.from_z ? p.zb_a[ch] : 0.f, zbx = p.from_z ? p.zb_x[ch] : 0.f;
       Acc av, bu;
-      scan_elem<Acc>(valid, ga, gb, u, L, p.from_ri, p.c, av, bu);
+      scan_elem<Acc>(valid, ga, gb, u, L, p.from_ri, p.from_z, zba, zbx, p.c, av, bu);
       H = fmaA(av, H, bu);
       A = A * av;
     }
@@ -229,7 +237,8 @@ __global__ __launch_bounds__(256, sizeof(Acc) == 4 ? 4 : 2) void scan_fwd_kernel
   __shared__ Acc sCarry[kCh];
   __shared__ Acc sLb[kCh][2][kWindow];
   __shared__ float4 sW[5][kCh / 4];          // conv w0..w3 and bias of the tile's channels
-  __shared__ float4 sL[kCh / 4];             // log sigma(Lambda) (gates from r, i)
+  __shared__ float4 sL[kCh / 4];             // log sigma(Lambda) (gates from r, i or z)
+  __shared__ float4 sZ[2][kCh / 4];          // the biases of the from_z mode
 
   const int B = p.B, T = p.T, D = p.D;
   const int tid = threadIdx.x;
@@ -298,16 +307,19 @@ __global__ __launch_bounds__(256, sizeof(Acc) == 4 ? 4 : 2) void scan_fwd_kernel
       for (int q = 0; q < 4; ++q) wk[q] = Io<IO>::load1(w + size_t(q) * D + c);
       if (p.conv_b) bias = p.conv_b[c];
     }
-    if (p.from_ri) L = log_sigmoidf(p.lam[c]);
+    if (p.from_ri || p.from_z) L = log_sigmoidf(p.lam[c]);
     float* w0f = reinterpret_cast<float*>(&sW[0][0]);
 #pragma unroll
     for (int q = 0; q < 4; ++q) w0f[q * kCh + tid] = wk[q];
     w0f[4 * kCh + tid] = bias;
     reinterpret_cast<float*>(sL)[tid] = L;
+    reinterpret_cast<float*>(&sZ[0][0])[tid] = p.from_z ? p.zb_a[c] : 0.f;
+    reinterpret_cast<float*>(&sZ[1][0])[tid] = p.from_z ? p.zb_x[c] : 0.f;
   }
   __syncthreads();
   const float4 w0 = sW[0][cg], w1 = sW[1][cg], w2 = sW[2][cg], w3 = sW[3][cg], cb = sW[4][cg];
   const float4 Lv = sL[cg];
+  const float4 zbav = sZ[0][cg], zbxv = sZ[1][cg];
 
   // ---- a_t and beta_t u_t of each step (identity map on steps past the end)
   Acc av[kFSteps][4], bu[kFSteps][4];
@@ -320,8 +332,8 @@ __global__ __launch_bounds__(256, sizeof(Acc) == 4 ? 4 : 2) void scan_fwd_kernel
       if (conv)
         u = conv_u<IO>(f4get(cb, j), f4get(w0, j), f4get(w1, j), f4get(w2, j), f4get(w3, j),
                        xr[s + 3].get(j), xr[s + 2].get(j), xr[s + 1].get(j), xr[s].get(j));
-      scan_elem<Acc>(valid, f4get(ga[s], j), f4get(gb[s], j), u, f4get(Lv, j), p.from_ri, p.c,
-                     av[s][j], bu[s][j]);
+      scan_elem<Acc>(valid, f4get(ga[s], j), f4get(gb[s], j), u, f4get(Lv, j), p.from_ri,
+                     p.from_z, f4get(zbav, j), f4get(zbxv, j), p.c, av[s][j], bu[s][j]);
     }
   }
 

@@ -85,6 +85,28 @@ def test_forward_without_conv(lib, io):
         _check(lib, p, conv=False, what="noconv", fused=True)
 
 
+def test_f32_gates_formed_in_the_scan(lib):
+    """fp32 forward whose scan fills the CUs (2 x 9 channel tiles x 16 chunks = 288
+    workgroups): the projections go straight to the scan, which forms the gates itself;
+    the same bits whether chunk carries come from published summaries or from memory."""
+    import torch
+    from gated_linear_rnn_amd import testing
+    from gpu_util import host
+    p = make(workloads.TRAIN_FWD, B=2, T=1000, D=576, io="f32", h0="normal", history="normal")
+    _check(lib, p, what="gates-in-scan")
+    d = device_inputs(p)
+    args = (d["x"], d["conv_w"], d["conv_b"], d["conv_state"], d["W_a"], d["W_x"], d["b_a"],
+            d["b_x"], d["lam"], d["h0"], p["c"])
+    outs = []
+    for polls in (2048, -1, 0):
+        y, hT, _, _ = testing.forward(testing.knobs(scan_direct_polls=polls), *args)
+        torch.cuda.synchronize()
+        outs.append((host(y), host(hT)))
+    for y, hT in outs[1:]:
+        np.testing.assert_array_equal(y, outs[0][0])
+        np.testing.assert_array_equal(hT, outs[0][1])
+
+
 def test_tiny_f32_workload_full(lib):
     p = workloads.make_inputs(workloads.TINY_F32)
     _check(lib, p, what="tiny")
