@@ -217,6 +217,28 @@ __device__ __forceinline__ Gate gate_from_z(float zr, float zi, float L, float c
   return gate_from_ri(sigmoidf_stable(zr), sigmoidf_stable(zi), L, c);
 }
 
+// a_t and m_t = sqrt(1 - a_t^2) of Eq. (3)-(4) from r_t in the precision of a scan state:
+// fp32 as above, or fp64 for an fp64 state (fp32 I/O), where a_t's fp32 rounding would
+// otherwise compound through the recurrence (about one rounding of a per step carried).
+// L is log sigma(Lambda) in the same precision.
+struct GateAmF { float a, m; };
+struct GateAmD { double a, m; };
+__device__ __forceinline__ GateAmF gate_am(float r, float L, float c) {
+  const Gate g = gate_from_ri(r, 0.f, L, c);
+  return {g.a, g.m};
+}
+__device__ __forceinline__ GateAmD gate_am(float r, double L, float c) {
+  const double ell = (double(c) * double(r)) * L;
+  return {exp(ell), sqrt(-expm1(2.0 * ell))};
+}
+__device__ __forceinline__ double log_sigmoid_d(float lam) {
+  const double t = log1p(exp(-fabs(double(lam))));
+  return lam >= 0.f ? -t : double(lam) - t;
+}
+template <typename Acc> __device__ __forceinline__ Acc log_sigmoid_acc(float lam);
+template <> __device__ __forceinline__ float log_sigmoid_acc<float>(float lam) { return log_sigmoidf(lam); }
+template <> __device__ __forceinline__ double log_sigmoid_acc<double>(float lam) { return log_sigmoid_d(lam); }
+
 // Fast form of the same gate math for the bf16 MFMA epilogue, on the hardware
 // transcendentals (v_exp_f32 = 2^x, v_rcp_f32, v_sqrt_f32; about 1 ulp each):
 //   sigma(z) = 1 / (1 + 2^(-z log2 e)), with the bias folded into the exp2 argument;

@@ -49,6 +49,13 @@ int scan_chunks(int T) { return (T + kChunk - 1) / kChunk; }
 __host__ __device__ inline int scan_fwd_chunks(int T) { return (T + kFChunk - 1) / kFChunk; }
 long scan_fwd_tiles(int B, int T, int D) { return long(B) * (D / kCh) * scan_fwd_chunks(T); }
 
+// The gates-from-projections mode exists for the fp64 scan state (fp32 I/O) only; the
+// fp32-state instantiation compiles it out.
+template <typename Acc>
+__device__ __forceinline__ bool from_z_mode(const ScanFwdArgs& p) {
+  return sizeof(Acc) == 8 && p.from_z;
+}
+
 // Sized for the finer forward chunking (the backward runs both scans on one buffer).
 size_t scan_status_bytes(int B, int T, int D, int acc_bytes) {
   const int ch = scan_fwd_chunks(T) > scan_chunks(T) ? scan_fwd_chunks(T) : scan_chunks(T);
@@ -149,9 +156,10 @@ __device__ void scan_chunk_summary(const ScanFwdArgs& p, int b, int ch, int chun
       if (conv) u = conv_u<IO>(w[4], w[0], w[1], w[2], w[3], x0, xat(t - 1), xat(t - 2), xat(t - 3));
       const size_t o = (size_t(b) * T + (valid ? t : 0)) * D + ch;
       const float ga = valid ? p.a[o] : 1.f, gb = valid ? p.beta[o] : 0.f;
-      const float zba = p.from_z ? p.zb_a[ch] : 0.f, zbx = p.from_z ? p.zb_x[ch] : 0.f;
+      const bool fz = from_z_mode<Acc>(p);
+      const float zba = fz ? p.zb_a[ch] : 0.f, zbx = fz ? p.zb_x[ch] : 0.f;
       Acc av, bu;
-      scan_elem<Acc>(valid, ga, gb, u, L, p.from_ri, p.from_z, zba, zbx, p.c, av, bu);
+      scan_elem<Acc>(valid, ga, gb, u, L, p.from_ri, fz, zba, zbx, p.c, av, bu);
       H = fmaA(av, H, bu);
       A = A * av;
     }
@@ -307,19 +315,24 @@ __global__ __launch_bounds__(256, sizeof(Acc) == 4 ? 4 : 2) void scan_fwd_kernel
       for (int q = 0; q < 4; ++q) wk[q] = Io<IO>::load1(w + size_t(q) * D + c);
       if (p.conv_b) bias = p.conv_b[c];
     }
-    if (p.from_ri || p.from_z) L = log_sigmoidf(p.lam[c]);
+    const bool fz = from_z_mode<Acc>(p);
+    if (p.from_ri || fz) L = log_sigmoidf(p.lam[c]);
     float* w0f = reinterpret_cast<float*>(&sW[0][0]);
 #pragma unroll
     for (int q = 0; q < 4; ++q) w0f[q * kCh + tid] = wk[q];
     w0f[4 * kCh + tid] = bias;
     reinterpret_cast<float*>(sL)[tid] = L;
-    reinterpret_cast<float*>(&sZ[0][0])[tid] = p.from_z ? p.zb_a[c] : 0.f;
-    reinterpret_cast<float*>(&sZ[1][0])[tid] = p.from_z ? p.zb_x[c] : 0.f;
+    if (sizeof(Acc) == 8) {
+      reinterpret_cast<float*>(&sZ[0][0])[tid] = fz ? p.zb_a[c] : 0.f;
+      reinterpret_cast<float*>(&sZ[1][0])[tid] = fz ? p.zb_x[c] : 0.f;
+    }
   }
   __syncthreads();
   const float4 w0 = sW[0][cg], w1 = sW[1][cg], w2 = sW[2][cg], w3 = sW[3][cg], cb = sW[4][cg];
   const float4 Lv = sL[cg];
-  const float4 zbav = sZ[0][cg], zbxv = sZ[1][cg];
+  const bool fz = from_z_mode<Acc>(p);
+  const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4 zbav = sizeof(Acc) == 8 ? sZ[0][cg] : zero4, zbxv = sizeof(Acc) == 8 ? sZ[1][cg] : zero4;
 
   // ---- a_t and beta_t u_t of each step (identity map on steps past the end)
   Acc av[kFSteps][4], bu[kFSteps][4];
@@ -332,8 +345,8 @@ __global__ __launch_bounds__(256, sizeof(Acc) == 4 ? 4 : 2) void scan_fwd_kernel
       if (conv)
         u = conv_u<IO>(f4get(cb, j), f4get(w0, j), f4get(w1, j), f4get(w2, j), f4get(w3, j),
                        xr[s + 3].get(j), xr[s + 2].get(j), xr[s + 1].get(j), xr[s].get(j));
-      scan_elem<Acc>(valid, f4get(ga[s], j), f4get(gb[s], j), u, f4get(Lv, j), p.from_ri,
-                     p.from_z, f4get(zbav, j), f4get(zbxv, j), p.c, av[s][j], bu[s][j]);
+      scan_elem<Acc>(valid, f4get(ga[s], j), f4get(gb[s], j), u, f4get(Lv, j), p.from_ri, fz,
+                     f4get(zbav, j), f4get(zbxv, j), p.c, av[s][j], bu[s][j]);
     }
   }
 
@@ -415,6 +428,7 @@ __global__ __launch_bounds__(256, sizeof(Acc) == 4 ? 4 : 2) void scan_fwd_kernel
 template <typename IO, typename Acc>
 hipError_t launch_scan_fwd(const ScanFwdArgs& a_in, hipStream_t s) {
   ScanFwdArgs a = a_in;
+  if (a.from_z && sizeof(Acc) != 8) return hipErrorInvalidValue;   // fp32 I/O only
   if (!a.prefilled) {
     const size_t words = 3ull * scan_fwd_chunks(a.T) * size_t(a.B) * a.D * sizeof(Acc) / 4;
     const hipError_t e =
@@ -470,14 +484,15 @@ __global__ __launch_bounds__(256) void scan_bwd_kernel(ScanBwdArgs p) {
   const IO* u = static_cast<const IO*>(p.u);
   const IO* dy = static_cast<const IO*>(p.dy);
   const Acc* h_all = static_cast<const Acc*>(p.h_all);
-  float4 Lv;
+  // log sigma(Lambda) of the 4 channels in the state's precision (a_t and m_t below too)
+  Acc Lv[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f4set(Lv, j, log_sigmoidf(p.lam[d + j]));
+  for (int j = 0; j < 4; ++j) Lv[j] = log_sigmoid_acc<Acc>(p.lam[d + j]);
   auto row_of = [&](int s) { return size_t(b) * T + (t0 + tg * kSteps + s); };
   auto valid = [&](int s) { return t0 + tg * kSteps + s < T; };
   // a_t of 4 channels from r_t (identity a = 1 on padded steps)
-  auto gate_a = [&](const float4& r, bool ok, int j) {
-    return ok ? gate_from_ri(f4get(r, j), 0.f, f4get(Lv, j), p.c).a : 1.f;
+  auto gate_a = [&](const float4& r, bool ok, int j) -> Acc {
+    return ok ? Acc(gate_am(f4get(r, j), Lv[j], p.c).a) : Acc(1);
   };
 
   // pass 1: local summary, backwards over this thread's steps: g -> A g + H
@@ -544,8 +559,7 @@ __global__ __launch_bounds__(256) void scan_bwd_kernel(ScanBwdArgs p) {
   for (int j = 0; j < 4; ++j) g[j] = fmaA(Ap[j], sCarry[4 * cg + j], Hp[j]);
   double sdza[4] = {0, 0, 0, 0}, sdzi[4] = {0, 0, 0, 0}, sdl[4] = {0, 0, 0, 0};
   const size_t ld2 = size_t(2) * D;
-  const Acc cL[4] = {Acc(p.c) * Acc(f4get(Lv, 0)), Acc(p.c) * Acc(f4get(Lv, 1)),
-                     Acc(p.c) * Acc(f4get(Lv, 2)), Acc(p.c) * Acc(f4get(Lv, 3))};
+  const Acc cL[4] = {Acc(p.c) * Lv[0], Acc(p.c) * Lv[1], Acc(p.c) * Lv[2], Acc(p.c) * Lv[3]};
   struct StepIn {
     float4 r, i, u, dy;
     Acc hp[4];
@@ -582,8 +596,8 @@ __global__ __launch_bounds__(256) void scan_bwd_kernel(ScanBwdArgs p) {
     float4 dza, dzi, dud;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const Gate gt = gate_from_ri(f4get(cur.r, j), f4get(cur.i, j), f4get(Lv, j), p.c);
-      const Acc a = ok ? gt.a : 1.f, m = ok ? gt.m : 0.f;
+      const auto gt = gate_am(f4get(cur.r, j), Lv[j], p.c);
+      const Acc a = ok ? Acc(gt.a) : Acc(1), m = ok ? Acc(gt.m) : Acc(0);
       const Acc r = f4get(cur.r, j), ii = f4get(cur.i, j), uv = f4get(cur.u, j);
       const Acc G = Acc(f4get(cur.dy, j)) + g[j];
       const Acc mterm = m > Acc(0) ? ((a * a) / m) * ii * uv : Acc(0);
