@@ -60,11 +60,12 @@ bool c_ok(float c) { return c >= 0.f && isfinite(c); }
 
 // ------------------------------------------------------------------ forward
 // bf16 I/O: u, then the fused RG-LRU kernel's look-back status and counters.
-// fp32 I/O: u, a, beta (the unfused gates) and the scan's look-back status and counter.
+// fp32 I/O: u, a, beta (the unfused gates, or the raw projections when the scan forms the
+// gates) and the scan's look-back status and counter.
 struct FwdWs {
   void* u;
-  float* a;      // unfused path: a (fp32 io: z^a, then a in place)
-  float* beta;   // unfused path: beta (fp32 io: z^x, then beta in place)
+  float* a;      // unfused path: a (fp32 io: z^a, then a in place, or z^a for the scan)
+  float* beta;   // unfused path: beta (fp32 io: z^x, then beta in place, or z^x for the scan)
   void* status;
   uint32_t* counter;
   float* tail;   // bf16 unfused path: the gate GEMM's split-tail partials
