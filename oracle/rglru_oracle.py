@@ -295,7 +295,8 @@ def backward(x, conv_w, conv_b, conv_state_in, W_a, W_x, b_a, b_x, lam, h0, c, i
     dx = np.zeros((B, T, D))
     for k in range(4):
         dconv_w[k] = (du * X[:, 3 - k:3 - k + T, :]).sum(axis=(0, 1))
-        dx[:, :T - k, :] += w[k] * du[:, k:, :]
+        if k < T:                      # tap k reaches x_tau from u_{tau+k}, tau + k < T
+            dx[:, :T - k, :] += w[k] * du[:, k:, :]
     out.update(dx=dx, dconv_w=dconv_w, dconv_b=du.sum(axis=(0, 1)))
     return out
 

@@ -98,3 +98,18 @@ def test_backward_matches_torch_autograd():
     for name in NAMES:
         np.testing.assert_allclose(g[name], t[name].grad.numpy(), rtol=1e-9, atol=1e-10,
                                    err_msg=name)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5])
+def test_backward_of_sequences_shorter_than_the_conv(T):
+    """Sequences of fewer steps than the conv's width: the transposed conv then drops the
+    taps that reach past the end (no index wraps round)."""
+    p, st, dy, dhT, c = _problem(22 + T, 2, T, 8)
+    t = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in p.items()}
+    y, hT = _torch_forward(t, st, c)
+    loss = (torch.as_tensor(dy) * y).sum() + (torch.as_tensor(dhT) * hT).sum()
+    loss.backward()
+    g = _grads(p, st, dy, dhT, c)
+    for name in NAMES:
+        np.testing.assert_allclose(g[name], t[name].grad.numpy(), rtol=1e-9, atol=1e-10,
+                                   err_msg=name)
