@@ -670,17 +670,23 @@ __global__ __launch_bounds__(256) void gate_elementwise_f32_kernel(GemmParams p,
   for (size_t o = size_t(blockIdx.x) * blockDim.x + threadIdx.x; o < n;
        o += size_t(gridDim.x) * blockDim.x) {
     const int ch = int(o % p.N);
-    const Gate g = gate_from_z(za[o] + p.ba[ch], zx[o] + p.bx[ch], log_sigmoidf(p.lam[ch]), p.c);
+    const float r = sigmoidf_stable(za[o] + p.ba[ch]);
+    const float i = sigmoidf_stable(zx[o] + p.bx[ch]);
+    if (EPI == kEpiRI) {
+      p.out0[o] = r;
+      p.out1[o] = i;
+      continue;
+    }
+    // a and m in fp64, then one rounding: an fp32 exponential's small rounding bias in a
+    // would compound through the recurrence
+    const GateAmD g = gate_am(r, double(log_sigmoidf(p.lam[ch])), p.c);
     if (EPI == kEpiAB) {
-      p.out0[o] = g.a;
-      p.out1[o] = g.m * g.i;
-    } else if (EPI == kEpiRI) {
-      p.out0[o] = g.r;
-      p.out1[o] = g.i;
+      p.out0[o] = float(g.a);
+      p.out1[o] = float(g.m * double(i));
     } else {
       const float* uf = reinterpret_cast<const float*>(p.u);
       float* yf = reinterpret_cast<float*>(p.y);
-      const float hn = fmaf(g.a, p.h[o], (g.m * g.i) * uf[o]);
+      const float hn = float(fma(g.a, double(p.h[o]), (g.m * double(i)) * double(uf[o])));
       p.h[o] = hn;
       yf[o] = hn;
     }

@@ -213,9 +213,6 @@ __device__ __forceinline__ Gate gate_from_ri(float r, float i, float L, float c)
   g.m = sqrtf(-expm1f(2.f * ell));
   return g;
 }
-__device__ __forceinline__ Gate gate_from_z(float zr, float zi, float L, float c) {
-  return gate_from_ri(sigmoidf_stable(zr), sigmoidf_stable(zi), L, c);
-}
 
 // a_t and m_t = sqrt(1 - a_t^2) of Eq. (3)-(4) from r_t in the precision of a scan state:
 // fp32 as above, or fp64 for an fp64 state (fp32 I/O), where a_t's fp32 rounding would

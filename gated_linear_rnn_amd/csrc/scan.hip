@@ -105,20 +105,27 @@ static int scan_groups(int chains) {
 
 // (a_t, beta_t u_t) of one element: the identity map past the end of the sequence, the gates
 // recomputed from (r, i) when the inputs are those.  Shared by the tile pass and the direct
-// chunk summary below, so both produce the same bits.
+// chunk summary below, so both produce the same bits.  With an fp64 state (fp32 I/O) the
+// recomputed a_t and m_t are fp64 too: an fp32 a_t would carry the small rounding bias of
+// the fp32 exponential into the recurrence, where it compounds over the steps.
 template <typename Acc>
 __device__ __forceinline__ void scan_elem(bool valid, float ga, float gb, float u, float L,
                                           bool from_ri, bool from_z, float zba, float zbx,
                                           float c, Acc& av, Acc& bu) {
+  if (sizeof(Acc) == 8 && valid && (from_ri || from_z)) {
+    const float r = from_z ? sigmoidf_stable(ga + zba) : ga;
+    const float i = from_z ? sigmoidf_stable(gb + zbx) : gb;
+    const GateAmD g = gate_am(r, double(L), c);
+    av = Acc(g.a);
+    bu = Acc(g.m * double(i)) * Acc(u);
+    return;
+  }
+  // (the projections mode exists for the fp64 state only: see from_z_mode)
   float a = 1.f, beta = 0.f;
   if (valid) {
     a = ga;
     beta = gb;
-    if (from_z) {   // the projections: r and i as gate_from_z forms them
-      a = sigmoidf_stable(ga + zba);
-      beta = sigmoidf_stable(gb + zbx);
-    }
-    if (from_ri || from_z) {
+    if (from_ri) {
       const Gate g = gate_from_ri(a, beta, L, c);
       a = g.a;
       beta = g.m * g.i;

@@ -83,6 +83,13 @@ def test_decode_small_elementwise(lib, io, B, D):
     _run(lib, p, 40)
 
 
+def test_decode_f32_many_steps(lib):
+    """600 fp32 steps: the state carried in fp32 between steps, each step's gates formed in
+    fp64 and rounded once, so no rounding bias of a_t compounds over the steps."""
+    p = workloads.make_inputs(workloads.DECODE.with_shape(B=2, D=128, T=600, io="f32"))
+    _run(lib, p, 600)
+
+
 @pytest.mark.parametrize("B,D", [(1, 2560), (2, 192), (3, 320), (4, 256), (4, 4096)])
 def test_decode_small_batch_single_launch(lib, B, D):
     """B <= 4 takes the one-launch matrix-vector form of the step (per-channel waves,

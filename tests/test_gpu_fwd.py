@@ -107,6 +107,16 @@ def test_f32_gates_formed_in_the_scan(lib):
         np.testing.assert_array_equal(hT, outs[0][1])
 
 
+@pytest.mark.parametrize("B,T,D", [(2, 2049, 704), (1, 4000, 64)])
+def test_f32_long_sequences(lib, B, T, D):
+    """fp32 I/O over thousands of steps with slowly decaying gates (a^c in [0.999, 0.9999]),
+    where a rounding bias in a_t would compound along the recurrence: 2 x 2049 x 704 forms
+    the gates inside the scan, 1 x 4000 x 64 (63 scan workgroups) in the elementwise
+    launch.  Every element against the oracle."""
+    p = make(workloads.LONG_FWD, B=B, T=T, D=D, io="f32", h0="normal", history="normal")
+    _check(lib, p, what="f32-long")
+
+
 def test_tiny_f32_workload_full(lib):
     p = workloads.make_inputs(workloads.TINY_F32)
     _check(lib, p, what="tiny")
