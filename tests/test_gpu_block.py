@@ -54,7 +54,12 @@ def _check(g, p, conv=True, what=""):
           f"err(out)={eo:.3e} err(h_T)={eh:.3e}", flush=True)
     assert eo <= TOL[io] and eh <= TOL[io]
     if conv:
-        np.testing.assert_array_equal(cso, o["conv_state_out"])   # a copy of p rows: exact
+        # the conv history is the last rows of p, the first linear's output: a GEMM result
+        # rounded once to the I/O dtype, which may land on the neighbouring value where the
+        # exact sum (the oracle's) sits next to a rounding boundary; compared to the bar
+        ec = err(cso, o["conv_state_out"])
+        print(f"{what} err(conv_state_out)={ec:.3e}", flush=True)
+        assert ec <= TOL[io]
 
 
 SMALL = [
@@ -148,7 +153,7 @@ def test_block_prefill_then_decode(lib, io):
     print(f"block prefill->decode io={io} err(prefill)={e0:.3e} err(decode)={e1:.3e} err(h)={eh:.3e}",
           flush=True)
     assert e0 <= TOL[io] and e1 <= TOL[io] and eh <= TOL[io]
-    np.testing.assert_array_equal(host(cso), want["conv_state_out"])
+    assert err(host(cso), want["conv_state_out"]) <= TOL[io]   # p rows: a rounded GEMM output
 
 
 def test_block_decode_full_shape_sampled_sequences(lib):
