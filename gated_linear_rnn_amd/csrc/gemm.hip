@@ -304,16 +304,20 @@ __global__ __launch_bounds__(C::NW * 64, C::NW >= 8 ? 2 : 1) void gemm_bf16_kern
           if (m >= p.M) continue;
           const size_t o = size_t(m) * p.N + ch;
           const float za = acc[mf][jc][v], zx = acc[mf][jc + HALF][v];
+          // (r, i) or (a, beta) are read once by the scan that follows: stored with the
+          // non-temporal hint, so they do not leave dirty lines in the Infinity Cache whose
+          // write-back would compete with that scan's reads (112 -> 98 us for the scan
+          // right after the gate GEMM at 8 x 2048 x 2560)
           if (MODE == kEpiRI) {
             float r, i;
             gate_fast_ri(za, zx, k, r, i);
-            p.out0[o] = r;
-            p.out1[o] = i;
+            __builtin_nontemporal_store(r, p.out0 + o);
+            __builtin_nontemporal_store(i, p.out1 + o);
           } else {  // kEpiAB
             float a, beta;
             gate_fast(za, zx, k, a, beta);
-            p.out0[o] = a;
-            p.out1[o] = beta;
+            __builtin_nontemporal_store(a, p.out0 + o);
+            __builtin_nontemporal_store(beta, p.out1 + o);
           }
         }
     }
@@ -451,13 +455,13 @@ __global__ __launch_bounds__(256) void tail_fixup_gate_kernel(GemmParams p, int 
   if (MODE == kEpiRI) {
     float rr, ii;
     gate_fast_ri(za, zx, k, rr, ii);
-    p.out0[o] = rr;
-    p.out1[o] = ii;
+    __builtin_nontemporal_store(rr, p.out0 + o);
+    __builtin_nontemporal_store(ii, p.out1 + o);
   } else {
     float a, beta;
     gate_fast(za, zx, k, a, beta);
-    p.out0[o] = a;
-    p.out1[o] = beta;
+    __builtin_nontemporal_store(a, p.out0 + o);
+    __builtin_nontemporal_store(beta, p.out1 + o);
   }
 }
 

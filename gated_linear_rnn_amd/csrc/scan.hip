@@ -422,9 +422,9 @@ __global__ __launch_bounds__(256, sizeof(Acc) == 4 ? 4 : 2) void scan_fwd_kernel
       const size_t o = (size_t(b) * T + t) * D + d;
       const float4 hf = make_float4(float(h[0]), float(h[1]), float(h[2]), float(h[3]));
       if (y) Io<IO>::store4_once(y + o, hf);
-      if (h_all) {
+      if (h_all) {   // read once, by the reverse scan: non-temporal like y
 #pragma unroll
-        for (int j = 0; j < 4; ++j) h_all[o + j] = h[j];
+        for (int j = 0; j < 4; ++j) __builtin_nontemporal_store(h[j], h_all + o + j);
       }
       if (t == T - 1 && p.h_T) *reinterpret_cast<float4*>(p.h_T + size_t(b) * D + d) = hf;
     }
