@@ -94,8 +94,10 @@ __global__ __launch_bounds__(CfgDecode::NW * 64, 2) void decode_partial_kernel(D
       for (int v = 0; v < 16; ++v) {
         const int m = m0 + wm * C::WTM + mf * 32 + acc_row(v, lane);
         if (m >= B) continue;
-        pa[size_t(m) * D + ch] = acc[mf][jc][v];
-        px[size_t(m) * D + ch] = acc[mf][jc + HALF][v];
+        // read once, by decode_update_kernel: non-temporal (24.5 -> 24.1 us per step at
+        // B = 256, D = 2560)
+        __builtin_nontemporal_store(acc[mf][jc][v], pa + size_t(m) * D + ch);
+        __builtin_nontemporal_store(acc[mf][jc + HALF][v], px + size_t(m) * D + ch);
       }
   }
 }
