@@ -16,9 +16,12 @@
 //     the thread's 4 steps and the x rows t-3 .. t+3 around them, from which the width-4
 //     conv (the "Recurrent block" Conv1D) is recomputed with the same fma order as the
 //     stand-alone conv, so u is bit-identical to the u the gate projection used (the conv
-//     weights of the tile's channels pass through LDS).  About 100 VGPRs: four workgroups
-//     share a CU, so while one waits on its predecessor or writes y, the others' loads
-//     are in flight;
+//     weights of the tile's channels pass through LDS).  At most 128 VGPRs at bf16 I/O:
+//     four workgroups share a CU, so while one waits on its predecessor or writes y, the
+//     others' loads are in flight;
+//   * the gates arrive as (a_t, beta_t), as (r_t, i_t), or (fp32 I/O) as the raw
+//     projections W_a u_t and W_x u_t; in the last two forms the tile evaluates Eq. (2)-(4)
+//     itself, in fp64 for the fp64 state;
 //   * each thread scans its 4 steps from zero to the affine summary (A = prod a, H), the
 //     16 time-group summaries are combined in LDS, and the tile summary is chained across
 //     tiles with a decoupled look-back, one lane per channel so that the 64 channels' polls
