@@ -107,7 +107,11 @@ size_t rglru_lru_workspace_bytes(int B, int T, int D, rglru_dtype io);
  * already the conv output: rglru_fwd is conv1d_causal4 followed by rglru_lru on the same
  * stream, and equals rglru_lru when conv_w is NULL.  For bf16 I/O one fused kernel runs
  * the gate GEMM on the matrix cores and the chunked scan in its epilogue (a_t and beta_t
- * never reach HBM); for fp32 I/O it is rglru_gates followed by rglru_scan.
+ * never reach HBM), except at shapes whose tiles would fill their last round of compute
+ * units poorly, where the gate GEMM and the scan run as two launches (a pure function of
+ * B, T, D).  For fp32 I/O both projections run as one GEMM launch and the scan forms
+ * a_t and beta_t from them in fp64; scans of fewer than 256 workgroups get them from a
+ * launch of their own instead (formed in fp64, rounded once to fp32).
  *   u [B,T,D] io; W_a, W_x [D,D] io; b_a, b_x, lambda [D] fp32; h0 [B,D] fp32 or NULL;
  *   y [B,T,D] io (output); h_T [B,D] fp32 (output, nullable).  Bitwise reproducible.
  */
@@ -118,7 +122,7 @@ int rglru_lru(int B, int T, int D, rglru_dtype io, float c, const void* u, const
 
 /*
  * The unfused halves of the RG-LRU layer, for callers that produce or consume the gates
- * themselves (rglru_lru for fp32 I/O is rglru_gates, then rglru_scan on the same stream).
+ * themselves (together they evaluate what rglru_lru does, to the bar of the I/O dtype).
  *
  * rglru_gates: Eq. (1)-(3) and the input scale of Eq. (4) for every (batch, time) row:
  *   r = sigma(W_a u + b_a), i = sigma(W_x u + b_x), a = exp(c r log sigma(Lambda)),
