@@ -603,13 +603,15 @@ __global__ __launch_bounds__(TM * TM / 16) void gemm_f32_kernel(
     bp[q] = Bm + size_t(min(n0 + lr[q], N - 1)) * ldb + lk[q];
   }
   double acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    float4 av[LPT], bv[LPT];
+  // The next k-step's operands are loaded into registers while the current one is
+  // computed, so each step waits on loads issued a whole step earlier.
+  float4 av[LPT], bv[LPT];
 #pragma unroll
-    for (int q = 0; q < LPT; ++q) {
-      av[q] = *reinterpret_cast<const float4*>(ap[q] + k0);
-      bv[q] = *reinterpret_cast<const float4*>(bp[q] + k0);
-    }
+  for (int q = 0; q < LPT; ++q) {
+    av[q] = *reinterpret_cast<const float4*>(ap[q]);
+    bv[q] = *reinterpret_cast<const float4*>(bp[q]);
+  }
+  for (int k0 = 0; k0 < K; k0 += 16) {
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < LPT; ++q) {
@@ -619,6 +621,13 @@ __global__ __launch_bounds__(TM * TM / 16) void gemm_f32_kernel(
       Bs[lk[q] + 2][lr[q]] = bv[q].z; Bs[lk[q] + 3][lr[q]] = bv[q].w;
     }
     __syncthreads();
+    if (k0 + 16 < K) {
+#pragma unroll
+      for (int q = 0; q < LPT; ++q) {
+        av[q] = *reinterpret_cast<const float4*>(ap[q] + k0 + 16);
+        bv[q] = *reinterpret_cast<const float4*>(bp[q] + k0 + 16);
+      }
+    }
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       float a[4], b[4];
