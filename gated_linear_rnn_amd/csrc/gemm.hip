@@ -577,12 +577,14 @@ hipError_t launch_geglu_gemm_bf16(const GegluGemmArgs& g, hipStream_t s) {
 // the GPU at least one workgroup per CU, else 32 x 32 tiles (64 threads, four times the
 // workgroups).  With B1 (grid.y = 2) the same launch also computes C1 = A B1^T: the two gate
 // projections of the fp32 forward in one launch.
-template <int TM>
-__global__ __launch_bounds__(TM * TM / 16) void gemm_f32_kernel(
+template <int TM, int R>
+__global__ __launch_bounds__((TM / R) * (TM / R)) void gemm_f32_kernel(
     const float* __restrict__ A, const float* __restrict__ B0, const float* __restrict__ B1,
     int M, int N, int K, int lda, int ldb, int ldc, float* C0, float* C1,
     const float* addend) {
-  constexpr int NTH = TM * TM / 16, TX = TM / 4, LPT = TM * 4 / NTH;
+  // TM x TM output tile, R x R outputs per thread
+  constexpr int TX = TM / R, NTH = TX * TX, LPT = TM * 4 / NTH;
+  static_assert(LPT >= 1 && TM * 4 % NTH == 0, "loader");
   __shared__ float As[16][TM + 4];
   __shared__ float Bs[16][TM + 4];
   const float* Bm = blockIdx.y ? B1 : B0;
@@ -602,7 +604,7 @@ __global__ __launch_bounds__(TM * TM / 16) void gemm_f32_kernel(
     ap[q] = A + size_t(min(m0 + lr[q], M - 1)) * lda + lk[q];
     bp[q] = Bm + size_t(min(n0 + lr[q], N - 1)) * ldb + lk[q];
   }
-  double acc[4][4] = {};
+  double acc[R][R] = {};
   // The next k-step's operands are loaded into registers while the current one is
   // computed, so each step waits on loads issued a whole step earlier.
   float4 av[LPT], bv[LPT];
@@ -630,24 +632,24 @@ __global__ __launch_bounds__(TM * TM / 16) void gemm_f32_kernel(
     }
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      float a[4], b[4];
+      float a[R], b[R];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[k][ty * 4 + i];
+      for (int i = 0; i < R; ++i) a[i] = As[k][ty * R + i];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = Bs[k][tx * 4 + j];
+      for (int j = 0; j < R; ++j) b[j] = Bs[k][tx * R + j];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < R; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(double(a[i]), double(b[j]), acc[i][j]);
+        for (int j = 0; j < R; ++j) acc[i][j] = fma(double(a[i]), double(b[j]), acc[i][j]);
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + ty * 4 + i;
+  for (int i = 0; i < R; ++i) {
+    const int m = m0 + ty * R + i;
     if (m >= M) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + tx * 4 + j;
+    for (int j = 0; j < R; ++j) {
+      const int n = n0 + tx * R + j;
       if (n >= N) continue;
       const size_t o = size_t(m) * ldc + n;
       double v = acc[i][j];
@@ -661,13 +663,18 @@ static hipError_t launch_gemm_f32(const float* A, const float* B0, const float* 
                                   int K, int lda, int ldb, int ldc, float* C0, float* C1,
                                   const float* addend, hipStream_t s) {
   const int pairs = B1 ? 2 : 1;
-  const long tiles64 = long((M + 63) / 64) * ((N + 63) / 64) * pairs;
-  if (tiles64 >= 256) {
+  // the largest tile that still gives every CU a workgroup (each output sums k in order
+  // whatever the tile, so the choice does not change the result)
+  auto tiles = [&](int tm) { return long((M + tm - 1) / tm) * ((N + tm - 1) / tm) * pairs; };
+  if (tiles(64) >= 256) {
     const dim3 grid(((M + 63) / 64) * ((N + 63) / 64), pairs);
-    gemm_f32_kernel<64><<<grid, 256, 0, s>>>(A, B0, B1, M, N, K, lda, ldb, ldc, C0, C1, addend);
-  } else {
+    gemm_f32_kernel<64, 4><<<grid, 256, 0, s>>>(A, B0, B1, M, N, K, lda, ldb, ldc, C0, C1, addend);
+  } else if (tiles(32) >= 256) {
     const dim3 grid(((M + 31) / 32) * ((N + 31) / 32), pairs);
-    gemm_f32_kernel<32><<<grid, 64, 0, s>>>(A, B0, B1, M, N, K, lda, ldb, ldc, C0, C1, addend);
+    gemm_f32_kernel<32, 4><<<grid, 64, 0, s>>>(A, B0, B1, M, N, K, lda, ldb, ldc, C0, C1, addend);
+  } else {
+    const dim3 grid(((M + 15) / 16) * ((N + 15) / 16), pairs);
+    gemm_f32_kernel<16, 2><<<grid, 64, 0, s>>>(A, B0, B1, M, N, K, lda, ldb, ldc, C0, C1, addend);
   }
   return hipGetLastError();
 }
