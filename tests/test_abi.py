@@ -271,3 +271,17 @@ def test_noalloc_decode_rejects_before_any_hip_call(lib):
     assert f(*args(2, 64, io=5)) == -3
     assert g.status_string(-8).startswith("RGLRU_ESCRATCH")
     assert f(*args(1024, 8192)) == -8                      # needs more than the fixed scratch
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU; --gpus N > 1 ends with a message and a nonzero status,
+    before any device work."""
+    import subprocess
+    import sys
+    from pathlib import Path
+    root = Path(__file__).resolve().parents[1]
+    r = subprocess.run([sys.executable, str(root / "bench.py"), "--gpus", "2"], cwd=root,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""
