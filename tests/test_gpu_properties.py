@@ -230,3 +230,63 @@ def test_forward_graph_replays_match_eager(lib, io):
         torch.cuda.synchronize()
         assert torch.equal(y, ref[0]) and torch.equal(hT, ref[1]) and torch.equal(cso, ref[2]), rep
         _ = (d["x"].float() * 3).sum().item()       # unrelated eager work between replays
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_backward_graph_replays_match_eager(lib, io):
+    """rglru_fwd_train + rglru_bwd_saved and rglru_bwd captured in one hipGraph (the reverse
+    scan's tickets and look-back status are reset by kernels inside the calls, not memset
+    nodes), replayed several times with eager work and synchronisations in between; every
+    replay gives the eager gradients bit for bit."""
+    w = workloads.TRAIN_BWD.with_shape(B=2, T=300, D=192, io=io, h0="normal", history="normal",
+                                       with_dy=True)
+    p = workloads.make_inputs(w)
+    d = device_inputs(p)
+    B, T, D = w.B, w.T, w.D
+    t = TORCH_IO[io]
+    f32 = dict(dtype=torch.float32, device="cuda")
+    dh_T = torch.randn((B, D), generator=torch.Generator().manual_seed(5)).cuda()
+
+    def grads():
+        return [torch.empty((B, T, D), **f32), torch.empty((4, D), **f32), torch.empty(D, **f32),
+                torch.empty((D, D), **f32), torch.empty((D, D), **f32), torch.empty(D, **f32),
+                torch.empty(D, **f32), torch.empty(D, **f32), torch.empty((B, D), **f32)]
+    g_bwd, g_saved = grads(), grads()
+    y = torch.empty((B, T, D), dtype=t, device="cuda")
+    hT = torch.empty((B, D), **f32)
+    cso = torch.empty((B, 3, D), dtype=t, device="cuda")
+    ws_b = lib.workspace(lib.bwd_workspace_bytes(B, T, D, t))
+    ws_f = lib.workspace(lib.fwd_train_workspace_bytes(B, T, D, t))
+    ws_s = lib.workspace(lib.bwd_saved_workspace_bytes(B, T, D, t))
+    saved = lib.workspace(lib.train_saved_bytes(B, T, D, t))
+    common = (d["x"], d["conv_w"], d["conv_b"], d["conv_state"], d["W_a"], d["W_x"])
+
+    def run():
+        lib.rglru_bwd(*common, d["b_a"], d["b_x"], d["lam"], d["h0"], d["dy"], dh_T, *g_bwd, ws_b,
+                      p["c"])
+        lib.rglru_fwd_train(*common, d["b_a"], d["b_x"], d["lam"], d["h0"], y, hT, cso, saved,
+                            ws_f, p["c"])
+        lib.rglru_bwd_saved(*common, d["lam"], d["h0"], d["dy"], dh_T, *g_saved, saved, ws_s,
+                            p["c"])
+
+    run()
+    torch.cuda.synchronize()
+    ref = [a.clone() for a in g_bwd + g_saved + [y, hT]]
+    for a, b in zip(g_bwd, g_saved):       # the two routes give the same gradients
+        assert torch.equal(a, b)
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            run()
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        for a in g_bwd + g_saved + [y, hT]:
+            a.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (a, r) in enumerate(zip(g_bwd + g_saved + [y, hT], ref)):
+            assert torch.equal(a, r), (rep, i)
+        _ = (d["x"].float() * 3).sum().item()       # unrelated eager work between replays
