@@ -254,6 +254,75 @@ def test_block_decode_rejects_invalid_arguments(lib):
     assert call(wsb=3) == -4
 
 
+
+@no_gpu
+def test_layer_halves_and_training_pair_reject_invalid_arguments(lib):
+    """rglru_lru, rglru_gates, rglru_scan, rglru_fwd_train and rglru_bwd_saved: bad shapes,
+    dtypes, missing or misaligned pointers, short workspaces and short saved buffers are
+    refused before any HIP call."""
+    big = 1 << 40
+
+    def lru(B=1, T=4, D=64, io=1, c=8.0, **o):
+        a = dict(u=A, Wa=A, Wx=A, ba=A, bx=A, lam=A, h0=None, y=A, hT=None, ws=A, wsb=big)
+        a.update(o)
+        return lib.rglru_lru(B, T, D, io, c, a["u"], a["Wa"], a["Wx"], a["ba"], a["bx"], a["lam"],
+                             a["h0"], a["y"], a["hT"], a["ws"], a["wsb"], None)
+    assert lru(B=0) == -1 and lru(D=32) == -2 and lru(io=9) == -3 and lru(c=-2.0) == -1
+    for k in ("u", "Wa", "Wx", "ba", "bx", "lam", "y"):
+        assert lru(**{k: None}) == -1, k
+    assert lru(y=BAD) == -1 and lru(ws=None) == -4 and lru(wsb=16) == -4
+
+    def gates(B=1, T=4, D=64, io=1, c=8.0, **o):
+        a = dict(u=A, Wa=A, Wx=A, ba=A, bx=A, lam=A, a=A, beta=A)
+        a.update(o)
+        return lib.rglru_gates(B, T, D, io, c, *[a[k] for k in ("u", "Wa", "Wx", "ba", "bx", "lam",
+                                                                 "a", "beta")], None)
+    assert gates(T=0) == -1 and gates(D=100) == -2 and gates(io=3) == -3
+    for k in ("u", "Wa", "Wx", "ba", "bx", "lam", "a", "beta"):
+        assert gates(**{k: None}) == -1, k
+    assert gates(beta=BAD) == -1
+
+    def scan(B=1, T=4, D=64, io=1, **o):
+        a = dict(x=A, cw=None, cb=None, cs=None, a=A, beta=A, h0=None, y=A, hT=None, ws=A, wsb=big)
+        a.update(o)
+        return lib.rglru_scan(B, T, D, io, *[a[k] for k in ("x", "cw", "cb", "cs", "a", "beta", "h0",
+                                                            "y", "hT", "ws")], a["wsb"], None)
+    assert scan(B=-1) == -1 and scan(D=65) == -2 and scan(io=7) == -3
+    for k in ("x", "a", "beta", "y"):
+        assert scan(**{k: None}) == -1, k
+    assert scan(a=BAD) == -1 and scan(ws=None) == -4 and scan(wsb=8) == -4
+
+    def fwd_train(B=1, T=4, D=64, io=1, c=8.0, **o):
+        a = dict(x=A, cw=None, cb=None, cs=None, Wa=A, Wx=A, ba=A, bx=A, lam=A, h0=None, y=A,
+                 hT=None, cso=None, saved=A, sb=big, ws=A, wsb=big)
+        a.update(o)
+        return lib.rglru_fwd_train(B, T, D, io, c, *[a[k] for k in (
+            "x", "cw", "cb", "cs", "Wa", "Wx", "ba", "bx", "lam", "h0", "y", "hT", "cso", "saved")],
+            a["sb"], a["ws"], a["wsb"], None)
+    assert fwd_train(B=0) == -1 and fwd_train(D=96) == -2 and fwd_train(io=4) == -3
+    for k in ("x", "Wa", "Wx", "ba", "bx", "lam", "y", "saved"):
+        assert fwd_train(**{k: None}) == -1, k
+    assert fwd_train(saved=BAD) == -1
+    assert fwd_train(sb=64) == -1                          # saved buffer too short
+    assert fwd_train(ws=None) == -4 and fwd_train(wsb=64) == -4
+
+    def bwd_saved(B=1, T=4, D=64, io=1, c=8.0, **o):
+        names = ("x", "cw", "cb", "cs", "Wa", "Wx", "lam", "h0", "dy", "dhT", "dx", "dcw", "dcb",
+                 "dWa", "dWx", "dba", "dbx", "dlam", "dh0", "saved")
+        a = dict.fromkeys(names, A)
+        a.update(cw=None, cb=None, cs=None, h0=None, dhT=None, dcw=None, dcb=None, dh0=None,
+                 sb=big, ws=A, wsb=big)
+        a.update(o)
+        return lib.rglru_bwd_saved(B, T, D, io, c, *[a[k] for k in names], a["sb"], a["ws"],
+                                   a["wsb"], None)
+    assert bwd_saved(T=0) == -1 and bwd_saved(D=80) == -2 and bwd_saved(io=6) == -3
+    for k in ("x", "Wa", "Wx", "lam", "dy", "dx", "dWa", "dWx", "dba", "dbx", "dlam"):
+        assert bwd_saved(**{k: None}) == -1, k
+    assert bwd_saved(cw=A) == -1                           # conv weights without their gradients
+    assert bwd_saved(dx=BAD) == -1
+    assert bwd_saved(sb=64) == -1                          # saved buffer too short
+    assert bwd_saved(ws=None) == -4 and bwd_saved(wsb=64) == -4
+
 @no_gpu
 def test_workspace_status_rejects_invalid_arguments(lib):
     assert lib.rglru_workspace_status(None, 1 << 20, None) == -1
